@@ -1,0 +1,228 @@
+"""Plain fp64 CPU oracle for rational-softmax attention.
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The product path
+(the HIP library and its Python binding) never imports it, and this module
+imports nothing from the product path.
+
+Everything here follows the definitions on the pages in their own order, in
+float64, with the full score matrix materialised one (batch, head) at a time.
+There is no tiling, fusion or reordering beyond what a definition states.
+
+Sources
+-------
+* "Ra-Family: Rational Neural Architecture" (luminamoon.nn README), section 3
+  "Rational Attention & Softmax", item ra_softmax: the shift Delta = x_max - x,
+  u = Delta/16, q = (1-u)/(1+u), phi = q**8 for Delta < 16 and exactly 0 for
+  Delta >= 16, and the denominator sum(phi) >= 1.  The same item gives the
+  closed-form derivative d(phi)/du = -16 phi / (1-u^2) for u < 1 (the page's
+  typeset formula lost its thin spaces; it is a product).
+* Same page, section 3, item ra_attention: (Q, K, V) -> O without the
+  [B, H, Nq, Nk] matrix; the functional form is a drop-in for
+  scaled_dot_product_attention with is_causal.
+* "nn -- neural-network layers on the grad tape", section "Layers",
+  nn_gqa_attention: the unfused order scaled scores -> masked softmax ->
+  weighted sum, which this oracle follows with ra_softmax in place of softmax.
+* noeira "Primitives" page, section "Attention and transformers":
+  RepeatKVHeads maps query head h to K/V head h // REP and its backward sums
+  the REP copies; a fully masked row gives a zero context, not NaN.
+
+Readings where the pages are silent (each is listed in the design notes):
+* p = phi / sum(phi) is the normalisation of the "denominator" the page names.
+* The row max is part of the function: the backward differentiates through it
+  (term R below).  For the exp softmax that term vanishes; for phi it does not.
+* Ties for the row max resolve to the lowest key index.
+* Causal masking is top-left aligned (key j allowed for query i iff j <= i),
+  as scaled_dot_product_attention's is_causal.
+* Masked entries (-inf logits, or keys outside the causal set) are excluded
+  from the max and from sum(phi), and get p = 0.  A row with no allowed entry
+  gives p = 0 and O = 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "SUPPORT_WIDTH",
+    "ra_phi",
+    "ra_softmax_rows",
+    "ra_softmax_rows_bwd",
+    "ra_attention_fwd",
+    "ra_attention_bwd",
+]
+
+# Delta at which phi reaches exactly zero (the compact support edge, u = 1).
+SUPPORT_WIDTH = 16.0
+
+
+def ra_phi(delta):
+    """phi(Delta) = ((1-u)/(1+u))**8 with u = Delta/16 for Delta < 16, else 0.
+
+    Ra-Family page, section 3, ra_softmax.  ``delta`` must be >= 0 or +inf
+    (+inf marks a masked entry and gives 0).
+    """
+    delta = np.asarray(delta, dtype=np.float64)
+    u = delta / SUPPORT_WIDTH
+    inside = u < 1.0
+    u_in = np.where(inside, u, 0.0)
+    q = (1.0 - u_in) / (1.0 + u_in)
+    return np.where(inside, q ** 8, 0.0)
+
+
+def _row_stats(x, allowed):
+    """Row max over allowed entries, its lowest index, Delta and phi.
+
+    Returns (m, a, delta, phi); rows with no allowed entry have m = -inf,
+    a = -1, delta = +inf and phi = 0.
+    """
+    xm = np.where(allowed, x, -np.inf)
+    m = xm.max(axis=-1)
+    a = np.argmax(xm, axis=-1)  # numpy returns the first maximal index
+    empty = ~allowed.any(axis=-1)
+    a = np.where(empty, -1, a)
+    with np.errstate(invalid="ignore"):
+        delta = np.where(allowed, m[..., None] - x, np.inf)
+    delta = np.where(empty[..., None], np.inf, delta)
+    phi = ra_phi(delta)
+    return m, a, delta, phi
+
+
+def ra_softmax_rows(x, return_stats=False):
+    """ra_softmax along the last axis of a 2-D array; -inf entries are masked.
+
+    Ra-Family page, section 3, ra_softmax; p = phi / sum(phi).
+    With ``return_stats`` also returns (phi, m, l) where l = sum(phi).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 2:
+        raise ValueError("ra_softmax_rows expects a 2-D array")
+    allowed = ~np.isneginf(x)
+    m, _, _, phi = _row_stats(x, allowed)
+    l = phi.sum(axis=-1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(l[..., None] > 0, phi / l[..., None], 0.0)
+    if return_stats:
+        return p, phi, m, l
+    return p
+
+
+def _softmax_vjp(p, delta, dp, a):
+    """Gradient of L through p = ra_softmax(s) for one block of rows.
+
+    With c_i = sum_j p_ij dp_ij, the direct term is
+    G_ij = p_ij (dp_ij - c_i) / (1 - u_ij^2) on the support (u < 1), else 0,
+    which is the chain rule through phi with the page's closed form
+    d(phi)/du = -16 phi/(1-u^2) and du/dDelta = 1/16, Delta = m - s.
+    The row max m = s[a] carries R_i = -sum_j G_ij, added at the argmax.
+    """
+    u = delta / SUPPORT_WIDTH
+    support = u < 1.0
+    c = (p * dp).sum(axis=-1)
+    u_in = np.where(support, u, 0.0)
+    g = np.where(support, p * (dp - c[..., None]) / (1.0 - u_in * u_in), 0.0)
+    r = -g.sum(axis=-1)
+    ds = g.copy()
+    rows = np.nonzero(a >= 0)[0]
+    ds[rows, a[rows]] += r[rows]
+    return ds
+
+
+def ra_softmax_rows_bwd(x, dp):
+    """Exact gradient dL/dx of ra_softmax_rows given dL/dp, max path included."""
+    x = np.asarray(x, dtype=np.float64)
+    dp = np.asarray(dp, dtype=np.float64)
+    allowed = ~np.isneginf(x)
+    m, a, delta, phi = _row_stats(x, allowed)
+    l = phi.sum(axis=-1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(l[..., None] > 0, phi / l[..., None], 0.0)
+    return _softmax_vjp(p, delta, dp, a)
+
+
+def _check_attention_shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, N, D]")
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if Bk != B or Dk != D or v.shape[:3] != k.shape[:3]:
+        raise ValueError("inconsistent q/k/v shapes")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hkv, Nq, Nk, D, Hq // Hkv
+
+
+def _allowed(Nq, Nk, causal, q_positions):
+    pos = np.arange(Nq) if q_positions is None else np.asarray(q_positions)
+    if not causal:
+        return np.ones((len(pos), Nk), dtype=bool)
+    return np.arange(Nk)[None, :] <= pos[:, None]
+
+
+def ra_attention_fwd(q, k, v, causal, scale, q_positions=None, heads=None):
+    """O = ra_softmax(scale * Q K^T) V with GQA and optional causal mask.
+
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D]; query head h reads K/V head
+    h // (Hq/Hkv).  ``q_positions`` gives the absolute positions of the
+    supplied query rows for the causal test (default 0..Nq-1), so a sample of
+    rows can be checked on its own.  ``heads`` restricts the work to a list of
+    (b, h) pairs (other heads of the outputs stay zero / -inf).
+
+    Returns (O, m, l, a): m is the row max of the scaled scores s, l the sum of
+    phi, a the lowest key index attaining the max (-1 for an empty row).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nk, D, rep = _check_attention_shapes(q, k, v)
+    allowed = _allowed(Nq, Nk, causal, q_positions)
+    o = np.zeros((B, Hq, Nq, v.shape[3]))
+    m = np.full((B, Hq, Nq), -np.inf)
+    l = np.zeros((B, Hq, Nq))
+    a = np.full((B, Hq, Nq), -1, dtype=np.int64)
+    todo = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
+    for b, h in todo:
+        g = h // rep
+        s = scale * (q[b, h] @ k[b, g].T)
+        mb, ab, _, phi = _row_stats(s, allowed)
+        lb = phi.sum(axis=-1)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            p = np.where(lb[:, None] > 0, phi / lb[:, None], 0.0)
+        o[b, h] = p @ v[b, g]
+        m[b, h], l[b, h], a[b, h] = mb, lb, ab
+    return o, m, l, a
+
+
+def ra_attention_bwd(q, k, v, do, causal, scale, groups=None):
+    """Gradients (dQ, dK, dV) of L = sum(O * dO) for ra_attention_fwd.
+
+    Follows the chain rule in the forward's order: dP = dO V^T; the softmax
+    vector-Jacobian product (direct closed-form term plus the row-max term);
+    dQ = scale dS K; dK and dV are summed over the REP query heads that share
+    a K/V head.  ``groups`` restricts the work to a list of (b, g) K/V groups
+    (all their query heads are processed).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nk, D, rep = _check_attention_shapes(q, k, v)
+    if do.shape != q.shape[:3] + v.shape[3:]:
+        raise ValueError("dO must have the shape of O")
+    allowed = _allowed(Nq, Nk, causal, None)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    todo = [(b, g) for b in range(B) for g in range(Hkv)] if groups is None else groups
+    for b, g in todo:
+        for h in range(g * rep, (g + 1) * rep):
+            s = scale * (q[b, h] @ k[b, g].T)
+            _, a, delta, phi = _row_stats(s, allowed)
+            lb = phi.sum(axis=-1)
+            with np.errstate(invalid="ignore", divide="ignore"):
+                p = np.where(lb[:, None] > 0, phi / lb[:, None], 0.0)
+            dp = do[b, h] @ v[b, g].T
+            ds = _softmax_vjp(p, delta, dp, a)
+            dq[b, h] = scale * (ds @ k[b, g])
+            dk[b, g] += scale * (ds.T @ q[b, h])
+            dv[b, g] += p.T @ do[b, h]
+    return dq, dk, dv

@@ -1,0 +1,370 @@
+"""Pins of the fp64 oracle to facts fixed by the pages and by mathematics.
+
+None of these compares the oracle with itself: each check uses hand-derived
+values (tests/golden/), a second closed form, an invariant, a special case that
+reduces to a library routine, or central finite differences.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- ra_softmax
+
+def test_worked_example_exact_phi_and_p():
+    rows = _read_rows("ra_softmax_worked_example.txt")
+    x = np.zeros((2, 3))
+    phi_exact = [[None] * 3 for _ in range(2)]
+    for r, c, logit, num, den in rows:
+        r, c = int(r), int(c)
+        x[r, c] = float(logit)
+        phi_exact[r][c] = Fraction(int(num), int(den))
+    p, phi, m, l = oracle.ra_softmax_rows(x, return_stats=True)
+    for r in range(2):
+        tot = sum(phi_exact[r])
+        assert float(tot) == pytest.approx(l[r], rel=1e-15)
+        assert m[r] == x[r].max()
+        for c in range(3):
+            assert phi[r, c] == pytest.approx(float(phi_exact[r][c]), rel=1e-14, abs=0)
+            assert p[r, c] == pytest.approx(float(phi_exact[r][c] / tot), rel=1e-14, abs=0)
+
+
+def test_support_edge_values():
+    for d, num, den in _read_rows("ra_softmax_support_edge.txt"):
+        want = float(Fraction(int(num), int(den)))
+        got = float(oracle.ra_phi(float(d)))
+        if want == 0.0:
+            assert got == 0.0, d
+        else:
+            assert got == pytest.approx(want, rel=1e-14, abs=0), d
+
+
+def test_phi_positive_just_inside_support():
+    d = np.nextafter(16.0, 0.0)
+    assert oracle.ra_phi(d) > 0.0
+    assert oracle.ra_phi(16.0) == 0.0
+
+
+def test_artanh_closed_form():
+    # q = (1-u)/(1+u) = exp(-2 artanh u), so phi = exp(-16 artanh(Delta/16)) on [0, 16).
+    rng = np.random.default_rng(1)
+    d = np.concatenate([rng.uniform(0, 16, 20000), [0.0, 1e-9, 15.999]])
+    want = np.exp(-16.0 * np.arctanh(d / 16.0))
+    got = oracle.ra_phi(d)
+    np.testing.assert_allclose(got, want, rtol=2e-13, atol=0)
+
+
+def test_exp_sandwich():
+    # artanh(u) >= u gives phi <= exp(-Delta); the series bound gives
+    # log(phi) + Delta >= -Delta^3 / (768 (1 - u^2)).
+    d = np.linspace(0, 15.99, 5001)
+    u = d / 16
+    lp = np.log(oracle.ra_phi(d))
+    assert np.all(lp <= -d + 1e-12)
+    assert np.all(lp + d >= -d ** 3 / (768 * (1 - u * u)) - 1e-12)
+
+
+def test_softmax_invariants():
+    rng = np.random.default_rng(2)
+    x = rng.normal(0, 6, size=(64, 37))
+    p, phi, m, l = oracle.ra_softmax_rows(x, return_stats=True)
+    assert np.all(phi.max(axis=1) == 1.0)                 # phi at the max is exactly 1
+    assert np.all(l >= 1.0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(p[x <= (m[:, None] - 16.0)] == 0.0)     # exact zeros off the support
+    assert np.all(p[x > (m[:, None] - 16.0)] > 0.0)
+
+
+def test_softmax_shift_invariance_exact():
+    rng = np.random.default_rng(3)
+    x = rng.integers(-30, 30, size=(40, 25)).astype(np.float64)
+    c = rng.integers(-1000, 1000, size=(40, 1)).astype(np.float64)
+    np.testing.assert_array_equal(oracle.ra_softmax_rows(x), oracle.ra_softmax_rows(x + c))
+
+
+def test_softmax_masking():
+    x = np.array([[3.0, -np.inf, 1.0, -np.inf],
+                  [-np.inf, -np.inf, -np.inf, -np.inf],
+                  [-np.inf, 7.0, -np.inf, -np.inf]])
+    p = oracle.ra_softmax_rows(x)
+    assert p[0, 1] == 0 and p[0, 3] == 0
+    want = oracle.ra_softmax_rows(np.array([[3.0, 1.0]]))[0]
+    np.testing.assert_allclose(p[0, [0, 2]], want, rtol=1e-15)
+    assert np.all(p[1] == 0.0)                            # fully masked row -> zeros, no NaN
+    np.testing.assert_array_equal(p[2], [0, 1, 0, 0])
+
+
+def test_softmax_close_to_exp_softmax_for_small_spread():
+    # For Delta <= delta the two softmaxes differ by a factor within exp(+-eps),
+    # eps = delta^3 / (768 (1 - (delta/16)^2)).
+    rng = np.random.default_rng(4)
+    delta = 0.3
+    x = rng.uniform(0, delta, size=(50, 17))
+    e = np.exp(x - x.max(axis=1, keepdims=True))
+    sm = e / e.sum(axis=1, keepdims=True)
+    eps = delta ** 3 / (768 * (1 - (delta / 16) ** 2))
+    ratio = oracle.ra_softmax_rows(x) / sm
+    assert np.all(ratio <= np.exp(eps) + 1e-15) and np.all(ratio >= np.exp(-eps) - 1e-15)
+
+
+def _fd_grad(f, x, h=1e-6):
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        xp = x.copy(); xp[i] += h
+        xm = x.copy(); xm[i] -= h
+        g[i] = (f(xp) - f(xm)) / (2 * h)
+    return g
+
+
+def test_softmax_bwd_matches_central_differences():
+    rng = np.random.default_rng(5)
+    x = rng.normal(0, 5, size=(4, 9))
+    x[0, 3] = x[0].max() - 15.0    # an entry near the support edge
+    dp = rng.normal(size=x.shape)
+    g = oracle.ra_softmax_rows_bwd(x, dp)
+    fd = _fd_grad(lambda z: float((oracle.ra_softmax_rows(z) * dp).sum()), x)
+    np.testing.assert_allclose(g, fd, rtol=0, atol=2e-8)
+    # shift invariance: every row of the gradient sums to zero
+    np.testing.assert_allclose(g.sum(axis=1), 0.0, atol=1e-14)
+
+
+# ------------------------------------------------------------- ra_attention
+
+def _rand_qkv(rng, B, Hq, Hkv, Nq, Nk, D, sigma=1.0):
+    q = rng.normal(0, sigma, size=(B, Hq, Nq, D))
+    k = rng.normal(0, sigma, size=(B, Hkv, Nk, D))
+    v = rng.normal(0, 1, size=(B, Hkv, Nk, D))
+    return q, k, v
+
+
+def test_single_key_returns_value():
+    rng = np.random.default_rng(6)
+    q, k, v = _rand_qkv(rng, 2, 3, 1, 5, 1, 4)
+    for causal in (False, True):
+        o = oracle.ra_attention_fwd(q, k, v, causal, 0.5)[0]
+        np.testing.assert_array_equal(o, np.broadcast_to(v[:, :1], o.shape))
+
+
+def test_equal_scores_give_prefix_mean():
+    rng = np.random.default_rng(7)
+    q = np.zeros((1, 2, 6, 4))
+    k = rng.normal(size=(1, 2, 6, 4))
+    v = rng.normal(size=(1, 2, 6, 4))
+    o = oracle.ra_attention_fwd(q, k, v, False, 0.5)[0]
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), atol=1e-15)
+    oc = oracle.ra_attention_fwd(q, k, v, True, 0.5)[0]
+    csum = np.cumsum(v, axis=2) / np.arange(1, 7)[None, None, :, None]
+    np.testing.assert_allclose(oc, csum, atol=1e-15)
+
+
+def test_one_hot_rows_select_value_exactly():
+    # Every other score at least 16 below the max -> phi = (1, 0, ...), O = v_argmax exactly.
+    B, H, N, D = 1, 2, 8, 8
+    rng = np.random.default_rng(8)
+    k = np.eye(N, D)[None, None].repeat(H, axis=1) * 1.0
+    target = rng.permutation(N)
+    q = np.zeros((B, H, N, D))
+    q[0, :, np.arange(N), target] = 40.0          # scale 1 -> score 40 at key target[i], 0 elsewhere
+    v = rng.normal(size=(B, H, N, D))
+    o = oracle.ra_attention_fwd(q, k, v, False, 1.0)[0]
+    np.testing.assert_array_equal(o[0, 0], v[0, 0, target])
+
+
+def test_identity_values_expose_probabilities():
+    rng = np.random.default_rng(9)
+    N = 7
+    q, k, _ = _rand_qkv(rng, 1, 1, 1, N, N, 5, sigma=2.0)
+    v = np.eye(N)[None, None]
+    for causal in (False, True):
+        o = oracle.ra_attention_fwd(q, k, v, causal, 0.7)[0]
+        s = 0.7 * q[0, 0] @ k[0, 0].T
+        if causal:
+            s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+        np.testing.assert_allclose(o[0, 0], oracle.ra_softmax_rows(s), rtol=0, atol=1e-15)
+
+
+def test_gqa_equals_mha_on_repeated_kv():
+    rng = np.random.default_rng(10)
+    q, k, v = _rand_qkv(rng, 2, 6, 2, 9, 9, 4)
+    rep = 3
+    kr, vr = np.repeat(k, rep, axis=1), np.repeat(v, rep, axis=1)
+    for causal in (False, True):
+        o1 = oracle.ra_attention_fwd(q, k, v, causal, 0.5)[0]
+        o2 = oracle.ra_attention_fwd(q, kr, vr, causal, 0.5)[0]
+        np.testing.assert_array_equal(o1, o2)
+        # head h must read K/V head h // rep (not h % Hkv)
+        o3 = oracle.ra_attention_fwd(q, np.tile(k, (1, rep, 1, 1)), np.tile(v, (1, rep, 1, 1)),
+                                     causal, 0.5)[0]
+        assert not np.allclose(o1, o3)
+
+
+def test_small_spread_matches_torch_sdpa():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, Nq, Nk, D = 2, 4, 2, 11, 11, 6
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, Nq, Nk, D)
+    scale = 0.37
+    q = q * 0.02            # |s| <= 0.1 -> every Delta <= 0.2
+    delta = 0.2
+    for causal in (False, True):
+        o = oracle.ra_attention_fwd(q, k, v, causal, scale)[0]
+        s = scale * np.einsum("bhnd,bhmd->bhnm", q, np.repeat(k, 2, axis=1))
+        assert np.abs(s).max() <= delta / 2
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(np.repeat(k, 2, axis=1)),
+            torch.from_numpy(np.repeat(v, 2, axis=1)), is_causal=causal, scale=scale).numpy()
+        eps = delta ** 3 / (768 * (1 - (delta / 16) ** 2))
+        bound = (np.exp(2 * eps) - 1) * np.abs(v).max()
+        assert np.abs(o - ref).max() <= bound
+        assert np.abs(o - ref).max() > 0
+
+
+def test_causality_future_keys_do_not_leak():
+    rng = np.random.default_rng(12)
+    q, k, v = _rand_qkv(rng, 1, 2, 2, 10, 10, 4)
+    o = oracle.ra_attention_fwd(q, k, v, True, 0.5)[0]
+    for t in range(9):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, t + 1:] = rng.normal(size=k2[:, :, t + 1:].shape)
+        v2[:, :, t + 1:] = rng.normal(size=v2[:, :, t + 1:].shape)
+        o2 = oracle.ra_attention_fwd(q, k2, v2, True, 0.5)[0]
+        np.testing.assert_array_equal(o[:, :, :t + 1], o2[:, :, :t + 1])
+        assert not np.allclose(o[:, :, t + 1], o2[:, :, t + 1])
+
+
+def test_query_positions_select_rows():
+    rng = np.random.default_rng(13)
+    q, k, v = _rand_qkv(rng, 1, 2, 1, 12, 12, 4)
+    full = oracle.ra_attention_fwd(q, k, v, True, 0.5)
+    rows = np.array([0, 5, 11])
+    part = oracle.ra_attention_fwd(q[:, :, rows], k, v, True, 0.5, q_positions=rows)
+    for a, b in zip(full, part):
+        np.testing.assert_array_equal(a[:, :, rows], b)
+
+
+def test_attention_stats():
+    rng = np.random.default_rng(14)
+    q, k, v = _rand_qkv(rng, 1, 2, 2, 8, 8, 4, sigma=2.0)
+    o, m, l, a = oracle.ra_attention_fwd(q, k, v, True, 0.5)
+    for h in range(2):
+        s = 0.5 * q[0, h] @ k[0, h].T
+        for i in range(8):
+            assert m[0, h, i] == s[i, : i + 1].max()
+            assert a[0, h, i] == int(np.argmax(s[i, : i + 1]))
+            assert l[0, h, i] >= 1.0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 1, 5, 6, 3), (2, 2, 2, 4, 4, 2)])
+def test_attention_bwd_matches_central_differences(causal, shape):
+    B, Hq, Hkv, Nq, Nk, D = shape
+    rng = np.random.default_rng(15)
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, Nq, Nk, D, sigma=1.5)
+    do = rng.normal(size=q.shape)
+    scale = 0.8
+    dq, dk, dv = oracle.ra_attention_bwd(q, k, v, do, causal, scale)
+
+    def loss(qq, kk, vv):
+        return float((oracle.ra_attention_fwd(qq, kk, vv, causal, scale)[0] * do).sum())
+
+    fq = _fd_grad(lambda z: loss(z, k, v), q)
+    fk = _fd_grad(lambda z: loss(q, z, v), k)
+    fv = _fd_grad(lambda z: loss(q, k, z), v)
+    np.testing.assert_allclose(dq, fq, rtol=0, atol=3e-8)
+    np.testing.assert_allclose(dk, fk, rtol=0, atol=3e-8)
+    np.testing.assert_allclose(dv, fv, rtol=0, atol=3e-8)
+
+
+def test_attention_bwd_wide_scores_near_support_edge():
+    # Scores spread wide enough that some entries sit inside (12, 16) and some beyond 16.
+    rng = np.random.default_rng(16)
+    q, k, v = _rand_qkv(rng, 1, 1, 1, 6, 6, 3, sigma=3.0)
+    do = rng.normal(size=q.shape)
+    s = q[0, 0] @ k[0, 0].T
+    assert (s.max(1, keepdims=True) - s > 16).any() and ((s.max(1, keepdims=True) - s) > 8).sum() > 3
+    dq, dk, dv = oracle.ra_attention_bwd(q, k, v, do, False, 1.0)
+
+    def loss(qq, kk):
+        return float((oracle.ra_attention_fwd(qq, kk, v, False, 1.0)[0] * do).sum())
+
+    np.testing.assert_allclose(dq, _fd_grad(lambda z: loss(z, k), q), atol=3e-8, rtol=0)
+    np.testing.assert_allclose(dk, _fd_grad(lambda z: loss(q, z), k), atol=3e-8, rtol=0)
+
+
+def test_attention_bwd_invariants():
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, N, D = 2, 4, 2, 13, 5
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, N, N, D)
+    do = rng.normal(size=q.shape)
+    for causal in (False, True):
+        dq, dk, dv = oracle.ra_attention_bwd(q, k, v, do, causal, 0.6)
+        # shift invariance of every softmax row -> sum_j dK_j = 0 per K/V head
+        np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+        # each row of P sums to one -> sum_j dV_j = sum over the group's query rows of dO
+        dsum = do.reshape(B, Hkv, Hq // Hkv, N, D).sum(axis=(2, 3))
+        np.testing.assert_allclose(dv.sum(axis=2), dsum, atol=1e-12)
+        # the loss depends on q_i . k_j only -> <Q, dQ> = <K, dK>
+        assert np.sum(q * dq) == pytest.approx(np.sum(k * dk), rel=1e-10, abs=1e-12)
+
+
+def test_bwd_max_path_term_is_needed():
+    # Planted mistake (in the oracle, on the CPU): dropping the row-max term R
+    # must break agreement with finite differences, so the FD pin sees it.
+    import oracle.ra_oracle as ro
+    rng = np.random.default_rng(18)
+    q, k, v = _rand_qkv(rng, 1, 1, 1, 5, 5, 3, sigma=1.5)
+    do = rng.normal(size=q.shape)
+
+    def loss(qq):
+        return float((oracle.ra_attention_fwd(qq, k, v, False, 1.0)[0] * do).sum())
+
+    fd = _fd_grad(loss, q)
+    orig = ro._softmax_vjp
+
+    def no_max_path(p, delta, dp, a):
+        return orig(p, delta, dp, np.full_like(a, -1))
+
+    ro._softmax_vjp = no_max_path
+    try:
+        dq_bad = oracle.ra_attention_bwd(q, k, v, do, False, 1.0)[0]
+    finally:
+        ro._softmax_vjp = orig
+    assert np.abs(dq_bad - fd).max() > 1e-3
+
+
+def test_planted_phi_exponent_error_breaks_golden():
+    # Planted mistake: phi = q^7 instead of q^8 must fail the worked-example pin.
+    import oracle.ra_oracle as ro
+    orig = ro.ra_phi
+
+    def wrong(delta):
+        d = np.asarray(delta, dtype=np.float64)
+        u = d / 16
+        inside = u < 1
+        uu = np.where(inside, u, 0)
+        return np.where(inside, ((1 - uu) / (1 + uu)) ** 7, 0.0)
+
+    ro.ra_phi = wrong
+    try:
+        with pytest.raises(AssertionError):
+            test_worked_example_exact_phi_and_p()
+    finally:
+        ro.ra_phi = orig
