@@ -1,0 +1,244 @@
+"""Benchmark of the rational-softmax attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode fwd_bwd|fwd] [--no-cpu]
+
+A step is one forward (ra_attn_fwd) plus one backward (ra_attn_bwd) over the causal bf16
+workload B=4, H=16, N=8192, D=128 (inputs resident in HBM before timing starts).  The
+value is counted TFLOP/s: 4*B*Hq*Nq*Nk*D for the forward, halved when causal, times 3.5 for
+forward + backward.  Prints one JSON line.
+
+Also reported: the forward alone on this workload and on the grouped-query workload
+(B=4, Hq=32, Hkv=8, N=4096, D=128, host RoPE), the row softmax at [16384, 8192], a roofline
+object for the dominant kernel (timed with HIP events on the stream the library launches
+on) and the fp64 oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
+GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", choices=["fwd_bwd", "fwd"], default="fwd_bwd")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-heads", type=int, default=1,
+                    help="(batch, head) pairs of the workload the oracle times")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Attn:
+    """Device-resident inputs/outputs of one workload and the C-ABI calls on them."""
+
+    def __init__(self, ra, w, need_grad):
+        import torch
+        import workloads as wl
+        self.ra, self.w = ra, w
+        inp = wl.make_attention_inputs(w)
+        self.host = inp
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        dev = lambda a: torch.from_numpy(a).to(dt).cuda()   # exact: values are dtype-representable
+        self.q, self.k, self.v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+        self.o = torch.empty_like(self.q)
+        self.stats = torch.empty((w.B, w.Hq, w.Nq, 2), dtype=torch.float32, device="cuda")
+        self.code = ra.RA_BF16 if w.dtype == "bf16" else ra.RA_F32
+        if need_grad:
+            self.do = dev(inp["do"])
+            self.dq, self.dk, self.dv = (torch.empty_like(t) for t in (self.q, self.k, self.v))
+            self.ws_bytes = ra.ra_attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, self.code)
+            self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.stream = torch.cuda.current_stream()
+
+    def fwd(self):
+        w = self.w
+        st = self.ra.ra_attn_fwd(self.q, self.k, self.v, self.o, self.stats, w.B, w.Hq, w.Hkv,
+                                 w.Nq, w.Nk, w.D, int(w.causal), w.scale, self.code, self.stream)
+        if st != 0:
+            raise RuntimeError(f"ra_attn_fwd: {self.ra.ra_status_string(st)}")
+
+    def bwd(self):
+        w = self.w
+        st = self.ra.ra_attn_bwd(self.q, self.k, self.v, self.o, self.do, self.stats, self.dq,
+                                 self.dk, self.dv, self.ws, self.ws_bytes, w.B, w.Hq, w.Hkv, w.Nq,
+                                 w.Nk, w.D, int(w.causal), w.scale, self.code, self.stream)
+        if st != 0:
+            raise RuntimeError(f"ra_attn_bwd: {self.ra.ra_status_string(st)}")
+
+
+def time_calls(stream, fn, n):
+    """Average duration (ms) of fn() over n calls, from HIP events recorded on `stream`."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    for i in range(n):
+        ev[2 * i].record(stream)
+        fn()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]))
+
+
+def cpu_baseline(w, heads, mode):
+    """The fp64 oracle on `heads` (batch, head) pairs of workload w (bounded sample)."""
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    except Exception:                      # pragma: no cover
+        cores = os.cpu_count() or 1
+    import workloads as wl
+    sub = wl.AttnWorkload(w.name + "_sample", w.dtype, w.causal, 1, heads, heads, w.Nq, w.Nk,
+                          w.D, seed=w.seed, with_grad=True)
+    inp = wl.make_attention_inputs(sub)
+    t0 = time.perf_counter()
+    oracle.ra_attention_fwd(inp["q"], inp["k"], inp["v"], w.causal, w.scale)
+    if mode == "fwd_bwd":
+        oracle.ra_attention_bwd(inp["q"], inp["k"], inp["v"], inp["do"], w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    flops = sub.counted_flops_fwd_bwd() if mode == "fwd_bwd" else sub.counted_flops_fwd()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.Hq} (batch, head) pairs of {w.name}, "
+                      f"{'forward+backward' if mode == 'fwd_bwd' else 'forward'}, fp64 NumPy, "
+                      f"{dt:.1f} s", "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import rational_softmax_tiled_amd as ra
+    import workloads as wl
+    ra.load_library()
+    dev = torch.cuda.get_device_properties(0)
+    log(f"device {dev.name} CUs={dev.multi_processor_count} arch={getattr(dev, 'gcnArchName', '?')}")
+
+    w = wl.WORKLOADS[MAIN]
+    need_grad = args.mode == "fwd_bwd"
+    log(f"generating {w.name}")
+    main_run = Attn(ra, w, need_grad)
+    stream = main_run.stream
+
+    def step():
+        main_run.fwd()
+        if need_grad:
+            main_run.bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    flops_step = w.counted_flops_fwd_bwd() if need_grad else w.counted_flops_fwd()
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms ({wall:.2f} s wall for {args.steps} steps): {value:.1f} TFLOP/s")
+
+    # per-entry-point durations over the same kind of calls
+    n_k = max(5, args.steps)
+    fwd_ms = time_calls(stream, main_run.fwd, n_k)
+    fwd_tflops = w.counted_flops_fwd() / (fwd_ms * 1e-3) / 1e12
+    log(f"forward {fwd_ms:.3f} ms: {fwd_tflops:.1f} TFLOP/s")
+    bwd_ms = None
+    if need_grad:
+        bwd_ms = time_calls(stream, main_run.bwd, n_k)
+        log(f"backward {bwd_ms:.3f} ms")
+    del main_run
+    torch.cuda.empty_cache()
+
+    log(f"generating {GQA}")
+    wg = wl.WORKLOADS[GQA]
+    gqa = Attn(ra, wg, False)
+    for _ in range(3):
+        gqa.fwd()
+    gqa_ms = time_calls(gqa.stream, gqa.fwd, n_k)
+    gqa_tflops = wg.counted_flops_fwd() / (gqa_ms * 1e-3) / 1e12
+    log(f"GQA forward {gqa_ms:.3f} ms: {gqa_tflops:.1f} TFLOP/s")
+    del gqa
+    torch.cuda.empty_cache()
+
+    # row softmax (HBM-bound): read + write once
+    x = torch.from_numpy(wl.make_rows(16384, 8192, seed=11)).cuda()
+    p = torch.empty_like(x)
+    sm = lambda: ra.ra_softmax_rows(x, p, 16384, 8192, ra.RA_F32, stream)
+    for _ in range(3):
+        sm()
+    sm_ms = time_calls(stream, sm, n_k)
+    sm_gbs = 2 * x.numel() * 4 / (sm_ms * 1e-3) / 1e9
+    log(f"softmax rows [16384, 8192] fp32 {sm_ms:.3f} ms: {sm_gbs:.0f} GB/s")
+
+    # dominant kernel: the forward attention kernel (one launch per ra_attn_fwd call)
+    dom_ms, dom_name, dom_flops = fwd_ms, "attn_fwd_kernel (ra_attn_fwd)", w.counted_flops_fwd()
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": dom_name, "avg_launch_ms": round(dom_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the fp64 oracle on a bounded sample")
+        cpu = cpu_baseline(w, args.cpu_heads, args.mode)
+        log(f"oracle: {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s on {cpu['cores']} threads")
+        cpu.pop("seconds")
+
+    out = {
+        "metric": "ra_attention fwd & fwd+bwd TFLOP/s (bf16, causal) + % of MFMA bf16 peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": args.mode, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "seq_len": w.Nq, "head_dim": w.D, "causal": w.causal, "global_batch": w.B},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"workload": w.name, "ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),
+                "frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4)},
+        "bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
+        "fwd_gqa": {"workload": wg.name, "ms": round(gqa_ms, 4), "tflops": round(gqa_tflops, 2),
+                    "frac_of_peak": round(gqa_tflops / PEAK_BF16_TFLOPS, 4)},
+        "softmax_rows": {"shape": [16384, 8192], "dtype": "f32", "ms": round(sm_ms, 4),
+                         "GB/s": round(sm_gbs, 1), "frac_of_hbm_peak": round(sm_gbs / PEAK_HBM_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

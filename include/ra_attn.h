@@ -1,0 +1,142 @@
+/*
+ * ra_attn.h -- C ABI of the rational-softmax attention library for AMD gfx950 (MI355X).
+ *
+ * The operation ("Ra-Family: Rational Neural Architecture", section 3 "Rational Attention &
+ * Softmax"): for each row of scores s, Delta_j = max(s) - s_j, u_j = Delta_j / 16,
+ * phi_j = ((1 - u_j) / (1 + u_j))^8 when u_j < 1 and exactly 0 otherwise, p_j = phi_j / sum(phi).
+ * Attention computes O = p(scale * Q K^T) V tile by tile without storing the score matrix
+ * (same section, item ra_attention, the functional drop-in for scaled_dot_product_attention).
+ * Grouped-query attention: query head h reads K/V head h / (Hq / Hkv) (noeira "Primitives"
+ * page, section "Attention and transformers", RepeatKVHeads).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are contiguous, row-major, in device memory: q, o, dq, d_o are [B, Hq, Nq, D];
+ *     k, v, dk, dv are [B, Hkv, Nk, D].  Output dtype equals input dtype.
+ *   - dtype: RA_F32 (fp32 storage, fp32 matrix-core products) or RA_BF16 (bf16 storage,
+ *     fp32 accumulation; probabilities are rounded to bf16 to nearest-even before the
+ *     P.V product).
+ *   - causal != 0 allows key j for query i iff j <= i (top-left alignment, as
+ *     scaled_dot_product_attention's is_causal).  Masked keys get p = 0 and take no part in
+ *     the row max or the sum of phi.
+ *   - stream is a hipStream_t (NULL = the default stream).  Kernels run asynchronously on it;
+ *     the caller keeps every buffer alive until the stream has passed the call.
+ *   - The caller owns all memory.  The library allocates nothing, frees nothing, does not
+ *     synchronise, keeps no pointer after returning and holds no global state; calls are
+ *     thread-safe.
+ *   - Every argument check runs before any launch: on an error status nothing is launched and
+ *     no output is written.  A failed launch returns RA_ERR_HIP.  Nothing is printed, nothing
+ *     aborts, no C++ exception crosses the ABI.
+ *   - Device tensors must be 16-byte aligned; stats and workspace 4-byte aligned.
+ *   - Supported head dims: D = 64 and D = 128.  scale must be finite and > 0.
+ *   - Inputs are assumed finite; NaN or Inf inputs give unspecified outputs.
+ */
+#ifndef RA_ATTN_H
+#define RA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ra_dtype { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+typedef enum ra_status {
+  RA_OK = 0,
+  RA_ERR_NULLPTR = 1,   /* a required pointer is NULL */
+  RA_ERR_SHAPE = 2,     /* a size is negative or B/H/N inconsistent */
+  RA_ERR_GQA = 3,       /* Hkv == 0 with Hq > 0, or Hq is not a multiple of Hkv */
+  RA_ERR_HEADDIM = 4,   /* D not in {64, 128} */
+  RA_ERR_DTYPE = 5,     /* dtype not RA_F32 / RA_BF16 */
+  RA_ERR_SCALE = 6,     /* scale not finite or <= 0 */
+  RA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than ra_attn_bwd_workspace_bytes */
+  RA_ERR_ALIGN = 8,     /* a pointer breaks the alignment rule above */
+  RA_ERR_TOO_LARGE = 9, /* a size exceeds the library's index range (see each call) */
+  RA_ERR_HIP = 10       /* the HIP runtime reported an error at launch */
+} ra_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* ra_status_string(int status);
+
+/* HIP error code (hipError_t as int) behind the last RA_ERR_HIP returned on this thread. */
+int ra_last_hip_error(void);
+
+/*
+ * ra_attn_fwd -- forward rational-softmax attention.
+ *   Source: Ra-Family page, section 3, items ra_softmax and ra_attention.
+ *   o[b,h,i,:] = sum_j p_ij v[b,g,j,:], p_i = ra_softmax(scale * q[b,h,i,:] . k[b,g,j,:] over
+ *   the allowed keys j), g = h / (Hq / Hkv).
+ *   stats: optional (NULL to skip), float [B, Hq, Nq, 2]: (m, l) per query row, where m is the
+ *   row max of the UNSCALED dot products q_i . k_j (the score max is scale * m) and l is the
+ *   sum of phi.  ra_attn_bwd consumes it unchanged.
+ *   Two passes over the keys: the first finds m, the second evaluates phi, sum(phi) and P.V;
+ *   a key tile whose entries all lie outside the compact support (u >= 1) for a group of
+ *   query rows is skipped for them, which leaves the result bit-identical.
+ *   Sizes: B*Hq*Nq == 0 -> RA_OK, nothing launched.  Nk == 0 -> o = 0 (and stats m = -inf,
+ *   l = 0): a row with no allowed key yields a zero output, not NaN.
+ *   Limits: Nq * D and Nk * D below 2^31, B * Hq * Nq below 2^31.
+ */
+int ra_attn_fwd(const void* q, const void* k, const void* v, void* o, float* stats,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                int causal, float scale, int dtype, void* stream);
+
+/*
+ * ra_attn_fwd_counted -- ra_attn_fwd plus tile-skip counters (diagnostics, not for timing).
+ *   counters: device pointer to 4 uint64, which the call ADDS to (zero them first):
+ *     [0] (wave, key-tile) pairs inside the causal range of the second pass,
+ *     [1] of those, pairs skipped because every entry lies outside the support,
+ *     [2] (workgroup, key-tile) pairs of the second pass,
+ *     [3] of those, tiles whose K/V load was skipped for the whole workgroup.
+ *   Everything else as ra_attn_fwd.
+ */
+int ra_attn_fwd_counted(const void* q, const void* k, const void* v, void* o, float* stats,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                        int64_t D, int causal, float scale, int dtype,
+                        unsigned long long* counters, void* stream);
+
+/*
+ * ra_attn_bwd_workspace_bytes -- size of the scratch buffer ra_attn_bwd needs (0 on invalid
+ * sizes).  The caller allocates it; its contents need not be initialised.
+ */
+size_t ra_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                   int64_t D, int dtype);
+
+/*
+ * ra_attn_bwd -- gradients of L = sum(O * dO) for ra_attn_fwd.
+ *   Source: Ra-Family page, section 3, item ra_softmax (closed-form derivative
+ *   d(phi)/du = -16 phi / (1 - u^2) for u < 1, recomputed from the saved row statistics
+ *   rather than stored powers) and item ra_attention ("closed-form backward recomputation",
+ *   saved state O(B*H*Nq*D)).  With dP = dO V^T and c_i = dO_i . O_i:
+ *     G_ij = p_ij (dP_ij - c_i) / (1 - u_ij^2) on the support, 0 elsewhere;
+ *     the row max also depends on the scores, which adds R_i = -sum_j G_ij at the lowest
+ *     key index attaining the max: dS = G + R e_{argmax};
+ *     dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO,
+ *   with dK and dV summed over the Hq/Hkv query heads sharing a K/V head (RepeatKVHeads).
+ *   o and stats must come from ra_attn_fwd with the same inputs; stats == NULL makes the
+ *   call recompute them first.  dq, dk, dv are overwritten (no accumulation).
+ *   workspace: at least ra_attn_bwd_workspace_bytes(...) bytes of device memory.
+ *   The result is deterministic (no floating-point atomics).
+ *   Sizes and limits as ra_attn_fwd; Nk == 0 -> dq = 0; B*Hkv*Nk > 0 with B*Hq*Nq == 0 ->
+ *   dk = dv = 0.
+ */
+int ra_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                const float* stats, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream);
+
+/*
+ * ra_softmax_rows -- ra_softmax along the last axis of a [rows, cols] matrix.
+ *   Source: Ra-Family page, section 3, item ra_softmax (ra_softmax(logits, dim=-1)).
+ *   Entries equal to -inf are masked: p = 0 there, and they take no part in the max or the
+ *   sum.  A row whose entries are all -inf gives p = 0.  x and p may alias (in-place).
+ *   Limits: rows < 2^31, cols < 2^31.  rows == 0 or cols == 0 -> RA_OK, nothing launched.
+ */
+int ra_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, int dtype,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_ATTN_H */

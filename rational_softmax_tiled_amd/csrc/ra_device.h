@@ -1,0 +1,192 @@
+// ra_device.h -- device-side building blocks of the rational-softmax attention kernels (gfx950).
+//
+// Matrix-core conventions (CDNA 32x32 MFMA, wave64):
+//   * v_mfma_f32_32x32x16_bf16: lane l supplies A[m = l%32][k = 8*(l/32) + j] and
+//     B[k = 8*(l/32) + j][n = l%32] for j = 0..7; the 32x32 fp32 result leaves lane l holding
+//     column n = l%32 and rows m = 8*(i/4) + 4*(l/32) + i%4 in accumulator element i.
+//   * For fp32 operands the same 16-wide K chunk is covered by eight v_mfma_f32_32x32x2_f32,
+//     the j-th using element j of each lane's 8-element fragment, so fragments have one layout
+//     for both types: "8 consecutive K-elements starting at 8*(l/32)".
+//   * The order of the K (contraction) index inside a chunk is free as long as both operands
+//     agree; the P.V product uses this to consume the score accumulator in place (see
+//     key_slot below).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;               // waves per workgroup
+constexpr int kThreads = kWave * kWaves;
+constexpr int kRowsPerWave = 32;        // query (or key) rows one wave owns
+constexpr int kNumXcd = 8;              // MI355X: 8 accelerator dies, each with its own L2
+
+template <typename T> struct Ty;
+template <> struct Ty<bf16> {
+  using frag = bf16x8;                  // 8 x bf16 = 16 bytes
+  using quad = bf16x4;
+  static constexpr int chunk = 8;       // elements per 16-byte chunk
+};
+template <> struct Ty<float> {
+  using frag = f32x8;                   // 8 x fp32 = 32 bytes
+  using quad = f32x4;
+  static constexpr int chunk = 4;
+};
+
+// ---------------------------------------------------------------- fragments
+
+__device__ __forceinline__ bf16x8 load_frag(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ f32x8 load_frag(const float* p) {
+  f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <typename T> __device__ __forceinline__ typename Ty<T>::frag zero_frag() {
+  return typename Ty<T>::frag{};
+}
+
+__device__ __forceinline__ void mma(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], c, 0, 0, 0);
+}
+
+// Row index (inside a 32x32 accumulator) of element i for this lane.
+__device__ __forceinline__ int acc_row(int i, int lane) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// Eight accumulator values (elements 8*ks .. 8*ks+7) as the B fragment of the next product.
+__device__ __forceinline__ bf16x8 pack_frag_bf16(const f32x16& s, int ks) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)s[8 * ks + j];   // v_cvt_pk_bf16_f32: nearest-even
+  return r;
+}
+__device__ __forceinline__ f32x8 pack_frag_f32(const f32x16& s, int ks) {
+  f32x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = s[8 * ks + j];
+  return r;
+}
+
+// Accumulator rows 16*ks + 8*(l/32) + j (j = 0..7) of lane l, produced by elements 8*ks + j,
+// are stored at "slot" 16*ks + 8*(l/32) + j of a transposed LDS tile so that an A fragment
+// read of 8 consecutive slots pairs with them.  key_slot maps a row (0..31) to its slot;
+// groups of four consecutive rows stay contiguous.
+__device__ __host__ constexpr int key_slot(int r) {
+  return 16 * ((r >> 4) & 1) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+}
+__device__ __host__ constexpr int quad_slot(int quad) {   // quad = 4 consecutive rows
+  return 32 * (quad >> 3) + key_slot((quad & 7) * 4);
+}
+
+// ---------------------------------------------------------------- rational softmax
+
+// phi for one entry: t = m - s in raw dot-product units (>= 0, +inf for a masked entry),
+// c = scale / 16.  u = t * c; q = (1-u)/(1+u) = 2/(1+u) - 1, clamped to [0, 1] so that
+// u >= 1 gives exactly 0; phi = q^8 by three squarings.  ("Ra-Family: Rational Neural
+// Architecture", section 3, ra_softmax.)
+__device__ __forceinline__ float ra_phi_t(float t, float c) {
+  float d = fmaf(t, c, 1.0f);
+  float r = __builtin_amdgcn_rcpf(d);
+  float q = fminf(fmaxf(fmaf(r, 2.0f, -1.0f), 0.0f), 1.0f);
+  float q2 = q * q;
+  float q4 = q2 * q2;
+  return q4 * q4;
+}
+
+// ---------------------------------------------------------------- wave / block helpers
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_min(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fminf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs.  Give each XCD a contiguous range
+// of logical workgroup ids so that neighbours (which share K/V) share one L2.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int per = n / kNumXcd, rem = n % kNumXcd;
+  const int x = i % kNumXcd, j = i / kNumXcd;
+  return (x < rem) ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
+// ---------------------------------------------------------------- LDS staging
+
+// Copy `ROWS` rows of a row-major [*, D] tile into LDS with row pitch PITCH (elements);
+// rows >= nvalid are zero-filled.  16-byte chunks, consecutive threads on consecutive
+// chunks of a row.
+template <typename T, int D, int ROWS, int PITCH>
+__device__ __forceinline__ void stage_rows(T* lds, const T* g, int nvalid, int tid) {
+  constexpr int CE = 16 / sizeof(T);
+  constexpr int CPR = D / CE;
+  constexpr int TOTAL = ROWS * CPR;
+#pragma unroll
+  for (int it = 0; it < (TOTAL + kThreads - 1) / kThreads; ++it) {
+    const int c = it * kThreads + tid;
+    if (TOTAL % kThreads == 0 || c < TOTAL) {
+      const int r = c / CPR, cc = c % CPR;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (r < nvalid) val = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + cc * CE);
+      *reinterpret_cast<u32x4*>(lds + r * PITCH + cc * CE) = val;
+    }
+  }
+}
+
+// Copy `ROWS` rows of a row-major [*, D] tile into LDS transposed: lds[d * PITCH + slot(row)],
+// with the slot order of key_slot inside every 32-row block.  Each thread moves a 4-row x
+// 8-column block: four 8-element global loads, eight 4-element LDS stores.
+template <typename T, int D, int ROWS, int PITCH>
+__device__ __forceinline__ void stage_rows_transposed(T* lds, const T* g, int nvalid, int tid) {
+  using quad_t = typename Ty<T>::quad;
+  constexpr int UNITS = (ROWS / 4) * (D / 8);
+#pragma unroll
+  for (int it = 0; it < (UNITS + kThreads - 1) / kThreads; ++it) {
+    const int u = it * kThreads + tid;
+    if (UNITS % kThreads == 0 || u < UNITS) {
+      const int quad = u / (D / 8), dc = u % (D / 8);
+      typename Ty<T>::frag rows[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * quad + r;
+        rows[r] = row < nvalid ? load_frag(g + (size_t)row * D + 8 * dc) : zero_frag<T>();
+      }
+      const int slot = quad_slot(quad);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        quad_t col = {rows[0][e], rows[1][e], rows[2][e], rows[3][e]};
+        *reinterpret_cast<quad_t*>(lds + (8 * dc + e) * PITCH + slot) = col;
+      }
+    }
+  }
+}
+
+}  // namespace ra

@@ -1,0 +1,287 @@
+// ra_fwd.hip -- forward rational-softmax attention for gfx950.
+//
+// "Ra-Family: Rational Neural Architecture", section 3 "Rational Attention & Softmax":
+// O = ra_softmax(scale * Q K^T) V computed tile by tile; the [B, H, Nq, Nk] scores never
+// reach memory.  phi has no online rescaling (phi(D + d) is not a multiple of phi(D)), so the
+// row max must be final before any phi is summed: pass 1 finds it, pass 2 evaluates phi,
+// sum(phi) and P.V.  Tiles whose entries all fall outside the compact support are skipped.
+//
+// Work decomposition
+//   * One wave owns 32 query rows of one head; a workgroup is 4 waves that share one K/V head
+//     (grouped-query: the REP query heads of a K/V head are packed into the same workgroup, so
+//     each K/V tile staged in LDS serves all of them).  Tasks (head-in-group, 32-row block)
+//     are enumerated head-fastest and dealt four per workgroup.
+//   * Scores are computed transposed, S^T = K Q^T (keys on the accumulator rows, queries on
+//     the lanes), so every lane owns one query row: its running max, phi sum and the
+//     P^T operand of O^T = V^T P^T stay in that lane, with no register shuffle.  V^T is staged
+//     transposed in LDS in the slot order that matches the accumulator layout.
+//   * Pass 1 keeps, per wave and key tile, the max score of the tile; after pass 1 a tile is
+//     skipped for a wave when (min_i m_i - tile max) * scale / 16 >= 1, evaluated with the same
+//     floating-point steps as phi itself, so skipping never changes a result bit.  A tile
+//     skipped by all four waves is not even loaded.  Causal tiles beyond a wave's diagonal are
+//     recorded as -inf and skipped the same way.
+#include "ra_device.h"
+#include "ra_internal.h"
+
+namespace ra {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* stats;
+  unsigned long long* counters;
+  int Hq, Hkv, Nq, Nk, rep;
+  int tasks_per_group;   // rep * ceil(Nq / 32)
+  int wg_per_group;      // ceil(tasks_per_group / 4)
+  int total_wg;
+  float c;               // scale / 16
+};
+
+constexpr int kMaxTiles = 512;   // key tiles with a recorded maximum (skip test); beyond: no skip
+
+template <typename T>
+__device__ __forceinline__ void store_quad(T* dst, f32x16 acc, int base, float s);
+
+template <>
+__device__ __forceinline__ void store_quad<bf16>(bf16* dst, f32x16 acc, int base, float s) {
+  bf16x4 v = {(bf16)(acc[base] * s), (bf16)(acc[base + 1] * s), (bf16)(acc[base + 2] * s),
+              (bf16)(acc[base + 3] * s)};
+  *reinterpret_cast<bf16x4*>(dst) = v;
+}
+template <>
+__device__ __forceinline__ void store_quad<float>(float* dst, f32x16 acc, int base, float s) {
+  f32x4 v = {acc[base] * s, acc[base + 1] * s, acc[base + 2] * s, acc[base + 3] * s};
+  *reinterpret_cast<f32x4*>(dst) = v;
+}
+
+// Mask entries of a 32x32 S^T block: key >= Nk, or (causal) key > query row.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int lane, int Nk) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = key0 + acc_row(i, lane);
+    if (key >= Nk || (CAUSAL && key > qrow)) s[i] = -INFINITY;
+  }
+}
+
+template <typename T, int D, int BN, bool CAUSAL, bool COUNT>
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
+  using frag_t = typename Ty<T>::frag;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int PK = D + PAD;    // K tile row pitch
+  constexpr int PV = BN + PAD;   // V^T tile row pitch
+  constexpr int KC = D / 16;     // 16-wide K chunks of the QK^T contraction
+  constexpr int SB = BN / 32;    // 32-key blocks per tile
+  constexpr int DB = D / 32;     // 32-row blocks of O^T
+
+  __shared__ __attribute__((aligned(16))) T k_lds[BN * PK];
+  __shared__ __attribute__((aligned(16))) T vt_lds[D * PV];
+  __shared__ float tmax_lds[kWaves][kMaxTiles];
+  __shared__ float mmin_lds[kWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // ---- work assignment
+  const int logical = xcd_remap(blockIdx.x, a.total_wg);
+  const int bg = logical / a.wg_per_group;
+  int wig = logical % a.wg_per_group;
+  if (CAUSAL) wig = a.wg_per_group - 1 - wig;   // long (late) query blocks first
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int task = wig * kWaves + wave;
+  const bool active = task < a.tasks_per_group;
+  const int h = g * a.rep + (active ? task % a.rep : 0);
+  const int q0 = (active ? task / a.rep : 0) * kRowsPerWave;
+  const int last_task = min(wig * kWaves + kWaves - 1, a.tasks_per_group - 1);
+  const int wg_qmax = min((last_task / a.rep) * kRowsPerWave + kRowsPerWave - 1, a.Nq - 1);
+  const int key_end = CAUSAL ? min(a.Nk, wg_qmax + 1) : a.Nk;
+  const int nt = (key_end + BN - 1) / BN;
+  const int wave_qmax = min(q0 + kRowsPerWave - 1, a.Nq - 1);
+  const int key_end_w = !active ? 0 : (CAUSAL ? min(a.Nk, wave_qmax + 1) : a.Nk);
+  const int nt_w = (key_end_w + BN - 1) / BN;
+
+  const T* qh = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h) * a.Nq * D;
+  const T* kg = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Nk * D;
+  const T* vg = static_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Nk * D;
+
+  // ---- Q fragments stay in registers for both passes (B operand of S^T = K Q^T)
+  const int qi = q0 + (lane & 31);
+  const int qrow = min(qi, a.Nq - 1);   // tail rows duplicate the last real row
+  frag_t qf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) qf[kc] = load_frag(qh + (size_t)qrow * D + 16 * kc + 8 * (lane >> 5));
+
+  const int frow = lane & 31;           // A-fragment row inside a 32-row block
+  const int fcol = 8 * (lane >> 5);     // A-fragment column offset
+
+  // ---- pass 1: row max of the raw dot products
+  float mx = -INFINITY;
+  for (int kt = 0; kt < nt; ++kt) {
+    __syncthreads();
+    stage_rows<T, D, BN, PK>(k_lds, kg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
+    __syncthreads();
+    float tl = -INFINITY;
+    if (kt < nt_w) {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        f32x16 s = {};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          mma(s, load_frag(k_lds + (sb * 32 + frow) * PK + 16 * kc + fcol), qf[kc]);
+        const int key0 = kt * BN + sb * 32;
+        if ((CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk) mask_block<CAUSAL>(s, key0, qrow, lane, a.Nk);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tl = fmaxf(tl, s[i]);
+      }
+    }
+    mx = fmaxf(mx, tl);
+    if (kt < kMaxTiles) {
+      const float wm = wave_max(tl);
+      if (lane == 0) tmax_lds[wave][kt] = wm;
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));   // lanes l and l+32 hold the same query row
+  {
+    const float mm = wave_min(mx);
+    if (lane == 0) mmin_lds[wave] = mm;
+  }
+  __syncthreads();
+
+  // ---- pass 2: phi, sum(phi), O^T = V^T P^T
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float lsum = 0.0f;
+  unsigned long long n_wave_tiles = 0, n_wave_skip = 0, n_wg_tiles = 0, n_wg_skip = 0;
+
+  for (int kt = 0; kt < nt; ++kt) {
+    bool my_skip, all_skip;
+    if (kt < kMaxTiles) {
+      all_skip = true;
+      my_skip = false;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float tm = tmax_lds[w][kt];
+        const bool s = (tm == -INFINITY) || (fmaf(mmin_lds[w] - tm, a.c, 1.0f) >= 2.0f);
+        all_skip = all_skip && s;
+        if (w == wave) my_skip = s;
+      }
+    } else {
+      my_skip = kt >= nt_w;
+      all_skip = false;
+    }
+    if (COUNT) {
+      n_wg_tiles += 1;
+      n_wg_skip += all_skip ? 1 : 0;
+      if (kt < nt_w) {
+        n_wave_tiles += 1;
+        n_wave_skip += my_skip ? 1 : 0;
+      }
+    }
+    if (all_skip) continue;   // uniform: every thread read the same LDS values
+    __syncthreads();
+    stage_rows<T, D, BN, PK>(k_lds, kg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
+    stage_rows_transposed<T, D, BN, PV>(vt_lds, vg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
+    __syncthreads();
+    if (my_skip) continue;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      f32x16 s = {};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        mma(s, load_frag(k_lds + (sb * 32 + frow) * PK + 16 * kc + fcol), qf[kc]);
+      const int key0 = kt * BN + sb * 32;
+      if ((CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk) mask_block<CAUSAL>(s, key0, qrow, lane, a.Nk);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = ra_phi_t(mx - s[i], a.c);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        frag_t pf;
+        if constexpr (sizeof(T) == 2) {
+          pf = pack_frag_bf16(s, ks);
+          // sum the rounded probabilities that enter the product, two per instruction
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            bf16x2 pr = {pf[j], pf[j + 1]};
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(bf16)1.0f, (bf16)1.0f}, lsum, false);
+          }
+        } else {
+          pf = pack_frag_f32(s, ks);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) lsum += pf[j];
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          mma(oacc[db], load_frag(vt_lds + (db * 32 + frow) * PV + sb * 32 + 16 * ks + fcol), pf);
+      }
+    }
+  }
+
+  // ---- epilogue: O = acc / l
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if (active && qi < a.Nq) {
+    T* orow = static_cast<T*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qi) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        store_quad<T>(orow + db * 32 + 8 * r4 + 4 * (lane >> 5), oacc[db], 4 * r4, inv);
+    if (a.stats != nullptr && lane < 32) {
+      float* st = a.stats + ((size_t)(b * a.Hq + h) * a.Nq + qi) * 2;
+      st[0] = mx;
+      st[1] = ltot;
+    }
+  }
+  if (COUNT && lane == 0) {
+    atomicAdd(a.counters + 0, n_wave_tiles);
+    atomicAdd(a.counters + 1, n_wave_skip);
+    if (wave == 0) {
+      atomicAdd(a.counters + 2, n_wg_tiles);
+      atomicAdd(a.counters + 3, n_wg_skip);
+    }
+  }
+}
+
+template <typename T, int D, int BN>
+static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
+                               unsigned long long* counters, hipStream_t stream) {
+  FwdArgs a;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.o = o;
+  a.stats = stats;
+  a.counters = counters;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.Nq = p.Nq;
+  a.Nk = p.Nk;
+  a.rep = p.Hq / p.Hkv;
+  a.tasks_per_group = a.rep * ((p.Nq + kRowsPerWave - 1) / kRowsPerWave);
+  a.wg_per_group = (a.tasks_per_group + kWaves - 1) / kWaves;
+  a.total_wg = p.B * p.Hkv * a.wg_per_group;
+  a.c = p.scale / 16.0f;
+  dim3 grid(a.total_wg), block(kThreads);
+  if (p.causal) {
+    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false>), grid, block, 0, stream, a);
+  } else {
+    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const AttnProblem& p, void* o, float* stats,
+                           unsigned long long* counters, hipStream_t stream) {
+  if (p.bf16) {
+    if (p.D == 64) return launch_typed<bf16, 64, 64>(p, o, stats, counters, stream);
+    return launch_typed<bf16, 128, 64>(p, o, stats, counters, stream);
+  }
+  if (p.D == 64) return launch_typed<float, 64, 32>(p, o, stats, counters, stream);
+  return launch_typed<float, 128, 32>(p, o, stats, counters, stream);
+}
+
+}  // namespace ra

@@ -1,0 +1,47 @@
+// ra_internal.h -- host-side problem descriptions and kernel launchers behind the C ABI.
+// The ABI layer validates every argument first; launchers assume valid, non-empty problems.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ra {
+
+struct AttnProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  int B, Hq, Hkv, Nq, Nk, D;
+  bool causal;
+  float scale;
+  bool bf16;  // false: fp32
+};
+
+// Forward: o (and stats when non-null); counters non-null selects the counting variant.
+hipError_t launch_attn_fwd(const AttnProblem& p, void* o, float* stats,
+                           unsigned long long* counters, hipStream_t stream);
+
+// Backward.  Workspace layout: see bwd_workspace_layout.
+struct BwdWorkspace {
+  float* stats;   // [B*Hq*Nq*2] (m, l), used when the caller passes none
+  float* c;       // [B*Hq*Nq]  dO_i . O_i
+  float* r;       // [B*Hq*Nq]  row-max gradient R_i
+  int* amax;      // [B*Hq*Nq]  lowest key index of the row max
+};
+size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq);
+BwdWorkspace bwd_workspace_layout(void* base, int64_t B, int64_t Hq, int64_t Nq);
+hipError_t launch_attn_bwd(const AttnProblem& p, const void* o, const void* d_o,
+                           const float* stats, void* dq, void* dk, void* dv,
+                           const BwdWorkspace& ws, hipStream_t stream);
+
+// Row softmax.
+hipError_t launch_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, bool bf16,
+                               hipStream_t stream);
+
+// Fill helpers (a kernel, not hipMemsetAsync, so the calls stay graph-capture friendly).
+hipError_t launch_fill_u32(void* dst, uint32_t value, size_t count, hipStream_t stream);
+hipError_t launch_fill_u16(void* dst, uint16_t value, size_t count, hipStream_t stream);
+hipError_t launch_fill_pairs(float* dst, float a, float b, size_t pairs, hipStream_t stream);
+
+}  // namespace ra

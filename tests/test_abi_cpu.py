@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad arguments before any
+launch.  No GPU is needed: every call here either fails validation or has nothing to do."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import rational_softmax_tiled_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra_attn.h")
+
+OK, NULLPTR, SHAPE, GQA, HEADDIM, DTYPE, SCALE, WORKSPACE, ALIGN, TOO_LARGE, HIP = range(11)
+
+# Fake, 256-byte aligned "device" addresses: never dereferenced, since every call fails
+# validation or is empty.
+P = 0x7F0000000000
+P2 = P + 0x100000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ra.library_path()):
+        from rational_softmax_tiled_amd import build
+        build.build()
+    return ra.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"ra_attn_fwd", "ra_attn_bwd", "ra_softmax_rows", "ra_attn_bwd_workspace_bytes",
+            "ra_attn_fwd_counted", "ra_status_string", "ra_last_hip_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(11):
+        s = ra.ra_status_string(code)
+        assert s.startswith("RA_")
+    assert "unknown" in ra.ra_status_string(99)
+
+
+def fwd(B=1, Hq=2, Hkv=1, Nq=8, Nk=8, D=64, causal=1, scale=0.125, dtype=ra.RA_BF16,
+        q=P, k=P, v=P, o=P2, stats=None):
+    return ra.ra_attn_fwd(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, 0)
+
+
+def test_fwd_validation(lib):
+    assert fwd(dtype=7) == DTYPE
+    assert fwd(B=-1) == SHAPE
+    assert fwd(Nk=-3) == SHAPE
+    assert fwd(Hq=3, Hkv=2) == GQA
+    assert fwd(Hq=2, Hkv=0) == GQA
+    assert fwd(D=96) == HEADDIM
+    assert fwd(D=32) == HEADDIM
+    for s in (0.0, -1.0, math.inf, math.nan):
+        assert fwd(scale=s) == SCALE
+    assert fwd(q=None) == NULLPTR
+    assert fwd(o=None) == NULLPTR
+    assert fwd(k=None) == NULLPTR
+    assert fwd(q=P + 8) == ALIGN
+    assert fwd(v=P + 4) == ALIGN
+    assert fwd(stats=P + 2) == ALIGN
+    assert fwd(Nq=1 << 25, D=128) == TOO_LARGE
+    assert fwd(B=1 << 12, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 10) == TOO_LARGE
+    assert fwd(B=1 << 40, Hq=1 << 40, Hkv=1, Nq=1 << 40) == TOO_LARGE  # no int64 overflow
+
+
+def test_fwd_empty_problems_launch_nothing(lib):
+    # nothing to compute: RA_OK without touching the (fake) pointers or the GPU
+    assert fwd(B=0) == OK
+    assert fwd(Nq=0) == OK
+    assert fwd(Hq=0, Hkv=0) == OK
+    assert fwd(B=0, q=None, k=None, v=None, o=None) == OK
+
+
+def test_counted_needs_counters(lib):
+    assert ra.ra_attn_fwd_counted(P, P, P, P2, None, 1, 2, 1, 8, 8, 64, 1, 0.125, ra.RA_BF16,
+                                  None, 0) == NULLPTR
+
+
+def test_workspace_size(lib):
+    n = ra.ra_attn_bwd_workspace_bytes(4, 16, 16, 8192, 8192, 128, ra.RA_BF16)
+    assert n >= 4 * 16 * 8192 * (2 * 4 + 3 * 4)
+    assert ra.ra_attn_bwd_workspace_bytes(4, 16, 16, 8192, 8192, 96, ra.RA_BF16) == 0
+    assert ra.ra_attn_bwd_workspace_bytes(1, 2, 1, 100, 100, 64, ra.RA_F32) < \
+        ra.ra_attn_bwd_workspace_bytes(1, 2, 1, 200, 100, 64, ra.RA_F32)
+
+
+def bwd(ws=P2, ws_bytes=1 << 30, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, D=64, scale=0.125,
+        dtype=ra.RA_BF16, q=P, dq=P2, dk=P2, stats=None):
+    return ra.ra_attn_bwd(q, P, P, P, P, stats, dq, dk, P2, ws, ws_bytes, B, Hq, Hkv, Nq, Nk,
+                          D, 1, scale, dtype, 0)
+
+
+def test_bwd_validation(lib):
+    assert bwd(dtype=3) == DTYPE
+    assert bwd(Hq=3, Hkv=2) == GQA
+    assert bwd(D=80) == HEADDIM
+    assert bwd(scale=-0.5) == SCALE
+    assert bwd(q=None) == NULLPTR
+    assert bwd(dk=None) == NULLPTR
+    assert bwd(dq=P2 + 2) == ALIGN
+    assert bwd(stats=P + 1) == ALIGN
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(ws_bytes=16) == WORKSPACE
+    assert bwd(B=0) == OK
+
+
+def test_softmax_rows_validation(lib):
+    assert ra.ra_softmax_rows(P, P, 4, 4, 9, 0) == DTYPE
+    assert ra.ra_softmax_rows(P, P, -1, 4, ra.RA_F32, 0) == SHAPE
+    assert ra.ra_softmax_rows(P, P, 1 << 31, 4, ra.RA_F32, 0) == TOO_LARGE
+    assert ra.ra_softmax_rows(None, P, 4, 4, ra.RA_F32, 0) == NULLPTR
+    assert ra.ra_softmax_rows(P + 2, P, 4, 4, ra.RA_F32, 0) == ALIGN
+    assert ra.ra_softmax_rows(P, P, 0, 4, ra.RA_F32, 0) == OK
+    assert ra.ra_softmax_rows(P, P, 4, 0, ra.RA_F32, 0) == OK
+
+
+def test_product_path_has_no_fallback():
+    # The binding must not reach the oracle or any CPU implementation.
+    import rational_softmax_tiled_amd
+    src = open(rational_softmax_tiled_amd.__file__).read()
+    assert "oracle" not in src.replace("no CPU or PyTorch fallback", "")
+    for name in os.listdir(os.path.join(ROOT, "rational_softmax_tiled_amd", "csrc")):
+        text = open(os.path.join(ROOT, "rational_softmax_tiled_amd", "csrc", name)).read()
+        assert "oracle" not in text.lower(), name
