@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mode", choices=["fwd_bwd", "fwd"], default="fwd_bwd")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--cpu-heads", type=int, default=1,
+    ap.add_argument("--cpu-heads", type=int, default=3,
                     help="(batch, head) pairs of the workload the oracle times")
     return ap.parse_args()
 

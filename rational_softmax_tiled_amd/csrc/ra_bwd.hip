@@ -1,4 +1,26 @@
-// ra_bwd.hip -- backward rational-softmax attention for gfx950 (in progress).
+// ra_bwd.hip -- backward rational-softmax attention for gfx950.
+//
+// Gradients of L = sum(O * dO).  From "Ra-Family: Rational Neural Architecture", section 3:
+// the closed-form derivative d(phi)/du = -16 phi / (1 - u^2) (u < 1), evaluated from recomputed
+// scores and the saved row statistics (m, l) only ("closed-form backward recomputation").
+// With dP = dO V^T, c_i = dO_i . O_i and u = (m_i - s_ij) / 16 (scaled scores):
+//   G_ij = p_ij (dP_ij - c_i) / (1 - u^2) = (dP_ij - c_i) / l_i * q^7 / (1 + u)^2,
+// the second form having no division by 1 - u^2 (q = (1-u)/(1+u), so q^8 / (1 - u^2) =
+// q^7 / (1+u)^2), and G = 0 off the support.  Unlike exp, phi is not shift-equivariant: the
+// row max m_i = s_{i,a_i} carries R_i = -sum_j G_ij, so dS = G + R e_{a_i}, a_i the lowest key
+// index attaining the max.  dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO, with dK and dV
+// summed over the query heads that share a K/V head.
+//
+// Two kernels, no floating-point atomics (deterministic):
+//   1. query-parallel (the forward's decomposition and S^T = K Q^T layout, so scores are
+//      bit-identical to the forward's): c_i from O and dO, dP^T = V dO^T, G^T,
+//      dQ^T += K^T G^T with K^T staged transposed, R_i and a_i; its epilogue adds the
+//      row-max term scale * R_i * k_{a_i} to dQ and saves c, R, a.
+//   2. key-parallel (one wave owns 32 keys, S = Q K^T so keys sit on the lanes): recomputes
+//      P and G, adds R_i at (i, a_i), accumulates dV^T += dO^T P and dK^T += Q^T dS over all
+//      query rows of the group's heads, with Q^T and dO^T staged transposed.
+#include <limits.h>
+
 #include "ra_device.h"
 #include "ra_internal.h"
 
@@ -23,9 +45,437 @@ BwdWorkspace bwd_workspace_layout(void* base, int64_t B, int64_t Hq, int64_t Nq)
   return ws;
 }
 
-hipError_t launch_attn_bwd(const AttnProblem&, const void*, const void*, const float*, void*, void*,
-                           void*, const BwdWorkspace&, hipStream_t) {
-  return hipErrorNotSupported;
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* d_o;
+  const float* stats;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* c;
+  float* r;
+  int* amax;
+  int Hq, Hkv, Nq, Nk, rep;
+  int tasks_per_group, wg_per_group, total_wg;   // query-parallel kernel
+  int kwg_per_group, total_kwg;                  // key-parallel kernel
+  float scale, c16;                              // c16 = scale / 16
+};
+
+constexpr int kKeysPerWg = kWaves * kRowsPerWave;   // key-parallel kernel: 128 keys per workgroup
+constexpr int kQTile = 32;                           // query rows per step of the key-parallel kernel
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+
+// The direct gradient factor for one entry: (dP - c) / l * q^7 / (1+u)^2, given t = m - s in
+// raw units and dpc = (dP - c) / l.  q is clamped exactly as in the forward, so entries off the
+// support (and masked ones, t = +inf) give 0.  Also returns p = q^8 / l through *p.
+__device__ __forceinline__ float ra_grad_t(float t, float c16, float dpc, float il, float* p) {
+  const float d = fmaf(t, c16, 1.0f);
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = fminf(fmaxf(fmaf(r, 2.0f, -1.0f), 0.0f), 1.0f);
+  const float q2 = q * q;
+  const float q4 = q2 * q2;
+  const float q6 = q4 * q2;
+  *p = (q4 * q4) * il;
+  return dpc * ((q6 * q) * (r * r));
+}
+
+template <typename T>
+__device__ __forceinline__ void store_quad_scaled(T* dst, const f32x16& acc, int base, float s,
+                                                 const float* add, float radd);
+
+template <>
+__device__ __forceinline__ void store_quad_scaled<bf16>(bf16* dst, const f32x16& acc, int base,
+                                                        float s, const float* add, float radd) {
+  bf16x4 v = {(bf16)(s * fmaf(radd, add[0], acc[base])), (bf16)(s * fmaf(radd, add[1], acc[base + 1])),
+              (bf16)(s * fmaf(radd, add[2], acc[base + 2])), (bf16)(s * fmaf(radd, add[3], acc[base + 3]))};
+  *reinterpret_cast<bf16x4*>(dst) = v;
+}
+template <>
+__device__ __forceinline__ void store_quad_scaled<float>(float* dst, const f32x16& acc, int base,
+                                                         float s, const float* add, float radd) {
+  f32x4 v = {s * fmaf(radd, add[0], acc[base]), s * fmaf(radd, add[1], acc[base + 1]),
+             s * fmaf(radd, add[2], acc[base + 2]), s * fmaf(radd, add[3], acc[base + 3])};
+  *reinterpret_cast<f32x4*>(dst) = v;
+}
+
+// Sum of a fragment's elements (bf16: the rounded values, two per dot instruction).
+__device__ __forceinline__ float frag_sum(const bf16x8& f, float acc) {
+#pragma unroll
+  for (int j = 0; j < 8; j += 2)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[j], f[j + 1]}, bf16x2{(bf16)1.0f, (bf16)1.0f}, acc, false);
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(const f32x8& f, float acc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc += f[j];
+  return acc;
+}
+
+template <typename T> __device__ __forceinline__ typename Ty<T>::frag pack_frag(const f32x16& s, int ks);
+template <> __device__ __forceinline__ bf16x8 pack_frag<bf16>(const f32x16& s, int ks) { return pack_frag_bf16(s, ks); }
+template <> __device__ __forceinline__ f32x8 pack_frag<float>(const f32x16& s, int ks) { return pack_frag_f32(s, ks); }
+
+// ------------------------------------------------------------------ query-parallel: dQ, R, a
+
+template <typename T, int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
+  using frag_t = typename Ty<T>::frag;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int PK = D + PAD;
+  constexpr int PT = BN + PAD;
+  constexpr int KC = D / 16, SB = BN / 32, DB = D / 32;
+
+  __shared__ __attribute__((aligned(16))) T k_lds[BN * PK];
+  __shared__ __attribute__((aligned(16))) T v_lds[BN * PK];
+  __shared__ __attribute__((aligned(16))) T kt_lds[D * PT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int logical = xcd_remap(blockIdx.x, a.total_wg);
+  const int bg = logical / a.wg_per_group;
+  int wig = logical % a.wg_per_group;
+  if (CAUSAL) wig = a.wg_per_group - 1 - wig;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int task = wig * kWaves + wave;
+  const bool active = task < a.tasks_per_group;
+  const int h = g * a.rep + (active ? task % a.rep : 0);
+  const int q0 = (active ? task / a.rep : 0) * kRowsPerWave;
+  const int last_task = min(wig * kWaves + kWaves - 1, a.tasks_per_group - 1);
+  const int wg_qmax = min((last_task / a.rep) * kRowsPerWave + kRowsPerWave - 1, a.Nq - 1);
+  const int nt = ((CAUSAL ? min(a.Nk, wg_qmax + 1) : a.Nk) + BN - 1) / BN;
+  const int wave_qmax = min(q0 + kRowsPerWave - 1, a.Nq - 1);
+  const int nt_w = !active ? 0 : ((CAUSAL ? min(a.Nk, wave_qmax + 1) : a.Nk) + BN - 1) / BN;
+
+  const size_t head = (size_t)(b * a.Hq + h) * a.Nq;
+  const T* kg = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Nk * D;
+  const T* vg = static_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Nk * D;
+  const int qi = q0 + (lane & 31);
+  const int qrow = min(qi, a.Nq - 1);
+  const int frow = lane & 31, fcol = 8 * (lane >> 5);
+
+  const T* qp = static_cast<const T*>(a.q) + (head + qrow) * D;
+  const T* dop = static_cast<const T*>(a.d_o) + (head + qrow) * D;
+  const T* op = static_cast<const T*>(a.o) + (head + qrow) * D;
+  frag_t qf[KC], df[KC];
+  float cpart = 0.0f;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    qf[kc] = load_frag(qp + 16 * kc + fcol);
+    df[kc] = load_frag(dop + 16 * kc + fcol);
+    const frag_t of = load_frag(op + 16 * kc + fcol);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cpart = fmaf(to_f(df[kc][j]), to_f(of[j]), cpart);
+  }
+  const float cval = cpart + __shfl_xor(cpart, 32);   // c_i = dO_i . O_i
+  const float m = a.stats[(head + qrow) * 2];
+  const float l = a.stats[(head + qrow) * 2 + 1];
+  const float il = l > 0.0f ? 1.0f / l : 0.0f;
+  const float cil = cval * il;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float rsum = 0.0f;
+  int amax = INT_MAX;
+
+  for (int kt = 0; kt < nt; ++kt) {
+    __syncthreads();
+    const T* kt_g = kg + (size_t)kt * BN * D;
+    stage_rows<T, D, BN, PK>(k_lds, kt_g, a.Nk - kt * BN, tid);
+    stage_rows<T, D, BN, PK>(v_lds, vg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
+    stage_rows_transposed<T, D, BN, PT>(kt_lds, kt_g, a.Nk - kt * BN, tid);
+    __syncthreads();
+    if (kt >= nt_w) continue;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) mma(s, load_frag(k_lds + (sb * 32 + frow) * PK + 16 * kc + fcol), qf[kc]);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) mma(dp, load_frag(v_lds + (sb * 32 + frow) * PK + 16 * kc + fcol), df[kc]);
+      const int key0 = kt * BN + sb * 32;
+      if ((CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + acc_row(i, lane);
+          if (key >= a.Nk || (CAUSAL && key > qrow)) s[i] = -INFINITY;
+        }
+      }
+      // lowest key attaining the row max (rare: only the tile holding it takes the branch)
+      float lm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lm = fmaxf(lm, s[i]);
+      if (__any(lm == m)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (s[i] == m) amax = min(amax, key0 + acc_row(i, lane));
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p;
+        s[i] = ra_grad_t(m - s[i], a.c16, fmaf(dp[i], il, -cil), il, &p);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const frag_t gf = pack_frag<T>(s, ks);
+        rsum = frag_sum(gf, rsum);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          mma(acc[db], load_frag(kt_lds + (db * 32 + frow) * PT + sb * 32 + 16 * ks + fcol), gf);
+      }
+    }
+  }
+
+  const float R = -(rsum + __shfl_xor(rsum, 32));
+  amax = min(amax, __shfl_xor(amax, 32));
+  if (active && qi < a.Nq) {
+    T* dqrow = static_cast<T*>(a.dq) + (head + qi) * D;
+    const bool has_max = amax < a.Nk;
+    const T* krow = kg + (size_t)(has_max ? amax : 0) * D;
+    const float radd = has_max ? R : 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
+        float kv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[e] = to_f(krow[d0 + e]);
+        store_quad_scaled<T>(dqrow + d0, acc[db], 4 * r4, a.scale, kv, radd);
+      }
+    if (lane < 32) {
+      a.c[head + qi] = cval;
+      a.r[head + qi] = R;
+      a.amax[head + qi] = has_max ? amax : -1;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ key-parallel: dK, dV
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
+  using frag_t = typename Ty<T>::frag;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int PQ = D + PAD;
+  constexpr int PT = kQTile + PAD;
+  constexpr int KC = D / 16, DB = D / 32;
+  // Q and dO row tiles (A operands of S and dP) go through LDS unless that would push the
+  // static LDS past 64 KiB (fp32, D = 128): then the fragments are read from global memory.
+  constexpr bool ROWS_IN_LDS = sizeof(T) == 2 || D == 64;
+  constexpr int ROW_TILE = ROWS_IN_LDS ? kQTile * PQ : 8;
+
+  __shared__ __attribute__((aligned(16))) T q_lds[ROW_TILE];
+  __shared__ __attribute__((aligned(16))) T do_lds[ROW_TILE];
+  __shared__ __attribute__((aligned(16))) T qt_lds[D * PT];
+  __shared__ __attribute__((aligned(16))) T dot_lds[D * PT];
+  __shared__ __attribute__((aligned(16))) float st_m[kQTile];
+  __shared__ __attribute__((aligned(16))) float st_il[kQTile];
+  __shared__ __attribute__((aligned(16))) float st_cil[kQTile];
+  __shared__ __attribute__((aligned(16))) float st_r[kQTile];
+  __shared__ __attribute__((aligned(16))) int st_a[kQTile];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int logical = xcd_remap(blockIdx.x, a.total_kwg);
+  const int bg = logical / a.kwg_per_group;
+  const int kb = logical % a.kwg_per_group;   // low key blocks (most causal work) first
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int key0_wg = kb * kKeysPerWg;
+  const int j0 = key0_wg + wave * kRowsPerWave;
+  const bool active = j0 < a.Nk;
+  const int frow = lane & 31, fcol = 8 * (lane >> 5);
+  const int key = j0 + frow;
+  const int krow = min(key, a.Nk - 1);
+
+  const size_t kvbase = (size_t)(b * a.Hkv + g) * a.Nk;
+  const T* kp = static_cast<const T*>(a.k) + (kvbase + krow) * D;
+  const T* vp = static_cast<const T*>(a.v) + (kvbase + krow) * D;
+  frag_t kf[KC], vf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    kf[kc] = load_frag(kp + 16 * kc + fcol);
+    vf[kc] = load_frag(vp + 16 * kc + fcol);
+  }
+  f32x16 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    acc_dk[db] = f32x16{};
+    acc_dv[db] = f32x16{};
+  }
+
+  const int nqt = (a.Nq + kQTile - 1) / kQTile;
+  const int qt0 = CAUSAL ? min(key0_wg / kQTile, nqt) : 0;
+  for (int hh = 0; hh < a.rep; ++hh) {
+    const int h = g * a.rep + hh;
+    const size_t head = (size_t)(b * a.Hq + h) * a.Nq;
+    const T* qh = static_cast<const T*>(a.q) + head * D;
+    const T* doh = static_cast<const T*>(a.d_o) + head * D;
+    for (int qt = qt0; qt < nqt; ++qt) {
+      const int i0 = qt * kQTile;
+      __syncthreads();
+      if constexpr (ROWS_IN_LDS) {
+        stage_rows<T, D, kQTile, PQ>(q_lds, qh + (size_t)i0 * D, a.Nq - i0, tid);
+        stage_rows<T, D, kQTile, PQ>(do_lds, doh + (size_t)i0 * D, a.Nq - i0, tid);
+      }
+      stage_rows_transposed<T, D, kQTile, PT>(qt_lds, qh + (size_t)i0 * D, a.Nq - i0, tid);
+      stage_rows_transposed<T, D, kQTile, PT>(dot_lds, doh + (size_t)i0 * D, a.Nq - i0, tid);
+      if (tid < kQTile) {
+        const int qi = i0 + tid;
+        if (qi < a.Nq) {
+          const float l = a.stats[(head + qi) * 2 + 1];
+          const float il = l > 0.0f ? 1.0f / l : 0.0f;
+          st_m[tid] = a.stats[(head + qi) * 2];
+          st_il[tid] = il;
+          st_cil[tid] = a.c[head + qi] * il;
+          st_r[tid] = a.r[head + qi];
+          st_a[tid] = a.amax[head + qi];
+        } else {
+          st_m[tid] = 0.0f;
+          st_il[tid] = 0.0f;
+          st_cil[tid] = 0.0f;
+          st_r[tid] = 0.0f;
+          st_a[tid] = -1;
+        }
+      }
+      __syncthreads();
+      if (!active || (CAUSAL && i0 + kQTile - 1 < j0)) continue;
+      f32x16 s = {}, dp = {};
+      if constexpr (ROWS_IN_LDS) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) mma(s, load_frag(q_lds + frow * PQ + 16 * kc + fcol), kf[kc]);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) mma(dp, load_frag(do_lds + frow * PQ + 16 * kc + fcol), vf[kc]);
+      } else {
+        const int qr = min(i0 + frow, a.Nq - 1);   // rows past Nq are masked below
+        const T* qrp = qh + (size_t)qr * D + fcol;
+        const T* dorp = doh + (size_t)qr * D + fcol;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) mma(s, load_frag(qrp + 16 * kc), kf[kc]);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) mma(dp, load_frag(dorp + 16 * kc), vf[kc]);
+      }
+      const bool edge = (CAUSAL && j0 + 31 > i0) || i0 + kQTile > a.Nq || j0 + 32 > a.Nk;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r0 = 8 * i4 + 4 * (lane >> 5);   // four consecutive query rows of this lane
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(st_m + r0);
+        const f32x4 il4 = *reinterpret_cast<const f32x4*>(st_il + r0);
+        const f32x4 cil4 = *reinterpret_cast<const f32x4*>(st_cil + r0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          float sv = s[i];
+          if (edge) {
+            const int qi = i0 + r0 + e;
+            if (key >= a.Nk || qi >= a.Nq || (CAUSAL && key > qi)) sv = -INFINITY;
+          }
+          float p;
+          const float gv = ra_grad_t(m4[e] - sv, a.c16, fmaf(dp[i], il4[e], -cil4[e]), il4[e], &p);
+          s[i] = p;
+          dp[i] = gv;
+        }
+      }
+      // row-max term: R_i joins dS at the lowest argmax key of row i
+      {
+        const int am = st_a[lane & 31];
+        if (__any(am >= j0 && am < j0 + 32)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = acc_row(i, lane);
+            if (st_a[r] == key) dp[i] += st_r[r];
+          }
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const frag_t pf = pack_frag<T>(s, ks);
+        const frag_t gf = pack_frag<T>(dp, ks);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          mma(acc_dv[db], load_frag(dot_lds + (db * 32 + frow) * PT + 16 * ks + fcol), pf);
+          mma(acc_dk[db], load_frag(qt_lds + (db * 32 + frow) * PT + 16 * ks + fcol), gf);
+        }
+      }
+    }
+  }
+
+  if (active && key < a.Nk) {
+    T* dkrow = static_cast<T*>(a.dk) + (kvbase + key) * D;
+    T* dvrow = static_cast<T*>(a.dv) + (kvbase + key) * D;
+    const float zero4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
+        store_quad_scaled<T>(dkrow + d0, acc_dk[db], 4 * r4, a.scale, zero4, 0.0f);
+        store_quad_scaled<T>(dvrow + d0, acc_dv[db], 4 * r4, 1.0f, zero4, 0.0f);
+      }
+  }
+}
+
+template <typename T, int D, int BN>
+static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const void* d_o,
+                                   const float* stats, void* dq, void* dk, void* dv,
+                                   const BwdWorkspace& ws, hipStream_t stream) {
+  BwdArgs a;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.o = o;
+  a.d_o = d_o;
+  a.stats = stats;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.c = ws.c;
+  a.r = ws.r;
+  a.amax = ws.amax;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.Nq = p.Nq;
+  a.Nk = p.Nk;
+  a.rep = p.Hq / p.Hkv;
+  a.tasks_per_group = a.rep * ((p.Nq + kRowsPerWave - 1) / kRowsPerWave);
+  a.wg_per_group = (a.tasks_per_group + kWaves - 1) / kWaves;
+  a.total_wg = p.B * p.Hkv * a.wg_per_group;
+  a.kwg_per_group = (p.Nk + kKeysPerWg - 1) / kKeysPerWg;
+  a.total_kwg = p.B * p.Hkv * a.kwg_per_group;
+  a.scale = p.scale;
+  a.c16 = p.scale / 16.0f;
+  dim3 block(kThreads);
+  if (p.causal) {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true>), dim3(a.total_wg), block, 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), dim3(a.total_kwg), block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false>), dim3(a.total_wg), block, 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), dim3(a.total_kwg), block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const AttnProblem& p, const void* o, const void* d_o,
+                           const float* stats, void* dq, void* dk, void* dv,
+                           const BwdWorkspace& ws, hipStream_t stream) {
+  if (stats == nullptr) {   // recompute (m, l) with the forward's statistics-only variant
+    hipError_t e = launch_attn_fwd(p, nullptr, ws.stats, nullptr, stream);
+    if (e != hipSuccess) return e;
+    stats = ws.stats;
+  }
+  if (p.bf16) {
+    if (p.D == 64) return launch_bwd_typed<bf16, 64, 64>(p, o, d_o, stats, dq, dk, dv, ws, stream);
+    return launch_bwd_typed<bf16, 128, 64>(p, o, d_o, stats, dq, dk, dv, ws, stream);
+  }
+  if (p.D == 64) return launch_bwd_typed<float, 64, 32>(p, o, d_o, stats, dq, dk, dv, ws, stream);
+  return launch_bwd_typed<float, 128, 32>(p, o, d_o, stats, dq, dk, dv, ws, stream);
 }
 
 }  // namespace ra

@@ -66,7 +66,7 @@ __device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int la
   }
 }
 
-template <typename T, int D, int BN, bool CAUSAL, bool COUNT>
+template <typename T, int D, int BN, bool CAUSAL, bool COUNT, bool WRITE_O>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   using frag_t = typename Ty<T>::frag;
   constexpr int PAD = 16 / sizeof(T);
@@ -182,7 +182,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
     if (all_skip) continue;   // uniform: every thread read the same LDS values
     __syncthreads();
     stage_rows<T, D, BN, PK>(k_lds, kg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
-    stage_rows_transposed<T, D, BN, PV>(vt_lds, vg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
+    if constexpr (WRITE_O)
+      stage_rows_transposed<T, D, BN, PV>(vt_lds, vg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
     __syncthreads();
     if (my_skip) continue;
 #pragma unroll
@@ -211,9 +212,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) lsum += pf[j];
         }
+        if constexpr (WRITE_O) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          mma(oacc[db], load_frag(vt_lds + (db * 32 + frow) * PV + sb * 32 + 16 * ks + fcol), pf);
+          for (int db = 0; db < DB; ++db)
+            mma(oacc[db], load_frag(vt_lds + (db * 32 + frow) * PV + sb * 32 + 16 * ks + fcol), pf);
+        }
       }
     }
   }
@@ -222,12 +225,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const float ltot = lsum + __shfl_xor(lsum, 32);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   if (active && qi < a.Nq) {
-    T* orow = static_cast<T*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qi) * D;
+    if constexpr (WRITE_O) {
+      T* orow = static_cast<T*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qi) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        store_quad<T>(orow + db * 32 + 8 * r4 + 4 * (lane >> 5), oacc[db], 4 * r4, inv);
+        for (int r4 = 0; r4 < 4; ++r4)
+          store_quad<T>(orow + db * 32 + 8 * r4 + 4 * (lane >> 5), oacc[db], 4 * r4, inv);
+    }
     if (a.stats != nullptr && lane < 32) {
       float* st = a.stats + ((size_t)(b * a.Hq + h) * a.Nq + qi) * 2;
       st[0] = mx;
@@ -264,12 +269,15 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   a.total_wg = p.B * p.Hkv * a.wg_per_group;
   a.c = p.scale / 16.0f;
   dim3 grid(a.total_wg), block(kThreads);
-  if (p.causal) {
-    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false>), grid, block, 0, stream, a);
+  if (o == nullptr) {   // statistics only (m, l), for a backward without saved stats
+    if (p.causal) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, false>), grid, block, 0, stream, a);
+  } else if (p.causal) {
+    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, true>), grid, block, 0, stream, a);
   } else {
-    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false>), grid, block, 0, stream, a);
+    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, true>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

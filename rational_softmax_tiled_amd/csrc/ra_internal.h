@@ -18,7 +18,8 @@ struct AttnProblem {
   bool bf16;  // false: fp32
 };
 
-// Forward: o (and stats when non-null); counters non-null selects the counting variant.
+// Forward: o (and stats when non-null); counters non-null selects the counting variant;
+// o == nullptr computes the statistics only (stats must then be non-null).
 hipError_t launch_attn_fwd(const AttnProblem& p, void* o, float* stats,
                            unsigned long long* counters, hipStream_t stream);
 
