@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-heads", type=int, default=3,
                     help="(batch, head) pairs of the workload the oracle times")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -135,6 +137,16 @@ def main():
     ra.load_library()
     dev = torch.cuda.get_device_properties(0)
     log(f"device {dev.name} CUs={dev.multi_processor_count} arch={getattr(dev, 'gcnArchName', '?')}")
+
+    if args.copy_calibration:
+        # a plain copy kernel of known size: 256 MiB read + 256 MiB written
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 268435456 bytes read, 268435456 bytes written")
+        del src, dst
 
     w = wl.WORKLOADS[MAIN]
     need_grad = args.mode == "fwd_bwd"

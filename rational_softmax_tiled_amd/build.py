@@ -29,6 +29,8 @@ COMMON_FLAGS = [
     "-fPIC",
     # keep the compiler from forming packed fp32 VALU instructions (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results feed VALU math directly: keep accumulators in VGPRs (no AGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
     "-I", INCLUDE,

@@ -100,16 +100,26 @@ __device__ __host__ constexpr int quad_slot(int quad) {   // quad = 4 consecutiv
 
 // ---------------------------------------------------------------- rational softmax
 
-// phi for one entry: t = m - s in raw dot-product units (>= 0, +inf for a masked entry),
-// c = scale / 16.  u = t * c; q = (1-u)/(1+u) = 2/(1+u) - 1, clamped to [0, 1] so that
-// u >= 1 gives exactly 0; phi = q^8 by three squarings.  ("Ra-Family: Rational Neural
-// Architecture", section 3, ra_softmax.)
+// phi for one entry from the raw score s, with c = scale / 16 and kd = 1 + m * c for the row's
+// raw max m: 1 + u = fma(s, -c, kd) (+inf for a masked entry, s = -inf); q = (1-u)/(1+u) =
+// 2/(1+u) - 1, clamped to [0, 1] so that u >= 1 gives exactly 0; phi = q^8 by three squarings.
+// ("Ra-Family: Rational Neural Architecture", section 3, ra_softmax.)
+__device__ __forceinline__ float ra_phi(float s, float c, float kd) {
+  const float d = fmaf(s, -c, kd);
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = fminf(fmaxf(fmaf(r, 2.0f, -1.0f), 0.0f), 1.0f);
+  const float q2 = q * q;
+  const float q4 = q2 * q2;
+  return q4 * q4;
+}
+
+// The same with Delta given directly in units where u = t * c (t >= 0, +inf when masked).
 __device__ __forceinline__ float ra_phi_t(float t, float c) {
-  float d = fmaf(t, c, 1.0f);
-  float r = __builtin_amdgcn_rcpf(d);
-  float q = fminf(fmaxf(fmaf(r, 2.0f, -1.0f), 0.0f), 1.0f);
-  float q2 = q * q;
-  float q4 = q2 * q2;
+  const float d = fmaf(t, c, 1.0f);
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = fminf(fmaxf(fmaf(r, 2.0f, -1.0f), 0.0f), 1.0f);
+  const float q2 = q * q;
+  const float q4 = q2 * q2;
   return q4 * q4;
 }
 
@@ -163,16 +173,19 @@ __device__ __forceinline__ void stage_rows(T* lds, const T* g, int nvalid, int t
 
 // Copy `ROWS` rows of a row-major [*, D] tile into LDS transposed: lds[d * PITCH + slot(row)],
 // with the slot order of key_slot inside every 32-row block.  Each thread moves a 4-row x
-// 8-column block: four 8-element global loads, eight 4-element LDS stores.
+// 8-column block: four 8-element global loads, eight 4-element LDS stores.  Consecutive lanes
+// take consecutive row quads of one column chunk, so the 16 lanes of an LDS store cycle fill
+// one contiguous slot row (no bank conflicts whatever the pitch).
 template <typename T, int D, int ROWS, int PITCH>
 __device__ __forceinline__ void stage_rows_transposed(T* lds, const T* g, int nvalid, int tid) {
   using quad_t = typename Ty<T>::quad;
-  constexpr int UNITS = (ROWS / 4) * (D / 8);
+  constexpr int QUADS = ROWS / 4;
+  constexpr int UNITS = QUADS * (D / 8);
 #pragma unroll
   for (int it = 0; it < (UNITS + kThreads - 1) / kThreads; ++it) {
     const int u = it * kThreads + tid;
     if (UNITS % kThreads == 0 || u < UNITS) {
-      const int quad = u / (D / 8), dc = u % (D / 8);
+      const int quad = u % QUADS, dc = u / QUADS;
       typename Ty<T>::frag rows[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -188,5 +201,82 @@ __device__ __forceinline__ void stage_rows_transposed(T* lds, const T* g, int nv
     }
   }
 }
+
+// ---------------------------------------------------------------- register-staged tiles
+// Two-phase versions of the stagers: load() issues the global loads into registers (they stay
+// in flight while the caller computes), store() writes them to LDS.  With two LDS buffers this
+// gives one barrier per tile and hides the global-load latency behind the tile's math.
+
+template <typename T, int D, int ROWS>
+struct RowTile {
+  static constexpr int CE = 16 / sizeof(T);
+  static constexpr int CPR = D / CE;
+  static constexpr int TOTAL = ROWS * CPR;
+  static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
+  u32x4 v[PER];
+
+  __device__ __forceinline__ void load(const T* g, int nvalid, int tid) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = it * kThreads + tid;
+      const int r = c / CPR, cc = c % CPR;
+      v[it] = u32x4{0u, 0u, 0u, 0u};
+      if ((TOTAL % kThreads == 0 || c < TOTAL) && r < nvalid)
+        v[it] = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + cc * CE);
+    }
+  }
+  template <int PITCH>
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = it * kThreads + tid;
+      if (TOTAL % kThreads == 0 || c < TOTAL) {
+        const int r = c / CPR, cc = c % CPR;
+        *reinterpret_cast<u32x4*>(lds + r * PITCH + cc * CE) = v[it];
+      }
+    }
+  }
+};
+
+template <typename T, int D, int ROWS>
+struct TransTile {
+  using frag_t = typename Ty<T>::frag;
+  using quad_t = typename Ty<T>::quad;
+  static constexpr int QUADS = ROWS / 4;
+  static constexpr int UNITS = QUADS * (D / 8);
+  static constexpr int PER = (UNITS + kThreads - 1) / kThreads;
+  frag_t rows[PER][4];
+
+  __device__ __forceinline__ void load(const T* g, int nvalid, int tid) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int u = it * kThreads + tid;
+      const int quad = u % QUADS, dc = u / QUADS;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * quad + r;
+        rows[it][r] = zero_frag<T>();
+        if ((UNITS % kThreads == 0 || u < UNITS) && row < nvalid)
+          rows[it][r] = load_frag(g + (size_t)row * D + 8 * dc);
+      }
+    }
+  }
+  template <int PITCH>
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int u = it * kThreads + tid;
+      if (UNITS % kThreads == 0 || u < UNITS) {
+        const int quad = u % QUADS, dc = u / QUADS;
+        const int slot = quad_slot(quad);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          quad_t col = {rows[it][0][e], rows[it][1][e], rows[it][2][e], rows[it][3][e]};
+          *reinterpret_cast<quad_t*>(lds + (8 * dc + e) * PITCH + slot) = col;
+        }
+      }
+    }
+  }
+};
 
 }  // namespace ra

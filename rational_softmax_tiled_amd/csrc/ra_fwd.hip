@@ -16,8 +16,9 @@
 //     P^T operand of O^T = V^T P^T stay in that lane, with no register shuffle.  V^T is staged
 //     transposed in LDS in the slot order that matches the accumulator layout.
 //   * Pass 1 keeps, per wave and key tile, the max score of the tile; after pass 1 a tile is
-//     skipped for a wave when (min_i m_i - tile max) * scale / 16 >= 1, evaluated with the same
-//     floating-point steps as phi itself, so skipping never changes a result bit.  A tile
+//     skipped for a wave when 1 + u >= 2 already at the tile max against the smallest row max
+//     of the wave, evaluated with the same monotone floating-point steps as phi itself, so
+//     skipping never changes a result bit.  A tile
 //     skipped by all four waves is not even loaded.  Causal tiles beyond a wave's diagonal are
 //     recorded as -inf and skipped the same way.
 #include "ra_device.h"
@@ -66,6 +67,16 @@ __device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int la
   }
 }
 
+// S^T block (32 keys x 32 query rows) of key sub-block sb of the staged K tile.
+template <typename T, int D, int PK>
+__device__ __forceinline__ f32x16 score_block(const T* k_tile, const typename Ty<T>::frag* qf, int sb,
+                                              int frow, int fcol) {
+  f32x16 s = {};
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) mma(s, load_frag(k_tile + (sb * 32 + frow) * PK + 16 * kc + fcol), qf[kc]);
+  return s;
+}
+
 template <typename T, int D, int BN, bool CAUSAL, bool COUNT, bool WRITE_O>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   using frag_t = typename Ty<T>::frag;
@@ -76,10 +87,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   constexpr int SB = BN / 32;    // 32-key blocks per tile
   constexpr int DB = D / 32;     // 32-row blocks of O^T
 
-  __shared__ __attribute__((aligned(16))) T k_lds[BN * PK];
-  __shared__ __attribute__((aligned(16))) T vt_lds[D * PV];
+  __shared__ __attribute__((aligned(16))) T k_lds[2][BN * PK];
+  __shared__ __attribute__((aligned(16))) T vt_lds[WRITE_O ? 2 : 1][WRITE_O ? D * PV : 8];
   __shared__ float tmax_lds[kWaves][kMaxTiles];
-  __shared__ float mmin_lds[kWaves];
+  __shared__ float kmin_lds[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -115,22 +126,26 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const int frow = lane & 31;           // A-fragment row inside a 32-row block
   const int fcol = 8 * (lane >> 5);     // A-fragment column offset
 
-  // ---- pass 1: row max of the raw dot products
+  auto needs_mask = [&](int key0) { return (CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk; };
+
+  // ---- pass 1: row max of the raw dot products (K tiles double-buffered through LDS)
+  RowTile<T, D, BN> kreg;
   float mx = -INFINITY;
+  if (nt > 0) {
+    kreg.load(kg, a.Nk, tid);
+    kreg.template store<PK>(k_lds[0], tid);
+  }
+  __syncthreads();
   for (int kt = 0; kt < nt; ++kt) {
-    __syncthreads();
-    stage_rows<T, D, BN, PK>(k_lds, kg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
-    __syncthreads();
+    const int buf = kt & 1;
+    if (kt + 1 < nt) kreg.load(kg + (size_t)(kt + 1) * BN * D, a.Nk - (kt + 1) * BN, tid);
     float tl = -INFINITY;
     if (kt < nt_w) {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
-        f32x16 s = {};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          mma(s, load_frag(k_lds + (sb * 32 + frow) * PK + 16 * kc + fcol), qf[kc]);
+        f32x16 s = score_block<T, D, PK>(k_lds[buf], qf, sb, frow, fcol);
         const int key0 = kt * BN + sb * 32;
-        if ((CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk) mask_block<CAUSAL>(s, key0, qrow, lane, a.Nk);
+        if (needs_mask(key0)) mask_block<CAUSAL>(s, key0, qrow, lane, a.Nk);
 #pragma unroll
         for (int i = 0; i < 16; ++i) tl = fmaxf(tl, s[i]);
       }
@@ -140,85 +155,108 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
       const float wm = wave_max(tl);
       if (lane == 0) tmax_lds[wave][kt] = wm;
     }
+    if (kt + 1 < nt) kreg.template store<PK>(k_lds[buf ^ 1], tid);
+    __syncthreads();
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));   // lanes l and l+32 hold the same query row
+  // 1 + u = fma(s, -c, kd) with kd = 1 + m c; the smallest kd of the wave bounds every row
+  const float kd = fmaf(mx, a.c, 1.0f);
   {
-    const float mm = wave_min(mx);
-    if (lane == 0) mmin_lds[wave] = mm;
+    const float km = wave_min(kd);
+    if (lane == 0) kmin_lds[wave] = km;
   }
   __syncthreads();
+
+  // A tile is skipped for a wave when every entry has 1 + u >= fma(tile max, -c, min kd) >= 2
+  // (phi = 0), and not even loaded when that holds for all four waves.
+  auto wave_skips = [&](int w, int kt) -> bool {
+    const float tm = tmax_lds[w][kt];
+    return (tm == -INFINITY) || (fmaf(tm, -a.c, kmin_lds[w]) >= 2.0f);
+  };
+  auto wg_skips = [&](int kt) -> bool {
+    if (kt >= kMaxTiles) return false;
+    bool all = true;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) all = all && wave_skips(w, kt);
+    return all;
+  };
 
   // ---- pass 2: phi, sum(phi), O^T = V^T P^T
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float lsum = 0.0f;
-  unsigned long long n_wave_tiles = 0, n_wave_skip = 0, n_wg_tiles = 0, n_wg_skip = 0;
+  unsigned long long n_wave_tiles = 0, n_wave_skip = 0, n_wg_skip = 0;
 
-  for (int kt = 0; kt < nt; ++kt) {
-    bool my_skip, all_skip;
-    if (kt < kMaxTiles) {
-      all_skip = true;
-      my_skip = false;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float tm = tmax_lds[w][kt];
-        const bool s = (tm == -INFINITY) || (fmaf(mmin_lds[w] - tm, a.c, 1.0f) >= 2.0f);
-        all_skip = all_skip && s;
-        if (w == wave) my_skip = s;
-      }
-    } else {
-      my_skip = kt >= nt_w;
-      all_skip = false;
+  TransTile<T, D, BN> vreg;
+  int cur = 0;
+  while (cur < nt && wg_skips(cur)) ++cur;
+  if (COUNT) n_wg_skip += cur;
+  if (cur < nt) {
+    kreg.load(kg + (size_t)cur * BN * D, a.Nk - cur * BN, tid);
+    kreg.template store<PK>(k_lds[0], tid);
+    if constexpr (WRITE_O) {
+      vreg.load(vg + (size_t)cur * BN * D, a.Nk - cur * BN, tid);
+      vreg.template store<PV>(vt_lds[0], tid);
     }
-    if (COUNT) {
-      n_wg_tiles += 1;
-      n_wg_skip += all_skip ? 1 : 0;
-      if (kt < nt_w) {
-        n_wave_tiles += 1;
-        n_wave_skip += my_skip ? 1 : 0;
-      }
+  }
+  __syncthreads();
+  int buf = 0;
+  while (cur < nt) {
+    int nxt = cur + 1;
+    while (nxt < nt && wg_skips(nxt)) ++nxt;
+    if (COUNT) n_wg_skip += nxt - cur - 1;
+    if (nxt < nt) {
+      kreg.load(kg + (size_t)nxt * BN * D, a.Nk - nxt * BN, tid);
+      if constexpr (WRITE_O) vreg.load(vg + (size_t)nxt * BN * D, a.Nk - nxt * BN, tid);
     }
-    if (all_skip) continue;   // uniform: every thread read the same LDS values
-    __syncthreads();
-    stage_rows<T, D, BN, PK>(k_lds, kg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
-    if constexpr (WRITE_O)
-      stage_rows_transposed<T, D, BN, PV>(vt_lds, vg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
-    __syncthreads();
-    if (my_skip) continue;
+    const bool my_skip = cur < kMaxTiles ? wave_skips(wave, cur) : cur >= nt_w;
+    if (COUNT && cur < nt_w) {
+      n_wave_tiles += 1;
+      n_wave_skip += my_skip ? 1 : 0;
+    }
+    if (!my_skip) {
+      // both score blocks first, so the phi math of one overlaps the products of the other
+      f32x16 s[SB];
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      f32x16 s = {};
+      for (int sb = 0; sb < SB; ++sb) s[sb] = score_block<T, D, PK>(k_lds[buf], qf, sb, frow, fcol);
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        mma(s, load_frag(k_lds + (sb * 32 + frow) * PK + 16 * kc + fcol), qf[kc]);
-      const int key0 = kt * BN + sb * 32;
-      if ((CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk) mask_block<CAUSAL>(s, key0, qrow, lane, a.Nk);
+      for (int sb = 0; sb < SB; ++sb) {
+        const int key0 = cur * BN + sb * 32;
+        if (needs_mask(key0)) mask_block<CAUSAL>(s[sb], key0, qrow, lane, a.Nk);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = ra_phi_t(mx - s[i], a.c);
+        for (int i = 0; i < 16; ++i) s[sb][i] = ra_phi(s[sb][i], a.c, kd);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        frag_t pf;
-        if constexpr (sizeof(T) == 2) {
-          pf = pack_frag_bf16(s, ks);
-          // sum the rounded probabilities that enter the product, two per instruction
+        for (int ks = 0; ks < 2; ++ks) {
+          frag_t pf;
+          if constexpr (sizeof(T) == 2) {
+            pf = pack_frag_bf16(s[sb], ks);
+            // sum the rounded probabilities that enter the product, two per instruction
 #pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            bf16x2 pr = {pf[j], pf[j + 1]};
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(bf16)1.0f, (bf16)1.0f}, lsum, false);
+            for (int j = 0; j < 8; j += 2) {
+              bf16x2 pr = {pf[j], pf[j + 1]};
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(bf16)1.0f, (bf16)1.0f}, lsum, false);
+            }
+          } else {
+            pf = pack_frag_f32(s[sb], ks);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) lsum += pf[j];
           }
-        } else {
-          pf = pack_frag_f32(s, ks);
+          if constexpr (WRITE_O) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) lsum += pf[j];
-        }
-        if constexpr (WRITE_O) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            mma(oacc[db], load_frag(vt_lds + (db * 32 + frow) * PV + sb * 32 + 16 * ks + fcol), pf);
+            for (int db = 0; db < DB; ++db)
+              mma(oacc[db], load_frag(vt_lds[buf] + (db * 32 + frow) * PV + sb * 32 + 16 * ks + fcol), pf);
+          }
         }
       }
     }
+    if (nxt < nt) {
+      kreg.template store<PK>(k_lds[buf ^ 1], tid);
+      if constexpr (WRITE_O) vreg.template store<PV>(vt_lds[buf ^ 1], tid);
+    }
+    __syncthreads();
+    buf ^= 1;
+    cur = nxt;
   }
 
   // ---- epilogue: O = acc / l
@@ -243,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
     atomicAdd(a.counters + 0, n_wave_tiles);
     atomicAdd(a.counters + 1, n_wave_skip);
     if (wave == 0) {
-      atomicAdd(a.counters + 2, n_wg_tiles);
+      atomicAdd(a.counters + 2, (unsigned long long)nt);
       atomicAdd(a.counters + 3, n_wg_skip);
     }
   }
