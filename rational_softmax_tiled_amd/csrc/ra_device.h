@@ -206,6 +206,34 @@ __device__ __forceinline__ void stage_rows_transposed(T* lds, const T* g, int nv
 // Two-phase versions of the stagers: load() issues the global loads into registers (they stay
 // in flight while the caller computes), store() writes them to LDS.  With two LDS buffers this
 // gives one barrier per tile and hides the global-load latency behind the tile's math.
+// Loads go through a buffer resource whose size is the tile's valid rows: the hardware returns
+// zeros past it, so ragged tails need no per-lane branch.
+
+// Buffer resource word 3 for raw (untyped) dword loads on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* base, int valid_rows, int D) {
+  const int bytes = valid_rows > 0 ? valid_rows * D * (int)sizeof(T) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Ty<T>::frag buf_load_frag(__amdgpu_buffer_rsrc_t r, int elem_off) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 v = buf_load16(r, elem_off * 2);
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    const u32x4 lo = buf_load16(r, elem_off * 4);
+    const u32x4 hi = buf_load16(r, elem_off * 4 + 16);
+    const f32x4 flo = __builtin_bit_cast(f32x4, lo), fhi = __builtin_bit_cast(f32x4, hi);
+    return f32x8{flo[0], flo[1], flo[2], flo[3], fhi[0], fhi[1], fhi[2], fhi[3]};
+  }
+}
 
 template <typename T, int D, int ROWS>
 struct RowTile {
@@ -215,14 +243,13 @@ struct RowTile {
   static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
   u32x4 v[PER];
 
+  // rows [0, nvalid) of the tile at g; the rest read as zeros
   __device__ __forceinline__ void load(const T* g, int nvalid, int tid) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(g, min(nvalid, ROWS), D);
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int c = it * kThreads + tid;
-      const int r = c / CPR, cc = c % CPR;
-      v[it] = u32x4{0u, 0u, 0u, 0u};
-      if ((TOTAL % kThreads == 0 || c < TOTAL) && r < nvalid)
-        v[it] = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + cc * CE);
+      const int c = (TOTAL % kThreads == 0) ? it * kThreads + tid : min(it * kThreads + tid, TOTAL - 1);
+      v[it] = buf_load16(r, c * 16);
     }
   }
   template <int PITCH>
@@ -248,17 +275,13 @@ struct TransTile {
   frag_t rows[PER][4];
 
   __device__ __forceinline__ void load(const T* g, int nvalid, int tid) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(g, min(nvalid, ROWS), D);
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int u = it * kThreads + tid;
+      const int u = (UNITS % kThreads == 0) ? it * kThreads + tid : min(it * kThreads + tid, UNITS - 1);
       const int quad = u % QUADS, dc = u / QUADS;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * quad + r;
-        rows[it][r] = zero_frag<T>();
-        if ((UNITS % kThreads == 0 || u < UNITS) && row < nvalid)
-          rows[it][r] = load_frag(g + (size_t)row * D + 8 * dc);
-      }
+      for (int rr = 0; rr < 4; ++rr) rows[it][rr] = buf_load_frag<T>(r, (4 * quad + rr) * D + 8 * dc);
     }
   }
   template <int PITCH>
@@ -278,5 +301,7 @@ struct TransTile {
     }
   }
 };
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 }  // namespace ra

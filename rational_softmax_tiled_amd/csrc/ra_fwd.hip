@@ -191,6 +191,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   TransTile<T, D, BN> vreg;
   int cur = 0;
   while (cur < nt && wg_skips(cur)) ++cur;
+  cur = uniform(cur);   // every lane computed the same index from the same LDS values
   if (COUNT) n_wg_skip += cur;
   if (cur < nt) {
     kreg.load(kg + (size_t)cur * BN * D, a.Nk - cur * BN, tid);
@@ -205,12 +206,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   while (cur < nt) {
     int nxt = cur + 1;
     while (nxt < nt && wg_skips(nxt)) ++nxt;
+    nxt = uniform(nxt);
     if (COUNT) n_wg_skip += nxt - cur - 1;
     if (nxt < nt) {
       kreg.load(kg + (size_t)nxt * BN * D, a.Nk - nxt * BN, tid);
       if constexpr (WRITE_O) vreg.load(vg + (size_t)nxt * BN * D, a.Nk - nxt * BN, tid);
     }
-    const bool my_skip = cur < kMaxTiles ? wave_skips(wave, cur) : cur >= nt_w;
+    const bool my_skip = uniform(cur < kMaxTiles ? wave_skips(wave, cur) : cur >= nt_w);
     if (COUNT && cur < nt_w) {
       n_wave_tiles += 1;
       n_wave_skip += my_skip ? 1 : 0;
