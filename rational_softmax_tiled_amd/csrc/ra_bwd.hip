@@ -418,6 +418,324 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ bf16 kernels
+// Same mathematics as the kernels above, laid out for gfx950: K/V (query-parallel kernel) and
+// Q/dO (key-parallel kernel) tiles are brought into LDS by DMA as XOR-swizzled row tiles,
+// double-buffered with one barrier per step; every transposed operand (K^T for dQ, Q^T for dK,
+// dO^T for dV) is read with the LDS transposing load from the same row tile, so nothing is
+// staged twice and no register holds a tile in flight.
+
+// Direct gradient and probability of one entry: with d = 1 + u = fma(s, -c, kd),
+// q = clamp(2/d - 1), p = q^8 * il and G = (dP * il - c * il) * q^7 / d^2.
+__device__ __forceinline__ float ra_grad(float s, float c16, float kd, float dp, float il, float cil,
+                                         float* p) {
+  const float d = fmaf(s, -c16, kd);
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = fminf(fmaxf(fmaf(r, 2.0f, -1.0f), 0.0f), 1.0f);
+  const float q2 = q * q;
+  const float q4 = q2 * q2;
+  const float q6 = q4 * q2;
+  *p = (q4 * q4) * il;
+  return fmaf(dp, il, -cil) * ((q6 * q) * (r * r));
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
+  constexpr int BN = 64, KC = D / 16, SB = BN / 32, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int logical = xcd_remap(blockIdx.x, a.total_wg);
+  const int bg = logical / a.wg_per_group;
+  int wig = logical % a.wg_per_group;
+  if (CAUSAL) wig = a.wg_per_group - 1 - wig;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int task = wig * kWaves + wave;
+  const bool active = task < a.tasks_per_group;
+  const int h = g * a.rep + (active ? task % a.rep : 0);
+  const int q0 = (active ? task / a.rep : 0) * kRowsPerWave;
+  const int last_task = min(wig * kWaves + kWaves - 1, a.tasks_per_group - 1);
+  const int wg_qmax = min((last_task / a.rep) * kRowsPerWave + kRowsPerWave - 1, a.Nq - 1);
+  const int nt = ((CAUSAL ? min(a.Nk, wg_qmax + 1) : a.Nk) + BN - 1) / BN;
+  const int wave_qmax = min(q0 + kRowsPerWave - 1, a.Nq - 1);
+  const int nt_w = !active ? 0 : ((CAUSAL ? min(a.Nk, wave_qmax + 1) : a.Nk) + BN - 1) / BN;
+
+  const size_t head = (size_t)(b * a.Hq + h) * a.Nq;
+  const bf16* kg = static_cast<const bf16*>(a.k) + (size_t)(b * a.Hkv + g) * a.Nk * D;
+  const bf16* vg = static_cast<const bf16*>(a.v) + (size_t)(b * a.Hkv + g) * a.Nk * D;
+  const int qi = q0 + (lane & 31);
+  const int qrow = min(qi, a.Nq - 1);
+  const int frow = lane & 31, fcol = 8 * (lane >> 5);
+
+  // tile 0 is in flight while the row terms are prepared
+  if (nt > 0) {
+    dma_tile<D, BN>(k_lds[0], kg, a.Nk, wave, lane);
+    dma_tile<D, BN>(v_lds[0], vg, a.Nk, wave, lane);
+  }
+  const bf16* qp = static_cast<const bf16*>(a.q) + (head + qrow) * D;
+  const bf16* dop = static_cast<const bf16*>(a.d_o) + (head + qrow) * D;
+  const bf16* op = static_cast<const bf16*>(a.o) + (head + qrow) * D;
+  bf16x8 qf[KC], df[KC];
+  float cpart = 0.0f;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    qf[kc] = load_frag(qp + 16 * kc + fcol);
+    df[kc] = load_frag(dop + 16 * kc + fcol);
+    const bf16x8 of = load_frag(op + 16 * kc + fcol);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cpart = fmaf((float)df[kc][j], (float)of[j], cpart);
+  }
+  const float cval = cpart + __shfl_xor(cpart, 32);   // c_i = dO_i . O_i
+  const float m = a.stats[(head + qrow) * 2];
+  const float l = a.stats[(head + qrow) * 2 + 1];
+  const float il = l > 0.0f ? 1.0f / l : 0.0f;
+  const float cil = cval * il;
+  const float kd = fmaf(m, a.c16, 1.0f);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float rsum = 0.0f;
+  int amax = INT_MAX;
+  wait_vmem();
+  __syncthreads();
+
+  for (int kt = 0; kt < nt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nt) {
+      dma_tile<D, BN>(k_lds[buf ^ 1], kg + (size_t)(kt + 1) * BN * D, a.Nk - (kt + 1) * BN, wave, lane);
+      dma_tile<D, BN>(v_lds[buf ^ 1], vg + (size_t)(kt + 1) * BN * D, a.Nk - (kt + 1) * BN, wave, lane);
+    }
+    if (kt < nt_w) {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) mma(s, swz_frag<bf16, D>(k_lds[buf], sb * 32 + frow, 16 * kc + fcol), qf[kc]);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) mma(dp, swz_frag<bf16, D>(v_lds[buf], sb * 32 + frow, 16 * kc + fcol), df[kc]);
+        const int key0 = kt * BN + sb * 32;
+        if ((CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + acc_row(i, lane);
+            if (key >= a.Nk || (CAUSAL && key > qrow)) s[i] = -INFINITY;
+          }
+        }
+        float lm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lm = fmaxf(lm, s[i]);
+        if (__any(lm == m)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (s[i] == m) amax = min(amax, key0 + acc_row(i, lane));
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p;
+          s[i] = ra_grad(s[i], a.c16, kd, dp[i], il, cil, &p);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 gf = pack_frag_bf16(s, ks);
+          rsum = frag_sum(gf, rsum);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            mma(acc[db], tr_frag<D>(k_lds[buf], sb * 32 + 16 * ks, db * 32, lane), gf);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  const float R = -(rsum + __shfl_xor(rsum, 32));
+  amax = min(amax, __shfl_xor(amax, 32));
+  if (active && qi < a.Nq) {
+    bf16* dqrow = static_cast<bf16*>(a.dq) + (head + qi) * D;
+    const bool has_max = amax < a.Nk;
+    const bf16* krow = kg + (size_t)(has_max ? amax : 0) * D;
+    const float radd = has_max ? R : 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
+        float kv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[e] = (float)krow[d0 + e];
+        store_quad_scaled<bf16>(dqrow + d0, acc[db], 4 * r4, a.scale, kv, radd);
+      }
+    if (lane < 32) {
+      a.c[head + qi] = cval;
+      a.r[head + qi] = R;
+      a.amax[head + qi] = has_max ? amax : -1;
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
+  constexpr int KC = D / 16, DB = D / 32;
+  constexpr int QT = kQTile;
+  __shared__ __attribute__((aligned(16))) bf16 q_lds[2][QT * D];
+  __shared__ __attribute__((aligned(16))) bf16 do_lds[2][QT * D];
+  __shared__ __attribute__((aligned(16))) float st_kd[2][QT];
+  __shared__ __attribute__((aligned(16))) float st_il[2][QT];
+  __shared__ __attribute__((aligned(16))) float st_cil[2][QT];
+  __shared__ __attribute__((aligned(16))) float st_r[2][QT];
+  __shared__ __attribute__((aligned(16))) int st_a[2][QT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int logical = xcd_remap(blockIdx.x, a.total_kwg);
+  const int bg = logical / a.kwg_per_group;
+  const int kb = logical % a.kwg_per_group;   // low key blocks (most causal work) first
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int key0_wg = kb * kKeysPerWg;
+  const int j0 = key0_wg + wave * kRowsPerWave;
+  const bool active = j0 < a.Nk;
+  const int frow = lane & 31, fcol = 8 * (lane >> 5);
+  const int key = j0 + frow;
+  const int krow = min(key, a.Nk - 1);
+
+  const int nqt = (a.Nq + QT - 1) / QT;
+  const int qt0 = CAUSAL ? min(key0_wg / QT, nqt) : 0;
+  const int per_head = nqt - qt0;
+  const int steps = a.rep * per_head;
+  const bf16* qbase = static_cast<const bf16*>(a.q);
+  const bf16* dobase = static_cast<const bf16*>(a.d_o);
+
+  // step -> (query head, first query row); Q/dO tiles by DMA, row terms through registers
+  float r_kd = 0.0f, r_il = 0.0f, r_cil = 0.0f, r_r = 0.0f;
+  int r_a = -1;
+  auto issue = [&](int step, int buf) {
+    const int hh = step / per_head, qt = qt0 + step % per_head;
+    const size_t head = (size_t)(b * a.Hq + g * a.rep + hh) * a.Nq;
+    const int i0 = qt * QT;
+    dma_tile<D, QT>(q_lds[buf], qbase + (head + i0) * D, a.Nq - i0, wave, lane);
+    dma_tile<D, QT>(do_lds[buf], dobase + (head + i0) * D, a.Nq - i0, wave, lane);
+    if (tid < QT) {
+      const int qi = i0 + tid;
+      if (qi < a.Nq) {
+        const float l = a.stats[(head + qi) * 2 + 1];
+        const float il = l > 0.0f ? 1.0f / l : 0.0f;
+        r_kd = fmaf(a.stats[(head + qi) * 2], a.c16, 1.0f);
+        r_il = il;
+        r_cil = a.c[head + qi] * il;
+        r_r = a.r[head + qi];
+        r_a = a.amax[head + qi];
+      } else {
+        r_kd = 1.0f;
+        r_il = 0.0f;
+        r_cil = 0.0f;
+        r_r = 0.0f;
+        r_a = -1;
+      }
+    }
+  };
+  auto publish = [&](int buf) {
+    if (tid < QT) {
+      st_kd[buf][tid] = r_kd;
+      st_il[buf][tid] = r_il;
+      st_cil[buf][tid] = r_cil;
+      st_r[buf][tid] = r_r;
+      st_a[buf][tid] = r_a;
+    }
+  };
+
+  const bf16* kp = static_cast<const bf16*>(a.k) + ((size_t)(b * a.Hkv + g) * a.Nk + krow) * D;
+  const bf16* vp = static_cast<const bf16*>(a.v) + ((size_t)(b * a.Hkv + g) * a.Nk + krow) * D;
+  if (steps > 0) issue(0, 0);
+  bf16x8 kf[KC], vf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    kf[kc] = load_frag(kp + 16 * kc + fcol);
+    vf[kc] = load_frag(vp + 16 * kc + fcol);
+  }
+  f32x16 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    acc_dk[db] = f32x16{};
+    acc_dv[db] = f32x16{};
+  }
+  publish(0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int st = 0; st < steps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < steps) issue(st + 1, buf ^ 1);
+    const int i0 = (qt0 + st % per_head) * QT;
+    if (active && !(CAUSAL && i0 + QT - 1 < j0)) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) mma(s, swz_frag<bf16, D>(q_lds[buf], frow, 16 * kc + fcol), kf[kc]);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) mma(dp, swz_frag<bf16, D>(do_lds[buf], frow, 16 * kc + fcol), vf[kc]);
+      const bool edge = (CAUSAL && j0 + 31 > i0) || i0 + QT > a.Nq || j0 + 32 > a.Nk;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r0 = 8 * i4 + 4 * (lane >> 5);   // four consecutive query rows of this lane
+        const f32x4 kd4 = *reinterpret_cast<const f32x4*>(&st_kd[buf][r0]);
+        const f32x4 il4 = *reinterpret_cast<const f32x4*>(&st_il[buf][r0]);
+        const f32x4 cil4 = *reinterpret_cast<const f32x4*>(&st_cil[buf][r0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          float sv = s[i];
+          if (edge) {
+            const int qi = i0 + r0 + e;
+            if (key >= a.Nk || qi >= a.Nq || (CAUSAL && key > qi)) sv = -INFINITY;
+          }
+          float p;
+          const float gv = ra_grad(sv, a.c16, kd4[e], dp[i], il4[e], cil4[e], &p);
+          s[i] = p;
+          dp[i] = gv;
+        }
+      }
+      {
+        const int am = st_a[buf][lane & 31];
+        if (__any(am >= j0 && am < j0 + 32)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = acc_row(i, lane);
+            if (st_a[buf][r] == key) dp[i] += st_r[buf][r];
+          }
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pf = pack_frag_bf16(s, ks);
+        const bf16x8 gf = pack_frag_bf16(dp, ks);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          mma(acc_dv[db], tr_frag<D>(do_lds[buf], 16 * ks, db * 32, lane), pf);
+          mma(acc_dk[db], tr_frag<D>(q_lds[buf], 16 * ks, db * 32, lane), gf);
+        }
+      }
+    }
+    if (st + 1 < steps) publish(buf ^ 1);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  if (active && key < a.Nk) {
+    const size_t kvbase = (size_t)(b * a.Hkv + g) * a.Nk;
+    bf16* dkrow = static_cast<bf16*>(a.dk) + (kvbase + key) * D;
+    bf16* dvrow = static_cast<bf16*>(a.dv) + (kvbase + key) * D;
+    const float zero4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
+        store_quad_scaled<bf16>(dkrow + d0, acc_dk[db], 4 * r4, a.scale, zero4, 0.0f);
+        store_quad_scaled<bf16>(dvrow + d0, acc_dv[db], 4 * r4, 1.0f, zero4, 0.0f);
+      }
+  }
+}
+
 template <typename T, int D, int BN>
 static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const void* d_o,
                                    const float* stats, void* dq, void* dk, void* dv,
@@ -448,16 +766,21 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   a.scale = p.scale;
   a.c16 = p.scale / 16.0f;
   dim3 block(kThreads);
+  constexpr bool kBf16 = sizeof(T) == 2;
   if (p.causal) {
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true>), dim3(a.total_wg), block, 0, stream, a);
+    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true>), dim3(a.total_wg), block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true>), dim3(a.total_wg), block, 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), dim3(a.total_kwg), block, 0, stream, a);
+    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true>), dim3(a.total_kwg), block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), dim3(a.total_kwg), block, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false>), dim3(a.total_wg), block, 0, stream, a);
+    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false>), dim3(a.total_wg), block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false>), dim3(a.total_wg), block, 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), dim3(a.total_kwg), block, 0, stream, a);
+    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false>), dim3(a.total_kwg), block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), dim3(a.total_kwg), block, 0, stream, a);
   }
   return hipGetLastError();
 }

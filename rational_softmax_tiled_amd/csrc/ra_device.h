@@ -26,6 +26,8 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short short8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr int kWaves = 4;               // waves per workgroup
@@ -301,6 +303,121 @@ struct TransTile {
     }
   }
 };
+
+// ---------------------------------------------------------------- swizzled row tiles
+// A tile of rows x D elements stored without padding; the 16-byte chunk cc of row r sits at
+// chunk position cc ^ swz(r).  The LDS serves 256 bytes per cycle (64 banks): 16 lanes of a
+// 16-byte read, 32 lanes of an 8-byte read.  swz makes both access patterns conflict-free:
+//   * row reads (16 consecutive rows, one chunk each): swz is a permutation over any 16
+//     consecutive rows (for 128-byte rows: over the 8 rows of each row parity);
+//   * transposed 8-byte reads (4 consecutive rows, 64 contiguous bytes each): the four rows'
+//     chunk groups of four land on distinct bank groups.
+template <typename T, int D>
+__device__ __forceinline__ constexpr int swz(int row) {
+  constexpr int CPR = D * (int)sizeof(T) / 16;   // chunks per row
+  if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Element offset of logical chunk cc of row r.
+template <typename T, int D>
+__device__ __forceinline__ int swz_off(int r, int cc) {
+  constexpr int CE = 16 / (int)sizeof(T);
+  return r * D + ((cc ^ swz<T, D>(r)) * CE);
+}
+
+// Row fragment: 8 consecutive elements starting at element column col (a multiple of 8).
+template <typename T, int D>
+__device__ __forceinline__ typename Ty<T>::frag swz_frag(const T* tile, int r, int col) {
+  constexpr int CE = 16 / (int)sizeof(T);
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const bf16x8*>(tile + swz_off<T, D>(r, col / CE));
+  } else {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + swz_off<T, D>(r, col / CE));
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + swz_off<T, D>(r, col / CE + 1));
+    return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// Transposed A fragment from a swizzled bf16 row tile T[row][col]: lane l receives
+// T[k0 + s(j)][c0 + l%32] for the 8 contraction slots j, where the row order
+// s = {4*(l/32) + 0..3, 8 + 4*(l/32) + 0..3} matches the accumulator layout of a 32x32
+// product (key_slot).  Two ds_read_b64_tr_b16: within each 16-lane group, lane L addresses
+// row rb + L/4, columns cb + 4*(L%4) .. +3, and receives column cb + L of rows rb .. rb+3.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* tile, int k0, int c0, int lane) {
+  typedef __attribute__((address_space(3))) short lds_short;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const int g = lane >> 4, L = lane & 15;
+  const int row = k0 + 4 * (g >> 1) + (L >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (L & 3);
+  const int sub = col & 7;
+  const int o1 = swz_off<bf16, D>(row, col >> 3) + sub;
+  const int o2 = swz_off<bf16, D>(row + 8, col >> 3) + sub;
+  const lds_short* base = (const lds_short*)(tile);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o1));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o2));
+  const short8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Register-prefetched swizzled row tile (store() writes chunk cc of row r at its swizzled spot).
+template <typename T, int D, int ROWS>
+struct SwzTile {
+  static constexpr int CE = 16 / sizeof(T);
+  static constexpr int CPR = D / CE;
+  static constexpr int TOTAL = ROWS * CPR;
+  static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
+  u32x4 v[PER];
+
+  __device__ __forceinline__ void load(const T* g, int nvalid, int tid) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(g, min(nvalid, ROWS), D);
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = (TOTAL % kThreads == 0) ? it * kThreads + tid : min(it * kThreads + tid, TOTAL - 1);
+      v[it] = buf_load16(r, c * 16);
+    }
+  }
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = it * kThreads + tid;
+      if (TOTAL % kThreads == 0 || c < TOTAL) {
+        const int r = c / CPR, cc = c % CPR;
+        *reinterpret_cast<u32x4*>(lds + swz_off<T, D>(r, cc)) = v[it];
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- LDS DMA (bf16 row tiles)
+// Loads a ROWS x D bf16 row tile straight into LDS with buffer_load ... lds (no registers):
+// every instruction fills 1 KiB of LDS, lane l writing chunk position l.  Choosing which global
+// chunk each lane fetches lays the tile out swizzled (swz).  Rows >= nvalid read as zeros.
+// The waves of the workgroup share the 1 KiB blocks.  The caller waits (vmcnt) and issues a
+// barrier before any wave reads the tile.
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_tile(bf16* lds, const bf16* g, int nvalid, int wave, int lane) {
+  constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  constexpr int BLOCKS = ROWS * D * 2 / 1024;      // 1 KiB blocks in the tile
+  static_assert((ROWS * D * 2) % 1024 == 0, "tile must be whole 1 KiB blocks");
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(g, min(nvalid, ROWS), D);
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int b0 = 0; b0 < BLOCKS; b0 += kWaves) {
+    const int b = b0 + wave;
+    if (BLOCKS % kWaves == 0 || b < BLOCKS) {
+      const int p = b * 64 + lane;                 // chunk position inside the tile
+      const int row = p / CPR, pos = p % CPR;
+      const int cc = pos ^ swz<bf16, D>(row);      // logical chunk stored at that position
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + b * 512), 16, (row * CPR + cc) * 16, 0, 0, 0);
+    }
+  }
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone): every outstanding vector-memory load,
+// LDS DMA included, has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

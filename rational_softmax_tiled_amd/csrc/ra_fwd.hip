@@ -13,14 +13,17 @@
 //     are enumerated head-fastest and dealt four per workgroup.
 //   * Scores are computed transposed, S^T = K Q^T (keys on the accumulator rows, queries on
 //     the lanes), so every lane owns one query row: its running max, phi sum and the
-//     P^T operand of O^T = V^T P^T stay in that lane, with no register shuffle.  V^T is staged
-//     transposed in LDS in the slot order that matches the accumulator layout.
+//     P^T operand of O^T = V^T P^T stay in that lane, with no register shuffle.  K and V are
+//     staged as XOR-swizzled row tiles; the V^T operand is read with the LDS transposing load
+//     in the slot order that matches the accumulator layout (fp32: V staged transposed).
 //   * Pass 1 keeps, per wave and key tile, the max score of the tile; after pass 1 a tile is
 //     skipped for a wave when 1 + u >= 2 already at the tile max against the smallest row max
 //     of the wave, evaluated with the same monotone floating-point steps as phi itself, so
 //     skipping never changes a result bit.  A tile
 //     skipped by all four waves is not even loaded.  Causal tiles beyond a wave's diagonal are
 //     recorded as -inf and skipped the same way.
+#include <type_traits>
+
 #include "ra_device.h"
 #include "ra_internal.h"
 
@@ -67,28 +70,31 @@ __device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int la
   }
 }
 
-// S^T block (32 keys x 32 query rows) of key sub-block sb of the staged K tile.
-template <typename T, int D, int PK>
+// S^T block (32 keys x 32 query rows) of key sub-block sb of the staged (swizzled) K tile.
+template <typename T, int D>
 __device__ __forceinline__ f32x16 score_block(const T* k_tile, const typename Ty<T>::frag* qf, int sb,
                                               int frow, int fcol) {
   f32x16 s = {};
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) mma(s, load_frag(k_tile + (sb * 32 + frow) * PK + 16 * kc + fcol), qf[kc]);
+  for (int kc = 0; kc < D / 16; ++kc) mma(s, swz_frag<T, D>(k_tile, sb * 32 + frow, 16 * kc + fcol), qf[kc]);
   return s;
 }
 
 template <typename T, int D, int BN, bool CAUSAL, bool COUNT, bool WRITE_O>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   using frag_t = typename Ty<T>::frag;
+  // bf16: V stays a swizzled row tile and the P.V operand is read transposed (ds_read_b64_tr_b16);
+  // fp32 has no transposed read: V is staged transposed, [d][key slot], row pitch PV.
+  constexpr bool VTR = sizeof(T) == 2;
   constexpr int PAD = 16 / sizeof(T);
-  constexpr int PK = D + PAD;    // K tile row pitch
-  constexpr int PV = BN + PAD;   // V^T tile row pitch
+  constexpr int PV = BN + PAD;
+  constexpr int V_ELEMS = VTR ? BN * D : D * PV;
   constexpr int KC = D / 16;     // 16-wide K chunks of the QK^T contraction
   constexpr int SB = BN / 32;    // 32-key blocks per tile
   constexpr int DB = D / 32;     // 32-row blocks of O^T
 
-  __shared__ __attribute__((aligned(16))) T k_lds[2][BN * PK];
-  __shared__ __attribute__((aligned(16))) T vt_lds[WRITE_O ? 2 : 1][WRITE_O ? D * PV : 8];
+  __shared__ __attribute__((aligned(16))) T k_lds[2][BN * D];
+  __shared__ __attribute__((aligned(16))) T v_lds[WRITE_O ? 2 : 1][WRITE_O ? V_ELEMS : 8];
   __shared__ float tmax_lds[kWaves][kMaxTiles];
   __shared__ float kmin_lds[kWaves];
 
@@ -129,11 +135,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   auto needs_mask = [&](int key0) { return (CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk; };
 
   // ---- pass 1: row max of the raw dot products (K tiles double-buffered through LDS)
-  RowTile<T, D, BN> kreg;
+  SwzTile<T, D, BN> kreg;
   float mx = -INFINITY;
   if (nt > 0) {
     kreg.load(kg, a.Nk, tid);
-    kreg.template store<PK>(k_lds[0], tid);
+    kreg.store(k_lds[0], tid);
   }
   __syncthreads();
   for (int kt = 0; kt < nt; ++kt) {
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
     if (kt < nt_w) {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
-        f32x16 s = score_block<T, D, PK>(k_lds[buf], qf, sb, frow, fcol);
+        f32x16 s = score_block<T, D>(k_lds[buf], qf, sb, frow, fcol);
         const int key0 = kt * BN + sb * 32;
         if (needs_mask(key0)) mask_block<CAUSAL>(s, key0, qrow, lane, a.Nk);
 #pragma unroll
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
       const float wm = wave_max(tl);
       if (lane == 0) tmax_lds[wave][kt] = wm;
     }
-    if (kt + 1 < nt) kreg.template store<PK>(k_lds[buf ^ 1], tid);
+    if (kt + 1 < nt) kreg.store(k_lds[buf ^ 1], tid);
     __syncthreads();
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));   // lanes l and l+32 hold the same query row
@@ -188,17 +194,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   float lsum = 0.0f;
   unsigned long long n_wave_tiles = 0, n_wave_skip = 0, n_wg_skip = 0;
 
-  TransTile<T, D, BN> vreg;
+  using VTile = typename std::conditional<VTR, SwzTile<T, D, BN>, TransTile<T, D, BN>>::type;
+  VTile vreg;
+  auto store_v = [&](T* dst) {
+    if constexpr (VTR) vreg.store(dst, tid);
+    else vreg.template store<PV>(dst, tid);
+  };
   int cur = 0;
   while (cur < nt && wg_skips(cur)) ++cur;
   cur = uniform(cur);   // every lane computed the same index from the same LDS values
   if (COUNT) n_wg_skip += cur;
   if (cur < nt) {
     kreg.load(kg + (size_t)cur * BN * D, a.Nk - cur * BN, tid);
-    kreg.template store<PK>(k_lds[0], tid);
+    kreg.store(k_lds[0], tid);
     if constexpr (WRITE_O) {
       vreg.load(vg + (size_t)cur * BN * D, a.Nk - cur * BN, tid);
-      vreg.template store<PV>(vt_lds[0], tid);
+      store_v(v_lds[0]);
     }
   }
   __syncthreads();
@@ -221,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
       // both score blocks first, so the phi math of one overlaps the products of the other
       f32x16 s[SB];
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb) s[sb] = score_block<T, D, PK>(k_lds[buf], qf, sb, frow, fcol);
+      for (int sb = 0; sb < SB; ++sb) s[sb] = score_block<T, D>(k_lds[buf], qf, sb, frow, fcol);
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         const int key0 = cur * BN + sb * 32;
@@ -246,15 +257,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
           }
           if constexpr (WRITE_O) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-              mma(oacc[db], load_frag(vt_lds[buf] + (db * 32 + frow) * PV + sb * 32 + 16 * ks + fcol), pf);
+            for (int db = 0; db < DB; ++db) {
+              if constexpr (VTR)
+                mma(oacc[db], tr_frag<D>(v_lds[buf], sb * 32 + 16 * ks, db * 32, lane), pf);
+              else
+                mma(oacc[db], load_frag(v_lds[buf] + (db * 32 + frow) * PV + sb * 32 + 16 * ks + fcol), pf);
+            }
           }
         }
       }
     }
     if (nxt < nt) {
-      kreg.template store<PK>(k_lds[buf ^ 1], tid);
-      if constexpr (WRITE_O) vreg.template store<PV>(vt_lds[buf ^ 1], tid);
+      kreg.store(k_lds[buf ^ 1], tid);
+      if constexpr (WRITE_O) store_v(v_lds[buf ^ 1]);
     }
     __syncthreads();
     buf ^= 1;
