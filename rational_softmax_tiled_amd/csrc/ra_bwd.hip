@@ -581,6 +581,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a)
   constexpr int QT = kQTile;
   __shared__ __attribute__((aligned(16))) bf16 q_lds[2][QT * D];
   __shared__ __attribute__((aligned(16))) bf16 do_lds[2][QT * D];
+  __shared__ __attribute__((aligned(16))) bf16 v_lds[kKeysPerWg * D];   // the workgroup's V rows
   __shared__ __attribute__((aligned(16))) float st_kd[2][QT];
   __shared__ __attribute__((aligned(16))) float st_il[2][QT];
   __shared__ __attribute__((aligned(16))) float st_cil[2][QT];
@@ -645,14 +646,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a)
   };
 
   const bf16* kp = static_cast<const bf16*>(a.k) + ((size_t)(b * a.Hkv + g) * a.Nk + krow) * D;
-  const bf16* vp = static_cast<const bf16*>(a.v) + ((size_t)(b * a.Hkv + g) * a.Nk + krow) * D;
+  // V rows of the workgroup stay in LDS (B operand of dP = dO V^T); K rows in registers
+  dma_tile<D, kKeysPerWg>(v_lds, static_cast<const bf16*>(a.v) + ((size_t)(b * a.Hkv + g) * a.Nk + key0_wg) * D,
+                          a.Nk - key0_wg, wave, lane);
   if (steps > 0) issue(0, 0);
-  bf16x8 kf[KC], vf[KC];
+  bf16x8 kf[KC];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    kf[kc] = load_frag(kp + 16 * kc + fcol);
-    vf[kc] = load_frag(vp + 16 * kc + fcol);
-  }
+  for (int kc = 0; kc < KC; ++kc) kf[kc] = load_frag(kp + 16 * kc + fcol);
   f32x16 acc_dk[DB], acc_dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -672,7 +672,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a)
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) mma(s, swz_frag<bf16, D>(q_lds[buf], frow, 16 * kc + fcol), kf[kc]);
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) mma(dp, swz_frag<bf16, D>(do_lds[buf], frow, 16 * kc + fcol), vf[kc]);
+      for (int kc = 0; kc < KC; ++kc)
+        mma(dp, swz_frag<bf16, D>(do_lds[buf], frow, 16 * kc + fcol),
+            swz_frag<bf16, D>(v_lds, wave * kRowsPerWave + frow, 16 * kc + fcol));
       const bool edge = (CAUSAL && j0 + 31 > i0) || i0 + QT > a.Nq || j0 + 32 > a.Nk;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {

@@ -274,7 +274,7 @@ struct TransTile {
   static constexpr int QUADS = ROWS / 4;
   static constexpr int UNITS = QUADS * (D / 8);
   static constexpr int PER = (UNITS + kThreads - 1) / kThreads;
-  frag_t rows[PER][4];
+  frag_t rows[PER > 0 ? PER : 1][4];   // ROWS == 0: an unused placeholder
 
   __device__ __forceinline__ void load(const T* g, int nvalid, int tid) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(g, min(nvalid, ROWS), D);
@@ -368,7 +368,7 @@ struct SwzTile {
   static constexpr int CPR = D / CE;
   static constexpr int TOTAL = ROWS * CPR;
   static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
-  u32x4 v[PER];
+  u32x4 v[PER > 0 ? PER : 1];   // ROWS == 0: an unused placeholder
 
   __device__ __forceinline__ void load(const T* g, int nvalid, int tid) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(g, min(nvalid, ROWS), D);

@@ -135,16 +135,25 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   auto needs_mask = [&](int key0) { return (CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk; };
 
   // ---- pass 1: row max of the raw dot products (K tiles double-buffered through LDS)
-  SwzTile<T, D, BN> kreg;
+  // Tiles reach LDS by DMA (bf16) or through registers (fp32), one tile ahead of the math.
+  SwzTile<T, D, (sizeof(T) == 2 ? 0 : BN)> kreg;
+  auto k_issue = [&](int kt, T* dst) {
+    if constexpr (sizeof(T) == 2) dma_tile<D, BN>(dst, kg + (size_t)kt * BN * D, a.Nk - kt * BN, wave, lane);
+    else kreg.load(kg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
+  };
+  auto k_land = [&](T* dst) {
+    if constexpr (sizeof(T) == 2) wait_vmem();
+    else kreg.store(dst, tid);
+  };
   float mx = -INFINITY;
   if (nt > 0) {
-    kreg.load(kg, a.Nk, tid);
-    kreg.store(k_lds[0], tid);
+    k_issue(0, k_lds[0]);
+    k_land(k_lds[0]);
   }
   __syncthreads();
   for (int kt = 0; kt < nt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nt) kreg.load(kg + (size_t)(kt + 1) * BN * D, a.Nk - (kt + 1) * BN, tid);
+    if (kt + 1 < nt) k_issue(kt + 1, k_lds[buf ^ 1]);
     float tl = -INFINITY;
     if (kt < nt_w) {
 #pragma unroll
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
       const float wm = wave_max(tl);
       if (lane == 0) tmax_lds[wave][kt] = wm;
     }
-    if (kt + 1 < nt) kreg.store(k_lds[buf ^ 1], tid);
+    if (kt + 1 < nt) k_land(k_lds[buf ^ 1]);
     __syncthreads();
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));   // lanes l and l+32 hold the same query row
@@ -194,23 +203,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   float lsum = 0.0f;
   unsigned long long n_wave_tiles = 0, n_wave_skip = 0, n_wg_skip = 0;
 
-  using VTile = typename std::conditional<VTR, SwzTile<T, D, BN>, TransTile<T, D, BN>>::type;
-  VTile vreg;
-  auto store_v = [&](T* dst) {
-    if constexpr (VTR) vreg.store(dst, tid);
-    else vreg.template store<PV>(dst, tid);
+  TransTile<T, D, (VTR ? 0 : BN)> vreg;   // fp32 only: V^T staged through registers
+  auto v_issue = [&](int kt, T* dst) {
+    if constexpr (VTR) dma_tile<D, BN>(dst, vg + (size_t)kt * BN * D, a.Nk - kt * BN, wave, lane);
+    else vreg.load(vg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
+  };
+  auto v_land = [&](T* dst) {
+    if constexpr (!VTR) vreg.template store<PV>(dst, tid);
   };
   int cur = 0;
   while (cur < nt && wg_skips(cur)) ++cur;
   cur = uniform(cur);   // every lane computed the same index from the same LDS values
   if (COUNT) n_wg_skip += cur;
   if (cur < nt) {
-    kreg.load(kg + (size_t)cur * BN * D, a.Nk - cur * BN, tid);
-    kreg.store(k_lds[0], tid);
-    if constexpr (WRITE_O) {
-      vreg.load(vg + (size_t)cur * BN * D, a.Nk - cur * BN, tid);
-      store_v(v_lds[0]);
-    }
+    k_issue(cur, k_lds[0]);
+    if constexpr (WRITE_O) v_issue(cur, v_lds[0]);
+    k_land(k_lds[0]);
+    if constexpr (WRITE_O) v_land(v_lds[0]);
   }
   __syncthreads();
   int buf = 0;
@@ -220,15 +229,82 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
     nxt = uniform(nxt);
     if (COUNT) n_wg_skip += nxt - cur - 1;
     if (nxt < nt) {
-      kreg.load(kg + (size_t)nxt * BN * D, a.Nk - nxt * BN, tid);
-      if constexpr (WRITE_O) vreg.load(vg + (size_t)nxt * BN * D, a.Nk - nxt * BN, tid);
+      k_issue(nxt, k_lds[buf ^ 1]);
+      if constexpr (WRITE_O) v_issue(nxt, v_lds[buf ^ 1]);
     }
     const bool my_skip = uniform(cur < kMaxTiles ? wave_skips(wave, cur) : cur >= nt_w);
     if (COUNT && cur < nt_w) {
       n_wave_tiles += 1;
       n_wave_skip += my_skip ? 1 : 0;
     }
-    if (!my_skip) {
+    bool done = my_skip;
+    if constexpr (VTR && WRITE_O && SB == 2) {
+      // Unmasked tile: one straight-line block whose issue order is pinned so that the wave's
+      // own VALU work overlaps its own MFMAs (issue is in order): S1 products run under the phi
+      // math of block 0, the P.V products of block 0 under the phi math of block 1, and LDS
+      // reads run ahead of the products that consume them.
+      if (!done && !needs_mask(cur * BN + 32)) {
+        constexpr int NV = 2 * DB;            // P.V products (and V fragments) per 32-key block
+        constexpr int EB = 16 / KC;           // phi elements per S1 product (stage B)
+        constexpr int EC = 16 / NV;           // phi elements per P.V0 product (stage C)
+        const bf16* kt_ = k_lds[buf];
+        const bf16* vt_ = v_lds[buf];
+        bf16x8 kf0[KC], kf1[KC], va[NV], vb[NV];
+        f32x16 s0 = {}, s1 = {};
+        // stage A: S0 = K0 Q^T, K1 fragments read behind it
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) kf0[kc] = swz_frag<bf16, D>(kt_, frow, 16 * kc + fcol);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          mma(s0, kf0[kc], qf[kc]);
+          kf1[kc] = swz_frag<bf16, D>(kt_, 32 + frow, 16 * kc + fcol);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // stage B: S1 products under phi(S0); V fragments of block 0 read
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          mma(s1, kf1[c], qf[c]);
+#pragma unroll
+          for (int e = 0; e < EB; ++e) s0[c * EB + e] = ra_phi(s0[c * EB + e], a.c, kd);
+          if (c < NV) va[c] = tr_frag<D>(vt_, 16 * (c / DB), 32 * (c % DB), lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int c = KC; c < NV; ++c) va[c] = tr_frag<D>(vt_, 16 * (c / DB), 32 * (c % DB), lane);
+        bf16x8 p0[2], p1[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          p0[ks] = pack_frag_bf16(s0, ks);
+#pragma unroll
+          for (int j = 0; j < 8; j += 2)
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[ks][j], p0[ks][j + 1]},
+                                                   bf16x2{(bf16)1.0f, (bf16)1.0f}, lsum, false);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // stage C: P.V products of block 0 under phi(S1); V fragments of block 1 read
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          mma(oacc[c % DB], va[c], p0[c / DB]);
+#pragma unroll
+          for (int e = 0; e < EC; ++e) s1[c * EC + e] = ra_phi(s1[c * EC + e], a.c, kd);
+          vb[c] = tr_frag<D>(vt_, 32 + 16 * (c / DB), 32 * (c % DB), lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          p1[ks] = pack_frag_bf16(s1, ks);
+#pragma unroll
+          for (int j = 0; j < 8; j += 2)
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[ks][j], p1[ks][j + 1]},
+                                                   bf16x2{(bf16)1.0f, (bf16)1.0f}, lsum, false);
+        }
+        // stage D: P.V products of block 1
+#pragma unroll
+        for (int c = 0; c < NV; ++c) mma(oacc[c % DB], vb[c], p1[c / DB]);
+        done = true;
+      }
+    }
+    if (!done) {
       // both score blocks first, so the phi math of one overlaps the products of the other
       f32x16 s[SB];
 #pragma unroll
@@ -268,8 +344,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
       }
     }
     if (nxt < nt) {
-      kreg.store(k_lds[buf ^ 1], tid);
-      if constexpr (WRITE_O) store_v(v_lds[buf ^ 1]);
+      k_land(k_lds[buf ^ 1]);
+      if constexpr (WRITE_O) v_land(v_lds[buf ^ 1]);
     }
     __syncthreads();
     buf ^= 1;
