@@ -575,30 +575,47 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   }
 }
 
+// bf16 dK/dV: eight waves, two per SIMD, so that one wave's phi-derivative VALU work runs under
+// the other's matrix products.  The workgroup owns 128 keys whose K and V rows stay in LDS;
+// waves w and w+4 own the same 32 keys and take the upper and lower 32 rows of each 64-row
+// query tile (Q and dO tiles double-buffered by LDS DMA), so each keeps its own dK^T/dV^T
+// partial sums; the two are added through LDS at the end (fixed order: deterministic).
+constexpr int kDkdvWaves = 8;
+constexpr int kDkdvThreads = kDkdvWaves * kWave;
+constexpr int kDkdvRows = 64;   // query rows per step (32 per half of the workgroup)
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
-  constexpr int KC = D / 16, DB = D / 32;
-  constexpr int QT = kQTile;
-  __shared__ __attribute__((aligned(16))) bf16 q_lds[2][QT * D];
-  __shared__ __attribute__((aligned(16))) bf16 do_lds[2][QT * D];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[kKeysPerWg * D];   // the workgroup's V rows
+__global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
+  constexpr int KC = D / 16, DB = D / 32, QT = kDkdvRows, NW = kDkdvWaves;
+  constexpr int TILE = QT * D;            // elements of one Q or dO tile
+  constexpr int KV = kKeysPerWg * D;      // elements of the K (or V) rows
+  // K | V | Q[2] | dO[2]; after the loop the same bytes hold the partial sums
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * KV + 4 * TILE];
+  static_assert(4 * 2 * DB * 16 * kWave * sizeof(float) <= sizeof(bf16) * (2 * KV + 4 * TILE),
+                "partial sums must fit in the tile buffers");
   __shared__ __attribute__((aligned(16))) float st_kd[2][QT];
   __shared__ __attribute__((aligned(16))) float st_il[2][QT];
   __shared__ __attribute__((aligned(16))) float st_cil[2][QT];
   __shared__ __attribute__((aligned(16))) float st_r[2][QT];
   __shared__ __attribute__((aligned(16))) int st_a[2][QT];
+  bf16* const k_lds = smem;
+  bf16* const v_lds = smem + KV;
+  bf16* const q_lds = smem + 2 * KV;              // + buf * TILE
+  bf16* const do_lds = smem + 2 * KV + 2 * TILE;  // + buf * TILE
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = wave & 3, half = wave >> 2;
   const int logical = xcd_remap(blockIdx.x, a.total_kwg);
   const int bg = logical / a.kwg_per_group;
   const int kb = logical % a.kwg_per_group;   // low key blocks (most causal work) first
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int key0_wg = kb * kKeysPerWg;
-  const int j0 = key0_wg + wave * kRowsPerWave;
+  const int j0 = key0_wg + kg * kRowsPerWave;
   const bool active = j0 < a.Nk;
   const int frow = lane & 31, fcol = 8 * (lane >> 5);
   const int key = j0 + frow;
-  const int krow = min(key, a.Nk - 1);
+  const int qr = 32 * half + frow;   // A-fragment row of this lane inside a Q/dO tile
+  const int kr = 32 * kg + frow;     // B-fragment row of this lane inside the K/V rows
 
   const int nqt = (a.Nq + QT - 1) / QT;
   const int qt0 = CAUSAL ? min(key0_wg / QT, nqt) : 0;
@@ -614,8 +631,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a)
     const int hh = step / per_head, qt = qt0 + step % per_head;
     const size_t head = (size_t)(b * a.Hq + g * a.rep + hh) * a.Nq;
     const int i0 = qt * QT;
-    dma_tile<D, QT>(q_lds[buf], qbase + (head + i0) * D, a.Nq - i0, wave, lane);
-    dma_tile<D, QT>(do_lds[buf], dobase + (head + i0) * D, a.Nq - i0, wave, lane);
+    dma_tile<D, QT, NW>(q_lds + buf * TILE, qbase + (head + i0) * D, a.Nq - i0, wave, lane);
+    dma_tile<D, QT, NW>(do_lds + buf * TILE, dobase + (head + i0) * D, a.Nq - i0, wave, lane);
     if (tid < QT) {
       const int qi = i0 + tid;
       if (qi < a.Nq) {
@@ -645,14 +662,10 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a)
     }
   };
 
-  const bf16* kp = static_cast<const bf16*>(a.k) + ((size_t)(b * a.Hkv + g) * a.Nk + krow) * D;
-  // V rows of the workgroup stay in LDS (B operand of dP = dO V^T); K rows in registers
-  dma_tile<D, kKeysPerWg>(v_lds, static_cast<const bf16*>(a.v) + ((size_t)(b * a.Hkv + g) * a.Nk + key0_wg) * D,
-                          a.Nk - key0_wg, wave, lane);
+  const size_t kv0 = ((size_t)(b * a.Hkv + g) * a.Nk + key0_wg) * D;
+  dma_tile<D, kKeysPerWg, NW>(k_lds, static_cast<const bf16*>(a.k) + kv0, a.Nk - key0_wg, wave, lane);
+  dma_tile<D, kKeysPerWg, NW>(v_lds, static_cast<const bf16*>(a.v) + kv0, a.Nk - key0_wg, wave, lane);
   if (steps > 0) issue(0, 0);
-  bf16x8 kf[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) kf[kc] = load_frag(kp + 16 * kc + fcol);
   f32x16 acc_dk[DB], acc_dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -666,22 +679,24 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a)
   for (int st = 0; st < steps; ++st) {
     const int buf = st & 1;
     if (st + 1 < steps) issue(st + 1, buf ^ 1);
-    const int i0 = (qt0 + st % per_head) * QT;
-    if (active && !(CAUSAL && i0 + QT - 1 < j0)) {
+    const int i0 = (qt0 + st % per_head) * QT + 32 * half;   // first query row of this wave
+    if (active && i0 < a.Nq && !(CAUSAL && i0 + 31 < j0)) {
+      const bf16* qt_ = q_lds + buf * TILE;
+      const bf16* dot_ = do_lds + buf * TILE;
       f32x16 s = {}, dp = {};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) mma(s, swz_frag<bf16, D>(q_lds[buf], frow, 16 * kc + fcol), kf[kc]);
+      for (int kc = 0; kc < KC; ++kc)
+        mma(s, swz_frag<bf16, D>(qt_, qr, 16 * kc + fcol), swz_frag<bf16, D>(k_lds, kr, 16 * kc + fcol));
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        mma(dp, swz_frag<bf16, D>(do_lds[buf], frow, 16 * kc + fcol),
-            swz_frag<bf16, D>(v_lds, wave * kRowsPerWave + frow, 16 * kc + fcol));
-      const bool edge = (CAUSAL && j0 + 31 > i0) || i0 + QT > a.Nq || j0 + 32 > a.Nk;
+        mma(dp, swz_frag<bf16, D>(dot_, qr, 16 * kc + fcol), swz_frag<bf16, D>(v_lds, kr, 16 * kc + fcol));
+      const bool edge = (CAUSAL && j0 + 31 > i0) || i0 + 32 > a.Nq || j0 + 32 > a.Nk;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int r0 = 8 * i4 + 4 * (lane >> 5);   // four consecutive query rows of this lane
-        const f32x4 kd4 = *reinterpret_cast<const f32x4*>(&st_kd[buf][r0]);
-        const f32x4 il4 = *reinterpret_cast<const f32x4*>(&st_il[buf][r0]);
-        const f32x4 cil4 = *reinterpret_cast<const f32x4*>(&st_cil[buf][r0]);
+        const f32x4 kd4 = *reinterpret_cast<const f32x4*>(&st_kd[buf][32 * half + r0]);
+        const f32x4 il4 = *reinterpret_cast<const f32x4*>(&st_il[buf][32 * half + r0]);
+        const f32x4 cil4 = *reinterpret_cast<const f32x4*>(&st_cil[buf][32 * half + r0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * i4 + e;
@@ -697,11 +712,11 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a)
         }
       }
       {
-        const int am = st_a[buf][lane & 31];
+        const int am = st_a[buf][32 * half + (lane & 31)];
         if (__any(am >= j0 && am < j0 + 32)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int r = acc_row(i, lane);
+            const int r = 32 * half + acc_row(i, lane);
             if (st_a[buf][r] == key) dp[i] += st_r[buf][r];
           }
         }
@@ -712,8 +727,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a)
         const bf16x8 gf = pack_frag_bf16(dp, ks);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          mma(acc_dv[db], tr_frag<D>(do_lds[buf], 16 * ks, db * 32, lane), pf);
-          mma(acc_dk[db], tr_frag<D>(q_lds[buf], 16 * ks, db * 32, lane), gf);
+          mma(acc_dv[db], tr_frag<D>(dot_, 32 * half + 16 * ks, db * 32, lane), pf);
+          mma(acc_dk[db], tr_frag<D>(qt_, 32 * half + 16 * ks, db * 32, lane), gf);
         }
       }
     }
@@ -722,18 +737,35 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a)
     __syncthreads();
   }
 
-  if (active && key < a.Nk) {
-    const size_t kvbase = (size_t)(b * a.Hkv + g) * a.Nk;
-    bf16* dkrow = static_cast<bf16*>(a.dk) + (kvbase + key) * D;
-    bf16* dvrow = static_cast<bf16*>(a.dv) + (kvbase + key) * D;
-    const float zero4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // the lower half hands its partial sums to the upper half through LDS ([kg][dk|dv][db][i4][lane]
+  // float4, 1 KiB per store instruction); every wave has left the loop behind a barrier
+  f32x4* part = reinterpret_cast<f32x4*>(smem);
+  auto slot = [&](int which, int db, int i4) { return ((((kg * 2 + which) * DB + db) * 4 + i4) * kWave) + lane; };
+  if (half == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
-        store_quad_scaled<bf16>(dkrow + d0, acc_dk[db], 4 * r4, a.scale, zero4, 0.0f);
-        store_quad_scaled<bf16>(dvrow + d0, acc_dv[db], 4 * r4, 1.0f, zero4, 0.0f);
+      for (int i4 = 0; i4 < 4; ++i4) {
+        part[slot(0, db, i4)] = f32x4{acc_dk[db][4 * i4], acc_dk[db][4 * i4 + 1], acc_dk[db][4 * i4 + 2], acc_dk[db][4 * i4 + 3]};
+        part[slot(1, db, i4)] = f32x4{acc_dv[db][4 * i4], acc_dv[db][4 * i4 + 1], acc_dv[db][4 * i4 + 2], acc_dv[db][4 * i4 + 3]};
+      }
+  }
+  __syncthreads();
+  if (half == 0 && active && key < a.Nk) {
+    const size_t kvbase = (size_t)(b * a.Hkv + g) * a.Nk;
+    bf16* dkrow = static_cast<bf16*>(a.dk) + (kvbase + key) * D;
+    bf16* dvrow = static_cast<bf16*>(a.dv) + (kvbase + key) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = db * 32 + 8 * i4 + 4 * (lane >> 5);
+        const f32x4 pk = part[slot(0, db, i4)];
+        const f32x4 pv = part[slot(1, db, i4)];
+        const float ak[4] = {pk[0], pk[1], pk[2], pk[3]};
+        const float av[4] = {pv[0], pv[1], pv[2], pv[3]};
+        store_quad_scaled<bf16>(dkrow + d0, acc_dk[db], 4 * i4, a.scale, ak, 1.0f);
+        store_quad_scaled<bf16>(dvrow + d0, acc_dv[db], 4 * i4, 1.0f, av, 1.0f);
       }
   }
 }
@@ -774,14 +806,14 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
     else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true>), dim3(a.total_wg), block, 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true>), dim3(a.total_kwg), block, 0, stream, a);
+    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true>), dim3(a.total_kwg), dim3(kDkdvThreads), 0, stream, a);
     else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), dim3(a.total_kwg), block, 0, stream, a);
   } else {
     if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false>), dim3(a.total_wg), block, 0, stream, a);
     else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false>), dim3(a.total_wg), block, 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false>), dim3(a.total_kwg), block, 0, stream, a);
+    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false>), dim3(a.total_kwg), dim3(kDkdvThreads), 0, stream, a);
     else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), dim3(a.total_kwg), block, 0, stream, a);
   }
   return hipGetLastError();

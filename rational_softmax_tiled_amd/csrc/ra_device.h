@@ -394,9 +394,9 @@ struct SwzTile {
 // Loads a ROWS x D bf16 row tile straight into LDS with buffer_load ... lds (no registers):
 // every instruction fills 1 KiB of LDS, lane l writing chunk position l.  Choosing which global
 // chunk each lane fetches lays the tile out swizzled (swz).  Rows >= nvalid read as zeros.
-// The waves of the workgroup share the 1 KiB blocks.  The caller waits (vmcnt) and issues a
+// The NW waves of the workgroup share the 1 KiB blocks.  The caller waits (vmcnt) and issues a
 // barrier before any wave reads the tile.
-template <int D, int ROWS>
+template <int D, int ROWS, int NW = kWaves>
 __device__ __forceinline__ void dma_tile(bf16* lds, const bf16* g, int nvalid, int wave, int lane) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per row
   constexpr int BLOCKS = ROWS * D * 2 / 1024;      // 1 KiB blocks in the tile
@@ -404,9 +404,9 @@ __device__ __forceinline__ void dma_tile(bf16* lds, const bf16* g, int nvalid, i
   const __amdgpu_buffer_rsrc_t r = tile_rsrc(g, min(nvalid, ROWS), D);
   typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
-  for (int b0 = 0; b0 < BLOCKS; b0 += kWaves) {
+  for (int b0 = 0; b0 < BLOCKS; b0 += NW) {
     const int b = b0 + wave;
-    if (BLOCKS % kWaves == 0 || b < BLOCKS) {
+    if (BLOCKS % NW == 0 || b < BLOCKS) {
       const int p = b * 64 + lane;                 // chunk position inside the tile
       const int row = p / CPR, pos = p % CPR;
       const int cc = pos ^ swz<bf16, D>(row);      // logical chunk stored at that position
