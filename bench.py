@@ -8,9 +8,16 @@ value is counted TFLOP/s: 4*B*Hq*Nq*Nk*D for the forward, halved when causal, ti
 forward + backward.  Prints one JSON line.
 
 Also reported: the forward alone on this workload and on the grouped-query workload
-(B=4, Hq=32, Hkv=8, N=4096, D=128, host RoPE), the row softmax at [16384, 8192], a roofline
-object for the dominant kernel (timed with HIP events on the stream the library launches
-on) and the fp64 oracle timed on a bounded sample on the host cores.
+(B=4, Hq=32, Hkv=8, N=4096, D=128, host RoPE), the two backward phases (ra_attn_bwd_dq,
+ra_attn_bwd_dkdv) alone, the row softmax at [16384, 8192], a roofline object for the
+dominant kernel (the longest of the forward, dQ and dK/dV kernels, each timed alone with HIP
+events on the stream the library launches it on) and the fp64 oracle timed on a bounded
+sample on the host cores.
+
+Algorithmic work per visited score element (i, j), D = head dim: forward 4*D flops (S = QK^T
+and PV); dQ phase 6*D (S, dP = dO V^T, dQ += dS K); dK/dV phase 8*D (S, dP, dV += P^T dO,
+dK += dS^T Q).  A causal launch visits B*Hq*Nq*Nk/2 elements (the counting convention of
+the headline metric).
 """
 from __future__ import annotations
 
@@ -29,6 +36,26 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 
 MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
+
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch) on the
+# main workload, each scaled by what the counter read for a plain copy of 256 MiB read + 256
+# MiB written (FETCH_SIZE counted half the bytes read: x2; WRITE_SIZE all of them: x1).  Valid
+# only for the kernel source the counters were taken on (sha256 of the files listed).
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+TRAFFIC = {
+    # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    "attn_fwd_kernel": ("77790d2bfe836db0a9271f2fcc5d7deb1695ab3f46cb21b30a0eecf4688c1bc6",
+                        265982.8, 135170.9),
+    "attn_bwd_dq_bf16_kernel": ("c7dcd75a7a88d0eecfe9e24f822c41d596e7a13513e1d98c5b62ba96c5c3a764",
+                                412653.9, 143453.6),
+    "attn_bwd_dkdv_bf16_kernel": ("c7dcd75a7a88d0eecfe9e24f822c41d596e7a13513e1d98c5b62ba96c5c3a764",
+                                  267475.1, 262200.0),
+}
+KERNEL_SOURCES = {
+    "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],
+    "attn_bwd_dq_bf16_kernel": ["ra_bwd.hip", "ra_device.h"],
+    "attn_bwd_dkdv_bf16_kernel": ["ra_bwd.hip", "ra_device.h"],
+}
 GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
 
 
@@ -86,6 +113,39 @@ class Attn:
                                  w.Nk, w.D, int(w.causal), w.scale, self.code, self.stream)
         if st != 0:
             raise RuntimeError(f"ra_attn_bwd: {self.ra.ra_status_string(st)}")
+
+    def bwd_dq(self):
+        w = self.w
+        st = self.ra.ra_attn_bwd_dq(self.q, self.k, self.v, self.o, self.do, self.stats, self.dq,
+                                    self.ws, self.ws_bytes, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D,
+                                    int(w.causal), w.scale, self.code, self.stream)
+        if st != 0:
+            raise RuntimeError(f"ra_attn_bwd_dq: {self.ra.ra_status_string(st)}")
+
+    def bwd_dkdv(self):
+        w = self.w
+        st = self.ra.ra_attn_bwd_dkdv(self.q, self.k, self.v, self.do, self.stats, self.dk, self.dv,
+                                      self.ws, self.ws_bytes, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D,
+                                      int(w.causal), w.scale, self.code, self.stream)
+        if st != 0:
+            raise RuntimeError(f"ra_attn_bwd_dkdv: {self.ra.ra_status_string(st)}")
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "rational_softmax_tiled_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(kernel):
+    """HBM bytes per launch from the recorded counters, or None if the kernel has changed."""
+    rec = TRAFFIC.get(kernel)
+    if rec is None or source_digest(KERNEL_SOURCES[kernel]) != rec[0]:
+        return None
+    return int(rec[1] * 1024 * FETCH_SCALE + rec[2] * 1024 * WRITE_SCALE)
 
 
 def time_calls(stream, fn, n):
@@ -181,10 +241,18 @@ def main():
     fwd_ms = time_calls(stream, main_run.fwd, n_k)
     fwd_tflops = w.counted_flops_fwd() / (fwd_ms * 1e-3) / 1e12
     log(f"forward {fwd_ms:.3f} ms: {fwd_tflops:.1f} TFLOP/s")
-    bwd_ms = None
+    elems = w.B * w.Hq * w.Nq * w.Nk / (2 if w.causal else 1)   # visited score elements
+    # (name, C entry point, ms per launch, algorithmic flops per launch)
+    kernels = [("attn_fwd_kernel", "ra_attn_fwd", fwd_ms, 4 * w.D * elems)]
+    bwd_ms = dq_ms = dkdv_ms = None
     if need_grad:
         bwd_ms = time_calls(stream, main_run.bwd, n_k)
         log(f"backward {bwd_ms:.3f} ms")
+        dq_ms = time_calls(stream, main_run.bwd_dq, n_k)       # leaves the row terms in place
+        dkdv_ms = time_calls(stream, main_run.bwd_dkdv, n_k)
+        log(f"backward phases: dQ {dq_ms:.3f} ms, dK/dV {dkdv_ms:.3f} ms")
+        kernels += [("attn_bwd_dq_bf16_kernel", "ra_attn_bwd_dq", dq_ms, 6 * w.D * elems),
+                    ("attn_bwd_dkdv_bf16_kernel", "ra_attn_bwd_dkdv", dkdv_ms, 8 * w.D * elems)]
     del main_run
     torch.cuda.empty_cache()
 
@@ -209,12 +277,18 @@ def main():
     sm_gbs = 2 * x.numel() * 4 / (sm_ms * 1e-3) / 1e9
     log(f"softmax rows [16384, 8192] fp32 {sm_ms:.3f} ms: {sm_gbs:.0f} GB/s")
 
-    # dominant kernel: the forward attention kernel (one launch per ra_attn_fwd call)
-    dom_ms, dom_name, dom_flops = fwd_ms, "attn_fwd_kernel (ra_attn_fwd)", w.counted_flops_fwd()
+    # dominant kernel: the longest launch of the step (one launch per entry-point call)
+    dom_name, dom_call, dom_ms, dom_flops = max(kernels, key=lambda t: t[2])
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": dom_name, "avg_launch_ms": round(dom_ms, 4)}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_bytes(dom_name), "kernel": f"{dom_name} ({dom_call})",
+                "avg_launch_ms": round(dom_ms, 4),
+                "flops_per_launch": dom_flops}
+    kernel_table = {n: {"ms": round(t, 4), "tflops": round(f / (t * 1e-3) / 1e12, 2),
+                        "traffic": traffic_bytes(n),
+                        "frac_of_peak": round(f / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                    for n, _, t, f in kernels}
 
     cpu = None
     if not args.no_cpu:
@@ -242,6 +316,7 @@ def main():
         "fwd": {"workload": w.name, "ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),
                 "frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4)},
         "bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
+        "kernels": kernel_table,
         "fwd_gqa": {"workload": wg.name, "ms": round(gqa_ms, 4), "tflops": round(gqa_tflops, 2),
                     "frac_of_peak": round(gqa_tflops / PEAK_BF16_TFLOPS, 4)},
         "softmax_rows": {"shape": [16384, 8192], "dtype": "f32", "ms": round(sm_ms, 4),

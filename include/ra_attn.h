@@ -126,6 +126,29 @@ int ra_attn_bwd(const void* q, const void* k, const void* v, const void* o, cons
                 int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream);
 
 /*
+ * ra_attn_bwd_dq, ra_attn_bwd_dkdv -- the two phases of ra_attn_bwd, callable on their own
+ * (same sources and formulas).  ra_attn_bwd is exactly ra_attn_bwd_dq followed by
+ * ra_attn_bwd_dkdv on the same stream, with the same arguments and workspace.
+ *   ra_attn_bwd_dq: query-parallel.  Writes dq and, into workspace, the per-row terms the
+ *     second phase needs: c_i = dO_i . O_i, the row-max gradient R_i and the lowest key index
+ *     of the row max.  With stats == NULL it first recomputes (m, l) into workspace.
+ *   ra_attn_bwd_dkdv: key-parallel.  Writes dk and dv from those per-row terms, so the
+ *     workspace must hold what ra_attn_bwd_dq wrote for the same inputs (stream order or an
+ *     explicit synchronisation between the two calls); pass the same stats pointer (NULL
+ *     reads the copy the first phase recomputed).  The workspace is only read.
+ *   Pointers a phase does not use (dk, dv for the first; o, dq for the second) may be NULL.
+ *   Checks, sizes, limits and determinism as ra_attn_bwd.
+ */
+int ra_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                   const float* stats, void* dq, void* workspace, size_t workspace_bytes,
+                   int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                   int causal, float scale, int dtype, void* stream);
+int ra_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_o,
+                     const float* stats, void* dk, void* dv, const void* workspace,
+                     size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                     int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream);
+
+/*
  * ra_softmax_rows -- ra_softmax along the last axis of a [rows, cols] matrix.
  *   Source: Ra-Family page, section 3, item ra_softmax (ra_softmax(logits, dim=-1)).
  *   Entries equal to -inf are masked: p = 0 there, and they take no part in the max or the

@@ -1,8 +1,8 @@
 """rational_softmax_tiled_amd -- rational-softmax attention on AMD MI355X (gfx950).
 
 A thin ctypes binding over ``libra_attn.so``.  The functions named like the C entry points
-(``ra_attn_fwd``, ``ra_attn_fwd_counted``, ``ra_attn_bwd``, ``ra_attn_bwd_workspace_bytes``,
-``ra_softmax_rows``) only marshal arguments: tensors become device pointers, the stream
+(``ra_attn_fwd``, ``ra_attn_fwd_counted``, ``ra_attn_bwd``, ``ra_attn_bwd_dq``,
+``ra_attn_bwd_dkdv``, ``ra_attn_bwd_workspace_bytes``, ``ra_softmax_rows``) only marshal arguments: tensors become device pointers, the stream
 becomes a ``hipStream_t``.  Every step of the computation runs in the library's HIP kernels;
 there is no CPU or PyTorch fallback, and importing the compute functions without the built
 library raises.
@@ -22,7 +22,7 @@ from typing import Optional
 __all__ = [
     "RA_F32", "RA_BF16", "RaError", "load_library", "library_path",
     "ra_status_string", "ra_attn_fwd", "ra_attn_fwd_counted", "ra_attn_bwd",
-    "ra_attn_bwd_workspace_bytes", "ra_softmax_rows",
+    "ra_attn_bwd_dq", "ra_attn_bwd_dkdv", "ra_attn_bwd_workspace_bytes", "ra_softmax_rows",
     "attn_fwd", "attn_bwd", "ra_attention", "ra_softmax",
 ]
 
@@ -78,6 +78,14 @@ def load_library():
                                 _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
                                 ctypes.c_int, _vp]
     lib.ra_attn_bwd.restype = ctypes.c_int
+    lib.ra_attn_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                   _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                   ctypes.c_float, ctypes.c_int, _vp]
+    lib.ra_attn_bwd_dq.restype = ctypes.c_int
+    lib.ra_attn_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                     _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                     ctypes.c_float, ctypes.c_int, _vp]
+    lib.ra_attn_bwd_dkdv.restype = ctypes.c_int
     lib.ra_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_int, _vp]
     lib.ra_softmax_rows.restype = ctypes.c_int
     _lib = lib
@@ -131,6 +139,22 @@ def ra_attn_bwd(q, k, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes, 
                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                       int(workspace_bytes), B, Hq, Hkv, Nq, Nk, D, int(causal),
                                       float(scale), int(dtype), _stream(stream))
+
+
+def ra_attn_bwd_dq(q, k, v, o, d_o, stats, dq, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, D,
+                   causal, scale, dtype, stream=None) -> int:
+    return load_library().ra_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o),
+                                         _ptr(stats), _ptr(dq), _ptr(workspace),
+                                         int(workspace_bytes), B, Hq, Hkv, Nq, Nk, D, int(causal),
+                                         float(scale), int(dtype), _stream(stream))
+
+
+def ra_attn_bwd_dkdv(q, k, v, d_o, stats, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk,
+                     D, causal, scale, dtype, stream=None) -> int:
+    return load_library().ra_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(stats),
+                                           _ptr(dk), _ptr(dv), _ptr(workspace),
+                                           int(workspace_bytes), B, Hq, Hkv, Nq, Nk, D,
+                                           int(causal), float(scale), int(dtype), _stream(stream))
 
 
 def ra_softmax_rows(x, p, rows, cols, dtype, stream=None) -> int:

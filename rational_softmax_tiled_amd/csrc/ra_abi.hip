@@ -133,17 +133,23 @@ size_t ra_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N
   return ra::bwd_workspace_bytes(B, Hq, Nq);
 }
 
-int ra_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
-                const float* stats, void* dq, void* dk, void* dv, void* workspace,
-                size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
-                int64_t D, int causal, float scale, int dtype, void* stream) {
+// Shared by ra_attn_bwd and its two phases.  A phase's own outputs and inputs are required;
+// the rest may be NULL.
+static int attn_bwd_common(const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* stats, void* dq, void* dk, void* dv,
+                           const void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
+                           int dtype, int phases, void* stream) {
   int st = check_sizes(B, Hq, Hkv, Nq, Nk, D, scale, dtype);
   if (st != RA_OK) return st;
   const int64_t qrows = B * Hq * Nq, krows = B * Hkv * Nk;
   if (qrows == 0 && krows == 0) return RA_OK;
   const bool need_q = qrows > 0, need_k = krows > 0;
-  if (need_q && (q == nullptr || dq == nullptr || o == nullptr || d_o == nullptr)) return RA_ERR_NULLPTR;
-  if (need_k && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) return RA_ERR_NULLPTR;
+  const bool ph_dq = (phases & ra::kBwdDq) != 0, ph_kv = (phases & ra::kBwdDkdv) != 0;
+  if (need_q && (q == nullptr || d_o == nullptr)) return RA_ERR_NULLPTR;
+  if (need_q && ph_dq && (dq == nullptr || o == nullptr)) return RA_ERR_NULLPTR;
+  if (need_k && (k == nullptr || v == nullptr)) return RA_ERR_NULLPTR;
+  if (need_k && ph_kv && (dk == nullptr || dv == nullptr)) return RA_ERR_NULLPTR;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(d_o, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return RA_ERR_ALIGN;
@@ -154,15 +160,40 @@ int ra_attn_bwd(const void* q, const void* k, const void* v, const void* o, cons
     if (!aligned(workspace, 4)) return RA_ERR_ALIGN;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!need_k) return fill_zero(dq, (size_t)qrows * D, dtype, s);   // Nk == 0
-  if (!need_q) {                                                      // no query rows
+  if (!need_k) return ph_dq ? fill_zero(dq, (size_t)qrows * D, dtype, s) : RA_OK;   // Nk == 0
+  if (!need_q) {                                                                      // no query rows
+    if (!ph_kv) return RA_OK;
     st = fill_zero(dk, (size_t)krows * D, dtype, s);
     if (st == RA_OK) st = fill_zero(dv, (size_t)krows * D, dtype, s);
     return st;
   }
   ra::AttnProblem p = make_problem(q, k, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype);
-  ra::BwdWorkspace ws = ra::bwd_workspace_layout(workspace, B, Hq, Nq);
-  return hip_status(ra::launch_attn_bwd(p, o, d_o, stats, dq, dk, dv, ws, s));
+  ra::BwdWorkspace ws = ra::bwd_workspace_layout(const_cast<void*>(workspace), B, Hq, Nq);
+  return hip_status(ra::launch_attn_bwd(p, o, d_o, stats, dq, dk, dv, ws, phases, s));
+}
+
+int ra_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                const float* stats, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                int64_t D, int causal, float scale, int dtype, void* stream) {
+  return attn_bwd_common(q, k, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes, B, Hq,
+                         Hkv, Nq, Nk, D, causal, scale, dtype, ra::kBwdAll, stream);
+}
+
+int ra_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                   const float* stats, void* dq, void* workspace, size_t workspace_bytes,
+                   int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                   int causal, float scale, int dtype, void* stream) {
+  return attn_bwd_common(q, k, v, o, d_o, stats, dq, nullptr, nullptr, workspace, workspace_bytes,
+                         B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, ra::kBwdDq, stream);
+}
+
+int ra_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_o,
+                     const float* stats, void* dk, void* dv, const void* workspace,
+                     size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                     int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream) {
+  return attn_bwd_common(q, k, v, nullptr, d_o, stats, nullptr, dk, dv, workspace, workspace_bytes,
+                         B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, ra::kBwdDkdv, stream);
 }
 
 int ra_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, int dtype, void* stream) {

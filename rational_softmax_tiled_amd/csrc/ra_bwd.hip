@@ -28,7 +28,7 @@ namespace ra {
 
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq) {
   const size_t rows = (size_t)B * Hq * Nq;
-  return rows * (2 * sizeof(float) + sizeof(float) + sizeof(float) + sizeof(int)) + 256;
+  return rows * (2 * sizeof(float) + 3 * sizeof(float) + sizeof(int) + 3 * sizeof(float)) + 256;
 }
 
 BwdWorkspace bwd_workspace_layout(void* base, int64_t B, int64_t Hq, int64_t Nq) {
@@ -42,6 +42,12 @@ BwdWorkspace bwd_workspace_layout(void* base, int64_t B, int64_t Hq, int64_t Nq)
   ws.r = reinterpret_cast<float*>(p);
   p += rows * sizeof(float);
   ws.amax = reinterpret_cast<int*>(p);
+  p += rows * sizeof(int);
+  ws.kd = reinterpret_cast<float*>(p);
+  p += rows * sizeof(float);
+  ws.il = reinterpret_cast<float*>(p);
+  p += rows * sizeof(float);
+  ws.cil = reinterpret_cast<float*>(p);
   return ws;
 }
 
@@ -58,6 +64,9 @@ struct BwdArgs {
   float* c;
   float* r;
   int* amax;
+  float* kd;    // per-row terms for the key-parallel kernel: 1 + c16 m, 1/l, c/l
+  float* il;
+  float* cil;
   int Hq, Hkv, Nq, Nk, rep;
   int tasks_per_group, wg_per_group, total_wg;   // query-parallel kernel
   int kwg_per_group, total_kwg;                  // key-parallel kernel
@@ -251,6 +260,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
       a.c[head + qi] = cval;
       a.r[head + qi] = R;
       a.amax[head + qi] = has_max ? amax : -1;
+      a.kd[head + qi] = fmaf(m, a.c16, 1.0f);
+      a.il[head + qi] = il;
+      a.cil[head + qi] = cil;
     }
   }
 }
@@ -571,6 +583,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
       a.c[head + qi] = cval;
       a.r[head + qi] = R;
       a.amax[head + qi] = has_max ? amax : -1;
+      a.kd[head + qi] = fmaf(m, a.c16, 1.0f);
+      a.il[head + qi] = il;
+      a.cil[head + qi] = cil;
     }
   }
 }
@@ -593,17 +608,14 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * KV + 4 * TILE];
   static_assert(4 * 2 * DB * 16 * kWave * sizeof(float) <= sizeof(bf16) * (2 * KV + 4 * TILE),
                 "partial sums must fit in the tile buffers");
-  __shared__ __attribute__((aligned(16))) float st_kd[2][QT];
-  __shared__ __attribute__((aligned(16))) float st_il[2][QT];
-  __shared__ __attribute__((aligned(16))) float st_cil[2][QT];
-  __shared__ __attribute__((aligned(16))) float st_r[2][QT];
-  __shared__ __attribute__((aligned(16))) int st_a[2][QT];
+  // per-row terms of the tile [buf][term][row]: 1 + c16*m, 1/l, c/l, R, argmax (int bits)
+  __shared__ __attribute__((aligned(16))) float st_lds[2][5][QT];
   bf16* const k_lds = smem;
   bf16* const v_lds = smem + KV;
   bf16* const q_lds = smem + 2 * KV;              // + buf * TILE
   bf16* const do_lds = smem + 2 * KV + 2 * TILE;  // + buf * TILE
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int kg = wave & 3, half = wave >> 2;
   const int logical = xcd_remap(blockIdx.x, a.total_kwg);
   const int bg = logical / a.kwg_per_group;
@@ -623,42 +635,23 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   const int steps = a.rep * per_head;
   const bf16* qbase = static_cast<const bf16*>(a.q);
   const bf16* dobase = static_cast<const bf16*>(a.d_o);
+  static_assert(QT == kWave, "one row term per lane of a DMA instruction");
 
-  // step -> (query head, first query row); Q/dO tiles by DMA, row terms through registers
-  float r_kd = 0.0f, r_il = 0.0f, r_cil = 0.0f, r_r = 0.0f;
-  int r_a = -1;
+  // step -> (query head, first query row).  Q/dO tiles and the tile's per-row terms (written by
+  // the query-parallel kernel) arrive by LDS DMA; rows past Nq read as zeros, which the masking
+  // of those rows makes harmless.
+  const float* term = wave == 0 ? a.kd : wave == 1 ? a.il : wave == 2 ? a.cil
+                    : wave == 3 ? a.r : reinterpret_cast<const float*>(a.amax);
   auto issue = [&](int step, int buf) {
     const int hh = step / per_head, qt = qt0 + step % per_head;
     const size_t head = (size_t)(b * a.Hq + g * a.rep + hh) * a.Nq;
     const int i0 = qt * QT;
     dma_tile<D, QT, NW>(q_lds + buf * TILE, qbase + (head + i0) * D, a.Nq - i0, wave, lane);
     dma_tile<D, QT, NW>(do_lds + buf * TILE, dobase + (head + i0) * D, a.Nq - i0, wave, lane);
-    if (tid < QT) {
-      const int qi = i0 + tid;
-      if (qi < a.Nq) {
-        const float l = a.stats[(head + qi) * 2 + 1];
-        const float il = l > 0.0f ? 1.0f / l : 0.0f;
-        r_kd = fmaf(a.stats[(head + qi) * 2], a.c16, 1.0f);
-        r_il = il;
-        r_cil = a.c[head + qi] * il;
-        r_r = a.r[head + qi];
-        r_a = a.amax[head + qi];
-      } else {
-        r_kd = 1.0f;
-        r_il = 0.0f;
-        r_cil = 0.0f;
-        r_r = 0.0f;
-        r_a = -1;
-      }
-    }
-  };
-  auto publish = [&](int buf) {
-    if (tid < QT) {
-      st_kd[buf][tid] = r_kd;
-      st_il[buf][tid] = r_il;
-      st_cil[buf][tid] = r_cil;
-      st_r[buf][tid] = r_r;
-      st_a[buf][tid] = r_a;
+    if (wave < 5) {
+      typedef __attribute__((address_space(3))) void lds_void;
+      const __amdgpu_buffer_rsrc_t r = tile_rsrc(term + head + i0, min(a.Nq - i0, QT), 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)&st_lds[buf][wave][0], 4, lane * 4, 0, 0, 0);
     }
   };
 
@@ -672,7 +665,6 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
     acc_dk[db] = f32x16{};
     acc_dv[db] = f32x16{};
   }
-  publish(0);
   wait_vmem();
   __syncthreads();
 
@@ -694,9 +686,9 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int r0 = 8 * i4 + 4 * (lane >> 5);   // four consecutive query rows of this lane
-        const f32x4 kd4 = *reinterpret_cast<const f32x4*>(&st_kd[buf][32 * half + r0]);
-        const f32x4 il4 = *reinterpret_cast<const f32x4*>(&st_il[buf][32 * half + r0]);
-        const f32x4 cil4 = *reinterpret_cast<const f32x4*>(&st_cil[buf][32 * half + r0]);
+        const f32x4 kd4 = *reinterpret_cast<const f32x4*>(&st_lds[buf][0][32 * half + r0]);
+        const f32x4 il4 = *reinterpret_cast<const f32x4*>(&st_lds[buf][1][32 * half + r0]);
+        const f32x4 cil4 = *reinterpret_cast<const f32x4*>(&st_lds[buf][2][32 * half + r0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * i4 + e;
@@ -712,12 +704,12 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
         }
       }
       {
-        const int am = st_a[buf][32 * half + (lane & 31)];
+        const int am = __float_as_int(st_lds[buf][4][32 * half + (lane & 31)]);
         if (__any(am >= j0 && am < j0 + 32)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int r = 32 * half + acc_row(i, lane);
-            if (st_a[buf][r] == key) dp[i] += st_r[buf][r];
+            if (__float_as_int(st_lds[buf][4][r]) == key) dp[i] += st_lds[buf][3][r];
           }
         }
       }
@@ -732,7 +724,6 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
         }
       }
     }
-    if (st + 1 < steps) publish(buf ^ 1);
     wait_vmem();
     __syncthreads();
   }
@@ -773,7 +764,7 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
 template <typename T, int D, int BN>
 static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const void* d_o,
                                    const float* stats, void* dq, void* dk, void* dv,
-                                   const BwdWorkspace& ws, hipStream_t stream) {
+                                   const BwdWorkspace& ws, int phases, hipStream_t stream) {
   BwdArgs a;
   a.q = p.q;
   a.k = p.k;
@@ -787,6 +778,9 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   a.c = ws.c;
   a.r = ws.r;
   a.amax = ws.amax;
+  a.kd = ws.kd;
+  a.il = ws.il;
+  a.cil = ws.cil;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.Nq = p.Nq;
@@ -799,40 +793,48 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   a.total_kwg = p.B * p.Hkv * a.kwg_per_group;
   a.scale = p.scale;
   a.c16 = p.scale / 16.0f;
-  dim3 block(kThreads);
   constexpr bool kBf16 = sizeof(T) == 2;
-  if (p.causal) {
-    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true>), dim3(a.total_wg), block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true>), dim3(a.total_wg), block, 0, stream, a);
-    hipError_t e = hipGetLastError();
+  const dim3 qgrid(a.total_wg), kgrid(a.total_kwg), block(kThreads);
+  const dim3 kblock(kBf16 ? kDkdvThreads : kThreads);
+  if (phases & kBwdDq) {
+    if (p.causal) {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true>), qgrid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true>), qgrid, block, 0, stream, a);
+    } else {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false>), qgrid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false>), qgrid, block, 0, stream, a);
+    }
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true>), dim3(a.total_kwg), dim3(kDkdvThreads), 0, stream, a);
-    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), dim3(a.total_kwg), block, 0, stream, a);
-  } else {
-    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false>), dim3(a.total_wg), block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false>), dim3(a.total_wg), block, 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false>), dim3(a.total_kwg), dim3(kDkdvThreads), 0, stream, a);
-    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), dim3(a.total_kwg), block, 0, stream, a);
+  }
+  if (phases & kBwdDkdv) {
+    if (p.causal) {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true>), kgrid, kblock, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), kgrid, kblock, 0, stream, a);
+    } else {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false>), kgrid, kblock, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), kgrid, kblock, 0, stream, a);
+    }
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd(const AttnProblem& p, const void* o, const void* d_o,
                            const float* stats, void* dq, void* dk, void* dv,
-                           const BwdWorkspace& ws, hipStream_t stream) {
-  if (stats == nullptr) {   // recompute (m, l) with the forward's statistics-only variant
-    hipError_t e = launch_attn_fwd(p, nullptr, ws.stats, nullptr, stream);
-    if (e != hipSuccess) return e;
+                           const BwdWorkspace& ws, int phases, hipStream_t stream) {
+  if (stats == nullptr) {
+    if (phases & kBwdDq) {   // recompute (m, l) with the forward's statistics-only variant
+      const hipError_t e = launch_attn_fwd(p, nullptr, ws.stats, nullptr, stream);
+      if (e != hipSuccess) return e;
+    }
     stats = ws.stats;
   }
   if (p.bf16) {
-    if (p.D == 64) return launch_bwd_typed<bf16, 64, 64>(p, o, d_o, stats, dq, dk, dv, ws, stream);
-    return launch_bwd_typed<bf16, 128, 64>(p, o, d_o, stats, dq, dk, dv, ws, stream);
+    if (p.D == 64) return launch_bwd_typed<bf16, 64, 64>(p, o, d_o, stats, dq, dk, dv, ws, phases, stream);
+    return launch_bwd_typed<bf16, 128, 64>(p, o, d_o, stats, dq, dk, dv, ws, phases, stream);
   }
-  if (p.D == 64) return launch_bwd_typed<float, 64, 32>(p, o, d_o, stats, dq, dk, dv, ws, stream);
-  return launch_bwd_typed<float, 128, 32>(p, o, d_o, stats, dq, dk, dv, ws, stream);
+  if (p.D == 64) return launch_bwd_typed<float, 64, 32>(p, o, d_o, stats, dq, dk, dv, ws, phases, stream);
+  return launch_bwd_typed<float, 128, 32>(p, o, d_o, stats, dq, dk, dv, ws, phases, stream);
 }
 
 }  // namespace ra

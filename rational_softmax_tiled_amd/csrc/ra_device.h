@@ -214,9 +214,10 @@ __device__ __forceinline__ void stage_rows_transposed(T* lds, const T* g, int nv
 // Buffer resource word 3 for raw (untyped) dword loads on gfx9-family parts.
 constexpr int kBufferWord3 = 0x00020000;
 
+// base and valid_rows must be the same in every lane (a resource lives in scalar registers).
 template <typename T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* base, int valid_rows, int D) {
-  const int bytes = valid_rows > 0 ? valid_rows * D * (int)sizeof(T) : 0;
+  const int bytes = __builtin_amdgcn_readfirstlane(valid_rows > 0 ? valid_rows * D * (int)sizeof(T) : 0);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, bytes, kBufferWord3);
 }
 

@@ -29,12 +29,19 @@ struct BwdWorkspace {
   float* c;       // [B*Hq*Nq]  dO_i . O_i
   float* r;       // [B*Hq*Nq]  row-max gradient R_i
   int* amax;      // [B*Hq*Nq]  lowest key index of the row max
+  float* kd;      // [B*Hq*Nq]  1 + (scale/16) m_i
+  float* il;      // [B*Hq*Nq]  1 / l_i (0 when l_i = 0)
+  float* cil;     // [B*Hq*Nq]  c_i / l_i
 };
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq);
 BwdWorkspace bwd_workspace_layout(void* base, int64_t B, int64_t Hq, int64_t Nq);
+// phases: kBwdDq (dQ and the per-row terms c, R, argmax into ws), kBwdDkdv (dK, dV from those
+// terms), or both.  stats == nullptr: the dQ phase recomputes (m, l) into ws.stats and the
+// dK/dV phase reads them there.
+enum { kBwdDq = 1, kBwdDkdv = 2, kBwdAll = 3 };
 hipError_t launch_attn_bwd(const AttnProblem& p, const void* o, const void* d_o,
                            const float* stats, void* dq, void* dk, void* dv,
-                           const BwdWorkspace& ws, hipStream_t stream);
+                           const BwdWorkspace& ws, int phases, hipStream_t stream);
 
 // Row softmax.
 hipError_t launch_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, bool bf16,

@@ -116,6 +116,29 @@ def test_bwd_validation(lib):
     assert bwd(B=0) == OK
 
 
+def test_bwd_phase_validation(lib):
+    def dq_phase(dq=P2, o=P, ws=P2, ws_bytes=1 << 30, B=1, D=64, dk=None):
+        return ra.ra_attn_bwd_dq(P, P, P, o, P, None, dq, ws, ws_bytes, B, 2, 1, 8, 8, D, 1,
+                                 0.125, ra.RA_BF16, 0)
+
+    def kv_phase(dk=P2, dv=P2, ws=P2, ws_bytes=1 << 30, B=1, D=64, scale=0.125):
+        return ra.ra_attn_bwd_dkdv(P, P, P, P, None, dk, dv, ws, ws_bytes, B, 2, 1, 8, 8, D, 1,
+                                   scale, ra.RA_BF16, 0)
+
+    # each phase needs its own outputs, not the other phase's
+    assert dq_phase(dq=None) == NULLPTR
+    assert dq_phase(o=None) == NULLPTR
+    assert kv_phase(dk=None) == NULLPTR
+    assert kv_phase(dv=None) == NULLPTR
+    assert dq_phase(ws=None) == WORKSPACE
+    assert kv_phase(ws_bytes=8) == WORKSPACE
+    assert dq_phase(D=96) == HEADDIM
+    assert kv_phase(scale=0.0) == SCALE
+    assert kv_phase(dv=P2 + 4) == ALIGN
+    assert dq_phase(B=0) == OK
+    assert kv_phase(B=0) == OK
+
+
 def test_softmax_rows_validation(lib):
     assert ra.ra_softmax_rows(P, P, 4, 4, 9, 0) == DTYPE
     assert ra.ra_softmax_rows(P, P, -1, 4, ra.RA_F32, 0) == SHAPE

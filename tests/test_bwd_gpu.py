@@ -199,3 +199,33 @@ def test_autograd_wrapper(gpu_lib):
     assert_close(o.detach().cpu().numpy().astype(np.float64), ref_o, "f32", "o")
     for t, r, n in zip((q, k, v), ref, ("dq", "dk", "dv")):
         assert_close(t.grad.cpu().numpy().astype(np.float64), r, "f32", n)
+
+
+@pytest.mark.parametrize("dtype,use_stats", [("bf16", True), ("bf16", False), ("f32", True)])
+def test_bwd_phases_equal_whole_call(gpu_lib, dtype, use_stats):
+    """ra_attn_bwd_dq then ra_attn_bwd_dkdv reproduces ra_attn_bwd bit for bit."""
+    import torch
+    ra = gpu_lib
+    B, Hq, Hkv, N, D = 2, 4, 2, 200, 128
+    inp = rand_inputs(B, Hq, Hkv, N, N, D, dtype, seed=23)
+    q, k, v, do = (to_dev(inp[n], dtype) for n in ("q", "k", "v", "do"))
+    code = ra.RA_BF16 if dtype == "bf16" else ra.RA_F32
+    scale = 0.0883883461356163
+    o = torch.empty_like(q)
+    stats = torch.empty((B, Hq, N, 2), dtype=torch.float32, device="cuda")
+    assert ra.ra_attn_fwd(q, k, v, o, stats, B, Hq, Hkv, N, N, D, True, scale, code) == 0
+    st = stats if use_stats else None
+    nbytes = ra.ra_attn_bwd_workspace_bytes(B, Hq, Hkv, N, N, D, code)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    whole = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    assert ra.ra_attn_bwd(q, k, v, o, do, st, *whole, ws, nbytes, B, Hq, Hkv, N, N, D, True,
+                          scale, code) == 0
+    dq, dk, dv = torch.full_like(q, 7.0), torch.full_like(k, 7.0), torch.full_like(v, 7.0)
+    ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    assert ra.ra_attn_bwd_dq(q, k, v, o, do, st, dq, ws2, nbytes, B, Hq, Hkv, N, N, D, True,
+                             scale, code) == 0
+    assert ra.ra_attn_bwd_dkdv(q, k, v, do, st, dk, dv, ws2, nbytes, B, Hq, Hkv, N, N, D, True,
+                               scale, code) == 0
+    torch.cuda.synchronize()
+    for x, y in zip((dq, dk, dv), whole):
+        assert torch.equal(x, y)
