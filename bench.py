@@ -44,12 +44,12 @@ MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("77790d2bfe836db0a9271f2fcc5d7deb1695ab3f46cb21b30a0eecf4688c1bc6",
-                        265982.8, 135170.9),
-    "attn_bwd_dq_bf16_kernel": ("c7dcd75a7a88d0eecfe9e24f822c41d596e7a13513e1d98c5b62ba96c5c3a764",
-                                412653.9, 143453.6),
-    "attn_bwd_dkdv_bf16_kernel": ("c7dcd75a7a88d0eecfe9e24f822c41d596e7a13513e1d98c5b62ba96c5c3a764",
-                                  267475.1, 262200.0),
+    "attn_fwd_kernel": ("999e756c7c3ec4b5c0005c7edf4494a1e075e35cb8788722c94c057fcba3d9f5",
+                        262389.5, 135210.7),
+    "attn_bwd_dq_bf16_kernel": ("34070eb4fe6ddf359d94a38466a7fdfcc16c99da59e24f1eaa3e7cf1bdd280b2",
+                                436229.6, 143475.5),
+    "attn_bwd_dkdv_bf16_kernel": ("34070eb4fe6ddf359d94a38466a7fdfcc16c99da59e24f1eaa3e7cf1bdd280b2",
+                                  273031.1, 274325.4),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],

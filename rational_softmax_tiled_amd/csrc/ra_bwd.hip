@@ -590,30 +590,43 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   }
 }
 
-// bf16 dK/dV: eight waves, two per SIMD, so that one wave's phi-derivative VALU work runs under
-// the other's matrix products.  The workgroup owns 128 keys whose K and V rows stay in LDS;
-// waves w and w+4 own the same 32 keys and take the upper and lower 32 rows of each 64-row
-// query tile (Q and dO tiles double-buffered by LDS DMA), so each keeps its own dK^T/dV^T
-// partial sums; the two are added through LDS at the end (fixed order: deterministic).
+// bf16 dK/dV: eight waves, two per SIMD.  The workgroup owns 128 keys whose K and V rows stay in
+// LDS; waves w and w+4 own the same 32 keys and split each 64-row query tile: the upper half
+// (waves 0-3) takes rows 0-31, the lower half (waves 4-7) rows 32-63.  Each keeps its own
+// dK^T/dV^T partial sums, added through LDS at the end (fixed order: deterministic).
+//
+// A step of a wave has three phases: products S, dP (MFMA), the phi-derivative arithmetic
+// (VALU), products dV, dK (MFMA).  The lower half runs one phase behind the upper one: in step t
+// it finishes tile t-1 (arithmetic, then dV/dK) and then forms S, dP of tile t, which it keeps in
+// registers across the barrier.  The two waves of a SIMD are then in different phases most of
+// the step, so one's vector work runs under the other's matrix products.  Each half has its own
+// loop (the half is fixed per wave), and both take steps + 1 barriers.
+//
+// LDS: K, V rows; the upper half-tiles (Q and dO rows 0-31) in two slots (tile t, t+1); the lower
+// half-tiles in three (t-1, t, t+1); the per-row terms of a tile in three.  Tile t+1 is fetched
+// by LDS DMA during step t, issued by the upper half after its own products.
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * kWave;
 constexpr int kDkdvRows = 64;   // query rows per step (32 per half of the workgroup)
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
-  constexpr int KC = D / 16, DB = D / 32, QT = kDkdvRows, NW = kDkdvWaves;
-  constexpr int TILE = QT * D;            // elements of one Q or dO tile
+  constexpr int KC = D / 16, DB = D / 32, QT = kDkdvRows, HR = QT / 2, NW = kDkdvWaves;
+  constexpr int HTILE = HR * D;           // elements of one half-tile (32 rows of Q or dO)
   constexpr int KV = kKeysPerWg * D;      // elements of the K (or V) rows
-  // K | V | Q[2] | dO[2]; after the loop the same bytes hold the partial sums
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * KV + 4 * TILE];
-  static_assert(4 * 2 * DB * 16 * kWave * sizeof(float) <= sizeof(bf16) * (2 * KV + 4 * TILE),
+  // K | V | Q_up[2] | dO_up[2] | Q_lo[3] | dO_lo[3]; after the loop the same bytes hold the
+  // partial sums
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * KV + 10 * HTILE];
+  static_assert(4 * 2 * DB * 16 * kWave * sizeof(float) <= sizeof(bf16) * (2 * KV + 10 * HTILE),
                 "partial sums must fit in the tile buffers");
-  // per-row terms of the tile [buf][term][row]: 1 + c16*m, 1/l, c/l, R, argmax (int bits)
-  __shared__ __attribute__((aligned(16))) float st_lds[2][5][QT];
+  // per-row terms of a tile [slot][term][row]: 1 + c16*m, 1/l, c/l, R, argmax (int bits)
+  __shared__ __attribute__((aligned(16))) float st_lds[3][5][QT];
   bf16* const k_lds = smem;
   bf16* const v_lds = smem + KV;
-  bf16* const q_lds = smem + 2 * KV;              // + buf * TILE
-  bf16* const do_lds = smem + 2 * KV + 2 * TILE;  // + buf * TILE
+  auto q_up = [&](int slot) { return smem + 2 * KV + slot * HTILE; };
+  auto do_up = [&](int slot) { return smem + 2 * KV + (2 + slot) * HTILE; };
+  auto q_lo = [&](int slot) { return smem + 2 * KV + (4 + slot) * HTILE; };
+  auto do_lo = [&](int slot) { return smem + 2 * KV + (7 + slot) * HTILE; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int kg = wave & 3, half = wave >> 2;
@@ -626,7 +639,6 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   const bool active = j0 < a.Nk;
   const int frow = lane & 31, fcol = 8 * (lane >> 5);
   const int key = j0 + frow;
-  const int qr = 32 * half + frow;   // A-fragment row of this lane inside a Q/dO tile
   const int kr = 32 * kg + frow;     // B-fragment row of this lane inside the K/V rows
 
   const int nqt = (a.Nq + QT - 1) / QT;
@@ -637,99 +649,135 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   const bf16* dobase = static_cast<const bf16*>(a.d_o);
   static_assert(QT == kWave, "one row term per lane of a DMA instruction");
 
-  // step -> (query head, first query row).  Q/dO tiles and the tile's per-row terms (written by
-  // the query-parallel kernel) arrive by LDS DMA; rows past Nq read as zeros, which the masking
-  // of those rows makes harmless.
-  const float* term = wave == 0 ? a.kd : wave == 1 ? a.il : wave == 2 ? a.cil
-                    : wave == 3 ? a.r : reinterpret_cast<const float*>(a.amax);
-  auto issue = [&](int step, int buf) {
-    const int hh = step / per_head, qt = qt0 + step % per_head;
-    const size_t head = (size_t)(b * a.Hq + g * a.rep + hh) * a.Nq;
-    const int i0 = qt * QT;
-    dma_tile<D, QT, NW>(q_lds + buf * TILE, qbase + (head + i0) * D, a.Nq - i0, wave, lane);
-    dma_tile<D, QT, NW>(do_lds + buf * TILE, dobase + (head + i0) * D, a.Nq - i0, wave, lane);
-    if (wave < 5) {
-      typedef __attribute__((address_space(3))) void lds_void;
-      const __amdgpu_buffer_rsrc_t r = tile_rsrc(term + head + i0, min(a.Nq - i0, QT), 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)&st_lds[buf][wave][0], 4, lane * 4, 0, 0, 0);
-    }
+  // step -> (query head, first query row of the tile)
+  auto tile_head = [&](int step) { return (size_t)(b * a.Hq + g * a.rep + step / per_head) * a.Nq; };
+  auto tile_row = [&](int step) { return (qt0 + step % per_head) * QT; };
+  // Q/dO half-tiles and the tile's per-row terms (written by the query-parallel kernel) by LDS
+  // DMA, issued by the upper half once its own work for the step is done (it would otherwise
+  // idle at the barrier while the lower half finishes); rows past Nq read as zeros, which the
+  // masking of those rows makes harmless.
+  const float* term = kg == 0 ? a.kd : kg == 1 ? a.il : kg == 2 ? a.cil : a.r;
+  auto issue = [&](int step) {
+    const size_t head = tile_head(step);
+    const int i0 = tile_row(step);
+    const size_t r0 = (head + i0) * D, r1 = (head + i0 + HR) * D;
+    const int bytes = min(a.Nq - i0, QT) * 4;
+    lds_dma<4>(term + head + i0, bytes, &st_lds[step % 3][kg][0], lane * 4);
+    if (kg == 3) lds_dma<4>(a.amax + head + i0, bytes, &st_lds[step % 3][4][0], lane * 4);
+    dma_tile<D, HR, NW / 2>(q_up(step & 1), qbase + r0, a.Nq - i0, kg, lane);
+    dma_tile<D, HR, NW / 2>(do_up(step & 1), dobase + r0, a.Nq - i0, kg, lane);
+    dma_tile<D, HR, NW / 2>(q_lo(step % 3), qbase + r1, a.Nq - i0 - HR, kg, lane);
+    dma_tile<D, HR, NW / 2>(do_lo(step % 3), dobase + r1, a.Nq - i0 - HR, kg, lane);
+  };
+  // does this wave's 32 x 32 block of tile `step` hold any allowed score?
+  auto block_live = [&](int step) {
+    const int i0 = tile_row(step) + HR * half;
+    return active && i0 < a.Nq && !(CAUSAL && i0 + 31 < j0);
   };
 
-  const size_t kv0 = ((size_t)(b * a.Hkv + g) * a.Nk + key0_wg) * D;
-  dma_tile<D, kKeysPerWg, NW>(k_lds, static_cast<const bf16*>(a.k) + kv0, a.Nk - key0_wg, wave, lane);
-  dma_tile<D, kKeysPerWg, NW>(v_lds, static_cast<const bf16*>(a.v) + kv0, a.Nk - key0_wg, wave, lane);
-  if (steps > 0) issue(0, 0);
+  // S^T and dP^T of this wave's block: lane = key, registers = the half-tile's 32 query rows
+  auto products_sdp = [&](const bf16* qt_, const bf16* dot_, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      mma(s, swz_frag<bf16, D>(qt_, frow, 16 * kc + fcol), swz_frag<bf16, D>(k_lds, kr, 16 * kc + fcol));
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      mma(dp, swz_frag<bf16, D>(dot_, frow, 16 * kc + fcol), swz_frag<bf16, D>(v_lds, kr, 16 * kc + fcol));
+  };
+  // s -> P, dp -> G (+ R at the argmax) for the half-tile rows starting at query row i0
+  auto derivative = [&](f32x16& s, f32x16& dp, int i0, int slot) {
+    const bool edge = (CAUSAL && j0 + 31 > i0) || i0 + 32 > a.Nq || j0 + 32 > a.Nk;
+    const float* st = &st_lds[slot][0][HR * half];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      // one group of four rows at a time: hoisting all groups' row terms costs 48 registers
+      __builtin_amdgcn_sched_barrier(0);
+      const int r0 = 8 * i4 + 4 * (lane >> 5);   // four consecutive query rows of this lane
+      const f32x4 kd4 = *reinterpret_cast<const f32x4*>(st + 0 * QT + r0);
+      const f32x4 il4 = *reinterpret_cast<const f32x4*>(st + 1 * QT + r0);
+      const f32x4 cil4 = *reinterpret_cast<const f32x4*>(st + 2 * QT + r0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        float sv = s[i];
+        if (edge) {
+          const int qi = i0 + r0 + e;
+          if (key >= a.Nk || qi >= a.Nq || (CAUSAL && key > qi)) sv = -INFINITY;
+        }
+        float p;
+        const float gv = ra_grad(sv, a.c16, kd4[e], dp[i], il4[e], cil4[e], &p);
+        s[i] = p;
+        dp[i] = gv;
+      }
+    }
+    const int am = __float_as_int(st[4 * QT + (lane & 31)]);
+    if (__any(am >= j0 && am < j0 + 32)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = acc_row(i, lane);
+        if (__float_as_int(st[4 * QT + r]) == key) dp[i] += st[3 * QT + r];
+      }
+    }
+  };
   f32x16 acc_dk[DB], acc_dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     acc_dk[db] = f32x16{};
     acc_dv[db] = f32x16{};
   }
+  // dV^T += dO^T P^T, dK^T += Q^T G^T over the half-tile's 32 rows
+  auto products_dkdv = [&](const f32x16& s, const f32x16& dp, const bf16* qt_, const bf16* dot_) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pf = pack_frag_bf16(s, ks);
+      const bf16x8 gf = pack_frag_bf16(dp, ks);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        mma(acc_dv[db], tr_frag<D>(dot_, 16 * ks, db * 32, lane), pf);
+        mma(acc_dk[db], tr_frag<D>(qt_, 16 * ks, db * 32, lane), gf);
+      }
+    }
+  };
+
+  const size_t kv0 = ((size_t)(b * a.Hkv + g) * a.Nk + key0_wg) * D;
+  dma_tile<D, kKeysPerWg, NW>(k_lds, static_cast<const bf16*>(a.k) + kv0, a.Nk - key0_wg, wave, lane);
+  dma_tile<D, kKeysPerWg, NW>(v_lds, static_cast<const bf16*>(a.v) + kv0, a.Nk - key0_wg, wave, lane);
+  if (steps > 0 && half == 0) issue(0);
   wait_vmem();
   __syncthreads();
 
-  for (int st = 0; st < steps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < steps) issue(st + 1, buf ^ 1);
-    const int i0 = (qt0 + st % per_head) * QT + 32 * half;   // first query row of this wave
-    if (active && i0 < a.Nq && !(CAUSAL && i0 + 31 < j0)) {
-      const bf16* qt_ = q_lds + buf * TILE;
-      const bf16* dot_ = do_lds + buf * TILE;
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        mma(s, swz_frag<bf16, D>(qt_, qr, 16 * kc + fcol), swz_frag<bf16, D>(k_lds, kr, 16 * kc + fcol));
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        mma(dp, swz_frag<bf16, D>(dot_, qr, 16 * kc + fcol), swz_frag<bf16, D>(v_lds, kr, 16 * kc + fcol));
-      const bool edge = (CAUSAL && j0 + 31 > i0) || i0 + 32 > a.Nq || j0 + 32 > a.Nk;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r0 = 8 * i4 + 4 * (lane >> 5);   // four consecutive query rows of this lane
-        const f32x4 kd4 = *reinterpret_cast<const f32x4*>(&st_lds[buf][0][32 * half + r0]);
-        const f32x4 il4 = *reinterpret_cast<const f32x4*>(&st_lds[buf][1][32 * half + r0]);
-        const f32x4 cil4 = *reinterpret_cast<const f32x4*>(&st_lds[buf][2][32 * half + r0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          float sv = s[i];
-          if (edge) {
-            const int qi = i0 + r0 + e;
-            if (key >= a.Nk || qi >= a.Nq || (CAUSAL && key > qi)) sv = -INFINITY;
-          }
-          float p;
-          const float gv = ra_grad(sv, a.c16, kd4[e], dp[i], il4[e], cil4[e], &p);
-          s[i] = p;
-          dp[i] = gv;
-        }
+  if (half == 0) {
+    for (int st = 0; st <= steps; ++st) {
+      if (st < steps && block_live(st)) {
+        f32x16 s, dp;
+        products_sdp(q_up(st & 1), do_up(st & 1), s, dp);
+        derivative(s, dp, tile_row(st), st % 3);
+        products_dkdv(s, dp, q_up(st & 1), do_up(st & 1));
       }
-      {
-        const int am = __float_as_int(st_lds[buf][4][32 * half + (lane & 31)]);
-        if (__any(am >= j0 && am < j0 + 32)) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = 32 * half + acc_row(i, lane);
-            if (__float_as_int(st_lds[buf][4][r]) == key) dp[i] += st_lds[buf][3][r];
-          }
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pf = pack_frag_bf16(s, ks);
-        const bf16x8 gf = pack_frag_bf16(dp, ks);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          mma(acc_dv[db], tr_frag<D>(dot_, 32 * half + 16 * ks, db * 32, lane), pf);
-          mma(acc_dk[db], tr_frag<D>(qt_, 32 * half + 16 * ks, db * 32, lane), gf);
-        }
-      }
+      if (st + 1 < steps) issue(st + 1);
+      wait_vmem();
+      __syncthreads();
     }
-    wait_vmem();
-    __syncthreads();
+  } else {
+    f32x16 s = {}, dp = {};
+    bool carried = false;   // s, dp hold S, dP of tile st - 1
+    for (int st = 0; st <= steps; ++st) {
+      if (carried) {
+        const int pv = (st - 1) % 3;
+        derivative(s, dp, tile_row(st - 1) + HR, pv);
+        products_dkdv(s, dp, q_lo(pv), do_lo(pv));
+      }
+      carried = st < steps && block_live(st);
+      if (carried) products_sdp(q_lo(st % 3), do_lo(st % 3), s, dp);
+      wait_vmem();
+      __syncthreads();
+    }
   }
 
   // the lower half hands its partial sums to the upper half through LDS ([kg][dk|dv][db][i4][lane]
-  // float4, 1 KiB per store instruction); every wave has left the loop behind a barrier
+  // float4, 1 KiB per store instruction); every wave has left its loop behind a barrier
   f32x4* part = reinterpret_cast<f32x4*>(smem);
   auto slot = [&](int which, int db, int i4) { return ((((kg * 2 + which) * DB + db) * 4 + i4) * kWave) + lane; };
   if (half == 1) {

@@ -397,23 +397,67 @@ struct SwzTile {
 // chunk each lane fetches lays the tile out swizzled (swz).  Rows >= nvalid read as zeros.
 // The NW waves of the workgroup share the 1 KiB blocks.  The caller waits (vmcnt) and issues a
 // barrier before any wave reads the tile.
+// One LDS DMA instruction: every lane fetches SIZE bytes (4 or 16) at byte offset
+// voffset + soffset of the buffer [g, g + bytes) (zeros past its end) and lane l stores them at LDS bytes
+// [SIZE*l, SIZE*l + SIZE) after `lds`.  Issued from inline assembly so that the compiler does
+// not track it as a pending LDS write, for which it would wait (vmcnt) before every later LDS
+// read and so serialise the prefetch; callers wait for it themselves (wait_vmem) and then issue
+// a barrier before reading what it wrote.  g, bytes and lds must be the same in every lane.  The
+// one wait state between the M0 write and the load is the hazard the ISA requires.
+template <int SIZE>
+__device__ __forceinline__ void lds_dma(const void* g, int bytes, const void* lds, int voffset,
+                                        int soffset = 0) {
+  static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4");
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const unsigned long long addr = (unsigned long long)g;
+  u32x4_t rsrc;
+  rsrc[0] = __builtin_amdgcn_readfirstlane((unsigned)addr);
+  rsrc[1] = __builtin_amdgcn_readfirstlane((unsigned)(addr >> 32) & 0xffffu);   // stride 0
+  rsrc[2] = __builtin_amdgcn_readfirstlane(bytes > 0 ? bytes : 0);               // num_records
+  rsrc[3] = kBufferWord3;
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(unsigned long)(const __attribute__((address_space(3))) char*)lds);
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(m0), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(m0), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
+                 : "memory", "m0");
+}
+
+// Block i of this wave's share of a ROWS x D tile copy (blocks i*NW + wave); a no-op past the end.
 template <int D, int ROWS, int NW = kWaves>
-__device__ __forceinline__ void dma_tile(bf16* lds, const bf16* g, int nvalid, int wave, int lane) {
+__device__ __forceinline__ void dma_block(bf16* lds, const bf16* g, int nvalid, int wave, int lane, int i) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per row
   constexpr int BLOCKS = ROWS * D * 2 / 1024;      // 1 KiB blocks in the tile
   static_assert((ROWS * D * 2) % 1024 == 0, "tile must be whole 1 KiB blocks");
-  const __amdgpu_buffer_rsrc_t r = tile_rsrc(g, min(nvalid, ROWS), D);
-  typedef __attribute__((address_space(3))) void lds_void;
-#pragma unroll
-  for (int b0 = 0; b0 < BLOCKS; b0 += NW) {
-    const int b = b0 + wave;
-    if (BLOCKS % NW == 0 || b < BLOCKS) {
-      const int p = b * 64 + lane;                 // chunk position inside the tile
-      const int row = p / CPR, pos = p % CPR;
-      const int cc = pos ^ swz<bf16, D>(row);      // logical chunk stored at that position
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + b * 512), 16, (row * CPR + cc) * 16, 0, 0, 0);
-    }
+  const int b = i * NW + wave;
+  if (BLOCKS % NW == 0 || b < BLOCKS) {
+    // the swizzle depends on the row modulo 16 only; a block spans 1024 / (2 D) rows, so when
+    // NW blocks cover a multiple of 16 rows every block of a wave has the same per-lane offset
+    // relative to the block's first byte (passed as the scalar offset)
+    constexpr bool kSharedLaneOffset = (NW * 512 / D) % 16 == 0;
+    const int bb = kSharedLaneOffset ? wave : b;
+    const int p = bb * 64 + lane;                  // chunk position inside the tile
+    const int row = p / CPR, pos = p % CPR;
+    const int cc = pos ^ swz<bf16, D>(row);        // logical chunk stored at that position
+    const int lane_off = (row * CPR + cc) * 16;
+    if constexpr (kSharedLaneOffset)
+      lds_dma<16>(g, min(nvalid, ROWS) * D * 2, lds + b * 512, lane_off, (b - bb) * 1024);
+    else
+      lds_dma<16>(g, min(nvalid, ROWS) * D * 2, lds + b * 512, lane_off);
   }
+}
+// Number of dma_block calls that cover this wave's share of the tile.
+template <int D, int ROWS, int NW = kWaves>
+constexpr int dma_blocks_per_wave() { return (ROWS * D * 2 / 1024 + NW - 1) / NW; }
+
+template <int D, int ROWS, int NW = kWaves>
+__device__ __forceinline__ void dma_tile(bf16* lds, const bf16* g, int nvalid, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < dma_blocks_per_wave<D, ROWS, NW>(); ++i) dma_block<D, ROWS, NW>(lds, g, nvalid, wave, lane, i);
 }
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone): every outstanding vector-memory load,

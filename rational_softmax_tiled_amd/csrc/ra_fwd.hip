@@ -128,6 +128,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   frag_t qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) qf[kc] = load_frag(qh + (size_t)qrow * D + 16 * kc + 8 * (lane >> 5));
+  // settle these loads here: otherwise the compiler waits for them (vmcnt) inside the tile loops,
+  // where the count would also cover the tile prefetch in flight
+  wait_vmem();
 
   const int frow = lane & 31;           // A-fragment row inside a 32-row block
   const int fcol = 8 * (lane >> 5);     // A-fragment column offset
