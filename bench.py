@@ -9,7 +9,7 @@ forward + backward.  Prints one JSON line.
 
 Also reported: the forward alone on this workload and on the grouped-query workload
 (B=4, Hq=32, Hkv=8, N=4096, D=128, host RoPE), the two backward phases (ra_attn_bwd_dq,
-ra_attn_bwd_dkdv) alone, the row softmax at [16384, 8192], a roofline object for the
+ra_attn_bwd_dkdv) alone, the row softmax and its backward at [16384, 8192], a roofline object for the
 dominant kernel (the longest of the forward, dQ and dK/dV kernels, each timed alone with HIP
 events on the stream the library launches it on) and the fp64 oracle timed on a bounded
 sample on the host cores.
@@ -276,6 +276,16 @@ def main():
     sm_ms = time_calls(stream, sm, n_k)
     sm_gbs = 2 * x.numel() * 4 / (sm_ms * 1e-3) / 1e9
     log(f"softmax rows [16384, 8192] fp32 {sm_ms:.3f} ms: {sm_gbs:.0f} GB/s")
+    # its backward (x and dp read, dx written once)
+    g = torch.from_numpy(np.random.default_rng(12).standard_normal((16384, 8192), dtype=np.float32)).cuda()
+    dx = torch.empty_like(x)
+    smb = lambda: ra.ra_softmax_rows_bwd(x, g, dx, 16384, 8192, ra.RA_F32, stream)
+    for _ in range(3):
+        smb()
+    smb_ms = time_calls(stream, smb, n_k)
+    smb_gbs = 3 * x.numel() * 4 / (smb_ms * 1e-3) / 1e9
+    log(f"softmax rows backward [16384, 8192] fp32 {smb_ms:.3f} ms: {smb_gbs:.0f} GB/s")
+    del g, dx
 
     # dominant kernel: the longest launch of the step (one launch per entry-point call)
     dom_name, dom_call, dom_ms, dom_flops = max(kernels, key=lambda t: t[2])
@@ -321,6 +331,9 @@ def main():
                     "frac_of_peak": round(gqa_tflops / PEAK_BF16_TFLOPS, 4)},
         "softmax_rows": {"shape": [16384, 8192], "dtype": "f32", "ms": round(sm_ms, 4),
                          "GB/s": round(sm_gbs, 1), "frac_of_hbm_peak": round(sm_gbs / PEAK_HBM_GBS, 4)},
+        "softmax_rows_bwd": {"shape": [16384, 8192], "dtype": "f32", "ms": round(smb_ms, 4),
+                             "GB/s": round(smb_gbs, 1),
+                             "frac_of_hbm_peak": round(smb_gbs / PEAK_HBM_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -158,6 +158,22 @@ int ra_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_
 int ra_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, int dtype,
                     void* stream);
 
+/*
+ * ra_softmax_rows_bwd -- gradient of ra_softmax_rows: dx = dL/dx given dp = dL/dp.
+ *   Source: Ra-Family page, section 3, item ra_softmax (closed-form derivative
+ *   d(phi)/du = -16 phi / (1 - u^2) for u < 1).  Per row, with p = ra_softmax(x),
+ *   c = sum_j p_j dp_j and u_j = (max - x_j) / 16:
+ *     G_j = p_j (dp_j - c) / (1 - u_j^2) on the support (u_j < 1), 0 elsewhere;
+ *   the row max depends on x as well, which adds R = -sum_j G_j at the lowest index attaining
+ *   the max: dx = G + R e_argmax.  p is recomputed from x (it is not an argument).
+ *   x, dp, dx: [rows, cols] of dtype.  Masked (-inf) entries of x get dx = 0; a row whose entries
+ *   are all -inf gives dx = 0.  dx may be the same buffer as x or as dp (each element of dx is
+ *   written after its own x and dp are read); other overlaps are not allowed.
+ *   Limits, sizes and errors as ra_softmax_rows.
+ */
+int ra_softmax_rows_bwd(const void* x, const void* dp, void* dx, int64_t rows, int64_t cols,
+                        int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,7 +2,8 @@
 
 A thin ctypes binding over ``libra_attn.so``.  The functions named like the C entry points
 (``ra_attn_fwd``, ``ra_attn_fwd_counted``, ``ra_attn_bwd``, ``ra_attn_bwd_dq``,
-``ra_attn_bwd_dkdv``, ``ra_attn_bwd_workspace_bytes``, ``ra_softmax_rows``) only marshal arguments: tensors become device pointers, the stream
+``ra_attn_bwd_dkdv``, ``ra_attn_bwd_workspace_bytes``, ``ra_softmax_rows``,
+``ra_softmax_rows_bwd``) only marshal arguments: tensors become device pointers, the stream
 becomes a ``hipStream_t``.  Every step of the computation runs in the library's HIP kernels;
 there is no CPU or PyTorch fallback, and importing the compute functions without the built
 library raises.
@@ -23,6 +24,7 @@ __all__ = [
     "RA_F32", "RA_BF16", "RaError", "load_library", "library_path",
     "ra_status_string", "ra_attn_fwd", "ra_attn_fwd_counted", "ra_attn_bwd",
     "ra_attn_bwd_dq", "ra_attn_bwd_dkdv", "ra_attn_bwd_workspace_bytes", "ra_softmax_rows",
+    "ra_softmax_rows_bwd",
     "attn_fwd", "attn_bwd", "ra_attention", "ra_softmax",
 ]
 
@@ -88,6 +90,8 @@ def load_library():
     lib.ra_attn_bwd_dkdv.restype = ctypes.c_int
     lib.ra_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_int, _vp]
     lib.ra_softmax_rows.restype = ctypes.c_int
+    lib.ra_softmax_rows_bwd.argtypes = [_vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp]
+    lib.ra_softmax_rows_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -160,6 +164,11 @@ def ra_attn_bwd_dkdv(q, k, v, d_o, stats, dk, dv, workspace, workspace_bytes, B,
 def ra_softmax_rows(x, p, rows, cols, dtype, stream=None) -> int:
     return load_library().ra_softmax_rows(_ptr(x), _ptr(p), rows, cols, int(dtype),
                                           _stream(stream))
+
+
+def ra_softmax_rows_bwd(x, dp, dx, rows, cols, dtype, stream=None) -> int:
+    return load_library().ra_softmax_rows_bwd(_ptr(x), _ptr(dp), _ptr(dx), rows, cols, int(dtype),
+                                              _stream(stream))
 
 
 # ------------------------------------------------------------ tensor-level helpers
@@ -255,14 +264,48 @@ def ra_attention(q, k, v, is_causal: bool = False, scale: Optional[float] = None
     return _FN.apply(q, k, v, bool(is_causal), scale)
 
 
+def _softmax_rows_2d(x):
+    """x as a contiguous [rows, cols] view with the softmax axis last."""
+    cols = x.shape[-1]
+    return x.contiguous(), x.numel() // max(cols, 1), cols
+
+
+class _RaSoftmaxFn:
+    """autograd.Function over ra_softmax_rows / ra_softmax_rows_bwd (built lazily: torch is
+    imported only when a tensor API is used)."""
+    _cls = None
+
+    @classmethod
+    def get(cls):
+        if cls._cls is None:
+            import torch
+
+            class Fn(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, xt):
+                    x2, rows, cols = _softmax_rows_2d(xt)
+                    p = torch.empty_like(x2)
+                    _check(ra_softmax_rows(x2, p, rows, cols, _dtype_code(x2)), "ra_softmax_rows")
+                    ctx.save_for_backward(x2)
+                    return p
+
+                @staticmethod
+                def backward(ctx, dp):
+                    (x2,) = ctx.saved_tensors
+                    dp2, rows, cols = _softmax_rows_2d(dp.to(x2.dtype))
+                    dx = torch.empty_like(x2)
+                    _check(ra_softmax_rows_bwd(x2, dp2, dx, rows, cols, _dtype_code(x2)),
+                           "ra_softmax_rows_bwd")
+                    return dx
+
+            cls._cls = Fn
+        return cls._cls
+
+
 def ra_softmax(x, dim: int = -1):
-    """ra_softmax along ``dim`` (forward only); -inf entries are masked."""
+    """ra_softmax along ``dim`` with autograd; -inf entries are masked (p = 0, dx = 0)."""
     import torch
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("ra_softmax supports float32 and bfloat16")
-    xt = x.movedim(dim, -1).contiguous()
-    cols = xt.shape[-1]
-    rows = xt.numel() // max(cols, 1)
-    p = torch.empty_like(xt)
-    _check(ra_softmax_rows(xt, p, rows, cols, _dtype_code(xt)), "ra_softmax_rows")
-    return p.movedim(-1, dim)
+    xt = x.movedim(dim, -1)
+    return _RaSoftmaxFn.get().apply(xt).movedim(-1, dim)

@@ -207,4 +207,17 @@ int ra_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, int dtyp
                                             static_cast<hipStream_t>(stream)));
 }
 
+int ra_softmax_rows_bwd(const void* x, const void* dp, void* dx, int64_t rows, int64_t cols,
+                        int dtype, void* stream) {
+  if (dtype != RA_F32 && dtype != RA_BF16) return RA_ERR_DTYPE;
+  if (rows < 0 || cols < 0) return RA_ERR_SHAPE;
+  if (rows >= kIndexLimit || cols >= kIndexLimit) return RA_ERR_TOO_LARGE;
+  if (rows == 0 || cols == 0) return RA_OK;
+  if (x == nullptr || dp == nullptr || dx == nullptr) return RA_ERR_NULLPTR;
+  const int es = elem_size(dtype);
+  if (!aligned(x, es) || !aligned(dp, es) || !aligned(dx, es)) return RA_ERR_ALIGN;
+  return hip_status(ra::launch_softmax_rows_bwd(x, dp, dx, rows, cols, dtype == RA_BF16,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -125,6 +125,20 @@ __device__ __forceinline__ float ra_phi_t(float t, float c) {
   return q4 * q4;
 }
 
+// The direct gradient factor for one entry: (dP - c) / l * q^7 / (1+u)^2, given t = m - s in
+// raw units and dpc = (dP - c) / l.  q is clamped exactly as in the forward, so entries off the
+// support (and masked ones, t = +inf) give 0.  Also returns p = q^8 / l through *p.
+__device__ __forceinline__ float ra_grad_t(float t, float c16, float dpc, float il, float* p) {
+  const float d = fmaf(t, c16, 1.0f);
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = fminf(fmaxf(fmaf(r, 2.0f, -1.0f), 0.0f), 1.0f);
+  const float q2 = q * q;
+  const float q4 = q2 * q2;
+  const float q6 = q4 * q2;
+  *p = (q4 * q4) * il;
+  return dpc * ((q6 * q) * (r * r));
+}
+
 // ---------------------------------------------------------------- wave / block helpers
 
 __device__ __forceinline__ float wave_max(float x) {

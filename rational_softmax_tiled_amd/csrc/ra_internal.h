@@ -46,6 +46,8 @@ hipError_t launch_attn_bwd(const AttnProblem& p, const void* o, const void* d_o,
 // Row softmax.
 hipError_t launch_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, bool bf16,
                                hipStream_t stream);
+hipError_t launch_softmax_rows_bwd(const void* x, const void* dp, void* dx, int64_t rows,
+                                   int64_t cols, bool bf16, hipStream_t stream);
 
 // Fill helpers (a kernel, not hipMemsetAsync, so the calls stay graph-capture friendly).
 hipError_t launch_fill_u32(void* dst, uint32_t value, size_t count, hipStream_t stream);

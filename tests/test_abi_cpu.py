@@ -149,6 +149,20 @@ def test_softmax_rows_validation(lib):
     assert ra.ra_softmax_rows(P, P, 4, 0, ra.RA_F32, 0) == OK
 
 
+def test_softmax_rows_bwd_validation(lib):
+    f = ra.ra_softmax_rows_bwd
+    assert f(P, P, P2, 4, 4, 9, 0) == DTYPE
+    assert f(P, P, P2, -1, 4, ra.RA_F32, 0) == SHAPE
+    assert f(P, P, P2, 1 << 31, 4, ra.RA_F32, 0) == TOO_LARGE
+    assert f(None, P, P2, 4, 4, ra.RA_F32, 0) == NULLPTR
+    assert f(P, None, P2, 4, 4, ra.RA_F32, 0) == NULLPTR
+    assert f(P, P, None, 4, 4, ra.RA_F32, 0) == NULLPTR
+    assert f(P, P + 2, P2, 4, 4, ra.RA_F32, 0) == ALIGN
+    assert f(P, P, P2 + 1, 4, 4, ra.RA_BF16, 0) == ALIGN
+    assert f(P, P, P2, 0, 4, ra.RA_F32, 0) == OK
+    assert f(None, None, None, 4, 0, ra.RA_F32, 0) == OK
+
+
 def test_product_path_has_no_fallback():
     # The binding must not reach the oracle or any CPU implementation.
     import rational_softmax_tiled_amd
