@@ -11,4 +11,5 @@ from .ra_oracle import (  # noqa: F401
     ra_phi,
     ra_softmax_rows,
     ra_softmax_rows_bwd,
+    rope_neox,
 )

@@ -139,6 +139,33 @@ def ra_softmax_rows_bwd(x, dp):
     return _softmax_vjp(p, delta, dp, a)
 
 
+def rope_neox(x, theta, positions=None, inverse=False):
+    """Split-halves (NEOX) rotary position embedding along the last axis, positions on axis -2.
+
+    "Primitives" page, section "Attention and transformers" (RoPE[SEQ, N_HEADS, HEAD_DIM,
+    THETA]: channel j is paired with channel j + HEAD_DIM/2) and the nurl page, section
+    "Layers" (nn_rope, NEOX half-split rotary).  The pages name the pairing and theta but not
+    the frequency schedule; the reading used here is inv_freq_j = theta^(-2j/D), j < D/2, with
+    angle = position * inv_freq_j, rotating each pair (x_j, x_{j+D/2}) counter-clockwise.
+    ``positions`` defaults to 0..N-1; ``inverse`` rotates by the negative angle (the transpose,
+    which maps output gradients to input gradients).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    N = x.shape[-2]
+    if D % 2:
+        raise ValueError("head dim must be even")
+    half = D // 2
+    pos = np.arange(N, dtype=np.float64) if positions is None else np.asarray(positions, np.float64)
+    inv_freq = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / D)
+    ang = pos[:, None] * inv_freq[None, :]
+    cos, sin = np.cos(ang), np.sin(ang)
+    if inverse:
+        sin = -sin
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
 def _check_attention_shapes(q, k, v):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be [B, H, N, D]")

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads as wl
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -368,3 +369,72 @@ def test_planted_phi_exponent_error_breaks_golden():
             test_worked_example_exact_phi_and_p()
     finally:
         ro.ra_phi = orig
+
+
+# ------------------------------------------------------------- NEOX RoPE
+
+def test_rope_position_zero_is_identity_and_norms_are_kept():
+    rng = np.random.default_rng(31)
+    x = rng.normal(size=(2, 3, 7, 8))
+    y = oracle.rope_neox(x, 10000.0)
+    np.testing.assert_array_equal(y[..., 0, :], x[..., 0, :])
+    half = 4
+    np.testing.assert_allclose(y[..., :half] ** 2 + y[..., half:] ** 2,
+                               x[..., :half] ** 2 + x[..., half:] ** 2, rtol=1e-13)
+
+
+def test_rope_inverse_undoes_forward():
+    rng = np.random.default_rng(32)
+    x = rng.normal(size=(3, 50, 16))
+    y = oracle.rope_neox(oracle.rope_neox(x, 500.0), 500.0, inverse=True)
+    np.testing.assert_allclose(y, x, atol=1e-13)
+
+
+def test_rope_pairs_channel_j_with_j_plus_half():
+    """Perturbing channel j moves only channels j and j + D/2 (not j + 1, the interleaved
+    pairing the page warns against)."""
+    D = 8
+    x = np.zeros((1, 5, D))
+    for j in range(D):
+        e = x.copy()
+        e[0, 3, j] = 1.0
+        y = oracle.rope_neox(e, 10000.0)[0, 3]
+        partner = (j + D // 2) % D
+        moved = set(np.nonzero(np.abs(y) > 0)[0].tolist())
+        assert moved <= {j, partner} and j in moved
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(33)
+    q = rng.normal(size=(1, 16))
+    k = rng.normal(size=(1, 16))
+    def score(m, n):
+        qm = oracle.rope_neox(q, 10000.0, positions=[m])
+        kn = oracle.rope_neox(k, 10000.0, positions=[n])
+        return float((qm * kn).sum())
+    for m, n, s in ((5, 2, 17), (0, 9, 3), (100, 100, -40)):
+        assert abs(score(m, n) - score(m + s, n + s)) < 1e-10
+
+
+def test_rope_first_frequency_turns_one_radian_per_position():
+    """inv_freq_0 = 1: the pair (x_0, x_{D/2}) turns by exactly the position (in radians);
+    the phase is read back with arctan2."""
+    x = np.zeros((1, 6, 8))
+    x[..., 0] = 1.0
+    y = oracle.rope_neox(x, 10000.0)
+    phase = np.unwrap(np.arctan2(y[0, :, 4], y[0, :, 0]))
+    np.testing.assert_allclose(phase, np.arange(6), atol=1e-12)
+    # the last pair turns at theta^(-2 (D/2-1) / D) radians per position
+    x = np.zeros((1, 6, 8))
+    x[..., 3] = 1.0
+    y = oracle.rope_neox(x, 10000.0)
+    phase = np.arctan2(y[0, :, 7], y[0, :, 3])
+    np.testing.assert_allclose(phase, np.arange(6) * 10000.0 ** (-6 / 8), atol=1e-12)
+
+
+def test_rope_matches_the_host_input_generator():
+    """The fp32 host RoPE that builds the grouped-query inputs, written separately, agrees
+    to fp32 accuracy."""
+    rng = np.random.default_rng(34)
+    x = rng.normal(size=(2, 64, 32)).astype(np.float32)
+    np.testing.assert_allclose(wl.neox_rope(x, 10000.0), oracle.rope_neox(x, 10000.0), atol=2e-5)
