@@ -264,6 +264,20 @@ def main():
     gqa_ms = time_calls(gqa.stream, gqa.fwd, n_k)
     gqa_tflops = wg.counted_flops_fwd() / (gqa_ms * 1e-3) / 1e12
     log(f"GQA forward {gqa_ms:.3f} ms: {gqa_tflops:.1f} TFLOP/s")
+    # the same workload with the NEOX rotation of Q and K done on the device (in place; the
+    # inputs are then rotated again each call, which changes values but not the work)
+    def rope_qk():
+        for t, H in ((gqa.q, wg.Hq), (gqa.k, wg.Hkv)):
+            st = ra.ra_rope_neox(t, t, None, wg.B * H, wg.Nq, wg.D, 10000.0, False, gqa.code, gqa.stream)
+            if st != 0:
+                raise RuntimeError(f"ra_rope_neox: {ra.ra_status_string(st)}")
+    for _ in range(3):
+        rope_qk()
+    rope_ms = time_calls(gqa.stream, rope_qk, n_k)
+    rope_bytes = 2 * (gqa.q.numel() + gqa.k.numel()) * gqa.q.element_size()
+    rope_gbs = rope_bytes / (rope_ms * 1e-3) / 1e9
+    log(f"GQA device RoPE on Q and K {rope_ms:.3f} ms: {rope_gbs:.0f} GB/s; forward incl. RoPE "
+        f"{gqa_ms + rope_ms:.3f} ms")
     del gqa
     torch.cuda.empty_cache()
 
@@ -328,7 +342,8 @@ def main():
         "bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
         "kernels": kernel_table,
         "fwd_gqa": {"workload": wg.name, "ms": round(gqa_ms, 4), "tflops": round(gqa_tflops, 2),
-                    "frac_of_peak": round(gqa_tflops / PEAK_BF16_TFLOPS, 4)},
+                    "frac_of_peak": round(gqa_tflops / PEAK_BF16_TFLOPS, 4),
+                    "device_rope_ms": round(rope_ms, 4), "device_rope_GB/s": round(rope_gbs, 1)},
         "softmax_rows": {"shape": [16384, 8192], "dtype": "f32", "ms": round(sm_ms, 4),
                          "GB/s": round(sm_gbs, 1), "frac_of_hbm_peak": round(sm_gbs / PEAK_HBM_GBS, 4)},
         "softmax_rows_bwd": {"shape": [16384, 8192], "dtype": "f32", "ms": round(smb_ms, 4),

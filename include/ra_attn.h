@@ -174,6 +174,23 @@ int ra_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, int dtyp
 int ra_softmax_rows_bwd(const void* x, const void* dp, void* dx, int64_t rows, int64_t cols,
                         int dtype, void* stream);
 
+/*
+ * ra_rope_neox -- split-halves (NEOX) rotary position embedding, for the queries and keys of
+ * ra_attn_fwd (the step before the attention call).
+ *   Source: "Primitives" page, section "Attention and transformers" (RoPE: channel j of a head
+ *   is paired with channel j + D/2, not j + 1) and the nurl page, section "Layers" (nn_rope).
+ *   For each of the `mats` contiguous [N, D] matrices of x (e.g. mats = B * H for [B, H, N, D]),
+ *   position p_n of row n and pair j < D/2, with angle = p_n * theta^(-2j/D):
+ *     y[n, j] = x[n, j] cos - x[n, j + D/2] sin,  y[n, j + D/2] = x[n, j + D/2] cos + x[n, j] sin.
+ *   inverse != 0 rotates by -angle: the transpose, which maps dL/dy to dL/dx.
+ *   positions: device int32 [N], or NULL for 0..N-1.  Angles are formed in fp64; the products
+ *   run in fp32 and round once to dtype.  y may be x (in place); other overlaps are not allowed.
+ *   Errors: D odd -> RA_ERR_HEADDIM; theta not finite or <= 0 -> RA_ERR_SCALE; N * D >= 2^31
+ *   -> RA_ERR_TOO_LARGE; mats, N or D == 0 -> RA_OK, nothing launched.
+ */
+int ra_rope_neox(const void* x, void* y, const int32_t* positions, int64_t mats, int64_t N,
+                 int64_t D, double theta, int inverse, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

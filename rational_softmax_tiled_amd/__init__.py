@@ -3,7 +3,7 @@
 A thin ctypes binding over ``libra_attn.so``.  The functions named like the C entry points
 (``ra_attn_fwd``, ``ra_attn_fwd_counted``, ``ra_attn_bwd``, ``ra_attn_bwd_dq``,
 ``ra_attn_bwd_dkdv``, ``ra_attn_bwd_workspace_bytes``, ``ra_softmax_rows``,
-``ra_softmax_rows_bwd``) only marshal arguments: tensors become device pointers, the stream
+``ra_softmax_rows_bwd``, ``ra_rope_neox``) only marshal arguments: tensors become device pointers, the stream
 becomes a ``hipStream_t``.  Every step of the computation runs in the library's HIP kernels;
 there is no CPU or PyTorch fallback, and importing the compute functions without the built
 library raises.
@@ -24,7 +24,7 @@ __all__ = [
     "RA_F32", "RA_BF16", "RaError", "load_library", "library_path",
     "ra_status_string", "ra_attn_fwd", "ra_attn_fwd_counted", "ra_attn_bwd",
     "ra_attn_bwd_dq", "ra_attn_bwd_dkdv", "ra_attn_bwd_workspace_bytes", "ra_softmax_rows",
-    "ra_softmax_rows_bwd",
+    "ra_softmax_rows_bwd", "ra_rope_neox", "ra_rope",
     "attn_fwd", "attn_bwd", "ra_attention", "ra_softmax",
 ]
 
@@ -92,6 +92,9 @@ def load_library():
     lib.ra_softmax_rows.restype = ctypes.c_int
     lib.ra_softmax_rows_bwd.argtypes = [_vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp]
     lib.ra_softmax_rows_bwd.restype = ctypes.c_int
+    lib.ra_rope_neox.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int,
+                                 ctypes.c_int, _vp]
+    lib.ra_rope_neox.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -262,6 +265,59 @@ def ra_attention(q, k, v, is_causal: bool = False, scale: Optional[float] = None
     D = q.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     return _FN.apply(q, k, v, bool(is_causal), scale)
+
+
+def ra_rope_neox(x, y, positions, mats, N, D, theta, inverse, dtype, stream=None) -> int:
+    return load_library().ra_rope_neox(_ptr(x), _ptr(y), _ptr(positions), mats, N, D,
+                                       float(theta), int(bool(inverse)), int(dtype),
+                                       _stream(stream))
+
+
+def _rope_apply(x, theta, positions, inverse):
+    import torch
+    xc = x.contiguous()
+    N, D = xc.shape[-2], xc.shape[-1]
+    mats = xc.numel() // max(N * D, 1)
+    pos = None
+    if positions is not None:
+        pos = torch.as_tensor(positions, dtype=torch.int32, device=xc.device).contiguous()
+        if pos.numel() != N:
+            raise ValueError("positions must have one entry per row (axis -2)")
+    y = torch.empty_like(xc)
+    _check(ra_rope_neox(xc, y, pos, mats, N, D, theta, inverse, _dtype_code(xc)), "ra_rope_neox")
+    return y
+
+
+class _RopeFn:
+    _cls = None
+
+    @classmethod
+    def get(cls):
+        if cls._cls is None:
+            import torch
+
+            class Fn(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, x, theta, positions, inverse):
+                    ctx.args = (theta, positions, inverse)
+                    return _rope_apply(x, theta, positions, inverse)
+
+                @staticmethod
+                def backward(ctx, dy):
+                    theta, positions, inverse = ctx.args
+                    return _rope_apply(dy, theta, positions, not inverse), None, None, None
+
+            cls._cls = Fn
+        return cls._cls
+
+
+def ra_rope(x, theta: float = 10000.0, positions=None, inverse: bool = False):
+    """NEOX (split-halves) rotary embedding along the last axis of x [..., N, D], positions on
+    axis -2 (default 0..N-1), with autograd (the gradient is the inverse rotation)."""
+    import torch
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("ra_rope supports float32 and bfloat16")
+    return _RopeFn.get().apply(x, float(theta), positions, bool(inverse))
 
 
 def _softmax_rows_2d(x):

@@ -220,4 +220,20 @@ int ra_softmax_rows_bwd(const void* x, const void* dp, void* dx, int64_t rows, i
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int ra_rope_neox(const void* x, void* y, const int32_t* positions, int64_t mats, int64_t N,
+                 int64_t D, double theta, int inverse, int dtype, void* stream) {
+  if (dtype != RA_F32 && dtype != RA_BF16) return RA_ERR_DTYPE;
+  if (mats < 0 || N < 0 || D < 0) return RA_ERR_SHAPE;
+  if (D % 2 != 0) return RA_ERR_HEADDIM;
+  if (!(theta > 0.0) || !isfinite(theta)) return RA_ERR_SCALE;
+  if (N >= kIndexLimit || D >= kIndexLimit || (__int128)N * D >= kIndexLimit) return RA_ERR_TOO_LARGE;
+  if (mats == 0 || N == 0 || D == 0) return RA_OK;
+  if (x == nullptr || y == nullptr) return RA_ERR_NULLPTR;
+  const int es = elem_size(dtype);
+  if (!aligned(x, es) || !aligned(y, es) || (positions != nullptr && !aligned(positions, 4)))
+    return RA_ERR_ALIGN;
+  return hip_status(ra::launch_rope_neox(x, y, positions, mats, N, D, theta, inverse != 0,
+                                         dtype == RA_BF16, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -49,6 +49,10 @@ hipError_t launch_softmax_rows(const void* x, void* p, int64_t rows, int64_t col
 hipError_t launch_softmax_rows_bwd(const void* x, const void* dp, void* dx, int64_t rows,
                                    int64_t cols, bool bf16, hipStream_t stream);
 
+// NEOX rotary embedding of `mats` [N, D] matrices (positions nullable: 0..N-1).
+hipError_t launch_rope_neox(const void* x, void* y, const int* positions, int64_t mats, int64_t N,
+                            int64_t D, double theta, bool inverse, bool bf16, hipStream_t stream);
+
 // Fill helpers (a kernel, not hipMemsetAsync, so the calls stay graph-capture friendly).
 hipError_t launch_fill_u32(void* dst, uint32_t value, size_t count, hipStream_t stream);
 hipError_t launch_fill_u16(void* dst, uint16_t value, size_t count, hipStream_t stream);

@@ -163,6 +163,22 @@ def test_softmax_rows_bwd_validation(lib):
     assert f(None, None, None, 4, 0, ra.RA_F32, 0) == OK
 
 
+def test_rope_validation(lib):
+    f = ra.ra_rope_neox
+    assert f(P, P2, None, 2, 8, 64, 10000.0, 0, 7, 0) == DTYPE
+    assert f(P, P2, None, -1, 8, 64, 10000.0, 0, ra.RA_F32, 0) == SHAPE
+    assert f(P, P2, None, 2, 8, 63, 10000.0, 0, ra.RA_F32, 0) == HEADDIM
+    for th in (0.0, -1.0, math.inf, math.nan):
+        assert f(P, P2, None, 2, 8, 64, th, 0, ra.RA_F32, 0) == SCALE
+    assert f(P, P2, None, 2, 1 << 26, 64, 10000.0, 0, ra.RA_F32, 0) == TOO_LARGE
+    assert f(None, P2, None, 2, 8, 64, 10000.0, 0, ra.RA_F32, 0) == NULLPTR
+    assert f(P, None, None, 2, 8, 64, 10000.0, 0, ra.RA_F32, 0) == NULLPTR
+    assert f(P + 2, P2, None, 2, 8, 64, 10000.0, 0, ra.RA_F32, 0) == ALIGN
+    assert f(P, P2, P + 2, 2, 8, 64, 10000.0, 0, ra.RA_F32, 0) == ALIGN
+    assert f(P, P2, None, 0, 8, 64, 10000.0, 0, ra.RA_F32, 0) == OK
+    assert f(None, None, None, 2, 0, 64, 10000.0, 0, ra.RA_F32, 0) == OK
+
+
 def test_product_path_has_no_fallback():
     # The binding must not reach the oracle or any CPU implementation.
     import rational_softmax_tiled_amd
