@@ -6,6 +6,7 @@ Pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_pins.py``.
 """
 from .ra_oracle import (  # noqa: F401
     SUPPORT_WIDTH,
+    causal_offset,
     ra_attention_bwd,
     ra_attention_fwd,
     ra_phi,

@@ -32,11 +32,21 @@ Readings where the pages are silent (each is listed in the design notes):
 * The row max is part of the function: the backward differentiates through it
   (term R below).  For the exp softmax that term vanishes; for phi it does not.
 * Ties for the row max resolve to the lowest key index.
-* Causal masking is top-left aligned (key j allowed for query i iff j <= i),
-  as scaled_dot_product_attention's is_causal.
+* Causal masking is top-left aligned by default (key j allowed for query i iff
+  j <= i), as scaled_dot_product_attention's is_causal.  The pages do not say
+  how the diagonal sits when Nq != Nk; the bottom-right alignment (query i
+  takes keys j <= i + Nk - Nq, so the last query sees every key, the layout of
+  queries that continue a key sequence) is offered as a second mode.
+* An explicit mask follows scaled_dot_product_attention's attn_mask, for which
+  ra_attention is the drop-in: a boolean mask takes part where it is True, a
+  floating mask is added to the scaled scores before the row max.  The
+  CrossAttention key padding mask of the "Primitives" page (1 = attend) is the
+  boolean case broadcast over heads and query rows.  The mask is a constant:
+  no gradient flows to it.
 * Masked entries (-inf logits, or keys outside the causal set) are excluded
   from the max and from sum(phi), and get p = 0.  A row with no allowed entry
-  gives p = 0 and O = 0.
+  gives p = 0 and O = 0 (the "Primitives" page, CrossAttention: a fully masked
+  row produces a zero context, not NaN), and zero gradients.
 """
 from __future__ import annotations
 
@@ -44,6 +54,7 @@ import numpy as np
 
 __all__ = [
     "SUPPORT_WIDTH",
+    "causal_offset",
     "ra_phi",
     "ra_softmax_rows",
     "ra_softmax_rows_bwd",
@@ -178,21 +189,57 @@ def _check_attention_shapes(q, k, v):
     return B, Hq, Hkv, Nq, Nk, D, Hq // Hkv
 
 
-def _allowed(Nq, Nk, causal, q_positions):
+CAUSAL_MODES = {False: None, 0: None, None: None, True: "top_left", 1: "top_left",
+                "top_left": "top_left", 2: "bottom_right", "bottom_right": "bottom_right"}
+
+
+def causal_offset(causal, Nq, Nk):
+    """Diagonal offset of the causal set (key j allowed for query i iff j <= i + offset), or
+    None without causal masking.  Top-left: 0; bottom-right: Nk - Nq."""
+    if causal not in CAUSAL_MODES:
+        raise ValueError(f"unknown causal mode {causal!r}")
+    mode = CAUSAL_MODES[causal]
+    if mode is None:
+        return None
+    return 0 if mode == "top_left" else Nk - Nq
+
+
+def _allowed(Nq, Nk, causal, q_positions, nq_total=None):
     pos = np.arange(Nq) if q_positions is None else np.asarray(q_positions)
-    if not causal:
+    off = causal_offset(causal, Nq if nq_total is None else nq_total, Nk)
+    if off is None:
         return np.ones((len(pos), Nk), dtype=bool)
-    return np.arange(Nk)[None, :] <= pos[:, None]
+    return np.arange(Nk)[None, :] <= pos[:, None] + off
 
 
-def ra_attention_fwd(q, k, v, causal, scale, q_positions=None, heads=None):
-    """O = ra_softmax(scale * Q K^T) V with GQA and optional causal mask.
+def _scores(qh, kg, scale, allowed, mask, b, h, shape):
+    """Scaled scores of one (batch, head) and the entries that take part: the causal set, the
+    True entries of a boolean mask, or the additive mask added to the scaled scores (its -inf
+    entries drop out)."""
+    s = scale * (qh @ kg.T)
+    if mask is None:
+        return s, allowed
+    mb = np.broadcast_to(mask, shape)[b, h]
+    if mb.dtype == np.bool_:
+        return s, allowed & mb
+    s = s + mb.astype(np.float64)
+    return s, allowed & ~np.isneginf(s)
+
+
+def ra_attention_fwd(q, k, v, causal, scale, q_positions=None, heads=None, mask=None,
+                     nq_total=None):
+    """O = ra_softmax(scale * Q K^T + mask) V with GQA and optional causal mask.
 
     q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D]; query head h reads K/V head
-    h // (Hq/Hkv).  ``q_positions`` gives the absolute positions of the
-    supplied query rows for the causal test (default 0..Nq-1), so a sample of
-    rows can be checked on its own.  ``heads`` restricts the work to a list of
-    (b, h) pairs (other heads of the outputs stay zero / -inf).
+    h // (Hq/Hkv).  ``causal``: False, True / "top_left" or "bottom_right".
+    ``mask``: None, or an array broadcastable to [B, Hq, Nq, Nk]: boolean
+    (True = attend) or floating (added to the scaled scores; -inf = masked).
+    ``q_positions`` gives the absolute positions of the supplied query rows for
+    the causal test (default 0..Nq-1) and ``nq_total`` the full query length
+    (default Nq, used by the bottom-right offset), so a sample of rows can be
+    checked on its own; a mask then covers the supplied rows only.  ``heads``
+    restricts the work to a list of (b, h) pairs (other heads of the outputs
+    stay zero / -inf).
 
     Returns (O, m, l, a): m is the row max of the scaled scores s, l the sum of
     phi, a the lowest key index attaining the max (-1 for an empty row).
@@ -201,7 +248,8 @@ def ra_attention_fwd(q, k, v, causal, scale, q_positions=None, heads=None):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, Hq, Hkv, Nq, Nk, D, rep = _check_attention_shapes(q, k, v)
-    allowed = _allowed(Nq, Nk, causal, q_positions)
+    allowed = _allowed(Nq, Nk, causal, q_positions, nq_total)
+    mask = None if mask is None else np.asarray(mask)
     o = np.zeros((B, Hq, Nq, v.shape[3]))
     m = np.full((B, Hq, Nq), -np.inf)
     l = np.zeros((B, Hq, Nq))
@@ -209,8 +257,8 @@ def ra_attention_fwd(q, k, v, causal, scale, q_positions=None, heads=None):
     todo = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
     for b, h in todo:
         g = h // rep
-        s = scale * (q[b, h] @ k[b, g].T)
-        mb, ab, _, phi = _row_stats(s, allowed)
+        s, allowed_bh = _scores(q[b, h], k[b, g], scale, allowed, mask, b, h, (B, Hq, Nq, Nk))
+        mb, ab, _, phi = _row_stats(s, allowed_bh)
         lb = phi.sum(axis=-1)
         with np.errstate(invalid="ignore", divide="ignore"):
             p = np.where(lb[:, None] > 0, phi / lb[:, None], 0.0)
@@ -219,14 +267,15 @@ def ra_attention_fwd(q, k, v, causal, scale, q_positions=None, heads=None):
     return o, m, l, a
 
 
-def ra_attention_bwd(q, k, v, do, causal, scale, groups=None):
+def ra_attention_bwd(q, k, v, do, causal, scale, groups=None, mask=None):
     """Gradients (dQ, dK, dV) of L = sum(O * dO) for ra_attention_fwd.
 
     Follows the chain rule in the forward's order: dP = dO V^T; the softmax
     vector-Jacobian product (direct closed-form term plus the row-max term);
     dQ = scale dS K; dK and dV are summed over the REP query heads that share
     a K/V head.  ``groups`` restricts the work to a list of (b, g) K/V groups
-    (all their query heads are processed).
+    (all their query heads are processed).  ``causal`` and ``mask`` as in
+    ra_attention_fwd (the mask gets no gradient).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -236,14 +285,15 @@ def ra_attention_bwd(q, k, v, do, causal, scale, groups=None):
     if do.shape != q.shape[:3] + v.shape[3:]:
         raise ValueError("dO must have the shape of O")
     allowed = _allowed(Nq, Nk, causal, None)
+    mask = None if mask is None else np.asarray(mask)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     todo = [(b, g) for b in range(B) for g in range(Hkv)] if groups is None else groups
     for b, g in todo:
         for h in range(g * rep, (g + 1) * rep):
-            s = scale * (q[b, h] @ k[b, g].T)
-            _, a, delta, phi = _row_stats(s, allowed)
+            s, allowed_bh = _scores(q[b, h], k[b, g], scale, allowed, mask, b, h, (B, Hq, Nq, Nk))
+            _, a, delta, phi = _row_stats(s, allowed_bh)
             lb = phi.sum(axis=-1)
             with np.errstate(invalid="ignore", divide="ignore"):
                 p = np.where(lb[:, None] > 0, phi / lb[:, None], 0.0)

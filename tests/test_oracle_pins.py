@@ -351,6 +351,204 @@ def test_bwd_max_path_term_is_needed():
     assert np.abs(dq_bad - fd).max() > 1e-3
 
 
+# ------------------------------------------------------------- masks and causal alignment
+
+def test_key_padding_equals_dropping_keys():
+    # A key that is masked out for a sample must act exactly as if it were absent.
+    rng = np.random.default_rng(40)
+    B, Hq, Hkv, Nq, Nk, D = 2, 4, 2, 5, 9, 4
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, Nq, Nk, D, sigma=1.5)
+    do = rng.normal(size=q.shape)
+    keep = np.ones((B, Nk), bool)
+    keep[0, [1, 4, 8]] = False
+    keep[1, [0, 2]] = False
+    kpm = keep[:, None, None, :]
+    o, m, l, a = oracle.ra_attention_fwd(q, k, v, False, 0.6, mask=kpm)
+    dq, dk, dv = oracle.ra_attention_bwd(q, k, v, do, False, 0.6, mask=kpm)
+    for b in range(B):
+        kb, vb = k[b:b + 1][:, :, keep[b]], v[b:b + 1][:, :, keep[b]]
+        o1, m1, l1, a1 = oracle.ra_attention_fwd(q[b:b + 1], kb, vb, False, 0.6)
+        np.testing.assert_allclose(o[b:b + 1], o1, rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(m[b:b + 1], m1)
+        np.testing.assert_array_equal(a[b:b + 1], np.nonzero(keep[b])[0][a1])
+        dq1, dk1, dv1 = oracle.ra_attention_bwd(q[b:b + 1], kb, vb, do[b:b + 1], False, 0.6)
+        np.testing.assert_allclose(dq[b:b + 1], dq1, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(dk[b:b + 1][:, :, keep[b]], dk1, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(dv[b:b + 1][:, :, keep[b]], dv1, rtol=0, atol=1e-14)
+        assert (dk[b][:, ~keep[b]] == 0).all() and (dv[b][:, ~keep[b]] == 0).all()
+
+
+def test_all_true_mask_and_zero_bias_change_nothing():
+    rng = np.random.default_rng(41)
+    q, k, v = _rand_qkv(rng, 1, 2, 1, 6, 7, 4, sigma=1.5)
+    for causal in (False, "top_left", "bottom_right"):
+        ref = oracle.ra_attention_fwd(q, k, v, causal, 0.5)
+        for mask in (np.ones((6, 7), bool), np.zeros((1, 1, 6, 7))):
+            got = oracle.ra_attention_fwd(q, k, v, causal, 0.5, mask=mask)
+            for x, y in zip(ref, got):
+                np.testing.assert_array_equal(x, y)
+
+
+def test_additive_mask_worked_example():
+    # Scores scale * q.k = [2, 1, 0] (q = 1, k = 2, 1, 0, scale 1) and V = I, so O = p.
+    q = np.ones((1, 1, 1, 1))
+    k = np.array([2.0, 1.0, 0.0]).reshape(1, 1, 3, 1)
+    v = np.eye(3).reshape(1, 1, 3, 3)
+    # bias (0, -7, +2) -> logits (2, -6, 2): the max 2 is tied at keys 0 and 2 (lowest: 0),
+    # Delta = (0, 8, 0), u = (0, 1/2, 0), phi = (1, (1/3)^8, 1)
+    o, m, l, a = oracle.ra_attention_fwd(q, k, v, False, 1.0, mask=np.array([0.0, -7.0, 2.0]))
+    third8 = Fraction(1, 3) ** 8
+    lsum = 2 + third8
+    np.testing.assert_allclose(o[0, 0, 0], [float(1 / lsum), float(third8 / lsum), float(1 / lsum)],
+                               rtol=1e-15, atol=0)
+    assert m[0, 0, 0] == 2.0 and a[0, 0, 0] == 0 and l[0, 0, 0] == pytest.approx(float(lsum), abs=1e-15)
+    # bias (0, -inf, 0) drops key 1: Delta = (0, -, 2), phi(2) = ((1 - 1/8) / (1 + 1/8))^8 = (7/9)^8
+    o, m, l, a = oracle.ra_attention_fwd(q, k, v, False, 1.0, mask=np.array([0.0, -np.inf, 0.0]))
+    p2 = Fraction(7, 9) ** 8
+    np.testing.assert_allclose(o[0, 0, 0], [float(1 / (1 + p2)), 0.0, float(p2 / (1 + p2))],
+                               rtol=1e-15, atol=0)
+    assert o[0, 0, 0, 1] == 0.0 and a[0, 0, 0] == 0
+
+
+def test_row_constant_bias_changes_nothing():
+    # phi depends on Delta = max - s only, so a constant added to a whole row changes nothing
+    rng = np.random.default_rng(42)
+    q, k, v = _rand_qkv(rng, 2, 2, 1, 5, 6, 3, sigma=1.5)
+    do = rng.normal(size=q.shape)
+    bias = np.broadcast_to(rng.normal(0, 3, size=(2, 2, 5, 1)), (2, 2, 5, 6))
+    ref_o = oracle.ra_attention_fwd(q, k, v, True, 0.7)[0]
+    got_o = oracle.ra_attention_fwd(q, k, v, True, 0.7, mask=bias)[0]
+    np.testing.assert_allclose(got_o, ref_o, rtol=0, atol=1e-13)
+    for x, y in zip(oracle.ra_attention_bwd(q, k, v, do, True, 0.7),
+                    oracle.ra_attention_bwd(q, k, v, do, True, 0.7, mask=bias)):
+        np.testing.assert_allclose(y, x, rtol=0, atol=1e-12)
+
+
+def test_bool_false_equals_minus_inf_bias():
+    rng = np.random.default_rng(43)
+    q, k, v = _rand_qkv(rng, 1, 3, 3, 6, 8, 4, sigma=1.5)
+    do = rng.normal(size=q.shape)
+    mb = rng.random((1, 3, 6, 8)) < 0.7
+    mf = np.where(mb, 0.0, -np.inf)
+    for x, y in zip(oracle.ra_attention_fwd(q, k, v, False, 0.5, mask=mb),
+                    oracle.ra_attention_fwd(q, k, v, False, 0.5, mask=mf)):
+        np.testing.assert_array_equal(x, y)
+    for x, y in zip(oracle.ra_attention_bwd(q, k, v, do, False, 0.5, mask=mb),
+                    oracle.ra_attention_bwd(q, k, v, do, False, 0.5, mask=mf)):
+        np.testing.assert_array_equal(x, y)
+
+
+def _brute_attention(q, k, v, scale, allowed):
+    """One head, pure Python loops, straight from the definitions (tiny inputs only)."""
+    Nq, Nk, D = len(q), len(k), len(v[0])
+    out = []
+    for i in range(Nq):
+        s = {j: scale * sum(q[i][d] * k[j][d] for d in range(len(q[i]))) for j in range(Nk)
+             if allowed(i, j)}
+        if not s:
+            out.append([0.0] * D)
+            continue
+        mx = max(s.values())
+        phi = {}
+        for j, x in s.items():
+            u = (mx - x) / 16.0
+            phi[j] = ((1 - u) / (1 + u)) ** 8 if u < 1 else 0.0
+        tot = sum(phi.values())
+        out.append([sum(phi[j] / tot * v[j][d] for j in phi) for d in range(D)])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(3, 7), (7, 3), (5, 5), (1, 6), (6, 1)])
+def test_bottom_right_causal_brute_force(Nq, Nk):
+    rng = np.random.default_rng(44 + Nq * 10 + Nk)
+    q, k, v = _rand_qkv(rng, 1, 1, 1, Nq, Nk, 3, sigma=1.5)
+    o = oracle.ra_attention_fwd(q, k, v, "bottom_right", 0.9)[0]
+    ref = _brute_attention(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), 0.9,
+                           lambda i, j: j <= i + Nk - Nq)
+    np.testing.assert_allclose(o[0, 0], ref, rtol=0, atol=1e-14)
+    top = oracle.ra_attention_fwd(q, k, v, "top_left", 0.9)[0]
+    ref_top = _brute_attention(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), 0.9,
+                               lambda i, j: j <= i)
+    np.testing.assert_allclose(top[0, 0], ref_top, rtol=0, atol=1e-14)
+    if Nq == Nk:
+        np.testing.assert_array_equal(o, top)
+    else:
+        assert not np.allclose(o, top)
+
+
+def test_bottom_right_is_the_tail_of_a_square_problem():
+    # Nq <= Nk: the queries continue a sequence whose first Nk - Nq queries are not asked for.
+    rng = np.random.default_rng(45)
+    q, k, v = _rand_qkv(rng, 2, 4, 2, 4, 10, 3, sigma=1.5)
+    do = rng.normal(size=q.shape)
+    qfull = np.concatenate([rng.normal(size=(2, 4, 6, 3)), q], axis=2)
+    dofull = np.concatenate([np.zeros((2, 4, 6, 3)), do], axis=2)
+    o = oracle.ra_attention_fwd(q, k, v, "bottom_right", 0.8)[0]
+    np.testing.assert_array_equal(o, oracle.ra_attention_fwd(qfull, k, v, True, 0.8)[0][:, :, 6:])
+    dq, dk, dv = oracle.ra_attention_bwd(q, k, v, do, "bottom_right", 0.8)
+    fq, fk, fv = oracle.ra_attention_bwd(qfull, k, v, dofull, True, 0.8)
+    np.testing.assert_allclose(dq, fq[:, :, 6:], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(dk, fk, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(dv, fv, rtol=0, atol=1e-14)
+
+
+def test_fully_masked_rows_are_zero_not_nan():
+    rng = np.random.default_rng(46)
+    B, Hq, Hkv, Nq, Nk, D = 1, 2, 1, 7, 4, 3
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, Nq, Nk, D, sigma=1.5)
+    do = rng.normal(size=q.shape)
+    mask = np.ones((B, Hq, Nq, Nk), bool)
+    mask[0, 1, 5] = False                      # an explicit fully masked row
+    # bottom-right with Nq > Nk: rows 0..2 have no key at all
+    o, m, l, a = oracle.ra_attention_fwd(q, k, v, "bottom_right", 0.5, mask=mask)
+    dq, dk, dv = oracle.ra_attention_bwd(q, k, v, do, "bottom_right", 0.5, mask=mask)
+    dead = np.zeros((B, Hq, Nq), bool)
+    dead[:, :, :Nq - Nk] = True
+    dead[0, 1, 5] = True
+    for x in (o, dq, dk, dv):
+        assert np.isfinite(x).all()
+    assert (o[dead] == 0).all() and (dq[dead] == 0).all()
+    assert (m[dead] == -np.inf).all() and (l[dead] == 0).all() and (a[dead] == -1).all()
+    assert (l[~dead] >= 1).all() and np.isfinite(m[~dead]).all()
+
+
+def test_sampled_rows_with_bottom_right_offset():
+    rng = np.random.default_rng(47)
+    q, k, v = _rand_qkv(rng, 1, 2, 1, 9, 13, 4, sigma=1.5)
+    mask = rng.random((1, 2, 9, 13)) < 0.8
+    full = oracle.ra_attention_fwd(q, k, v, "bottom_right", 0.5, mask=mask)
+    rows = np.array([0, 4, 8])
+    part = oracle.ra_attention_fwd(q[:, :, rows], k, v, "bottom_right", 0.5, q_positions=rows,
+                                   nq_total=9, mask=mask[:, :, rows])
+    for x, y in zip(full, part):
+        np.testing.assert_array_equal(x[:, :, rows], y)
+
+
+@pytest.mark.parametrize("case", ["keypad_bottom_right", "bias_top_left", "bias_bool_none"])
+def test_masked_attention_bwd_matches_central_differences(case):
+    rng = np.random.default_rng(48)
+    B, Hq, Hkv, Nq, Nk, D = 1, 2, 1, 4, 6, 3
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, Nq, Nk, D, sigma=1.5)
+    do = rng.normal(size=q.shape)
+    if case == "keypad_bottom_right":
+        causal, mask = "bottom_right", np.array([True, False, True, True, False, True])[None, None, None]
+    elif case == "bias_top_left":
+        causal, mask = "top_left", rng.normal(0, 2, size=(1, 1, Nq, Nk))
+    else:
+        bias = rng.normal(0, 2, size=(B, Hq, Nq, Nk))
+        bias[rng.random(bias.shape) < 0.25] = -np.inf
+        causal, mask = False, bias
+    scale = 0.8
+    dq, dk, dv = oracle.ra_attention_bwd(q, k, v, do, causal, scale, mask=mask)
+
+    def loss(qq, kk, vv):
+        return float((oracle.ra_attention_fwd(qq, kk, vv, causal, scale, mask=mask)[0] * do).sum())
+
+    np.testing.assert_allclose(dq, _fd_grad(lambda z: loss(z, k, v), q), rtol=0, atol=3e-8)
+    np.testing.assert_allclose(dk, _fd_grad(lambda z: loss(q, z, v), k), rtol=0, atol=3e-8)
+    np.testing.assert_allclose(dv, _fd_grad(lambda z: loss(q, k, z), v), rtol=0, atol=3e-8)
+
+
 def test_planted_phi_exponent_error_breaks_golden():
     # Planted mistake: phi = q^7 instead of q^8 must fail the worked-example pin.
     import oracle.ra_oracle as ro
