@@ -9,7 +9,9 @@ forward + backward.  Prints one JSON line.
 
 Also reported: the forward alone on this workload and on the grouped-query workload
 (B=4, Hq=32, Hkv=8, N=4096, D=128, host RoPE), the two backward phases (ra_attn_bwd_dq,
-ra_attn_bwd_dkdv) alone, the row softmax and its backward at [16384, 8192], a roofline object for the
+ra_attn_bwd_dkdv) alone, a padded batch through the explicit-mask entry points (B=4, H=16,
+N=4096, D=128, causal, key padding mask with per-sample lengths) beside the same workload
+unmasked, the row softmax and its backward at [16384, 8192], a roofline object for the
 dominant kernel (the longest of the forward, dQ and dK/dV kernels, each timed alone with HIP
 events on the stream the library launches it on) and the fp64 oracle timed on a bounded
 sample on the host cores.
@@ -44,12 +46,12 @@ MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("999e756c7c3ec4b5c0005c7edf4494a1e075e35cb8788722c94c057fcba3d9f5",
-                        262389.5, 135210.7),
-    "attn_bwd_dq_bf16_kernel": ("34070eb4fe6ddf359d94a38466a7fdfcc16c99da59e24f1eaa3e7cf1bdd280b2",
-                                436229.6, 143475.5),
-    "attn_bwd_dkdv_bf16_kernel": ("34070eb4fe6ddf359d94a38466a7fdfcc16c99da59e24f1eaa3e7cf1bdd280b2",
-                                  273031.1, 274325.4),
+    "attn_fwd_kernel": ("e229c2aa2d32bd1a8d25815dc54f9c374c23d70506011bd5c0935941b15869fb",
+                        262687.6, 135188.6),
+    "attn_bwd_dq_bf16_kernel": ("22ec73d818cbcef5ba8b2caa94d4418363582ddf35747528875310d8d94e5412",
+                                437394.7, 143448.3),
+    "attn_bwd_dkdv_bf16_kernel": ("22ec73d818cbcef5ba8b2caa94d4418363582ddf35747528875310d8d94e5412",
+                                  268073.4, 262146.6),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],
@@ -113,6 +115,23 @@ class Attn:
                                  w.Nk, w.D, int(w.causal), w.scale, self.code, self.stream)
         if st != 0:
             raise RuntimeError(f"ra_attn_bwd: {self.ra.ra_status_string(st)}")
+
+    def fwd_masked(self, mask):
+        w = self.w
+        st = self.ra.ra_attn_fwd_masked(self.q, self.k, self.v, self.o, self.stats, w.B, w.Hq,
+                                        w.Hkv, w.Nq, w.Nk, w.D, int(w.causal), w.scale, self.code,
+                                        *mask, self.stream)
+        if st != 0:
+            raise RuntimeError(f"ra_attn_fwd_masked: {self.ra.ra_status_string(st)}")
+
+    def bwd_masked(self, mask):
+        w = self.w
+        st = self.ra.ra_attn_bwd_masked(self.q, self.k, self.v, self.o, self.do, self.stats,
+                                        self.dq, self.dk, self.dv, self.ws, self.ws_bytes, w.B,
+                                        w.Hq, w.Hkv, w.Nq, w.Nk, w.D, int(w.causal), w.scale,
+                                        self.code, *mask, self.stream)
+        if st != 0:
+            raise RuntimeError(f"ra_attn_bwd_masked: {self.ra.ra_status_string(st)}")
 
     def bwd_dq(self):
         w = self.w
@@ -281,6 +300,26 @@ def main():
     del gqa
     torch.cuda.empty_cache()
 
+    # explicit-mask path: a padded batch, key padding mask [B, N] (1 = attend) on top of causal
+    wp = wl.padded_batch_workload()
+    log(f"generating {wp.name}")
+    pad = Attn(ra, wp, True)
+    keep = torch.from_numpy(wl.padded_batch_keep(wp)).cuda()
+    kpm = (keep, ra.RA_MASK_BOOL, (wp.Nk, 0, 0, 1))
+    pad_masked = lambda: (pad.fwd_masked(kpm), pad.bwd_masked(kpm))
+    pad_plain = lambda: (pad.fwd(), pad.bwd())
+    for _ in range(3):
+        pad_masked()
+        pad_plain()
+    pm_ms = time_calls(pad.stream, pad_masked, n_k)
+    pp_ms = time_calls(pad.stream, pad_plain, n_k)
+    pmf_ms = time_calls(pad.stream, lambda: pad.fwd_masked(kpm), n_k)
+    pm_tflops = wp.counted_flops_fwd_bwd() / (pm_ms * 1e-3) / 1e12
+    log(f"padded batch (key padding, causal) fwd+bwd {pm_ms:.3f} ms ({pm_tflops:.1f} TFLOP/s "
+        f"counted as the unmasked causal workload), forward {pmf_ms:.3f} ms; unmasked {pp_ms:.3f} ms")
+    del pad, keep
+    torch.cuda.empty_cache()
+
     # row softmax (HBM-bound): read + write once
     x = torch.from_numpy(wl.make_rows(16384, 8192, seed=11)).cuda()
     p = torch.empty_like(x)
@@ -344,6 +383,11 @@ def main():
         "fwd_gqa": {"workload": wg.name, "ms": round(gqa_ms, 4), "tflops": round(gqa_tflops, 2),
                     "frac_of_peak": round(gqa_tflops / PEAK_BF16_TFLOPS, 4),
                     "device_rope_ms": round(rope_ms, 4), "device_rope_GB/s": round(rope_gbs, 1)},
+        "masked_padded_batch": {"workload": wp.name, "lengths": list(wl.padded_batch_lengths(wp)),
+                                "mask": "key padding [B, N] bool, causal top-left",
+                                "fwd_bwd_ms": round(pm_ms, 4), "fwd_ms": round(pmf_ms, 4),
+                                "tflops_counted": round(pm_tflops, 2),
+                                "unmasked_fwd_bwd_ms": round(pp_ms, 4)},
         "softmax_rows": {"shape": [16384, 8192], "dtype": "f32", "ms": round(sm_ms, 4),
                          "GB/s": round(sm_gbs, 1), "frac_of_hbm_peak": round(sm_gbs / PEAK_HBM_GBS, 4)},
         "softmax_rows_bwd": {"shape": [16384, 8192], "dtype": "f32", "ms": round(smb_ms, 4),

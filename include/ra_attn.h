@@ -15,9 +15,13 @@
  *   - dtype: RA_F32 (fp32 storage, fp32 matrix-core products) or RA_BF16 (bf16 storage,
  *     fp32 accumulation; probabilities are rounded to bf16 to nearest-even before the
  *     P.V product).
- *   - causal != 0 allows key j for query i iff j <= i (top-left alignment, as
- *     scaled_dot_product_attention's is_causal).  Masked keys get p = 0 and take no part in
- *     the row max or the sum of phi.
+ *   - causal: RA_CAUSAL_NONE (0); RA_CAUSAL_TOP_LEFT (1) allows key j for query i iff j <= i
+ *     (scaled_dot_product_attention's is_causal); RA_CAUSAL_BOTTOM_RIGHT (2) allows j <= i +
+ *     Nk - Nq, so the last query sees every key (queries that continue the key sequence; the
+ *     pages fix no alignment for Nq != Nk, and the two agree when Nq == Nk).  Any other value
+ *     -> RA_ERR_MASK.  Masked keys get p = 0 and take no part in the row max or the sum of
+ *     phi.  A query row with no allowed key gives o = 0 (stats m = -inf, l = 0) and dq = 0,
+ *     not NaN ("Primitives" page, CrossAttention: a fully masked row gives a zero context).
  *   - stream is a hipStream_t (NULL = the default stream).  Kernels run asynchronously on it;
  *     the caller keeps every buffer alive until the stream has passed the call.
  *   - The caller owns all memory.  The library allocates nothing, frees nothing, does not
@@ -53,8 +57,40 @@ typedef enum ra_status {
   RA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than ra_attn_bwd_workspace_bytes */
   RA_ERR_ALIGN = 8,     /* a pointer breaks the alignment rule above */
   RA_ERR_TOO_LARGE = 9, /* a size exceeds the library's index range (see each call) */
-  RA_ERR_HIP = 10       /* the HIP runtime reported an error at launch */
+  RA_ERR_HIP = 10,      /* the HIP runtime reported an error at launch */
+  RA_ERR_MASK = 11      /* causal mode not 0/1/2, or an invalid ra_mask (kind, strides) */
 } ra_status;
+
+typedef enum ra_causal {
+  RA_CAUSAL_NONE = 0,
+  RA_CAUSAL_TOP_LEFT = 1,
+  RA_CAUSAL_BOTTOM_RIGHT = 2
+} ra_causal;
+
+/*
+ * ra_mask -- an explicit attention mask, the attn_mask of the scaled_dot_product_attention
+ * drop-in (Ra-Family page, section 3, item ra_attention) and the CrossAttention key padding
+ * mask ("Primitives" page, section "Attention and transformers": 1 = attend, 0 = ignore).
+ *   Element (b, h, i, j) -- batch b, query head h, query row i, key j -- is read at element
+ *   offset b*stride_b + h*stride_h + i*stride_q + j*stride_k of data (device memory; strides
+ *   >= 0, a zero stride broadcasts).  A [B, Nk] key padding mask is strides (Nk, 0, 0, 1); one
+ *   [Nq, Nk] mask shared by every batch and head is (0, 0, Nk, 1).
+ *   kind RA_MASK_BOOL: uint8 elements, nonzero = attend, zero = masked.
+ *   kind RA_MASK_ADD: elements of the attention dtype (fp32 or bf16), added to the scaled score
+ *     scale * q_i . k_j before the row max; -inf masks the entry.  Finite values or -inf only.
+ *   kind RA_MASK_NONE (or a NULL ra_mask pointer): no mask.
+ *   The mask is an input constant: no gradient is computed for it.
+ *   Limits: every offset of one (b, h) slice plus tile tails, ((Nq + 64) * stride_q +
+ *   (Nk + 128) * stride_k + 1) elements, below 2^31 bytes -> else RA_ERR_TOO_LARGE.
+ *   data must be aligned to its element size (RA_ERR_ALIGN).
+ */
+typedef enum ra_mask_kind { RA_MASK_NONE = 0, RA_MASK_BOOL = 1, RA_MASK_ADD = 2 } ra_mask_kind;
+
+typedef struct ra_mask {
+  const void* data;
+  int kind;
+  int64_t stride_b, stride_h, stride_q, stride_k;
+} ra_mask;
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* ra_status_string(int status);
@@ -80,6 +116,17 @@ int ra_last_hip_error(void);
 int ra_attn_fwd(const void* q, const void* k, const void* v, void* o, float* stats,
                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
                 int causal, float scale, int dtype, void* stream);
+
+/*
+ * ra_attn_fwd_masked -- ra_attn_fwd with an explicit mask (see ra_mask; NULL = none), on top
+ *   of the causal mode.  p_i = ra_softmax over the allowed keys of scale * q_i . k_j (+ the
+ *   additive mask).  stats m is then the row max of q_i . k_j + mask_ij / scale (the unscaled
+ *   units of ra_attn_fwd).  Same checks, sizes and limits as ra_attn_fwd, plus the ra_mask
+ *   checks (RA_ERR_MASK, RA_ERR_ALIGN, RA_ERR_TOO_LARGE).
+ */
+int ra_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* stats,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                       int causal, float scale, int dtype, const ra_mask* mask, void* stream);
 
 /*
  * ra_attn_fwd_counted -- ra_attn_fwd plus tile-skip counters (diagnostics, not for timing).
@@ -124,6 +171,17 @@ int ra_attn_bwd(const void* q, const void* k, const void* v, const void* o, cons
                 const float* stats, void* dq, void* dk, void* dv, void* workspace,
                 size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
                 int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream);
+
+/*
+ * ra_attn_bwd_masked -- ra_attn_bwd for ra_attn_fwd_masked: the same mask (and causal mode)
+ *   must be passed as to the forward that produced o and stats.  Masked entries get P = 0 and
+ *   dS = 0; the mask receives no gradient.  Checks as ra_attn_bwd plus the ra_mask checks.
+ */
+int ra_attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                       const float* stats, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                       int64_t Nk, int64_t D, int causal, float scale, int dtype,
+                       const ra_mask* mask, void* stream);
 
 /*
  * ra_attn_bwd_dq, ra_attn_bwd_dkdv -- the two phases of ra_attn_bwd, callable on their own

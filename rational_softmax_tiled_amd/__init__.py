@@ -1,10 +1,11 @@
 """rational_softmax_tiled_amd -- rational-softmax attention on AMD MI355X (gfx950).
 
 A thin ctypes binding over ``libra_attn.so``.  The functions named like the C entry points
-(``ra_attn_fwd``, ``ra_attn_fwd_counted``, ``ra_attn_bwd``, ``ra_attn_bwd_dq``,
-``ra_attn_bwd_dkdv``, ``ra_attn_bwd_workspace_bytes``, ``ra_softmax_rows``,
-``ra_softmax_rows_bwd``, ``ra_rope_neox``) only marshal arguments: tensors become device pointers, the stream
-becomes a ``hipStream_t``.  Every step of the computation runs in the library's HIP kernels;
+(``ra_attn_fwd``, ``ra_attn_fwd_masked``, ``ra_attn_fwd_counted``, ``ra_attn_bwd``,
+``ra_attn_bwd_masked``, ``ra_attn_bwd_dq``, ``ra_attn_bwd_dkdv``, ``ra_attn_bwd_workspace_bytes``,
+``ra_softmax_rows``, ``ra_softmax_rows_bwd``, ``ra_rope_neox``) only marshal arguments: tensors
+become device pointers, a mask becomes an ``ra_mask`` descriptor, the stream becomes a
+``hipStream_t``.  Every step of the computation runs in the library's HIP kernels;
 there is no CPU or PyTorch fallback, and importing the compute functions without the built
 library raises.
 
@@ -21,8 +22,10 @@ import os
 from typing import Optional
 
 __all__ = [
-    "RA_F32", "RA_BF16", "RaError", "load_library", "library_path",
-    "ra_status_string", "ra_attn_fwd", "ra_attn_fwd_counted", "ra_attn_bwd",
+    "RA_F32", "RA_BF16", "RA_CAUSAL_NONE", "RA_CAUSAL_TOP_LEFT", "RA_CAUSAL_BOTTOM_RIGHT",
+    "RA_MASK_NONE", "RA_MASK_BOOL", "RA_MASK_ADD", "RaMask", "RaError", "load_library",
+    "library_path", "ra_status_string", "ra_attn_fwd", "ra_attn_fwd_masked",
+    "ra_attn_fwd_counted", "ra_attn_bwd", "ra_attn_bwd_masked",
     "ra_attn_bwd_dq", "ra_attn_bwd_dkdv", "ra_attn_bwd_workspace_bytes", "ra_softmax_rows",
     "ra_softmax_rows_bwd", "ra_rope_neox", "ra_rope",
     "attn_fwd", "attn_bwd", "ra_attention", "ra_softmax",
@@ -30,6 +33,15 @@ __all__ = [
 
 RA_F32 = 0
 RA_BF16 = 1
+RA_CAUSAL_NONE, RA_CAUSAL_TOP_LEFT, RA_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
+RA_MASK_NONE, RA_MASK_BOOL, RA_MASK_ADD = 0, 1, 2
+
+
+class RaMask(ctypes.Structure):
+    """The C ``ra_mask`` descriptor: data pointer, kind, element strides over (b, h, i, j)."""
+    _fields_ = [("data", ctypes.c_void_p), ("kind", ctypes.c_int),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_q", ctypes.c_int64), ("stride_k", ctypes.c_int64)]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libra_attn.so")
@@ -71,6 +83,14 @@ def load_library():
     lib.ra_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                 ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp]
     lib.ra_attn_fwd.restype = ctypes.c_int
+    _mp = ctypes.POINTER(RaMask)
+    lib.ra_attn_fwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                       ctypes.c_int, ctypes.c_float, ctypes.c_int, _mp, _vp]
+    lib.ra_attn_fwd_masked.restype = ctypes.c_int
+    lib.ra_attn_bwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _i64,
+                                       ctypes.c_int, ctypes.c_float, ctypes.c_int, _mp, _vp]
+    lib.ra_attn_bwd_masked.restype = ctypes.c_int
     lib.ra_attn_fwd_counted.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                         _i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, _vp]
     lib.ra_attn_fwd_counted.restype = ctypes.c_int
@@ -129,6 +149,26 @@ def ra_attn_fwd(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, 
                                       _stream(stream))
 
 
+def _mask_struct(mask, kind, strides):
+    """A pointer to an RaMask (None for kind RA_MASK_NONE).  A NULL ``mask`` with another kind
+    is passed on, so the library reports it (RA_ERR_NULLPTR)."""
+    if kind == RA_MASK_NONE:
+        return None
+    sb, sh, sq, sk = (int(x) for x in strides)
+    return ctypes.pointer(RaMask(_ptr(mask), int(kind), sb, sh, sq, sk))
+
+
+def ra_attn_fwd_masked(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, mask,
+                       mask_kind, mask_strides, stream=None) -> int:
+    """ra_attn_fwd_masked; ``mask`` (tensor or address), ``mask_kind`` (RA_MASK_*) and
+    ``mask_strides`` (element strides over batch, query head, query row, key) form the
+    ra_mask descriptor."""
+    return load_library().ra_attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(stats), B,
+                                             Hq, Hkv, Nq, Nk, D, int(causal), float(scale),
+                                             int(dtype), _mask_struct(mask, mask_kind, mask_strides),
+                                             _stream(stream))
+
+
 def ra_attn_fwd_counted(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, counters,
                         stream=None) -> int:
     return load_library().ra_attn_fwd_counted(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(stats), B,
@@ -146,6 +186,17 @@ def ra_attn_bwd(q, k, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes, 
                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                       int(workspace_bytes), B, Hq, Hkv, Nq, Nk, D, int(causal),
                                       float(scale), int(dtype), _stream(stream))
+
+
+def ra_attn_bwd_masked(q, k, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                       Nq, Nk, D, causal, scale, dtype, mask, mask_kind, mask_strides,
+                       stream=None) -> int:
+    return load_library().ra_attn_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o),
+                                             _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv),
+                                             _ptr(workspace), int(workspace_bytes), B, Hq, Hkv, Nq,
+                                             Nk, D, int(causal), float(scale), int(dtype),
+                                             _mask_struct(mask, mask_kind, mask_strides),
+                                             _stream(stream))
 
 
 def ra_attn_bwd_dq(q, k, v, o, d_o, stats, dq, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, D,
@@ -205,20 +256,76 @@ def _shapes(q, k, v):
     return B, Hq, Hkv, Nq, Nk, D
 
 
-def attn_fwd(q, k, v, causal: bool, scale: Optional[float] = None, with_stats: bool = True):
-    """Allocate O (and stats) and run ra_attn_fwd on the current stream."""
+def causal_code(is_causal) -> int:
+    """RA_CAUSAL_* for False / True ("top_left", scaled_dot_product_attention's is_causal) /
+    "bottom_right" (or the integer codes)."""
+    if is_causal is None or is_causal is False or (isinstance(is_causal, int) and is_causal == 0):
+        return RA_CAUSAL_NONE
+    if is_causal is True or is_causal == "top_left" or (isinstance(is_causal, int) and is_causal == 1):
+        return RA_CAUSAL_TOP_LEFT
+    if is_causal == "bottom_right" or (isinstance(is_causal, int) and is_causal == 2):
+        return RA_CAUSAL_BOTTOM_RIGHT
+    raise ValueError(f"is_causal must be False, True, 'top_left' or 'bottom_right', not {is_causal!r}")
+
+
+def mask_descriptor(q, k, attn_mask=None, key_padding_mask=None):
+    """(tensor, RA_MASK_* kind, element strides) for the library, or None.
+
+    ``attn_mask`` follows scaled_dot_product_attention: broadcastable to [B, Hq, Nq, Nk];
+    boolean (True = attend) or of q's dtype (added to the scaled scores, -inf masks).  It is
+    passed as a strided view (broadcast dimensions get stride 0), not copied.
+    ``key_padding_mask``: [B, Nk], 1 / True = attend, 0 / False = ignore (the CrossAttention
+    polarity, the inverse of torch's nn.MultiheadAttention key_padding_mask); a non-boolean
+    one becomes a boolean [B, Nk] tensor.  At most one of the two."""
+    import torch
+    if attn_mask is not None and key_padding_mask is not None:
+        raise ValueError("pass attn_mask or key_padding_mask, not both")
+    B, Hq, Nq, _ = q.shape
+    Nk = k.shape[2]
+    if key_padding_mask is not None:
+        kpm = key_padding_mask
+        if tuple(kpm.shape) != (B, Nk):
+            raise ValueError(f"key_padding_mask must be [B, Nk] = [{B}, {Nk}], got {tuple(kpm.shape)}")
+        if kpm.dtype not in (torch.bool, torch.uint8):
+            kpm = kpm != 0
+        if kpm.device != q.device:
+            raise ValueError("key_padding_mask must be on the device of q")
+        return kpm, RA_MASK_BOOL, (kpm.stride(0), 0, 0, kpm.stride(1))
+    if attn_mask is None:
+        return None
+    if attn_mask.device != q.device:
+        raise ValueError("attn_mask must be on the device of q")
+    if attn_mask.dtype == torch.bool:
+        kind = RA_MASK_BOOL
+    elif attn_mask.dtype == q.dtype:
+        kind = RA_MASK_ADD
+    else:
+        raise TypeError(f"attn_mask must be bool or {q.dtype}, not {attn_mask.dtype}")
+    m = attn_mask.expand(B, Hq, Nq, Nk)
+    return m, kind, tuple(m.stride())
+
+
+def attn_fwd(q, k, v, causal, scale: Optional[float] = None, with_stats: bool = True, mask=None):
+    """Allocate O (and stats) and run ra_attn_fwd (ra_attn_fwd_masked with ``mask``, a
+    mask_descriptor) on the current stream.  ``causal``: see causal_code."""
     import torch
     B, Hq, Hkv, Nq, Nk, D = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q)
     stats = torch.empty((B, Hq, Nq, 2), dtype=torch.float32, device=q.device) if with_stats else None
-    _check(ra_attn_fwd(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, _dtype_code(q)),
-           "ra_attn_fwd")
+    cc = causal_code(causal)
+    if mask is None:
+        _check(ra_attn_fwd(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, cc, scale, _dtype_code(q)),
+               "ra_attn_fwd")
+    else:
+        _check(ra_attn_fwd_masked(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, cc, scale,
+                                  _dtype_code(q), *mask), "ra_attn_fwd_masked")
     return o, stats
 
 
-def attn_bwd(q, k, v, o, d_o, stats, causal: bool, scale: Optional[float] = None):
-    """Allocate dQ, dK, dV and a workspace and run ra_attn_bwd on the current stream."""
+def attn_bwd(q, k, v, o, d_o, stats, causal, scale: Optional[float] = None, mask=None):
+    """Allocate dQ, dK, dV and a workspace and run ra_attn_bwd (ra_attn_bwd_masked with
+    ``mask``) on the current stream."""
     import torch
     B, Hq, Hkv, Nq, Nk, D = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
@@ -227,8 +334,13 @@ def attn_bwd(q, k, v, o, d_o, stats, causal: bool, scale: Optional[float] = None
     code = _dtype_code(q)
     nbytes = ra_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, code)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    _check(ra_attn_bwd(q, k, v, o, d_o, stats, dq, dk, dv, ws, nbytes, B, Hq, Hkv, Nq, Nk, D,
-                       causal, scale, code), "ra_attn_bwd")
+    cc = causal_code(causal)
+    if mask is None:
+        _check(ra_attn_bwd(q, k, v, o, d_o, stats, dq, dk, dv, ws, nbytes, B, Hq, Hkv, Nq, Nk, D,
+                           cc, scale, code), "ra_attn_bwd")
+    else:
+        _check(ra_attn_bwd_masked(q, k, v, o, d_o, stats, dq, dk, dv, ws, nbytes, B, Hq, Hkv, Nq,
+                                  Nk, D, cc, scale, code, *mask), "ra_attn_bwd_masked")
     return dq, dk, dv
 
 
@@ -237,17 +349,17 @@ def _autograd_fn():
 
     class _RaAttentionFn(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, causal, scale):
-            o, stats = attn_fwd(q, k, v, causal, scale, with_stats=True)
+        def forward(ctx, q, k, v, causal, scale, mask):
+            o, stats = attn_fwd(q, k, v, causal, scale, with_stats=True, mask=mask)
             ctx.save_for_backward(q, k, v, o, stats)
-            ctx.causal, ctx.scale = causal, scale
+            ctx.causal, ctx.scale, ctx.mask = causal, scale, mask
             return o
 
         @staticmethod
         def backward(ctx, d_o):
             q, k, v, o, stats = ctx.saved_tensors
-            dq, dk, dv = attn_bwd(q, k, v, o, d_o, stats, ctx.causal, ctx.scale)
-            return dq, dk, dv, None, None
+            dq, dk, dv = attn_bwd(q, k, v, o, d_o, stats, ctx.causal, ctx.scale, mask=ctx.mask)
+            return dq, dk, dv, None, None, None
 
     return _RaAttentionFn
 
@@ -255,16 +367,25 @@ def _autograd_fn():
 _FN = None
 
 
-def ra_attention(q, k, v, is_causal: bool = False, scale: Optional[float] = None):
-    """Rational-softmax attention, a drop-in for scaled_dot_product_attention (no attn_mask,
-    no dropout).  q: [B, Hq, N, D], k, v: [B, Hkv, N, D] with Hq a multiple of Hkv; bf16 or
-    fp32 contiguous device tensors; D in {64, 128}.  Differentiable."""
+def ra_attention(q, k, v, attn_mask=None, is_causal=False, scale: Optional[float] = None,
+                 key_padding_mask=None):
+    """Rational-softmax attention, a drop-in for scaled_dot_product_attention (no dropout).
+
+    q: [B, Hq, Nq, D], k, v: [B, Hkv, Nk, D] with Hq a multiple of Hkv; bf16 or fp32
+    contiguous device tensors; D in {64, 128}.  ``is_causal``: False, True (= "top_left", key
+    j <= query i) or "bottom_right" (j <= i + Nk - Nq).  ``attn_mask`` / ``key_padding_mask``:
+    see mask_descriptor; they combine with is_causal.  A query row with no allowed key gives a
+    zero output.  Differentiable in q, k and v (the masks get no gradient)."""
     global _FN
     if _FN is None:
         _FN = _autograd_fn()
+    for m in (attn_mask, key_padding_mask):
+        if m is not None and getattr(m, "requires_grad", False):
+            raise ValueError("ra_attention computes no gradient for a mask; detach it")
     D = q.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    return _FN.apply(q, k, v, bool(is_causal), scale)
+    mask = mask_descriptor(q, k, attn_mask, key_padding_mask)
+    return _FN.apply(q, k, v, causal_code(is_causal), scale, mask)
 
 
 def ra_rope_neox(x, y, positions, mats, N, D, theta, inverse, dtype, stream=None) -> int:

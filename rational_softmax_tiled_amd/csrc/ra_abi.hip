@@ -4,7 +4,11 @@
 #include <stdint.h>
 
 #include "ra_attn.h"
+#include "ra_device.h"
 #include "ra_internal.h"
+
+static_assert(RA_MASK_BOOL == ra::kMaskBool && RA_MASK_ADD == ra::kMaskAdd && RA_MASK_NONE == ra::kMaskNone,
+              "mask kinds of the ABI and the kernels agree");
 
 namespace {
 
@@ -39,9 +43,35 @@ int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int6
   return RA_OK;
 }
 
+size_t elem_size(int dtype) { return dtype == RA_BF16 ? 2 : 4; }
+
+bool mask_present(const ra_mask* mask) { return mask != nullptr && mask->kind != RA_MASK_NONE; }
+
+// The causal mode and the mask descriptor.  Besides the slice itself, every offset a kernel
+// forms (tile tails included: up to 64 query rows past Nq and 128 keys past Nk) must stay below
+// 2^31 bytes; the kernels read those tails through a resource that ends at the slice.
+int check_mask(const ra_mask* mask, int causal, int64_t B, int64_t Hq, int64_t Nq, int64_t Nk,
+               int dtype) {
+  if (causal != RA_CAUSAL_NONE && causal != RA_CAUSAL_TOP_LEFT && causal != RA_CAUSAL_BOTTOM_RIGHT)
+    return RA_ERR_MASK;
+  if (!mask_present(mask)) return RA_OK;
+  if (mask->kind != RA_MASK_BOOL && mask->kind != RA_MASK_ADD) return RA_ERR_MASK;
+  if (mask->stride_b < 0 || mask->stride_h < 0 || mask->stride_q < 0 || mask->stride_k < 0)
+    return RA_ERR_MASK;
+  if (B * Hq * Nq > 0 && Nk > 0 && mask->data == nullptr) return RA_ERR_NULLPTR;
+  const int64_t es = mask->kind == RA_MASK_BOOL ? 1 : (int64_t)elem_size(dtype);
+  if (!aligned(mask->data, (uintptr_t)es)) return RA_ERR_ALIGN;
+  const __int128 reach = ((__int128)(Nq + 64) * mask->stride_q + (__int128)(Nk + 128) * mask->stride_k + 1) * es;
+  if (reach >= (__int128)kIndexLimit) return RA_ERR_TOO_LARGE;
+  const __int128 heads = ((__int128)(B > 0 ? B - 1 : 0) * mask->stride_b +
+                          (__int128)(Hq > 0 ? Hq - 1 : 0) * mask->stride_h) * es;
+  if (heads >= ((__int128)1 << 62)) return RA_ERR_TOO_LARGE;
+  return RA_OK;
+}
+
 ra::AttnProblem make_problem(const void* q, const void* k, const void* v, int64_t B, int64_t Hq,
                              int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
-                             int dtype) {
+                             int dtype, const ra_mask* mask) {
   ra::AttnProblem p;
   p.q = q;
   p.k = k;
@@ -52,13 +82,22 @@ ra::AttnProblem make_problem(const void* q, const void* k, const void* v, int64_
   p.Nq = (int)Nq;
   p.Nk = (int)Nk;
   p.D = (int)D;
-  p.causal = causal != 0;
   p.scale = scale;
   p.bf16 = dtype == RA_BF16;
+  const bool masked = mask_present(mask);
+  // the masked kernels always test the causal diagonal; without causality it sits past the keys
+  p.causal = causal != RA_CAUSAL_NONE || masked;
+  p.coff = causal == RA_CAUSAL_BOTTOM_RIGHT ? (int)(Nk - Nq) : causal == RA_CAUSAL_TOP_LEFT ? 0 : (int)Nk;
+  p.mask = masked ? mask->data : nullptr;
+  p.mask_kind = masked ? mask->kind : RA_MASK_NONE;
+  p.msb = masked ? mask->stride_b : 0;
+  p.msh = masked ? mask->stride_h : 0;
+  p.msq = masked ? (int)mask->stride_q : 0;
+  p.msk = masked ? (int)mask->stride_k : 0;
+  const int64_t es = masked && mask->kind == RA_MASK_BOOL ? 1 : (int64_t)elem_size(dtype);
+  p.mask_bytes = masked ? (int)(((Nq - 1) * mask->stride_q + (Nk - 1) * mask->stride_k + 1) * es) : 0;
   return p;
 }
-
-size_t elem_size(int dtype) { return dtype == RA_BF16 ? 2 : 4; }
 
 int fill_zero(void* dst, size_t elems, int dtype, hipStream_t s) {
   if (elems == 0) return RA_OK;
@@ -68,8 +107,10 @@ int fill_zero(void* dst, size_t elems, int dtype, hipStream_t s) {
 
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* stats, int64_t B,
                int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
-               int dtype, unsigned long long* counters, void* stream) {
+               int dtype, const ra_mask* mask, unsigned long long* counters, void* stream) {
   int st = check_sizes(B, Hq, Hkv, Nq, Nk, D, scale, dtype);
+  if (st != RA_OK) return st;
+  st = check_mask(mask, causal, B, Hq, Nq, Nk, dtype);
   if (st != RA_OK) return st;
   const int64_t rows = B * Hq * Nq;
   if (rows == 0) return RA_OK;
@@ -85,7 +126,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* stat
       st = hip_status(ra::launch_fill_pairs(stats, -INFINITY, 0.0f, (size_t)rows, s));
     return st;
   }
-  ra::AttnProblem p = make_problem(q, k, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype);
+  ra::AttnProblem p = make_problem(q, k, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, mask);
   return hip_status(ra::launch_attn_fwd(p, o, stats, counters, s));
 }
 
@@ -106,6 +147,7 @@ const char* ra_status_string(int status) {
     case RA_ERR_ALIGN: return "RA_ERR_ALIGN: pointer misaligned";
     case RA_ERR_TOO_LARGE: return "RA_ERR_TOO_LARGE: size beyond the supported index range";
     case RA_ERR_HIP: return "RA_ERR_HIP: HIP runtime error at launch";
+    case RA_ERR_MASK: return "RA_ERR_MASK: invalid causal mode or mask descriptor";
     default: return "unknown ra_status";
   }
 }
@@ -115,7 +157,15 @@ int ra_last_hip_error(void) { return g_last_hip_error; }
 int ra_attn_fwd(const void* q, const void* k, const void* v, void* o, float* stats, int64_t B,
                 int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
                 int dtype, void* stream) {
-  return fwd_common(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, stream);
+  return fwd_common(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, nullptr,
+                    stream);
+}
+
+int ra_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* stats,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                       int causal, float scale, int dtype, const ra_mask* mask, void* stream) {
+  return fwd_common(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, mask, nullptr,
+                    stream);
 }
 
 int ra_attn_fwd_counted(const void* q, const void* k, const void* v, void* o, float* stats,
@@ -123,7 +173,7 @@ int ra_attn_fwd_counted(const void* q, const void* k, const void* v, void* o, fl
                         int causal, float scale, int dtype, unsigned long long* counters,
                         void* stream) {
   if (counters == nullptr) return RA_ERR_NULLPTR;
-  return fwd_common(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, counters,
+  return fwd_common(q, k, v, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, counters,
                     stream);
 }
 
@@ -139,8 +189,10 @@ static int attn_bwd_common(const void* q, const void* k, const void* v, const vo
                            const void* d_o, const float* stats, void* dq, void* dk, void* dv,
                            const void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq,
                            int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
-                           int dtype, int phases, void* stream) {
+                           int dtype, const ra_mask* mask, int phases, void* stream) {
   int st = check_sizes(B, Hq, Hkv, Nq, Nk, D, scale, dtype);
+  if (st != RA_OK) return st;
+  st = check_mask(mask, causal, B, Hq, Nq, Nk, dtype);
   if (st != RA_OK) return st;
   const int64_t qrows = B * Hq * Nq, krows = B * Hkv * Nk;
   if (qrows == 0 && krows == 0) return RA_OK;
@@ -167,7 +219,7 @@ static int attn_bwd_common(const void* q, const void* k, const void* v, const vo
     if (st == RA_OK) st = fill_zero(dv, (size_t)krows * D, dtype, s);
     return st;
   }
-  ra::AttnProblem p = make_problem(q, k, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype);
+  ra::AttnProblem p = make_problem(q, k, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, mask);
   ra::BwdWorkspace ws = ra::bwd_workspace_layout(const_cast<void*>(workspace), B, Hq, Nq);
   return hip_status(ra::launch_attn_bwd(p, o, d_o, stats, dq, dk, dv, ws, phases, s));
 }
@@ -177,7 +229,16 @@ int ra_attn_bwd(const void* q, const void* k, const void* v, const void* o, cons
                 size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                 int64_t D, int causal, float scale, int dtype, void* stream) {
   return attn_bwd_common(q, k, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes, B, Hq,
-                         Hkv, Nq, Nk, D, causal, scale, dtype, ra::kBwdAll, stream);
+                         Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, ra::kBwdAll, stream);
+}
+
+int ra_attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                       const float* stats, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                       int64_t Nk, int64_t D, int causal, float scale, int dtype,
+                       const ra_mask* mask, void* stream) {
+  return attn_bwd_common(q, k, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes, B, Hq,
+                         Hkv, Nq, Nk, D, causal, scale, dtype, mask, ra::kBwdAll, stream);
 }
 
 int ra_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* d_o,
@@ -185,7 +246,7 @@ int ra_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, c
                    int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
                    int causal, float scale, int dtype, void* stream) {
   return attn_bwd_common(q, k, v, o, d_o, stats, dq, nullptr, nullptr, workspace, workspace_bytes,
-                         B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, ra::kBwdDq, stream);
+                         B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, ra::kBwdDq, stream);
 }
 
 int ra_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_o,
@@ -193,7 +254,7 @@ int ra_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_
                      size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
                      int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream) {
   return attn_bwd_common(q, k, v, nullptr, d_o, stats, nullptr, dk, dv, workspace, workspace_bytes,
-                         B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, ra::kBwdDkdv, stream);
+                         B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, ra::kBwdDkdv, stream);
 }
 
 int ra_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, int dtype, void* stream) {

@@ -71,7 +71,15 @@ struct BwdArgs {
   int tasks_per_group, wg_per_group, total_wg;   // query-parallel kernel
   int kwg_per_group, total_kwg;                  // key-parallel kernel
   float scale, c16;                              // c16 = scale / 16
+  int coff;        // causal diagonal: key j allowed for query row i iff j <= i + coff
+  MaskArgs mask;   // explicit mask (MASKED kernels)
 };
+
+// Row statistics of a row with no allowed key (m = -inf) are mapped so that every entry lands
+// off the support: t = m - s = +inf, 1 + u = +inf.  The argmax test compares with NaN instead,
+// so such a row records no argmax.
+__device__ __forceinline__ float live_max(float m) { return m == -INFINITY ? INFINITY : m; }
+__device__ __forceinline__ float argmax_probe(float m) { return m == -INFINITY ? __builtin_nanf("") : m; }
 
 constexpr int kKeysPerWg = kWaves * kRowsPerWave;   // key-parallel kernel: 128 keys per workgroup
 constexpr int kQTile = 32;                           // query rows per step of the key-parallel kernel
@@ -117,7 +125,7 @@ template <> __device__ __forceinline__ f32x8 pack_frag<float>(const f32x16& s, i
 
 // ------------------------------------------------------------------ query-parallel: dQ, R, a
 
-template <typename T, int D, int BN, bool CAUSAL>
+template <typename T, int D, int BN, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
   using frag_t = typename Ty<T>::frag;
   constexpr int PAD = 16 / sizeof(T);
@@ -141,9 +149,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
   const int q0 = (active ? task / a.rep : 0) * kRowsPerWave;
   const int last_task = min(wig * kWaves + kWaves - 1, a.tasks_per_group - 1);
   const int wg_qmax = min((last_task / a.rep) * kRowsPerWave + kRowsPerWave - 1, a.Nq - 1);
-  const int nt = ((CAUSAL ? min(a.Nk, wg_qmax + 1) : a.Nk) + BN - 1) / BN;
+  const int nt = ((CAUSAL ? max(0, min(a.Nk, wg_qmax + a.coff + 1)) : a.Nk) + BN - 1) / BN;
   const int wave_qmax = min(q0 + kRowsPerWave - 1, a.Nq - 1);
-  const int nt_w = !active ? 0 : ((CAUSAL ? min(a.Nk, wave_qmax + 1) : a.Nk) + BN - 1) / BN;
+  const int nt_w = !active ? 0 : ((CAUSAL ? max(0, min(a.Nk, wave_qmax + a.coff + 1)) : a.Nk) + BN - 1) / BN;
 
   const size_t head = (size_t)(b * a.Hq + h) * a.Nq;
   const T* kg = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Nk * D;
@@ -170,6 +178,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
   const float l = a.stats[(head + qrow) * 2 + 1];
   const float il = l > 0.0f ? 1.0f / l : 0.0f;
   const float cil = cval * il;
+  const float mt = live_max(m), mprobe = argmax_probe(m);
+  const MaskSlice<T> ms(a.mask, b, h);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -193,26 +203,29 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) mma(dp, load_frag(v_lds + (sb * 32 + frow) * PK + 16 * kc + fcol), df[kc]);
       const int key0 = kt * BN + sb * 32;
-      if ((CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk) {
+      if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
+        if constexpr (MASKED) {
+          unsigned mv[16];
+          ms.load(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk, ms.sk);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + acc_row(i, lane);
-          if (key >= a.Nk || (CAUSAL && key > qrow)) s[i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
         }
+        const int lb = key0 + 4 * (lane >> 5);
+        keep_rows(s, -kNoBound, min(a.Nk - lb, CAUSAL ? qrow + a.coff + 1 - lb : kNoBound));
       }
       // lowest key attaining the row max (rare: only the tile holding it takes the branch)
       float lm = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) lm = fmaxf(lm, s[i]);
-      if (__any(lm == m)) {
+      if (__any(lm == mprobe)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (s[i] == m) amax = min(amax, key0 + acc_row(i, lane));
+          if (s[i] == mprobe) amax = min(amax, key0 + acc_row(i, lane));
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p;
-        s[i] = ra_grad_t(m - s[i], a.c16, fmaf(dp[i], il, -cil), il, &p);
+        s[i] = ra_grad_t(mt - s[i], a.c16, fmaf(dp[i], il, -cil), il, &p);
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -246,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
       a.c[head + qi] = cval;
       a.r[head + qi] = R;
       a.amax[head + qi] = has_max ? amax : -1;
-      a.kd[head + qi] = fmaf(m, a.c16, 1.0f);
+      a.kd[head + qi] = m == -INFINITY ? INFINITY : fmaf(m, a.c16, 1.0f);
       a.il[head + qi] = il;
       a.cil[head + qi] = cil;
     }
@@ -255,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ key-parallel: dK, dV
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
   using frag_t = typename Ty<T>::frag;
   constexpr int PAD = 16 / sizeof(T);
@@ -306,9 +319,11 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
 
   const int nqt = (a.Nq + kQTile - 1) / kQTile;
-  const int qt0 = CAUSAL ? min(key0_wg / kQTile, nqt) : 0;
+  // first query tile holding a row i >= key0_wg - coff (the lowest key's first allowed row)
+  const int qt0 = CAUSAL ? min(max(key0_wg - a.coff, 0) / kQTile, nqt) : 0;
   for (int hh = 0; hh < a.rep; ++hh) {
     const int h = g * a.rep + hh;
+    const MaskSlice<T> ms(a.mask, b, h);
     const size_t head = (size_t)(b * a.Hq + h) * a.Nq;
     const T* qh = static_cast<const T*>(a.q) + head * D;
     const T* doh = static_cast<const T*>(a.d_o) + head * D;
@@ -326,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
         if (qi < a.Nq) {
           const float l = a.stats[(head + qi) * 2 + 1];
           const float il = l > 0.0f ? 1.0f / l : 0.0f;
-          st_m[tid] = a.stats[(head + qi) * 2];
+          st_m[tid] = live_max(a.stats[(head + qi) * 2]);
           st_il[tid] = il;
           st_cil[tid] = a.c[head + qi] * il;
           st_r[tid] = a.r[head + qi];
@@ -340,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
         }
       }
       __syncthreads();
-      if (!active || (CAUSAL && i0 + kQTile - 1 < j0)) continue;
+      if (!active || (CAUSAL && i0 + kQTile - 1 + a.coff < j0)) continue;
       f32x16 s = {}, dp = {};
       if constexpr (ROWS_IN_LDS) {
 #pragma unroll
@@ -356,7 +371,19 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) mma(dp, load_frag(dorp + 16 * kc), vf[kc]);
       }
-      const bool edge = (CAUSAL && j0 + 31 > i0) || i0 + kQTile > a.Nq || j0 + 32 > a.Nk;
+      const bool edge = MASKED || (CAUSAL && j0 + 31 > i0 + a.coff) || i0 + kQTile > a.Nq || j0 + 32 > a.Nk;
+      if (edge) {
+        if constexpr (MASKED) {
+          unsigned mv[16];
+          ms.load(mv, key * ms.sk + (i0 + 4 * (lane >> 5)) * ms.sq, ms.sq);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
+        }
+        // query row i0 + 4 (lane >> 5) + r is kept iff r < Nq - i0 - 4 (lane >> 5), key <= row +
+        // coff (causal) and key < Nk
+        const int lb = 4 * (lane >> 5);
+        keep_rows(s, (CAUSAL ? key - a.coff - i0 : -kNoBound) - lb, key >= a.Nk ? -kNoBound : a.Nq - i0 - lb);
+      }
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int r0 = 8 * i4 + 4 * (lane >> 5);   // four consecutive query rows of this lane
@@ -366,13 +393,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * i4 + e;
-          float sv = s[i];
-          if (edge) {
-            const int qi = i0 + r0 + e;
-            if (key >= a.Nk || qi >= a.Nq || (CAUSAL && key > qi)) sv = -INFINITY;
-          }
           float p;
-          const float gv = ra_grad_t(m4[e] - sv, a.c16, fmaf(dp[i], il4[e], -cil4[e]), il4[e], &p);
+          const float gv = ra_grad_t(m4[e] - s[i], a.c16, fmaf(dp[i], il4[e], -cil4[e]), il4[e], &p);
           s[i] = p;
           dp[i] = gv;
         }
@@ -437,7 +459,7 @@ __device__ __forceinline__ float ra_grad(float s, float c16, float kd, float dp,
   return fmaf(dp, il, -cil) * ((q6 * q) * (r * r));
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int BN = 64, KC = D / 16, SB = BN / 32, DB = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * D];
@@ -455,9 +477,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const int q0 = (active ? task / a.rep : 0) * kRowsPerWave;
   const int last_task = min(wig * kWaves + kWaves - 1, a.tasks_per_group - 1);
   const int wg_qmax = min((last_task / a.rep) * kRowsPerWave + kRowsPerWave - 1, a.Nq - 1);
-  const int nt = ((CAUSAL ? min(a.Nk, wg_qmax + 1) : a.Nk) + BN - 1) / BN;
+  const int nt = ((CAUSAL ? max(0, min(a.Nk, wg_qmax + a.coff + 1)) : a.Nk) + BN - 1) / BN;
   const int wave_qmax = min(q0 + kRowsPerWave - 1, a.Nq - 1);
-  const int nt_w = !active ? 0 : ((CAUSAL ? min(a.Nk, wave_qmax + 1) : a.Nk) + BN - 1) / BN;
+  const int nt_w = !active ? 0 : ((CAUSAL ? max(0, min(a.Nk, wave_qmax + a.coff + 1)) : a.Nk) + BN - 1) / BN;
 
   const size_t head = (size_t)(b * a.Hq + h) * a.Nq;
   const bf16* kg = static_cast<const bf16*>(a.k) + (size_t)(b * a.Hkv + g) * a.Nk * D;
@@ -489,7 +511,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const float l = a.stats[(head + qrow) * 2 + 1];
   const float il = l > 0.0f ? 1.0f / l : 0.0f;
   const float cil = cval * il;
-  const float kd = fmaf(m, a.c16, 1.0f);
+  const float kd = m == -INFINITY ? INFINITY : fmaf(m, a.c16, 1.0f);
+  const float mprobe = argmax_probe(m);
+  const MaskSlice<bf16> ms(a.mask, b, h);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -514,20 +538,23 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) mma(dp, swz_frag<bf16, D>(v_lds[buf], sb * 32 + frow, 16 * kc + fcol), df[kc]);
         const int key0 = kt * BN + sb * 32;
-        if ((CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk) {
+        if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
+          if constexpr (MASKED) {
+            unsigned mv[16];
+            ms.load(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk, ms.sk);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + acc_row(i, lane);
-            if (key >= a.Nk || (CAUSAL && key > qrow)) s[i] = -INFINITY;
+            for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
           }
+          const int lb = key0 + 4 * (lane >> 5);
+          keep_rows(s, -kNoBound, min(a.Nk - lb, CAUSAL ? qrow + a.coff + 1 - lb : kNoBound));
         }
         float lm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) lm = fmaxf(lm, s[i]);
-        if (__any(lm == m)) {
+        if (__any(lm == mprobe)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (s[i] == m) amax = min(amax, key0 + acc_row(i, lane));
+            if (s[i] == mprobe) amax = min(amax, key0 + acc_row(i, lane));
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -569,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
       a.c[head + qi] = cval;
       a.r[head + qi] = R;
       a.amax[head + qi] = has_max ? amax : -1;
-      a.kd[head + qi] = fmaf(m, a.c16, 1.0f);
+      a.kd[head + qi] = m == -INFINITY ? INFINITY : fmaf(m, a.c16, 1.0f);
       a.il[head + qi] = il;
       a.cil[head + qi] = cil;
     }
@@ -595,7 +622,7 @@ constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * kWave;
 constexpr int kDkdvRows = 64;   // query rows per step (32 per half of the workgroup)
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int KC = D / 16, DB = D / 32, QT = kDkdvRows, HR = QT / 2, NW = kDkdvWaves;
   constexpr int HTILE = HR * D;           // elements of one half-tile (32 rows of Q or dO)
@@ -628,7 +655,7 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   const int kr = 32 * kg + frow;     // B-fragment row of this lane inside the K/V rows
 
   const int nqt = (a.Nq + QT - 1) / QT;
-  const int qt0 = CAUSAL ? min(key0_wg / QT, nqt) : 0;
+  const int qt0 = CAUSAL ? min(max(key0_wg - a.coff, 0) / QT, nqt) : 0;
   const int per_head = nqt - qt0;
   const int steps = a.rep * per_head;
   const bf16* qbase = static_cast<const bf16*>(a.q);
@@ -658,7 +685,14 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   // does this wave's 32 x 32 block of tile `step` hold any allowed score?
   auto block_live = [&](int step) {
     const int i0 = tile_row(step) + HR * half;
-    return active && i0 < a.Nq && !(CAUSAL && i0 + 31 < j0);
+    return active && i0 < a.Nq && !(CAUSAL && i0 + 31 + a.coff < j0);
+  };
+  // explicit mask elements of this wave's block of tile `step` (read ahead of the products)
+  auto mask_load = [&](int step, unsigned (&mv)[16]) {
+    if constexpr (MASKED) {
+      const MaskSlice<bf16> ms(a.mask, b, g * a.rep + step / per_head);
+      ms.load(mv, key * ms.sk + (tile_row(step) + HR * half + 4 * (lane >> 5)) * ms.sq, ms.sq);
+    }
   };
 
   // S^T and dP^T of this wave's block: lane = key, registers = the half-tile's 32 query rows
@@ -673,8 +707,18 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
       mma(dp, swz_frag<bf16, D>(dot_, frow, 16 * kc + fcol), swz_frag<bf16, D>(v_lds, kr, 16 * kc + fcol));
   };
   // s -> P, dp -> G (+ R at the argmax) for the half-tile rows starting at query row i0
-  auto derivative = [&](f32x16& s, f32x16& dp, int i0, int slot) {
-    const bool edge = (CAUSAL && j0 + 31 > i0) || i0 + 32 > a.Nq || j0 + 32 > a.Nk;
+  auto derivative = [&](f32x16& s, f32x16& dp, const unsigned (&mv)[16], int i0, int slot) {
+    const bool edge = MASKED || (CAUSAL && j0 + 31 > i0 + a.coff) || i0 + 32 > a.Nq || j0 + 32 > a.Nk;
+    if (edge) {   // one uniform branch around the whole block's masking
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = mask_value(a.mask.kind, a.mask.inv_scale, s[i], mv[i]);
+      }
+      // query row i0 + 4 (lane >> 5) + r is kept iff r < Nq - i0 - 4 (lane >> 5), key <= row + coff
+      // (causal) and key < Nk
+      const int lb = 4 * (lane >> 5);
+      keep_rows(s, (CAUSAL ? key - a.coff - i0 : -kNoBound) - lb, key >= a.Nk ? -kNoBound : a.Nq - i0 - lb);
+    }
     const float* st = &st_lds[slot][0][HR * half];
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -687,13 +731,8 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * i4 + e;
-        float sv = s[i];
-        if (edge) {
-          const int qi = i0 + r0 + e;
-          if (key >= a.Nk || qi >= a.Nq || (CAUSAL && key > qi)) sv = -INFINITY;
-        }
         float p;
-        const float gv = ra_grad(sv, a.c16, kd4[e], dp[i], il4[e], cil4[e], &p);
+        const float gv = ra_grad(s[i], a.c16, kd4[e], dp[i], il4[e], cil4[e], &p);
         s[i] = p;
         dp[i] = gv;
       }
@@ -738,8 +777,10 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
     for (int st = 0; st <= steps; ++st) {
       if (st < steps && block_live(st)) {
         f32x16 s, dp;
+        unsigned mv[16];
+        mask_load(st, mv);
         products_sdp(q_up(st & 1), do_up(st & 1), s, dp);
-        derivative(s, dp, tile_row(st), st % 3);
+        derivative(s, dp, mv, tile_row(st), st % 3);
         products_dkdv(s, dp, q_up(st & 1), do_up(st & 1));
       }
       if (st + 1 < steps) issue(st + 1);
@@ -748,15 +789,19 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
     }
   } else {
     f32x16 s = {}, dp = {};
-    bool carried = false;   // s, dp hold S, dP of tile st - 1
+    unsigned mv[16];
+    bool carried = false;   // s, dp (and mv) hold S, dP (and the mask block) of tile st - 1
     for (int st = 0; st <= steps; ++st) {
       if (carried) {
         const int pv = (st - 1) % 3;
-        derivative(s, dp, tile_row(st - 1) + HR, pv);
+        derivative(s, dp, mv, tile_row(st - 1) + HR, pv);
         products_dkdv(s, dp, q_lo(pv), do_lo(pv));
       }
       carried = st < steps && block_live(st);
-      if (carried) products_sdp(q_lo(st % 3), do_lo(st % 3), s, dp);
+      if (carried) {
+        mask_load(st, mv);
+        products_sdp(q_lo(st % 3), do_lo(st % 3), s, dp);
+      }
       wait_vmem();
       __syncthreads();
     }
@@ -827,27 +872,37 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   a.total_kwg = p.B * p.Hkv * a.kwg_per_group;
   a.scale = p.scale;
   a.c16 = p.scale / 16.0f;
+  a.coff = p.coff;
+  a.mask = mask_args(p);
   constexpr bool kBf16 = sizeof(T) == 2;
   const dim3 qgrid(a.total_wg), kgrid(a.total_kwg), block(kThreads);
   const dim3 kblock(kBf16 ? kDkdvThreads : kThreads);
+  // the masked kernels are the causal ones (coff = Nk when there is no causality)
+  const bool masked = p.mask_kind != kMaskNone;
   if (phases & kBwdDq) {
-    if (p.causal) {
-      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true>), qgrid, block, 0, stream, a);
-      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true>), qgrid, block, 0, stream, a);
+    if (masked) {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, true>), qgrid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, true>), qgrid, block, 0, stream, a);
+    } else if (p.causal) {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false>), qgrid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, false>), qgrid, block, 0, stream, a);
     } else {
-      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false>), qgrid, block, 0, stream, a);
-      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false>), qgrid, block, 0, stream, a);
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, false>), qgrid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false, false>), qgrid, block, 0, stream, a);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & kBwdDkdv) {
-    if (p.causal) {
-      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true>), kgrid, kblock, 0, stream, a);
-      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), kgrid, kblock, 0, stream, a);
+    if (masked) {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, true>), kgrid, kblock, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true, true>), kgrid, kblock, 0, stream, a);
+    } else if (p.causal) {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, false>), kgrid, kblock, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true, false>), kgrid, kblock, 0, stream, a);
     } else {
-      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false>), kgrid, kblock, 0, stream, a);
-      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), kgrid, kblock, 0, stream, a);
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, false>), kgrid, kblock, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false, false>), kgrid, kblock, 0, stream, a);
     }
   }
   return hipGetLastError();

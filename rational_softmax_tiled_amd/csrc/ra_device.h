@@ -14,6 +14,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "ra_internal.h"
 
 namespace ra {
 
@@ -73,6 +74,18 @@ __device__ __forceinline__ void mma(f32x16& c, const f32x8& a, const f32x8& b) {
 // Row index (inside a 32x32 accumulator) of element i for this lane.
 __device__ __forceinline__ int acc_row(int i, int lane) {
   return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// Keeps the entries of a 32 x 32 accumulator block whose row offset acc_row(i, lane) -
+// 4 (lane >> 5) = 8 (i >> 2) + (i & 3) lies in [lo, hi) and sets the others to -inf.  The causal
+// and tail tests of a block reduce to these two per-lane bounds (compared with constants).
+constexpr int kNoBound = 1 << 30;
+__device__ __forceinline__ void keep_rows(f32x16& s, int lo, int hi) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * (i >> 2) + (i & 3);
+    if (r < lo || r >= hi) s[i] = -INFINITY;
+  }
 }
 
 // Eight accumulator values (elements 8*ks .. 8*ks+7) as the B fragment of the next product.
@@ -479,5 +492,85 @@ __device__ __forceinline__ void dma_tile(bf16* lds, const bf16* g, int nvalid, i
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// ---------------------------------------------------------------- explicit attention masks
+// Element (b, h, i, j) of a mask (query head h, query row i, key j) sits at element offset
+// b*sb + h*sh + i*sq + j*sk; zero strides broadcast.  kMaskBool: uint8, nonzero = attend, zero
+// masks the score.  kMaskAdd: additive, in the dtype of q, added to the scaled score; the kernels
+// work on raw dot products, so it enters as bias / scale.  One (b, h) slice is read through a
+// buffer resource of `bytes` bytes: offsets past it read as zero (a masked-out bool, a zero bias),
+// and every offset inside the slice fits in 31 bits (the host checks both).
+enum { kMaskNone = 0, kMaskBool = 1, kMaskAdd = 2 };
+
+struct MaskArgs {
+  const void* ptr;       // nullptr: no explicit mask
+  long long sb, sh;      // element strides over batch and query head
+  int sq, sk;            // element strides over query rows and keys
+  int bytes;             // bytes of one (b, h) slice, tails included
+  int kind;
+  float inv_scale;       // 1 / scale
+};
+
+inline MaskArgs mask_args(const AttnProblem& p) {
+  MaskArgs m;
+  m.ptr = p.mask_kind != kMaskNone ? p.mask : nullptr;
+  m.sb = p.msb;
+  m.sh = p.msh;
+  m.sq = p.msq;
+  m.sk = p.msk;
+  m.bytes = p.mask_bytes;
+  m.kind = p.mask_kind;
+  m.inv_scale = 1.0f / p.scale;
+  return m;
+}
+
+// A score with its mask element applied (v as MaskSlice::load returns it).
+__device__ __forceinline__ float mask_value(int kind, float inv_scale, float s, unsigned v) {
+  return kind == kMaskBool ? (v != 0u ? s : -INFINITY) : fmaf(__uint_as_float(v), inv_scale, s);
+}
+
+// The (b, h) slice of a mask with its 32 x 32 block loads.  `step` is the byte distance between
+// the elements of consecutive accumulator rows (the key stride when keys sit on the accumulator
+// rows, the query-row stride when query rows do); element i of a lane is read at voff plus the
+// offset of its accumulator row, which is the same in every lane (a scalar offset).
+template <typename T>
+struct MaskSlice {
+  __amdgpu_buffer_rsrc_t r;
+  int sq, sk, kind;
+  float inv_scale;
+
+  __device__ __forceinline__ MaskSlice(const MaskArgs& m, int b, int h) {
+    const int es = m.kind == kMaskBool ? 1 : (int)sizeof(T);
+    const unsigned long long addr =
+        reinterpret_cast<unsigned long long>(m.ptr) + (unsigned long long)(b * m.sb + h * m.sh) * es;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)addr);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(addr >> 32));
+    void* base = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+    r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(m.bytes), kBufferWord3);
+    sq = m.sq * es;
+    sk = m.sk * es;
+    kind = m.kind;
+    inv_scale = m.inv_scale;
+  }
+
+  // raw values of the 16 elements of a lane (bool: the byte; additive: the bits as fp32)
+  __device__ __forceinline__ void load(unsigned (&v)[16], int voff, int step) const {
+    if (kind == kMaskBool) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b8(r, voff, uniform((8 * (i >> 2) + (i & 3)) * step), 0);
+    } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, voff, uniform((8 * (i >> 2) + (i & 3)) * step), 0) << 16;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, uniform((8 * (i >> 2) + (i & 3)) * step), 0);
+    }
+  }
+
+  __device__ __forceinline__ float apply(float s, unsigned v) const { return mask_value(kind, inv_scale, s, v); }
+};
 
 }  // namespace ra

@@ -41,6 +41,8 @@ struct FwdArgs {
   int wg_per_group;      // ceil(tasks_per_group / 4)
   int total_wg;
   float c;               // scale / 16
+  int coff;              // causal diagonal: key j allowed for query row i iff j <= i + coff
+  MaskArgs mask;         // explicit mask (MASKED kernels)
 };
 
 constexpr int kMaxTiles = 512;   // key tiles with a recorded maximum (skip test); beyond: no skip
@@ -60,14 +62,20 @@ __device__ __forceinline__ void store_quad<float>(float* dst, f32x16 acc, int ba
   *reinterpret_cast<f32x4*>(dst) = v;
 }
 
-// Mask entries of a 32x32 S^T block: key >= Nk, or (causal) key > query row.
-template <bool CAUSAL>
-__device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int lane, int Nk) {
+// Mask entries of a 32x32 S^T block (keys on the accumulator rows, query row qrow on the lane):
+// the explicit mask first, then key >= Nk, or (causal) key > qrow + coff.
+template <bool CAUSAL, bool MASKED, typename T>
+__device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int lane, int Nk, int coff,
+                                           const MaskSlice<T>& ms) {
+  if constexpr (MASKED) {
+    unsigned mv[16];
+    ms.load(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk, ms.sk);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int key = key0 + acc_row(i, lane);
-    if (key >= Nk || (CAUSAL && key > qrow)) s[i] = -INFINITY;
+    for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
   }
+  // key = key0 + 4 (lane >> 5) + r is kept iff key < Nk and (causal) key <= qrow + coff
+  const int lb = key0 + 4 * (lane >> 5);
+  keep_rows(s, -kNoBound, min(Nk - lb, CAUSAL ? qrow + coff + 1 - lb : kNoBound));
 }
 
 // S^T block (32 keys x 32 query rows) of key sub-block sb of the staged (swizzled) K tile.
@@ -80,7 +88,7 @@ __device__ __forceinline__ f32x16 score_block(const T* k_tile, const typename Ty
   return s;
 }
 
-template <typename T, int D, int BN, bool CAUSAL, bool COUNT, bool WRITE_O>
+template <typename T, int D, int BN, bool CAUSAL, bool COUNT, bool WRITE_O, bool MASKED>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   using frag_t = typename Ty<T>::frag;
   // bf16: V stays a swizzled row tile and the P.V operand is read transposed (ds_read_b64_tr_b16);
@@ -112,10 +120,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const int q0 = (active ? task / a.rep : 0) * kRowsPerWave;
   const int last_task = min(wig * kWaves + kWaves - 1, a.tasks_per_group - 1);
   const int wg_qmax = min((last_task / a.rep) * kRowsPerWave + kRowsPerWave - 1, a.Nq - 1);
-  const int key_end = CAUSAL ? min(a.Nk, wg_qmax + 1) : a.Nk;
+  const int key_end = CAUSAL ? max(0, min(a.Nk, wg_qmax + a.coff + 1)) : a.Nk;
   const int nt = (key_end + BN - 1) / BN;
   const int wave_qmax = min(q0 + kRowsPerWave - 1, a.Nq - 1);
-  const int key_end_w = !active ? 0 : (CAUSAL ? min(a.Nk, wave_qmax + 1) : a.Nk);
+  const int key_end_w = !active ? 0 : (CAUSAL ? max(0, min(a.Nk, wave_qmax + a.coff + 1)) : a.Nk);
   const int nt_w = (key_end_w + BN - 1) / BN;
 
   const T* qh = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h) * a.Nq * D;
@@ -135,7 +143,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const int frow = lane & 31;           // A-fragment row inside a 32-row block
   const int fcol = 8 * (lane >> 5);     // A-fragment column offset
 
-  auto needs_mask = [&](int key0) { return (CAUSAL && key0 + 31 > q0) || key0 + 32 > a.Nk; };
+  auto needs_mask = [&](int key0) { return MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk; };
+  const MaskSlice<T> ms(a.mask, b, h);
 
   // ---- pass 1: row max of the raw dot products (K tiles double-buffered through LDS)
   // Tiles reach LDS by DMA (bf16) or through registers (fp32), one tile ahead of the math.
@@ -163,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
       for (int sb = 0; sb < SB; ++sb) {
         f32x16 s = score_block<T, D>(k_lds[buf], qf, sb, frow, fcol);
         const int key0 = kt * BN + sb * 32;
-        if (needs_mask(key0)) mask_block<CAUSAL>(s, key0, qrow, lane, a.Nk);
+        if (needs_mask(key0)) mask_block<CAUSAL, MASKED>(s, key0, qrow, lane, a.Nk, a.coff, ms);
 #pragma unroll
         for (int i = 0; i < 16; ++i) tl = fmaxf(tl, s[i]);
       }
@@ -177,8 +186,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
     __syncthreads();
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));   // lanes l and l+32 hold the same query row
-  // 1 + u = fma(s, -c, kd) with kd = 1 + m c; the smallest kd of the wave bounds every row
-  const float kd = fmaf(mx, a.c, 1.0f);
+  // 1 + u = fma(s, -c, kd) with kd = 1 + m c; the smallest kd of the wave bounds every row.  A
+  // row with no allowed key (m = -inf) takes kd = +inf: every 1 + u is then +inf, phi = 0.
+  const float kd = mx == -INFINITY ? INFINITY : fmaf(mx, a.c, 1.0f);
   {
     const float km = wave_min(kd);
     if (lane == 0) kmin_lds[wave] = km;
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         const int key0 = cur * BN + sb * 32;
-        if (needs_mask(key0)) mask_block<CAUSAL>(s[sb], key0, qrow, lane, a.Nk);
+        if (needs_mask(key0)) mask_block<CAUSAL, MASKED>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[sb][i] = ra_phi(s[sb][i], a.c, kd);
 #pragma unroll
@@ -402,16 +412,21 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   a.wg_per_group = (a.tasks_per_group + kWaves - 1) / kWaves;
   a.total_wg = p.B * p.Hkv * a.wg_per_group;
   a.c = p.scale / 16.0f;
+  a.coff = p.coff;
+  a.mask = mask_args(p);
   dim3 grid(a.total_wg), block(kThreads);
-  if (o == nullptr) {   // statistics only (m, l), for a backward without saved stats
-    if (p.causal) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, false>), grid, block, 0, stream, a);
+  if (p.mask_kind != kMaskNone) {   // the masked kernels are the causal ones (coff = Nk: no causality)
+    if (o == nullptr) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, true, true>), grid, block, 0, stream, a);
+  } else if (o == nullptr) {   // statistics only (m, l), for a backward without saved stats
+    if (p.causal) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, false, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, false, false>), grid, block, 0, stream, a);
   } else if (p.causal) {
-    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, true>), grid, block, 0, stream, a);
+    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, true, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, true, false>), grid, block, 0, stream, a);
   } else {
-    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, true>), grid, block, 0, stream, a);
+    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, true, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -13,9 +13,15 @@ struct AttnProblem {
   const void* k;
   const void* v;
   int B, Hq, Hkv, Nq, Nk, D;
-  bool causal;
+  bool causal;   // the causal kernels: key j allowed for query i iff j <= i + coff
+  int coff;      // 0 top-left, Nk - Nq bottom-right, Nk for an explicit mask without causality
   float scale;
-  bool bf16;  // false: fp32
+  bool bf16;     // false: fp32
+  // explicit mask (kind 0: none); element strides, slice bytes as in MaskArgs (ra_device.h)
+  const void* mask;
+  int mask_kind;
+  long long msb, msh;
+  int msq, msk, mask_bytes;
 };
 
 // Forward: o (and stats when non-null); counters non-null selects the counting variant;

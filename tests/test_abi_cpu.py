@@ -12,7 +12,7 @@ import rational_softmax_tiled_amd as ra
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ra_attn.h")
 
-OK, NULLPTR, SHAPE, GQA, HEADDIM, DTYPE, SCALE, WORKSPACE, ALIGN, TOO_LARGE, HIP = range(11)
+OK, NULLPTR, SHAPE, GQA, HEADDIM, DTYPE, SCALE, WORKSPACE, ALIGN, TOO_LARGE, HIP, MASK = range(12)
 
 # Fake, 256-byte aligned "device" addresses: never dereferenced, since every call fails
 # validation or is empty.
@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(11):
+    for code in range(12):
         s = ra.ra_status_string(code)
         assert s.startswith("RA_")
     assert "unknown" in ra.ra_status_string(99)
@@ -187,3 +187,54 @@ def test_product_path_has_no_fallback():
     for name in os.listdir(os.path.join(ROOT, "rational_softmax_tiled_amd", "csrc")):
         text = open(os.path.join(ROOT, "rational_softmax_tiled_amd", "csrc", name)).read()
         assert "oracle" not in text.lower(), name
+
+
+def mfwd(kind=ra.RA_MASK_BOOL, strides=(0, 0, 8, 1), data=P + 0x200000, causal=0, B=1, Hq=2, Nq=8,
+         Nk=8, dtype=ra.RA_BF16):
+    return ra.ra_attn_fwd_masked(P, P, P, P2, None, B, Hq, 1, Nq, Nk, 64, causal, 0.125, dtype, data,
+                                 kind, strides, 0)
+
+
+def test_causal_mode_validation(lib):
+    assert fwd(causal=3) == MASK
+    assert fwd(causal=-1) == MASK
+    assert bwd(B=1, q=P) == bwd()   # causal 1 is valid
+    assert ra.ra_attn_bwd(P, P, P, P, P, None, P2, P2, P2, P2, 1 << 30, 1, 2, 1, 8, 8, 64, 5, 0.125,
+                          ra.RA_BF16, 0) == MASK
+    assert mfwd(causal=9) == MASK
+    # the mode is checked even when there is nothing to compute
+    assert fwd(causal=4, B=0) == MASK
+
+
+def test_mask_validation(lib):
+    assert mfwd(kind=3) == MASK
+    assert mfwd(kind=-1) == MASK
+    assert mfwd(strides=(0, 0, -8, 1)) == MASK
+    assert mfwd(strides=(-1, 0, 8, 1)) == MASK
+    assert mfwd(data=None) == NULLPTR
+    assert mfwd(kind=ra.RA_MASK_ADD, data=P + 1) == ALIGN              # bf16 elements
+    assert mfwd(kind=ra.RA_MASK_ADD, data=P + 2, dtype=ra.RA_F32) == ALIGN
+    assert mfwd(kind=ra.RA_MASK_BOOL, data=P + 1, B=0) == OK           # bytes: any address
+    # one slice (plus tile tails) must stay below 2^31 bytes
+    # (Nq + 64) * stride_q + (Nk + 128) * stride_k elements, Nq = Nk = 8
+    assert mfwd(strides=(0, 0, 1 << 25, 1)) == TOO_LARGE
+    assert mfwd(kind=ra.RA_MASK_ADD, strides=(0, 0, 1 << 24, 1)) == TOO_LARGE
+    assert mfwd(strides=(0, 0, 1, 1 << 24)) == TOO_LARGE
+    assert mfwd(strides=(1 << 62, 0, 8, 1), B=3) == TOO_LARGE          # no int64 overflow
+    # no mask (NULL descriptor or kind NONE) behaves as ra_attn_fwd
+    assert ra.ra_attn_fwd_masked(P, P, P, P2, None, 1, 3, 2, 8, 8, 64, 0, 0.125, ra.RA_BF16, None,
+                                 ra.RA_MASK_NONE, (0, 0, 0, 0), 0) == GQA
+    assert mfwd(kind=ra.RA_MASK_NONE, data=None, B=0) == OK
+    assert mfwd(B=0) == OK and mfwd(Nq=0) == OK
+
+
+def test_masked_bwd_validation(lib):
+    def mbwd(kind=ra.RA_MASK_BOOL, strides=(8, 0, 0, 1), data=P + 0x200000, ws=P2, causal=2, B=1):
+        return ra.ra_attn_bwd_masked(P, P, P, P, P, None, P2, P2, P2, ws, 1 << 30, B, 2, 1, 8, 8, 64,
+                                     causal, 0.125, ra.RA_BF16, data, kind, strides, 0)
+    assert mbwd(kind=7) == MASK
+    assert mbwd(causal=3) == MASK
+    assert mbwd(strides=(8, 0, 0, -1)) == MASK
+    assert mbwd(data=None) == NULLPTR
+    assert mbwd(ws=None) == WORKSPACE
+    assert mbwd(B=0) == OK

@@ -72,6 +72,28 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# A padded batch for the explicit-mask path: B sequences of different lengths padded to N, with a
+# [B, N] key padding mask (1 = attend up to the sample's length), the CrossAttention key padding
+# mask of the noeira "Primitives" page.  Inputs follow the recipe above; the lengths are fixed.
+PADDED_BATCH = AttnWorkload("bf16_causal_keypad_B4_H16_N4096_D128", "bf16", True, 4, 16, 16,
+                            4096, 4096, 128, seed=6, with_grad=True)
+PADDED_LENGTHS = (4096, 3000, 2048, 1111)
+
+
+def padded_batch_workload() -> AttnWorkload:
+    return PADDED_BATCH
+
+
+def padded_batch_lengths(w: AttnWorkload = PADDED_BATCH):
+    """Per-sample valid lengths of the padded batch (keys at or past the length are masked)."""
+    assert w == PADDED_BATCH
+    return PADDED_LENGTHS
+
+
+def padded_batch_keep(w: AttnWorkload = PADDED_BATCH) -> np.ndarray:
+    """The [B, Nk] boolean key padding mask: True where key j < length of sample b."""
+    return np.arange(w.Nk)[None, :] < np.asarray(padded_batch_lengths(w))[:, None]
+
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
