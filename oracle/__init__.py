@@ -8,6 +8,7 @@ from .ra_oracle import (  # noqa: F401
     SUPPORT_WIDTH,
     causal_offset,
     ra_attention_bwd,
+    ra_attention_decode,
     ra_attention_fwd,
     ra_phi,
     ra_softmax_rows,

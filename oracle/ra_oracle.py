@@ -60,6 +60,7 @@ __all__ = [
     "ra_softmax_rows_bwd",
     "ra_attention_fwd",
     "ra_attention_bwd",
+    "ra_attention_decode",
 ]
 
 # Delta at which phi reaches exactly zero (the compact support edge, u = 1).
@@ -148,6 +149,37 @@ def ra_softmax_rows_bwd(x, dp):
     with np.errstate(invalid="ignore", divide="ignore"):
         p = np.where(l[..., None] > 0, phi / l[..., None], 0.0)
     return _softmax_vjp(p, delta, dp, a)
+
+
+def ra_attention_decode(q, k, v, scale, seqlens=None, causal=False):
+    """Attention of a few query rows per head against a key/value cache.
+
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D] hold the caches, of which sample b uses its first
+    ``seqlens[b]`` keys (default all Nk).  ``causal``: False; True / "top_left" (query i takes
+    keys j <= i); "bottom_right" (query i sits at position seqlens[b] - Nq + i of the sample's
+    sequence and takes keys j <= seqlens[b] - Nq + i).  By definition this is ra_attention_fwd
+    of each sample on its own cache prefix, so the bottom-right offset is seqlens[b] - Nq.
+    Returns (O, m, l, a) as ra_attention_fwd.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nk, D, rep = _check_attention_shapes(q, k, v)
+    lens = np.full(B, Nk, dtype=np.int64) if seqlens is None else np.asarray(seqlens, np.int64)
+    if lens.shape != (B,) or (lens < 0).any() or (lens > Nk).any():
+        raise ValueError("seqlens must hold B lengths in [0, Nk]")
+    o = np.zeros((B, Hq, Nq, v.shape[3]))
+    m = np.full((B, Hq, Nq), -np.inf)
+    l = np.zeros((B, Hq, Nq))
+    a = np.full((B, Hq, Nq), -1, dtype=np.int64)
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        ob, mb, lb, ab = ra_attention_fwd(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n],
+                                          causal, scale)
+        o[b], m[b], l[b], a[b] = ob[0], mb[0], lb[0], ab[0]
+    return o, m, l, a
 
 
 def rope_neox(x, theta, positions=None, inverse=False):

@@ -549,6 +549,67 @@ def test_masked_attention_bwd_matches_central_differences(case):
     np.testing.assert_allclose(dv, _fd_grad(lambda z: loss(q, k, z), v), rtol=0, atol=3e-8)
 
 
+# ------------------------------------------------------------- decode against a cache
+
+def test_decode_continues_the_prefill():
+    # Decoding the last Nq queries of a sequence of length L against its cache equals the last
+    # Nq rows of the causal (top-left) prefill of the whole sequence.
+    rng = np.random.default_rng(50)
+    B, Hq, Hkv, Nq, Nk, D = 3, 4, 2, 2, 12, 4
+    lens = np.array([12, 7, 2])
+    k = rng.normal(0, 1.5, size=(B, Hkv, Nk, D))
+    v = rng.normal(size=(B, Hkv, Nk, D))
+    qfull = rng.normal(0, 1.5, size=(B, Hq, Nk, D))
+    q = np.stack([qfull[b, :, lens[b] - Nq:lens[b]] for b in range(B)])
+    o, m, l, a = oracle.ra_attention_decode(q, k, v, 0.6, seqlens=lens, causal="bottom_right")
+    for b in range(B):
+        n = lens[b]
+        pf = oracle.ra_attention_fwd(qfull[b:b + 1, :, :n], k[b:b + 1, :, :n], v[b:b + 1, :, :n],
+                                     True, 0.6)
+        for x, y in zip((o, m, l, a), pf):
+            np.testing.assert_array_equal(x[b], y[0, :, n - Nq:n])
+
+
+def test_decode_brute_force_and_edges():
+    rng = np.random.default_rng(51)
+    B, Hq, Hkv, Nq, Nk, D = 4, 2, 1, 3, 9, 3
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, Nq, Nk, D, sigma=1.5)
+    lens = np.array([9, 4, 0, 1])
+    for causal in (False, "top_left", "bottom_right"):
+        o, m, l, a = oracle.ra_attention_decode(q, k, v, 0.7, seqlens=lens, causal=causal)
+        for b in range(B):
+            n = int(lens[b])
+            def allowed(i, j, n=n):
+                if j >= n:
+                    return False
+                if causal == "top_left":
+                    return j <= i
+                if causal == "bottom_right":
+                    return j <= i + n - Nq
+                return True
+            for h in range(Hq):
+                ref = _brute_attention(q[b, h].tolist(), k[b, h // 2].tolist(), v[b, h // 2].tolist(),
+                                       0.7, allowed)
+                np.testing.assert_allclose(o[b, h], ref, rtol=0, atol=1e-14)
+        assert (o[2] == 0).all() and (m[2] == -np.inf).all() and (l[2] == 0).all()
+    # no lengths: the whole cache, the same as the plain forward
+    for x, y in zip(oracle.ra_attention_decode(q, k, v, 0.7, causal="bottom_right"),
+                    oracle.ra_attention_fwd(q, k, v, "bottom_right", 0.7)):
+        np.testing.assert_array_equal(x, y)
+    with pytest.raises(ValueError):
+        oracle.ra_attention_decode(q, k, v, 0.7, seqlens=np.array([1, 2, 3, 10]))
+
+
+def test_decode_gqa_equals_mha_on_repeated_cache():
+    rng = np.random.default_rng(52)
+    q, k, v = _rand_qkv(rng, 2, 8, 2, 1, 20, 4, sigma=1.5)
+    lens = np.array([20, 13])
+    o1 = oracle.ra_attention_decode(q, k, v, 0.5, seqlens=lens)[0]
+    o2 = oracle.ra_attention_decode(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), 0.5,
+                                    seqlens=lens)[0]
+    np.testing.assert_array_equal(o1, o2)
+
+
 def test_planted_phi_exponent_error_breaks_golden():
     # Planted mistake: phi = q^7 instead of q^8 must fail the worked-example pin.
     import oracle.ra_oracle as ro
