@@ -11,7 +11,9 @@ Also reported: the forward alone on this workload and on the grouped-query workl
 (B=4, Hq=32, Hkv=8, N=4096, D=128, host RoPE), the two backward phases (ra_attn_bwd_dq,
 ra_attn_bwd_dkdv) alone, a padded batch through the explicit-mask entry points (B=4, H=16,
 N=4096, D=128, causal, key padding mask with per-sample lengths) beside the same workload
-unmasked, the row softmax and its backward at [16384, 8192], a roofline object for the
+unmasked, the split-KV decode step (B=16, Hq=32, Hkv=8, one query row per head, caches of up to
+16384 keys with per-sample lengths; HBM GB/s of the K/V bytes the lengths require), the row
+softmax and its backward at [16384, 8192], a roofline object for the
 dominant kernel (the longest of the forward, dQ and dK/dV kernels, each timed alone with HIP
 events on the stream the library launches it on) and the fp64 oracle timed on a bounded
 sample on the host cores.
@@ -116,10 +118,11 @@ class Attn:
         if st != 0:
             raise RuntimeError(f"ra_attn_bwd: {self.ra.ra_status_string(st)}")
 
-    def fwd_masked(self, mask):
+    def fwd_masked(self, mask, causal=None):
         w = self.w
+        cc = int(w.causal) if causal is None else causal
         st = self.ra.ra_attn_fwd_masked(self.q, self.k, self.v, self.o, self.stats, w.B, w.Hq,
-                                        w.Hkv, w.Nq, w.Nk, w.D, int(w.causal), w.scale, self.code,
+                                        w.Hkv, w.Nq, w.Nk, w.D, cc, w.scale, self.code,
                                         *mask, self.stream)
         if st != 0:
             raise RuntimeError(f"ra_attn_fwd_masked: {self.ra.ra_status_string(st)}")
@@ -320,6 +323,38 @@ def main():
     del pad, keep
     torch.cuda.empty_cache()
 
+    # split-KV decode: one query row per head against caches of per-sample lengths (HBM-bound)
+    wd = wl.decode_workload()
+    log(f"generating {wd.name}")
+    dec = Attn(ra, wd, False)
+    lens_np = wl.decode_seqlens(wd)
+    lens = torch.from_numpy(lens_np).cuda()
+    dws_bytes = ra.ra_attn_decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.Nq, wd.Nk, wd.D, dec.code)
+    dws = torch.empty(dws_bytes, dtype=torch.uint8, device="cuda")
+
+    def decode_step():
+        st = ra.ra_attn_decode(dec.q, dec.k, dec.v, dec.o, None, lens, dws, dws_bytes, wd.B, wd.Hq,
+                               wd.Hkv, wd.Nq, wd.Nk, wd.D, ra.RA_CAUSAL_BOTTOM_RIGHT, wd.scale,
+                               dec.code, dec.stream)
+        if st != 0:
+            raise RuntimeError(f"ra_attn_decode: {ra.ra_status_string(st)}")
+    for _ in range(3):
+        decode_step()
+    dec_ms = time_calls(dec.stream, decode_step, max(20, n_k))
+    kv_bytes = int(lens_np.astype(np.int64).sum()) * wd.Hkv * wd.D * 2 * dec.q.element_size()
+    dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    # the same step through the tiled forward, the cache lengths as a key padding mask
+    keep = torch.arange(wd.Nk, device="cuda")[None, :] < lens[:, None]
+    kpm = (keep, ra.RA_MASK_BOOL, (wd.Nk, 0, 0, 1))
+    br = ra.RA_CAUSAL_BOTTOM_RIGHT   # one query row: every key below the sample's length
+    for _ in range(2):
+        dec.fwd_masked(kpm, br)
+    decf_ms = time_calls(dec.stream, lambda: dec.fwd_masked(kpm, br), n_k)
+    log(f"decode {wd.name}: {dec_ms:.4f} ms, {dec_gbs:.0f} GB/s of K/V ({kv_bytes / 2**20:.0f} MiB); "
+        f"tiled forward with the lengths as a mask {decf_ms:.4f} ms")
+    del dec, dws, keep
+    torch.cuda.empty_cache()
+
     # row softmax (HBM-bound): read + write once
     x = torch.from_numpy(wl.make_rows(16384, 8192, seed=11)).cuda()
     p = torch.empty_like(x)
@@ -388,6 +423,10 @@ def main():
                                 "fwd_bwd_ms": round(pm_ms, 4), "fwd_ms": round(pmf_ms, 4),
                                 "tflops_counted": round(pm_tflops, 2),
                                 "unmasked_fwd_bwd_ms": round(pp_ms, 4)},
+        "decode": {"workload": wd.name, "entry": "ra_attn_decode", "ms": round(dec_ms, 4),
+                   "kv_bytes": kv_bytes, "GB/s": round(dec_gbs, 1),
+                   "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+                   "tiled_fwd_masked_ms": round(decf_ms, 4)},
         "softmax_rows": {"shape": [16384, 8192], "dtype": "f32", "ms": round(sm_ms, 4),
                          "GB/s": round(sm_gbs, 1), "frac_of_hbm_peak": round(sm_gbs / PEAK_HBM_GBS, 4)},
         "softmax_rows_bwd": {"shape": [16384, 8192], "dtype": "f32", "ms": round(smb_ms, 4),

@@ -207,6 +207,40 @@ int ra_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_
                      int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream);
 
 /*
+ * ra_attn_decode_workspace_bytes -- scratch size ra_attn_decode needs for these sizes (0 when the
+ * sizes are invalid for it or there is nothing to compute).  Caller-allocated, 256-byte aligned,
+ * contents need not be initialised.
+ */
+size_t ra_attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                      int64_t D, int dtype);
+
+/*
+ * ra_attn_decode -- attention of a few query rows per head against a key/value cache, split over
+ * the keys (decode and short-prefix steps).
+ *   Source: Ra-Family page, section 3, items ra_softmax and ra_attention.  phi has no online
+ *   rescaling, so partial results over key ranges cannot be merged as exp-softmax partials are:
+ *   the call makes three passes on the stream -- (1) scores and per-range row maxima, (2) with the
+ *   row max over all ranges, phi, its partial sums and partial P.V per range, (3) the sums over
+ *   ranges in a fixed order and the division.  K and V are each read once.
+ *   q, o: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D], the caches, of which sample b uses its first
+ *   seqlens[b] keys (seqlens: device int32 [B], or NULL for all Nk; values are clamped to
+ *   [0, Nk]).  causal: RA_CAUSAL_NONE; RA_CAUSAL_TOP_LEFT (query i takes keys j <= i);
+ *   RA_CAUSAL_BOTTOM_RIGHT (query i is position seqlens[b] - Nq + i of its sequence and takes
+ *   keys j <= seqlens[b] - Nq + i).  stats (optional) as ra_attn_fwd.  Equivalent to
+ *   ra_attn_fwd on each sample's cache prefix; a sample with seqlens[b] = 0 (or a row with no
+ *   allowed key) gives o = 0.
+ *   Restrictions: dtype RA_BF16 only (RA_ERR_DTYPE otherwise); (Hq / Hkv) * Nq <= 32, the query
+ *   rows of one K/V head (RA_ERR_SHAPE otherwise; use ra_attn_fwd for longer query blocks).
+ *   Forward only.  Deterministic.  Other checks, sizes and limits as ra_attn_fwd; workspace at
+ *   least ra_attn_decode_workspace_bytes(...) bytes, 256-byte aligned (RA_ERR_WORKSPACE,
+ *   RA_ERR_ALIGN).
+ */
+int ra_attn_decode(const void* q, const void* k, const void* v, void* o, float* stats,
+                   const int32_t* seqlens, void* workspace, size_t workspace_bytes, int64_t B,
+                   int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                   float scale, int dtype, void* stream);
+
+/*
  * ra_softmax_rows -- ra_softmax along the last axis of a [rows, cols] matrix.
  *   Source: Ra-Family page, section 3, item ra_softmax (ra_softmax(logits, dim=-1)).
  *   Entries equal to -inf are masked: p = 0 there, and they take no part in the max or the

@@ -3,7 +3,8 @@
 A thin ctypes binding over ``libra_attn.so``.  The functions named like the C entry points
 (``ra_attn_fwd``, ``ra_attn_fwd_masked``, ``ra_attn_fwd_counted``, ``ra_attn_bwd``,
 ``ra_attn_bwd_masked``, ``ra_attn_bwd_dq``, ``ra_attn_bwd_dkdv``, ``ra_attn_bwd_workspace_bytes``,
-``ra_softmax_rows``, ``ra_softmax_rows_bwd``, ``ra_rope_neox``) only marshal arguments: tensors
+``ra_attn_decode``, ``ra_attn_decode_workspace_bytes``, ``ra_softmax_rows``,
+``ra_softmax_rows_bwd``, ``ra_rope_neox``) only marshal arguments: tensors
 become device pointers, a mask becomes an ``ra_mask`` descriptor, the stream becomes a
 ``hipStream_t``.  Every step of the computation runs in the library's HIP kernels;
 there is no CPU or PyTorch fallback, and importing the compute functions without the built
@@ -26,7 +27,8 @@ __all__ = [
     "RA_MASK_NONE", "RA_MASK_BOOL", "RA_MASK_ADD", "RaMask", "RaError", "load_library",
     "library_path", "ra_status_string", "ra_attn_fwd", "ra_attn_fwd_masked",
     "ra_attn_fwd_counted", "ra_attn_bwd", "ra_attn_bwd_masked",
-    "ra_attn_bwd_dq", "ra_attn_bwd_dkdv", "ra_attn_bwd_workspace_bytes", "ra_softmax_rows",
+    "ra_attn_bwd_dq", "ra_attn_bwd_dkdv", "ra_attn_bwd_workspace_bytes", "ra_attn_decode",
+    "ra_attn_decode_workspace_bytes", "attn_decode", "ra_softmax_rows",
     "ra_softmax_rows_bwd", "ra_rope_neox", "ra_rope",
     "attn_fwd", "attn_bwd", "ra_attention", "ra_softmax",
 ]
@@ -108,6 +110,12 @@ def load_library():
                                      _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                      ctypes.c_float, ctypes.c_int, _vp]
     lib.ra_attn_bwd_dkdv.restype = ctypes.c_int
+    lib.ra_attn_decode_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+    lib.ra_attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.ra_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64,
+                                   _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+                                   ctypes.c_int, _vp]
+    lib.ra_attn_decode.restype = ctypes.c_int
     lib.ra_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_int, _vp]
     lib.ra_softmax_rows.restype = ctypes.c_int
     lib.ra_softmax_rows_bwd.argtypes = [_vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp]
@@ -215,6 +223,18 @@ def ra_attn_bwd_dkdv(q, k, v, d_o, stats, dk, dv, workspace, workspace_bytes, B,
                                            int(causal), float(scale), int(dtype), _stream(stream))
 
 
+def ra_attn_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, dtype) -> int:
+    return load_library().ra_attn_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, int(dtype))
+
+
+def ra_attn_decode(q, k, v, o, stats, seqlens, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, D,
+                   causal, scale, dtype, stream=None) -> int:
+    return load_library().ra_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(stats),
+                                         _ptr(seqlens), _ptr(workspace), int(workspace_bytes), B,
+                                         Hq, Hkv, Nq, Nk, D, int(causal), float(scale),
+                                         int(dtype), _stream(stream))
+
+
 def ra_softmax_rows(x, p, rows, cols, dtype, stream=None) -> int:
     return load_library().ra_softmax_rows(_ptr(x), _ptr(p), rows, cols, int(dtype),
                                           _stream(stream))
@@ -254,6 +274,31 @@ def _shapes(q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
     return B, Hq, Hkv, Nq, Nk, D
+
+
+def attn_decode(q, k_cache, v_cache, seqlens=None, causal=False, scale: Optional[float] = None,
+                with_stats: bool = False):
+    """Decode step: q [B, Hq, Nq, D] (bf16, (Hq / Hkv) * Nq <= 32) against the caches
+    k_cache, v_cache [B, Hkv, Nk, D], sample b using its first seqlens[b] keys (int32 device
+    tensor [B], or None for all).  ``causal``: see causal_code ("bottom_right": query i is
+    position seqlens[b] - Nq + i).  Allocates O (and stats) and a workspace; runs
+    ra_attn_decode on the current stream.  Forward only."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, D = _shapes(q, k_cache, v_cache)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    stats = torch.empty((B, Hq, Nq, 2), dtype=torch.float32, device=q.device) if with_stats else None
+    lens = None
+    if seqlens is not None:
+        lens = torch.as_tensor(seqlens, dtype=torch.int32, device=q.device).contiguous()
+        if tuple(lens.shape) != (B,):
+            raise ValueError(f"seqlens must be [B] = [{B}]")
+    code = _dtype_code(q)
+    nbytes = ra_attn_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, code)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(ra_attn_decode(q, k_cache, v_cache, o, stats, lens, ws, nbytes, B, Hq, Hkv, Nq, Nk, D,
+                          causal_code(causal), scale, code), "ra_attn_decode")
+    return (o, stats) if with_stats else o
 
 
 def causal_code(is_causal) -> int:

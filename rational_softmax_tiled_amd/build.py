@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libra_attn.so")
-SOURCES = ["ra_abi.hip", "ra_fwd.hip", "ra_bwd.hip", "ra_softmax.hip", "ra_rope.hip"]
+SOURCES = ["ra_abi.hip", "ra_fwd.hip", "ra_bwd.hip", "ra_decode.hip", "ra_softmax.hip", "ra_rope.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

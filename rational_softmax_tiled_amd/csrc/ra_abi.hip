@@ -257,6 +257,66 @@ int ra_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_
                          B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, ra::kBwdDkdv, stream);
 }
 
+// Decode: the query rows of one K/V head (rep * Nq) must fit one wave's 32 MFMA columns.
+static int check_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                        int causal, float scale, int dtype) {
+  int st = check_sizes(B, Hq, Hkv, Nq, Nk, D, scale, dtype);
+  if (st != RA_OK) return st;
+  if (dtype != RA_BF16) return RA_ERR_DTYPE;
+  if (causal != RA_CAUSAL_NONE && causal != RA_CAUSAL_TOP_LEFT && causal != RA_CAUSAL_BOTTOM_RIGHT)
+    return RA_ERR_MASK;
+  if (Hkv > 0 && (Hq / Hkv) * Nq > 32) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+size_t ra_attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                      int64_t D, int dtype) {
+  if (check_decode(B, Hq, Hkv, Nq, Nk, D, RA_CAUSAL_NONE, 1.0f, dtype) != RA_OK) return 0;
+  if (B * Hq * Nq == 0 || Nk == 0) return 0;
+  return ra::decode_plan(B, Hkv, Nk, (Hq / Hkv) * Nq, D).bytes;
+}
+
+int ra_attn_decode(const void* q, const void* k, const void* v, void* o, float* stats,
+                   const int32_t* seqlens, void* workspace, size_t workspace_bytes, int64_t B,
+                   int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                   float scale, int dtype, void* stream) {
+  int st = check_decode(B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype);
+  if (st != RA_OK) return st;
+  const int64_t rows = B * Hq * Nq;
+  if (rows == 0) return RA_OK;
+  if (q == nullptr || o == nullptr) return RA_ERR_NULLPTR;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return RA_ERR_NULLPTR;
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, 16) || !aligned(v, 16)) return RA_ERR_ALIGN;
+  if ((stats != nullptr && !aligned(stats, 4)) || (seqlens != nullptr && !aligned(seqlens, 4)))
+    return RA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (Nk == 0) {
+    st = fill_zero(o, (size_t)rows * D, dtype, s);
+    if (st == RA_OK && stats != nullptr)
+      st = hip_status(ra::launch_fill_pairs(stats, -INFINITY, 0.0f, (size_t)rows, s));
+    return st;
+  }
+  const size_t need = ra::decode_plan(B, Hkv, Nk, (Hq / Hkv) * Nq, D).bytes;
+  if (workspace == nullptr || workspace_bytes < need) return RA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return RA_ERR_ALIGN;
+  ra::DecodeProblem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.stats = stats;
+  p.seqlens = seqlens;
+  p.B = (int)B;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.D = (int)D;
+  p.causal = causal;
+  p.scale = scale;
+  return hip_status(ra::launch_attn_decode(p, workspace, s));
+}
+
 int ra_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, int dtype, void* stream) {
   if (dtype != RA_F32 && dtype != RA_BF16) return RA_ERR_DTYPE;
   if (rows < 0 || cols < 0) return RA_ERR_SHAPE;

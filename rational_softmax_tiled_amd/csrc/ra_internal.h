@@ -49,6 +49,29 @@ hipError_t launch_attn_bwd(const AttnProblem& p, const void* o, const void* d_o,
                            const float* stats, void* dq, void* dk, void* dv,
                            const BwdWorkspace& ws, int phases, hipStream_t stream);
 
+// Split-KV decode (bf16): R = (Hq / Hkv) * Nq <= 32 query rows per K/V head against caches of
+// Nk rows, sample b using its first seqlens[b] (nullable: all).  causal: 0, 1 top-left,
+// 2 bottom-right per sample.
+struct DecodeProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* stats;
+  const int* seqlens;
+  int B, Hq, Hkv, Nq, Nk, D;
+  int causal;
+  float scale;
+};
+// Keys per wave, chunks per (batch, K/V head) group and the workspace carve-up (a function of
+// the sizes only, so the size query and the launch agree).
+struct DecodePlan {
+  int64_t chunk, S;
+  size_t scores_bytes, pmax_bytes, psum_bytes, pacc_bytes, gmax_bytes, bytes;
+};
+DecodePlan decode_plan(int64_t B, int64_t Hkv, int64_t Nk, int64_t R, int64_t D);
+hipError_t launch_attn_decode(const DecodeProblem& p, void* workspace, hipStream_t stream);
+
 // Row softmax.
 hipError_t launch_softmax_rows(const void* x, void* p, int64_t rows, int64_t cols, bool bf16,
                                hipStream_t stream);

@@ -238,3 +238,36 @@ def test_masked_bwd_validation(lib):
     assert mbwd(data=None) == NULLPTR
     assert mbwd(ws=None) == WORKSPACE
     assert mbwd(B=0) == OK
+
+
+def dec(B=1, Hq=8, Hkv=2, Nq=1, Nk=100, D=128, causal=2, dtype=ra.RA_BF16, ws=P2, ws_bytes=1 << 30,
+        seqlens=None, stats=None, q=P, o=P2):
+    return ra.ra_attn_decode(q, P, P, o, stats, seqlens, ws, ws_bytes, B, Hq, Hkv, Nq, Nk, D, causal,
+                             0.1, dtype, 0)
+
+
+def test_decode_validation(lib):
+    assert dec(dtype=ra.RA_F32) == DTYPE
+    assert dec(Hq=8, Hkv=2, Nq=9) == SHAPE          # 4 * 9 = 36 query rows per K/V head > 32
+    assert dec(Hq=64, Hkv=1, Nq=1) == SHAPE
+    assert dec(Hq=3, Hkv=2) == GQA
+    assert dec(causal=3) == MASK
+    assert dec(D=96) == HEADDIM
+    assert dec(q=None) == NULLPTR
+    assert dec(o=P2 + 8) == ALIGN
+    assert dec(stats=P + 2) == ALIGN
+    assert dec(seqlens=P + 2) == ALIGN
+    assert dec(ws=None) == WORKSPACE
+    assert dec(ws_bytes=1000) == WORKSPACE
+    assert dec(ws=P2 + 16) == ALIGN                 # 256-byte aligned workspace
+    assert dec(B=0) == OK and dec(Nq=0) == OK
+
+
+def test_decode_workspace_size(lib):
+    f = ra.ra_attn_decode_workspace_bytes
+    assert f(16, 32, 8, 1, 16384, 128, ra.RA_BF16) > 16 * 8 * 16384 * 4 * 4   # scores of 4 rows
+    assert f(16, 32, 8, 1, 16384, 128, ra.RA_F32) == 0
+    assert f(1, 8, 2, 9, 100, 128, ra.RA_BF16) == 0
+    assert f(0, 8, 2, 1, 100, 128, ra.RA_BF16) == 0
+    assert f(1, 8, 2, 1, 100, 64, ra.RA_BF16) < f(1, 8, 2, 1, 10000, 64, ra.RA_BF16)
+    assert f(1, 8, 2, 1, 100, 64, ra.RA_BF16) % 256 == 0

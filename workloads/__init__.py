@@ -90,6 +90,24 @@ def padded_batch_lengths(w: AttnWorkload = PADDED_BATCH):
     return PADDED_LENGTHS
 
 
+# A decode step: one new query row per head against per-sample K/V caches of different lengths
+# (grouped-query heads, the cache capacity Nk).  Lengths are drawn uniformly from [Nk/4, Nk]
+# with their own seeded generator; inputs follow the recipe above (Q [B, Hq, 1, D], caches
+# [B, Hkv, Nk, D]).
+DECODE = AttnWorkload("bf16_decode_gqa_B16_Hq32_Hkv8_Nq1_Nk16384_D128", "bf16", True, 16, 32, 8,
+                      1, 16384, 128, seed=7)
+
+
+def decode_workload() -> AttnWorkload:
+    return DECODE
+
+
+def decode_seqlens(w: AttnWorkload = DECODE) -> np.ndarray:
+    """int32 [B] cache lengths of the decode workload."""
+    rng = np.random.default_rng(w.seed + 1000)
+    return rng.integers(w.Nk // 4, w.Nk + 1, size=w.B).astype(np.int32)
+
+
 def padded_batch_keep(w: AttnWorkload = PADDED_BATCH) -> np.ndarray:
     """The [B, Nk] boolean key padding mask: True where key j < length of sample b."""
     return np.arange(w.Nk)[None, :] < np.asarray(padded_batch_lengths(w))[:, None]
