@@ -48,12 +48,12 @@ MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("e229c2aa2d32bd1a8d25815dc54f9c374c23d70506011bd5c0935941b15869fb",
-                        262687.6, 135188.6),
-    "attn_bwd_dq_bf16_kernel": ("22ec73d818cbcef5ba8b2caa94d4418363582ddf35747528875310d8d94e5412",
-                                437394.7, 143448.3),
-    "attn_bwd_dkdv_bf16_kernel": ("22ec73d818cbcef5ba8b2caa94d4418363582ddf35747528875310d8d94e5412",
-                                  268073.4, 262146.6),
+    "attn_fwd_kernel": ("6653cd967a4953efcb0f2cbf692f7e37306c601efa2e940f67e80e09393d0fc9",
+                        260443.4, 135194.4),
+    "attn_bwd_dq_bf16_kernel": ("bf2d5e5ed05b6b20ff21fb2a8dc6b861524093e699c8fac433d9f30a005ef9fd",
+                                437586.9, 143456.0),
+    "attn_bwd_dkdv_bf16_kernel": ("bf2d5e5ed05b6b20ff21fb2a8dc6b861524093e699c8fac433d9f30a005ef9fd",
+                                  267493.3, 262148.8),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],

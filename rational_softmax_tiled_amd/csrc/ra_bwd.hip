@@ -488,10 +488,15 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const int qrow = min(qi, a.Nq - 1);
   const int frow = lane & 31, fcol = 8 * (lane >> 5);
 
+  // one resource per matrix (K, V of the group), the tile picked by a scalar offset
+  const u32x4 k_rsrc = dma_rsrc(kg, a.Nk * D * 2), v_rsrc = dma_rsrc(vg, a.Nk * D * 2);
+  const int lane_off = dma_lane_offset<D, kWaves>(wave, lane);
+  const unsigned k_m0[2] = {lds_addr(k_lds[0]), lds_addr(k_lds[1])};
+  const unsigned v_m0[2] = {lds_addr(v_lds[0]), lds_addr(v_lds[1])};
   // tile 0 is in flight while the row terms are prepared
   if (nt > 0) {
-    dma_tile<D, BN>(k_lds[0], kg, a.Nk, wave, lane);
-    dma_tile<D, BN>(v_lds[0], vg, a.Nk, wave, lane);
+    dma_tile_at<D, BN>(k_rsrc, 0, k_m0[0], lane_off, wave);
+    dma_tile_at<D, BN>(v_rsrc, 0, v_m0[0], lane_off, wave);
   }
   const bf16* qp = static_cast<const bf16*>(a.q) + (head + qrow) * D;
   const bf16* dop = static_cast<const bf16*>(a.d_o) + (head + qrow) * D;
@@ -526,8 +531,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   for (int kt = 0; kt < nt; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nt) {
-      dma_tile<D, BN>(k_lds[buf ^ 1], kg + (size_t)(kt + 1) * BN * D, a.Nk - (kt + 1) * BN, wave, lane);
-      dma_tile<D, BN>(v_lds[buf ^ 1], vg + (size_t)(kt + 1) * BN * D, a.Nk - (kt + 1) * BN, wave, lane);
+      dma_tile_at<D, BN>(k_rsrc, (kt + 1) * BN * D * 2, k_m0[buf ^ 1], lane_off, wave);
+      dma_tile_at<D, BN>(v_rsrc, (kt + 1) * BN * D * 2, v_m0[buf ^ 1], lane_off, wave);
     }
     if (kt < nt_w) {
 #pragma unroll
@@ -662,36 +667,58 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   const bf16* dobase = static_cast<const bf16*>(a.d_o);
   static_assert(QT == kWave, "one row term per lane of a DMA instruction");
 
-  // step -> (query head, first query row of the tile)
-  auto tile_head = [&](int step) { return (size_t)(b * a.Hq + g * a.rep + step / per_head) * a.Nq; };
-  auto tile_row = [&](int step) { return (qt0 + step % per_head) * QT; };
-  // Q/dO half-tiles and the tile's per-row terms (written by the query-parallel kernel) by LDS
-  // DMA, issued by the upper half once its own work for the step is done (it would otherwise
-  // idle at the barrier while the lower half finishes); rows past Nq read as zeros, which the
-  // masking of those rows makes harmless.
-  const float* term = kg == 0 ? a.kd : kg == 1 ? a.il : kg == 2 ? a.cil : a.r;
-  auto issue = [&](int step) {
-    const size_t head = tile_head(step);
-    const int i0 = tile_row(step);
-    const size_t r0 = (head + i0) * D, r1 = (head + i0 + HR) * D;
-    const int bytes = min(a.Nq - i0, QT) * 4;
-    lds_dma<4>(term + head + i0, bytes, &st_lds[step % 3][kg][0], lane * 4);
-    if (kg == 3) lds_dma<4>(a.amax + head + i0, bytes, &st_lds[step % 3][4][0], lane * 4);
-    dma_tile<D, HR, NW / 2>(q_up(step & 1), qbase + r0, a.Nq - i0, kg, lane);
-    dma_tile<D, HR, NW / 2>(do_up(step & 1), dobase + r0, a.Nq - i0, kg, lane);
-    dma_tile<D, HR, NW / 2>(q_lo(step % 3), qbase + r1, a.Nq - i0 - HR, kg, lane);
-    dma_tile<D, HR, NW / 2>(do_lo(step % 3), dobase + r1, a.Nq - i0 - HR, kg, lane);
+  // Step -> (query head hh of the group, query tile qt, slot of the three-slot buffers), advanced
+  // one step at a time: the steps walk the tiles qt0 .. nqt-1 of each head in turn.  Scalar
+  // divisions and pointer conversions per step cost more than they seem: a wave issues at most
+  // one instruction every four cycles.
+  struct Cursor {
+    int hh, qt, slot3;
   };
-  // does this wave's 32 x 32 block of tile `step` hold any allowed score?
-  auto block_live = [&](int step) {
-    const int i0 = tile_row(step) + HR * half;
+  auto advance = [&](Cursor c) {
+    c.slot3 = c.slot3 == 2 ? 0 : c.slot3 + 1;
+    if (++c.qt == nqt) {
+      c.qt = qt0;
+      ++c.hh;
+    }
+    return c;
+  };
+  auto head_row = [&](const Cursor& c) { return (b * a.Hq + g * a.rep + c.hh) * a.Nq; };
+  // Q/dO half-tiles and the tile's per-row terms (written by the query-parallel kernel) by LDS
+  // DMA, issued by the upper half at the start of the step before the tile is needed; rows past
+  // Nq read as zeros, which the masking of those rows makes harmless.  One resource covers the
+  // 64 rows of Q (and of dO): the lower half-tile is its second 8 KiB.
+  const float* term = kg == 0 ? a.kd : kg == 1 ? a.il : kg == 2 ? a.cil : a.r;
+  const unsigned smem_b = lds_addr(smem), st_b = lds_addr(&st_lds[0][0][0]);
+  const int tile_lane = dma_lane_offset<D, NW / 2>(kg, lane);
+  constexpr int TILE_BLOCKS = dma_blocks_per_wave<D, HR, NW / 2>();
+  auto issue = [&](const Cursor& c, int slot2) {
+    const int row = head_row(c), i0 = c.qt * QT;
+    const int rows = min(a.Nq - i0, QT);
+    const u32x4 tr = dma_rsrc(term + row + i0, rows * 4);
+    lds_dma_at<4>(tr, st_b + (c.slot3 * 5 + kg) * QT * 4, lane * 4, 0);
+    if (kg == 3) lds_dma_at<4>(dma_rsrc(a.amax + row + i0, rows * 4), st_b + (c.slot3 * 5 + 4) * QT * 4, lane * 4, 0);
+    const u32x4 qr = dma_rsrc(qbase + (size_t)(row + i0) * D, rows * D * 2);
+    const u32x4 dr = dma_rsrc(dobase + (size_t)(row + i0) * D, rows * D * 2);
+    const unsigned up = smem_b + (2 * KV + slot2 * HTILE) * 2, lo = smem_b + (2 * KV + (4 + c.slot3) * HTILE) * 2;
+#pragma unroll
+    for (int i = 0; i < TILE_BLOCKS; ++i) {
+      const int blk = (i * (NW / 2) + kg) * 1024, soff = i * (NW / 2) * 1024;
+      lds_dma_at<16>(qr, up + blk, tile_lane, soff);
+      lds_dma_at<16>(dr, up + 2 * HTILE * 2 + blk, tile_lane, soff);
+      lds_dma_at<16>(qr, lo + blk, tile_lane, soff + HR * D * 2);
+      lds_dma_at<16>(dr, lo + 3 * HTILE * 2 + blk, tile_lane, soff + HR * D * 2);
+    }
+  };
+  // does this wave's 32 x 32 block of the tile at query row i0 hold any allowed score?
+  auto block_live = [&](const Cursor& c) {
+    const int i0 = c.qt * QT + HR * half;
     return active && i0 < a.Nq && !(CAUSAL && i0 + 31 + a.coff < j0);
   };
-  // explicit mask elements of this wave's block of tile `step` (read ahead of the products)
-  auto mask_load = [&](int step, unsigned (&mv)[16]) {
+  // explicit mask elements of this wave's block (read ahead of the products)
+  auto mask_load = [&](const Cursor& c, unsigned (&mv)[16]) {
     if constexpr (MASKED) {
-      const MaskSlice<bf16> ms(a.mask, b, g * a.rep + step / per_head);
-      ms.load(mv, key * ms.sk + (tile_row(step) + HR * half + 4 * (lane >> 5)) * ms.sq, ms.sq);
+      const MaskSlice<bf16> ms(a.mask, b, g * a.rep + c.hh);
+      ms.load(mv, key * ms.sk + (c.qt * QT + HR * half + 4 * (lane >> 5)) * ms.sq, ms.sq);
     }
   };
 
@@ -769,41 +796,49 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   const size_t kv0 = ((size_t)(b * a.Hkv + g) * a.Nk + key0_wg) * D;
   dma_tile<D, kKeysPerWg, NW>(k_lds, static_cast<const bf16*>(a.k) + kv0, a.Nk - key0_wg, wave, lane);
   dma_tile<D, kKeysPerWg, NW>(v_lds, static_cast<const bf16*>(a.v) + kv0, a.Nk - key0_wg, wave, lane);
-  if (steps > 0 && half == 0) issue(0);
+  const Cursor first{0, qt0, 0};
+  if (steps > 0 && half == 0) issue(first, 0);
   wait_vmem();
   __syncthreads();
 
   if (half == 0) {
+    Cursor cur = first, nxt = advance(first);   // steps st and st + 1
     for (int st = 0; st <= steps; ++st) {
-      if (st < steps && block_live(st)) {
+      // the next tile's copies go out first: their buffers were last read before the barrier
+      // that ended step st - 1, and they have the whole step to land
+      if (st + 1 < steps) issue(nxt, (st + 1) & 1);
+      if (st < steps && block_live(cur)) {
         f32x16 s, dp;
         unsigned mv[16];
-        mask_load(st, mv);
+        mask_load(cur, mv);
         products_sdp(q_up(st & 1), do_up(st & 1), s, dp);
-        derivative(s, dp, mv, tile_row(st), st % 3);
+        derivative(s, dp, mv, cur.qt * QT, cur.slot3);
         products_dkdv(s, dp, q_up(st & 1), do_up(st & 1));
       }
-      if (st + 1 < steps) issue(st + 1);
       wait_vmem();
       __syncthreads();
+      cur = nxt;
+      nxt = advance(nxt);
     }
   } else {
     f32x16 s = {}, dp = {};
     unsigned mv[16];
     bool carried = false;   // s, dp (and mv) hold S, dP (and the mask block) of tile st - 1
+    Cursor prev = first, cur = first;
     for (int st = 0; st <= steps; ++st) {
       if (carried) {
-        const int pv = (st - 1) % 3;
-        derivative(s, dp, mv, tile_row(st - 1) + HR, pv);
-        products_dkdv(s, dp, q_lo(pv), do_lo(pv));
+        derivative(s, dp, mv, prev.qt * QT + HR, prev.slot3);
+        products_dkdv(s, dp, q_lo(prev.slot3), do_lo(prev.slot3));
       }
-      carried = st < steps && block_live(st);
+      carried = st < steps && block_live(cur);
       if (carried) {
-        mask_load(st, mv);
-        products_sdp(q_lo(st % 3), do_lo(st % 3), s, dp);
+        mask_load(cur, mv);
+        products_sdp(q_lo(cur.slot3), do_lo(cur.slot3), s, dp);
       }
       wait_vmem();
       __syncthreads();
+      prev = cur;
+      cur = advance(cur);
     }
   }
 

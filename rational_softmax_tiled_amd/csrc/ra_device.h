@@ -424,6 +424,43 @@ struct SwzTile {
 // chunk each lane fetches lays the tile out swizzled (swz).  Rows >= nvalid read as zeros.
 // The NW waves of the workgroup share the 1 KiB blocks.  The caller waits (vmcnt) and issues a
 // barrier before any wave reads the tile.
+// LDS byte address of a __shared__ object: one address-space conversion, kept in a scalar register
+// by callers that add constant offsets to it rather than converting every pointer.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (unsigned)(unsigned long)(const __attribute__((address_space(3))) char*)p);
+}
+
+// Raw buffer resource words for [g, g + bytes) (stride 0, raw dword format; zeros past the end).
+// g and bytes must be the same in every lane.
+__device__ __forceinline__ u32x4 dma_rsrc(const void* g, int bytes) {
+  const unsigned long long addr = (unsigned long long)g;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)addr);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(addr >> 32) & 0xffffu);   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes > 0 ? bytes : 0);               // num_records
+  r[3] = kBufferWord3;
+  return r;
+}
+
+// One LDS DMA instruction from a prepared resource: every lane fetches SIZE bytes at byte offset
+// voffset + soffset of the buffer and lane l stores them at LDS byte address m0 + SIZE * l.  The
+// one wait state between the M0 write and the load is the hazard the ISA requires.
+template <int SIZE>
+__device__ __forceinline__ void lds_dma_at(const u32x4& rsrc, unsigned m0, int voffset, int soffset) {
+  static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4");
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voffset), "s"(rsrc),
+                    "s"(__builtin_amdgcn_readfirstlane(soffset))
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voffset), "s"(rsrc),
+                    "s"(__builtin_amdgcn_readfirstlane(soffset))
+                 : "memory", "m0");
+}
+
 // One LDS DMA instruction: every lane fetches SIZE bytes (4 or 16) at byte offset
 // voffset + soffset of the buffer [g, g + bytes) (zeros past its end) and lane l stores them at LDS bytes
 // [SIZE*l, SIZE*l + SIZE) after `lds`.  Issued from inline assembly so that the compiler does
@@ -434,24 +471,19 @@ struct SwzTile {
 template <int SIZE>
 __device__ __forceinline__ void lds_dma(const void* g, int bytes, const void* lds, int voffset,
                                         int soffset = 0) {
-  static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4");
-  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-  const unsigned long long addr = (unsigned long long)g;
-  u32x4_t rsrc;
-  rsrc[0] = __builtin_amdgcn_readfirstlane((unsigned)addr);
-  rsrc[1] = __builtin_amdgcn_readfirstlane((unsigned)(addr >> 32) & 0xffffu);   // stride 0
-  rsrc[2] = __builtin_amdgcn_readfirstlane(bytes > 0 ? bytes : 0);               // num_records
-  rsrc[3] = kBufferWord3;
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(unsigned long)(const __attribute__((address_space(3))) char*)lds);
-  if constexpr (SIZE == 16)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(m0), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(m0), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
-                 : "memory", "m0");
+  lds_dma_at<SIZE>(dma_rsrc(g, bytes), lds_addr(lds), voffset, soffset);
+}
+
+// Per-lane byte offset of dma_block's copies when the NW waves' blocks share one lane layout (the
+// case dma_block calls kSharedLaneOffset): block b = i * NW + wave then sits at scalar offset
+// i * NW * 1024 of the tile and LDS bytes b * 1024.
+template <int D, int NW>
+__device__ __forceinline__ int dma_lane_offset(int wave, int lane) {
+  static_assert((NW * 512 / D) % 16 == 0, "the waves' blocks must share the lane layout");
+  constexpr int CPR = D / 8;
+  const int p = wave * 64 + lane;
+  const int row = p / CPR, pos = p % CPR;
+  return (row * CPR + (pos ^ swz<bf16, D>(row))) * 16;
 }
 
 // Block i of this wave's share of a ROWS x D tile copy (blocks i*NW + wave); a no-op past the end.
@@ -485,6 +517,19 @@ template <int D, int ROWS, int NW = kWaves>
 __device__ __forceinline__ void dma_tile(bf16* lds, const bf16* g, int nvalid, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < dma_blocks_per_wave<D, ROWS, NW>(); ++i) dma_block<D, ROWS, NW>(lds, g, nvalid, wave, lane, i);
+}
+
+// dma_tile from a resource over a whole matrix (the tile starts at byte tile_off of it; rows past
+// the resource's end read as zeros) to LDS byte address m0, with lane_off = dma_lane_offset: no
+// per-tile pointer arithmetic or address-space conversion.
+template <int D, int ROWS, int NW = kWaves>
+__device__ __forceinline__ void dma_tile_at(const u32x4& rsrc, int tile_off, unsigned m0, int lane_off,
+                                            int wave) {
+  constexpr int BLOCKS = ROWS * D * 2 / 1024;
+  static_assert(BLOCKS % NW == 0, "every wave copies the same number of blocks");
+#pragma unroll
+  for (int i = 0; i < BLOCKS / NW; ++i)
+    lds_dma_at<16>(rsrc, m0 + (i * NW + wave) * 1024, lane_off, tile_off + i * NW * 1024);
 }
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone): every outstanding vector-memory load,

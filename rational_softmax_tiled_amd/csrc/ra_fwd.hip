@@ -149,8 +149,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   // ---- pass 1: row max of the raw dot products (K tiles double-buffered through LDS)
   // Tiles reach LDS by DMA (bf16) or through registers (fp32), one tile ahead of the math.
   SwzTile<T, D, (sizeof(T) == 2 ? 0 : BN)> kreg;
+  // bf16: one resource per matrix (K, V of the head), the tile picked by a scalar offset
+  const u32x4 k_rsrc = dma_rsrc(kg, a.Nk * D * (int)sizeof(T));
+  const u32x4 v_rsrc = dma_rsrc(vg, a.Nk * D * (int)sizeof(T));
+  const int lane_off = sizeof(T) == 2 ? dma_lane_offset<D, kWaves>(wave, lane) : 0;
   auto k_issue = [&](int kt, T* dst) {
-    if constexpr (sizeof(T) == 2) dma_tile<D, BN>(dst, kg + (size_t)kt * BN * D, a.Nk - kt * BN, wave, lane);
+    if constexpr (sizeof(T) == 2) dma_tile_at<D, BN>(k_rsrc, kt * BN * D * 2, lds_addr(dst), lane_off, wave);
     else kreg.load(kg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
   };
   auto k_land = [&](T* dst) {
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
 
   TransTile<T, D, (VTR ? 0 : BN)> vreg;   // fp32 only: V^T staged through registers
   auto v_issue = [&](int kt, T* dst) {
-    if constexpr (VTR) dma_tile<D, BN>(dst, vg + (size_t)kt * BN * D, a.Nk - kt * BN, wave, lane);
+    if constexpr (VTR) dma_tile_at<D, BN>(v_rsrc, kt * BN * D * 2, lds_addr(dst), lane_off, wave);
     else vreg.load(vg + (size_t)kt * BN * D, a.Nk - kt * BN, tid);
   };
   auto v_land = [&](T* dst) {
