@@ -48,12 +48,12 @@ MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("6653cd967a4953efcb0f2cbf692f7e37306c601efa2e940f67e80e09393d0fc9",
-                        260443.4, 135194.4),
-    "attn_bwd_dq_bf16_kernel": ("bf2d5e5ed05b6b20ff21fb2a8dc6b861524093e699c8fac433d9f30a005ef9fd",
-                                437586.9, 143456.0),
-    "attn_bwd_dkdv_bf16_kernel": ("bf2d5e5ed05b6b20ff21fb2a8dc6b861524093e699c8fac433d9f30a005ef9fd",
-                                  267493.3, 262148.8),
+    "attn_fwd_kernel": ("9bc204fcce00ec4c0ea7b06a945a0b3c8d4aa5d21a751e84f19600250d8d9c55",
+                        263081.4, 135185.8),
+    "attn_bwd_dq_bf16_kernel": ("0b7a589acb1aef8c9ebfb43ff181b8e5515f34e5caea6fa093d7a96519563485",
+                                436104.5, 143458.2),
+    "attn_bwd_dkdv_bf16_kernel": ("0b7a589acb1aef8c9ebfb43ff181b8e5515f34e5caea6fa093d7a96519563485",
+                                  267522.4, 262146.3),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],
@@ -67,7 +67,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", choices=["fwd_bwd", "fwd"], default="fwd_bwd")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-heads", type=int, default=3,

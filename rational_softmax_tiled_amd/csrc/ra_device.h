@@ -170,6 +170,25 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Max over the 64 lanes with DPP row operations only (no LDS round trip): quad swaps and row
+// rotations leave every lane of a 16-lane row with the row max; row_bcast:15 then folds row r-1
+// into rows 1 and 3, and row_bcast:31 folds lane 31 into rows 2 and 3.  Exact in lane 63 (other
+// lanes hold partial maxima).  Rows a broadcast does not target keep x (old operand = x).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+  const int i = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_max_lane63(float x) {
+  x = fmaxf(x, dpp_f32<0xB1, 0xf>(x));    // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f32<0x4E, 0xf>(x));    // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f32<0x124, 0xf>(x));   // row_ror:4
+  x = fmaxf(x, dpp_f32<0x128, 0xf>(x));   // row_ror:8
+  x = fmaxf(x, dpp_f32<0x142, 0xa>(x));   // row_bcast:15 into rows 1, 3
+  x = fmaxf(x, dpp_f32<0x143, 0xc>(x));   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs.  Give each XCD a contiguous range
 // of logical workgroup ids so that neighbours (which share K/V) share one L2.
 __device__ __forceinline__ int xcd_remap(int i, int n) {
@@ -535,6 +554,14 @@ __device__ __forceinline__ void dma_tile_at(const u32x4& rsrc, int tile_off, uns
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone): every outstanding vector-memory load,
 // LDS DMA included, has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// s_waitcnt vmcnt(N): at most the N youngest vector-memory loads still outstanding (loads
+// complete in issue order, so every older one, LDS DMA included, has landed).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

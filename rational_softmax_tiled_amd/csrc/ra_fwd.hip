@@ -63,8 +63,8 @@ __device__ __forceinline__ void store_quad<float>(float* dst, f32x16 acc, int ba
 }
 
 // Mask entries of a 32x32 S^T block (keys on the accumulator rows, query row qrow on the lane):
-// the explicit mask first, then key >= Nk, or (causal) key > qrow + coff.
-template <bool CAUSAL, bool MASKED, typename T>
+// the explicit mask first, then key >= Nk or key > qrow + coff (coff = Nk: no causal limit).
+template <bool MASKED, typename T>
 __device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int lane, int Nk, int coff,
                                            const MaskSlice<T>& ms) {
   if constexpr (MASKED) {
@@ -73,9 +73,9 @@ __device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int la
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
   }
-  // key = key0 + 4 (lane >> 5) + r is kept iff key < Nk and (causal) key <= qrow + coff
+  // key = key0 + 4 (lane >> 5) + r is kept iff key < Nk and key <= qrow + coff
   const int lb = key0 + 4 * (lane >> 5);
-  keep_rows(s, -kNoBound, min(Nk - lb, CAUSAL ? qrow + coff + 1 - lb : kNoBound));
+  keep_rows(s, -kNoBound, min(Nk - lb, qrow + coff + 1 - lb));
 }
 
 // S^T block (32 keys x 32 query rows) of key sub-block sb of the staged (swizzled) K tile.
@@ -88,8 +88,41 @@ __device__ __forceinline__ f32x16 score_block(const T* k_tile, const typename Ty
   return s;
 }
 
-template <typename T, int D, int BN, bool CAUSAL, bool COUNT, bool WRITE_O, bool MASKED>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
+// Both 32-key blocks of a 64-key bf16 tile.  All K fragments of block 0 are read before its
+// products start and block 1's are read under them, so no product waits on a read issued just
+// before it (LDS latency is several product times).
+template <int D>
+__device__ __forceinline__ void score_pair(const bf16* k_tile, const bf16x8* qf, int frow, int fcol,
+                                           f32x16& s0, f32x16& s1) {
+  constexpr int KC = D / 16;
+  bf16x8 kf0[KC], kf1[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) kf0[kc] = swz_frag<bf16, D>(k_tile, frow, 16 * kc + fcol);
+  __builtin_amdgcn_sched_barrier(0);
+  s0 = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    mma(s0, kf0[kc], qf[kc]);
+    kf1[kc] = swz_frag<bf16, D>(k_tile, 32 + frow, 16 * kc + fcol);
+  }
+  // issue order: product, read, product, read, ...
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  s1 = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) mma(s1, kf1[kc], qf[kc]);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Every launch takes the causal form: key j is allowed for query row i iff j <= i + coff, with
+// coff = 0 (top-left), Nk - Nq (bottom-right) or Nk (not causal: every key allowed).
+template <typename T, int D, int BN, bool COUNT, bool WRITE_O, bool MASKED>
+// bf16: two waves per SIMD (at most 256 VGPRs), the second wave fills the first one's waits.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void attn_fwd_kernel(FwdArgs a) {
   using frag_t = typename Ty<T>::frag;
   // bf16: V stays a swizzled row tile and the P.V operand is read transposed (ds_read_b64_tr_b16);
   // fp32 has no transposed read: V is staged transposed, [d][key slot], row pitch PV.
@@ -112,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const int logical = xcd_remap(blockIdx.x, a.total_wg);
   const int bg = logical / a.wg_per_group;
   int wig = logical % a.wg_per_group;
-  if (CAUSAL) wig = a.wg_per_group - 1 - wig;   // long (late) query blocks first
+  wig = a.wg_per_group - 1 - wig;   // long (late) query blocks first
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int task = wig * kWaves + wave;
   const bool active = task < a.tasks_per_group;
@@ -120,10 +153,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const int q0 = (active ? task / a.rep : 0) * kRowsPerWave;
   const int last_task = min(wig * kWaves + kWaves - 1, a.tasks_per_group - 1);
   const int wg_qmax = min((last_task / a.rep) * kRowsPerWave + kRowsPerWave - 1, a.Nq - 1);
-  const int key_end = CAUSAL ? max(0, min(a.Nk, wg_qmax + a.coff + 1)) : a.Nk;
+  const int key_end = max(0, min(a.Nk, wg_qmax + a.coff + 1));
   const int nt = (key_end + BN - 1) / BN;
   const int wave_qmax = min(q0 + kRowsPerWave - 1, a.Nq - 1);
-  const int key_end_w = !active ? 0 : (CAUSAL ? max(0, min(a.Nk, wave_qmax + a.coff + 1)) : a.Nk);
+  const int key_end_w = !active ? 0 : max(0, min(a.Nk, wave_qmax + a.coff + 1));
   const int nt_w = (key_end_w + BN - 1) / BN;
 
   const T* qh = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h) * a.Nq * D;
@@ -143,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const int frow = lane & 31;           // A-fragment row inside a 32-row block
   const int fcol = 8 * (lane >> 5);     // A-fragment column offset
 
-  auto needs_mask = [&](int key0) { return MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk; };
+  auto needs_mask = [&](int key0) { return MASKED || key0 + 31 > q0 + a.coff || key0 + 32 > a.Nk; };
   const MaskSlice<T> ms(a.mask, b, h);
 
   // ---- pass 1: row max of the raw dot products (K tiles double-buffered through LDS)
@@ -162,32 +195,90 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
     else kreg.store(dst, tid);
   };
   float mx = -INFINITY;
-  if (nt > 0) {
+  // bf16 with V buffers: pass 1 streams K through four LDS stages (the V buffers are idle until
+  // pass 2), three tiles ahead of the math.  Only without a mask: the mask loads are vector
+  // loads too, and the counted waits below assume the copies are the only ones in flight.
+  constexpr bool DEEP = sizeof(T) == 2 && WRITE_O && !MASKED;
+  constexpr int kCopies = DEEP ? BN * D * 2 / 1024 / kWaves : 1;   // DMA loads per wave per tile
+  // Stage s of the K ring sits at a fixed LDS address, so with the stage a compile-time constant
+  // every fragment read is a loop-invariant lane address plus an immediate offset.
+  constexpr int kStages = DEEP ? 4 : 2;
+  auto k_stage = [&](auto S) -> T* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st < 2) return k_lds[st];
+    else return v_lds[st - 2];
+  };
+  if constexpr (DEEP) {
+    k_issue(0, k_stage(std::integral_constant<int, 0>{}));
+    if (nt > 1) k_issue(1, k_stage(std::integral_constant<int, 1>{}));
+    if (nt > 2) k_issue(2, k_stage(std::integral_constant<int, 2>{}));
+    // tile 0 landed; the copies of tiles 1 and 2 may stay in flight
+    if (nt >= 3) wait_vmem_n<2 * kCopies>();
+    else if (nt == 2) wait_vmem_n<kCopies>();
+    else wait_vmem();
+  } else if (nt > 0) {
     k_issue(0, k_lds[0]);
     k_land(k_lds[0]);
   }
   __syncthreads();
-  for (int kt = 0; kt < nt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nt) k_issue(kt + 1, k_lds[buf ^ 1]);
+  // one step of pass 1 on tile kt, held in stage S
+  auto p1_step = [&](int kt, auto S) {
+    constexpr int st = decltype(S)::value;
+    // the stage receiving tile kt + kStages - 1 was last read in step kt - 1, which every wave
+    // has left (barrier at the end of each step)
+    constexpr int st_in = (st + kStages - 1) % kStages;
+    if (kt + kStages - 1 < nt) k_issue(kt + kStages - 1, k_stage(std::integral_constant<int, st_in>{}));
+    const T* kt_lds = k_stage(S);
     float tl = -INFINITY;
     if (kt < nt_w) {
+      if constexpr (sizeof(T) == 2 && SB == 2) {
+        f32x16 sc[2];
+        score_pair<D>(kt_lds, qf, frow, fcol, sc[0], sc[1]);
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-        f32x16 s = score_block<T, D>(k_lds[buf], qf, sb, frow, fcol);
-        const int key0 = kt * BN + sb * 32;
-        if (needs_mask(key0)) mask_block<CAUSAL, MASKED>(s, key0, qrow, lane, a.Nk, a.coff, ms);
+        for (int sb = 0; sb < 2; ++sb) {
+          const int key0 = kt * BN + sb * 32;
+          if (needs_mask(key0)) mask_block<MASKED>(sc[sb], key0, qrow, lane, a.Nk, a.coff, ms);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tl = fmaxf(tl, s[i]);
+          for (int i = 0; i < 16; ++i) tl = fmaxf(tl, sc[sb][i]);
+        }
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+          f32x16 sc = score_block<T, D>(kt_lds, qf, sb, frow, fcol);
+          const int key0 = kt * BN + sb * 32;
+          if (needs_mask(key0)) mask_block<MASKED>(sc, key0, qrow, lane, a.Nk, a.coff, ms);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tl = fmaxf(tl, sc[i]);
+        }
       }
     }
     mx = fmaxf(mx, tl);
     if (kt < kMaxTiles) {
-      const float wm = wave_max(tl);
-      if (lane == 0) tmax_lds[wave][kt] = wm;
+      const float wm = wave_max_lane63(tl);
+      if (lane == 63) tmax_lds[wave][kt] = wm;
     }
-    if (kt + 1 < nt) k_land(k_lds[buf ^ 1]);
+    if constexpr (DEEP) {
+      // tile kt + 1 landed; the copies issued after it (tiles kt + 2, kt + 3) may stay in flight
+      if (kt + 3 < nt) wait_vmem_n<2 * kCopies>();
+      else if (kt + 2 < nt) wait_vmem_n<kCopies>();
+      else if (kt + 1 < nt) wait_vmem();
+    } else {
+      if (kt + 1 < nt) k_land(k_stage(std::integral_constant<int, (st + 1) % kStages>{}));
+    }
     __syncthreads();
+  };
+  for (int kt = 0; kt < nt;) {
+    p1_step(kt, std::integral_constant<int, 0>{});
+    if (++kt >= nt) break;
+    p1_step(kt, std::integral_constant<int, 1>{});
+    ++kt;
+    if constexpr (kStages == 4) {
+      if (kt >= nt) break;
+      p1_step(kt, std::integral_constant<int, 2 % kStages>{});
+      if (++kt >= nt) break;
+      p1_step(kt, std::integral_constant<int, 3 % kStages>{});
+      ++kt;
+    }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));   // lanes l and l+32 hold the same query row
   // 1 + u = fma(s, -c, kd) with kd = 1 + m c; the smallest kd of the wave bounds every row.  A
@@ -239,8 +330,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
     if constexpr (WRITE_O) v_land(v_lds[0]);
   }
   __syncthreads();
-  int buf = 0;
-  while (cur < nt) {
+  // one step of pass 2 on tile cur, held in buffer BUF (a compile-time constant, so every LDS
+  // read is a loop-invariant lane address plus an immediate offset)
+  auto p2_step = [&](auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
     int nxt = cur + 1;
     while (nxt < nt && wg_skips(nxt)) ++nxt;
     nxt = uniform(nxt);
@@ -268,13 +361,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
         const bf16* vt_ = v_lds[buf];
         bf16x8 kf0[KC], kf1[KC], va[NV], vb[NV];
         f32x16 s0 = {}, s1 = {};
-        // stage A: S0 = K0 Q^T, K1 fragments read behind it
+        // stage A: S0 = K0 Q^T, K1 fragments read behind it (all K0 reads issued first)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) kf0[kc] = swz_frag<bf16, D>(kt_, frow, 16 * kc + fcol);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           mma(s0, kf0[kc], qf[kc]);
           kf1[kc] = swz_frag<bf16, D>(kt_, 32 + frow, 16 * kc + fcol);
+        }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         // stage B: S1 products under phi(S0); V fragments of block 0 read
@@ -329,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         const int key0 = cur * BN + sb * 32;
-        if (needs_mask(key0)) mask_block<CAUSAL, MASKED>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
+        if (needs_mask(key0)) mask_block<MASKED>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[sb][i] = ra_phi(s[sb][i], a.c, kd);
 #pragma unroll
@@ -365,8 +464,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
       if constexpr (WRITE_O) v_land(v_lds[buf ^ 1]);
     }
     __syncthreads();
-    buf ^= 1;
     cur = nxt;
+  };
+  while (cur < nt) {
+    p2_step(std::integral_constant<int, 0>{});
+    if (cur >= nt) break;
+    p2_step(std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = acc / l
@@ -419,18 +522,15 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   a.coff = p.coff;
   a.mask = mask_args(p);
   dim3 grid(a.total_wg), block(kThreads);
-  if (p.mask_kind != kMaskNone) {   // the masked kernels are the causal ones (coff = Nk: no causality)
-    if (o == nullptr) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, true, true>), grid, block, 0, stream, a);
+  if (p.mask_kind != kMaskNone) {
+    if (o == nullptr) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true>), grid, block, 0, stream, a);
   } else if (o == nullptr) {   // statistics only (m, l), for a backward without saved stats
-    if (p.causal) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, false, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, false, false>), grid, block, 0, stream, a);
-  } else if (p.causal) {
-    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, true, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, false, true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, false>), grid, block, 0, stream, a);
+  } else if (counters) {
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, true, true, false>), grid, block, 0, stream, a);
   } else {
-    if (counters) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
