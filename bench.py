@@ -49,11 +49,11 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "attn_fwd_kernel": ("9bc204fcce00ec4c0ea7b06a945a0b3c8d4aa5d21a751e84f19600250d8d9c55",
-                        263081.4, 135185.8),
-    "attn_bwd_dq_bf16_kernel": ("0b7a589acb1aef8c9ebfb43ff181b8e5515f34e5caea6fa093d7a96519563485",
-                                436104.5, 143458.2),
-    "attn_bwd_dkdv_bf16_kernel": ("0b7a589acb1aef8c9ebfb43ff181b8e5515f34e5caea6fa093d7a96519563485",
-                                  267522.4, 262146.3),
+                        263126.5, 135188.0),
+    "attn_bwd_dq_bf16_kernel": ("dc3a211ec90d98d32aa9694e2a00fde212e0f6d6eb27e097d871649e906dc7bb",
+                                437095.2, 143467.9),
+    "attn_bwd_dkdv_bf16_kernel": ("dc3a211ec90d98d32aa9694e2a00fde212e0f6d6eb27e097d871649e906dc7bb",
+                                  267518.1, 262144.7),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],

@@ -723,15 +723,42 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   };
 
   // S^T and dP^T of this wave's block: lane = key, registers = the half-tile's 32 query rows
+  // S and dP run as two independent chains with their four operand reads pinned two products
+  // ahead (left alone, the compiler read each operand just before its product, so every product
+  // waited out an LDS latency)
   auto products_sdp = [&](const bf16* qt_, const bf16* dot_, f32x16& s, f32x16& dp) {
     s = f32x16{};
     dp = f32x16{};
+    if constexpr (MASKED) {   // no registers to spare for the read-ahead
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      mma(s, swz_frag<bf16, D>(qt_, frow, 16 * kc + fcol), swz_frag<bf16, D>(k_lds, kr, 16 * kc + fcol));
+      for (int kc = 0; kc < KC; ++kc)
+        mma(s, swz_frag<bf16, D>(qt_, frow, 16 * kc + fcol), swz_frag<bf16, D>(k_lds, kr, 16 * kc + fcol));
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      mma(dp, swz_frag<bf16, D>(dot_, frow, 16 * kc + fcol), swz_frag<bf16, D>(v_lds, kr, 16 * kc + fcol));
+      for (int kc = 0; kc < KC; ++kc)
+        mma(dp, swz_frag<bf16, D>(dot_, frow, 16 * kc + fcol), swz_frag<bf16, D>(v_lds, kr, 16 * kc + fcol));
+      return;
+    }
+    bf16x8 qa[KC], ka[KC], da[KC], va[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      qa[kc] = swz_frag<bf16, D>(qt_, frow, 16 * kc + fcol);
+      ka[kc] = swz_frag<bf16, D>(k_lds, kr, 16 * kc + fcol);
+      da[kc] = swz_frag<bf16, D>(dot_, frow, 16 * kc + fcol);
+      va[kc] = swz_frag<bf16, D>(v_lds, kr, 16 * kc + fcol);
+    }
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      mma(s, qa[kc], ka[kc]);
+      mma(dp, da[kc], va[kc]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int kc = 0; kc < KC - 2; ++kc) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
   // s -> P, dp -> G (+ R at the argmax) for the half-tile rows starting at query row i0
   auto derivative = [&](f32x16& s, f32x16& dp, const unsigned (&mv)[16], int i0, int slot) {
@@ -765,12 +792,27 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
       }
     }
     const int am = __float_as_int(st[4 * QT + (lane & 31)]);
-    if (__any(am >= j0 && am < j0 + 32)) {
+    if constexpr (MASKED) {   // no registers to spare for the batched reads below
+      if (__any(am >= j0 && am < j0 + 32)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = acc_row(i, lane);
-        if (__float_as_int(st[4 * QT + r]) == key) dp[i] += st[3 * QT + r];
+        for (int i = 0; i < 16; ++i) {
+          const int r = acc_row(i, lane);
+          if (__float_as_int(st[4 * QT + r]) == key) dp[i] += st[3 * QT + r];
+        }
       }
+    } else if (__any(am >= j0 && am < j0 + 32)) {
+      // this lane's 16 rows are four runs of four consecutive rows: eight 16-byte reads issued
+      // together (one read and wait per element serialised sixteen LDS latencies)
+      f32x4 am4[4], r4[4];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r0 = 8 * i4 + 4 * (lane >> 5);
+        am4[i4] = *reinterpret_cast<const f32x4*>(st + 4 * QT + r0);
+        r4[i4] = *reinterpret_cast<const f32x4*>(st + 3 * QT + r0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (__float_as_int(am4[i >> 2][i & 3]) == key) dp[i] += r4[i >> 2][i & 3];
     }
   };
   f32x16 acc_dk[DB], acc_dv[DB];
@@ -781,16 +823,45 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   }
   // dV^T += dO^T P^T, dK^T += Q^T G^T over the half-tile's 32 rows
   auto products_dkdv = [&](const f32x16& s, const f32x16& dp, const bf16* qt_, const bf16* dot_) {
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pf = pack_frag_bf16(s, ks);
+        const bf16x8 gf = pack_frag_bf16(dp, ks);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          mma(acc_dv[db], tr_frag<D>(dot_, 16 * ks, db * 32, lane), pf);
+          mma(acc_dk[db], tr_frag<D>(qt_, 16 * ks, db * 32, lane), gf);
+        }
+      }
+      return;
+    }
+    // transposed operand reads (two ds_read_b64_tr_b16 each) pinned two products ahead
+    constexpr int NP = 2 * DB;
+    bf16x8 pf[2], gf[2], ta[NP], tb[NP];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pf = pack_frag_bf16(s, ks);
-      const bf16x8 gf = pack_frag_bf16(dp, ks);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        mma(acc_dv[db], tr_frag<D>(dot_, 16 * ks, db * 32, lane), pf);
-        mma(acc_dk[db], tr_frag<D>(qt_, 16 * ks, db * 32, lane), gf);
-      }
+      pf[ks] = pack_frag_bf16(s, ks);
+      gf[ks] = pack_frag_bf16(dp, ks);
     }
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      ta[c] = tr_frag<D>(dot_, 16 * (c / DB), (c % DB) * 32, lane);
+      tb[c] = tr_frag<D>(qt_, 16 * (c / DB), (c % DB) * 32, lane);
+    }
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      mma(acc_dv[c % DB], ta[c], pf[c / DB]);
+      mma(acc_dk[c % DB], tb[c], gf[c / DB]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int c = 0; c < NP - 2; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   const size_t kv0 = ((size_t)(b * a.Hkv + g) * a.Nk + key0_wg) * D;
