@@ -459,6 +459,17 @@ __device__ __forceinline__ float ra_grad(float s, float c16, float kd, float dp,
   return fmaf(dp, il, -cil) * ((q6 * q) * (r * r));
 }
 
+// The gradient alone (the dQ kernel needs no p): q^7 r^2 as (q^3 r)^2 q, six multiplications
+// instead of seven.
+__device__ __forceinline__ float ra_grad_only(float s, float c16, float kd, float dp, float il, float cil) {
+  const float d = fmaf(s, -c16, kd);
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = fminf(fmaxf(fmaf(r, 2.0f, -1.0f), 0.0f), 1.0f);
+  const float q3 = (q * q) * q;
+  const float w = q3 * r;
+  return fmaf(dp, il, -cil) * ((w * w) * q);
+}
+
 template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int BN = 64, KC = D / 16, SB = BN / 32, DB = D / 32;
@@ -562,10 +573,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
             if (s[i] == mprobe) amax = min(amax, key0 + acc_row(i, lane));
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p;
-          s[i] = ra_grad(s[i], a.c16, kd, dp[i], il, cil, &p);
-        }
+        for (int i = 0; i < 16; ++i) s[i] = ra_grad_only(s[i], a.c16, kd, dp[i], il, cil);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const bf16x8 gf = pack_frag_bf16(s, ks);
