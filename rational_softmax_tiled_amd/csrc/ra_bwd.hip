@@ -726,7 +726,7 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   auto mask_load = [&](const Cursor& c, unsigned (&mv)[16]) {
     if constexpr (MASKED) {
       const MaskSlice<bf16> ms(a.mask, b, g * a.rep + c.hh);
-      ms.load(mv, key * ms.sk + (c.qt * QT + HR * half + 4 * (lane >> 5)) * ms.sq, ms.sq);
+      ms.load_rows(mv, key * ms.sk + (c.qt * QT + HR * half + 4 * (lane >> 5)) * ms.sq, ms.sq);
     }
   };
 

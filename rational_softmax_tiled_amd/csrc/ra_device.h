@@ -625,7 +625,9 @@ struct MaskSlice {
     inv_scale = m.inv_scale;
   }
 
-  // raw values of the 16 elements of a lane (bool: the byte; additive: the bits as fp32)
+  // raw values of the 16 elements of a lane (bool: the byte; additive: the bits as fp32).
+  // Element i sits at voff + (8 (i >> 2) + (i & 3)) * step bytes: four runs of four, one load
+  // per element.
   __device__ __forceinline__ void load(unsigned (&v)[16], int voff, int step) const {
     if (kind == kMaskBool) {
 #pragma unroll
@@ -640,6 +642,21 @@ struct MaskSlice {
       for (int i = 0; i < 16; ++i)
         v[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, uniform((8 * (i >> 2) + (i & 3)) * step), 0);
     }
+  }
+
+  // load() along query rows, where a zero stride (a mask broadcast over rows, as key padding is)
+  // takes one load for all sixteen elements
+  __device__ __forceinline__ void load_rows(unsigned (&v)[16], int voff, int step) const {
+    if (step == 0) {
+      unsigned x;
+      if (kind == kMaskBool) x = __builtin_amdgcn_raw_buffer_load_b8(r, voff, 0, 0);
+      else if constexpr (sizeof(T) == 2) x = (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0) << 16;
+      else x = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = x;
+      return;
+    }
+    load(v, voff, step);
   }
 
   __device__ __forceinline__ float apply(float s, unsigned v) const { return mask_value(kind, inv_scale, s, v); }
