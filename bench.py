@@ -48,12 +48,12 @@ MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("9bc204fcce00ec4c0ea7b06a945a0b3c8d4aa5d21a751e84f19600250d8d9c55",
-                        263126.5, 135188.0),
-    "attn_bwd_dq_bf16_kernel": ("dc3a211ec90d98d32aa9694e2a00fde212e0f6d6eb27e097d871649e906dc7bb",
-                                437095.2, 143467.9),
-    "attn_bwd_dkdv_bf16_kernel": ("dc3a211ec90d98d32aa9694e2a00fde212e0f6d6eb27e097d871649e906dc7bb",
-                                  267518.1, 262144.7),
+    "attn_fwd_kernel": ("7ec132e6cbc4fde158bb0918667f3d4f76fbe83238282e31a0d59b3acdaf2406",
+                        263372.8, 135184.4),
+    "attn_bwd_dq_bf16_kernel": ("203558b8a601047e73706c682a815eef3855493e6d4829c56f7a226db2df863f",
+                                437374.7, 143455.9),
+    "attn_bwd_dkdv_bf16_kernel": ("203558b8a601047e73706c682a815eef3855493e6d4829c56f7a226db2df863f",
+                                  267527.0, 262145.8),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],
