@@ -30,15 +30,16 @@ struct DecodeArgs {
   bf16* o;
   float* stats;
   const int* seqlens;   // [B] cache lengths (nullptr: all Nk)
-  float* scores;        // [groups][S][chunk / 32][R][2][16] raw dot products
+  float* scores;        // [groups][nk32 / 32][R][2][16] raw dot products, by 32-key block
   float* pmax;          // [groups][S][R] row max of a chunk
   float* psum;          // [groups][S][R] sum of phi of a chunk
   float* pacc;          // [groups][S][R][D] unnormalised P.V of a chunk
   float* gmax;          // [groups][R] row max over all chunks (written by chunk 0's wave)
-  int Hq, Hkv, Nq, Nk, rep, R;
-  int chunk;            // keys per wave, a multiple of 32
-  int S;                // chunks per group: ceil(Nk / chunk)
-  int wg_per_group;     // ceil(S / kWaves)
+  int B, Hq, Hkv, Nq, Nk, rep, R;
+  int nk32;             // Nk rounded up to 32: the keys of a group in the scores
+  int chunk_min, chunk_max;   // bounds of the keys per wave, multiples of 32
+  int S;                // partial-result slots per group: ceil(Nk / chunk_min)
+  int waves;            // waves launched
   int causal;           // 0 none, 1 top-left, 2 bottom-right (per sample)
   float c;              // scale / 16
 };
@@ -54,6 +55,97 @@ __device__ __forceinline__ int key_limit(const DecodeArgs& a, int len, int r) {
   if (a.causal == 1) lim = min(lim, i);
   else if (a.causal == 2) lim = min(lim, i + len - a.Nq);
   return lim;
+}
+
+// The work split of the step over the actual cache lengths, the same in every wave and in the
+// combine: every wave takes `chunk` consecutive keys of one (batch, K/V head) group.  Groups are
+// numbered bg = b Hkv + g; the chunks of all groups are numbered in that order, and wave v takes
+// chunk v.  The launch has W = groups ceil(Nk / chunk_max) waves, the count that full caches
+// need.  With shorter caches the chunk shrinks to total / (W - groups) keys (rounded up to 32,
+// at least chunk_min), so the chunks still number at most total / chunk + groups <= W and
+// every wave has about the same number of keys: no SIMD idles while others stream twice the
+// keys.
+constexpr int kDecodeTarget = 1024;
+// chunk size from the total number of keys
+__device__ __forceinline__ int decode_chunk_of(const DecodeArgs& a, long long total) {
+  const long long spare = (long long)a.waves - (long long)a.B * a.Hkv;
+  if (spare <= 0) return a.chunk_max;   // one chunk per group already
+  long long c = (total + spare - 1) / spare;
+  c = (c + 31) / 32 * 32;
+  c = c < a.chunk_min ? a.chunk_min : (c > a.chunk_max ? a.chunk_max : c);
+  return uniform((int)c);
+}
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int decode_chunk(const DecodeArgs& a) {
+  const int lane = threadIdx.x & 63;
+  long long total = 0;
+  for (int b0 = 0; b0 < a.B; b0 += kWave) {
+    const int b = b0 + lane;
+    total += wave_sum_int(b < a.B ? cache_len(a, b) : 0);
+  }
+  return decode_chunk_of(a, total * a.Hkv);
+}
+// A pointer the same in every lane, rebuilt from its first lane so that the compiler keeps buffer
+// resources made from it in scalar registers (no per-load waterfall loop).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const unsigned long long x = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+  return reinterpret_cast<T*>(((unsigned long long)hi << 32) | lo);
+}
+struct DecodeWork {
+  int chunk;
+  int bg, s;      // group and chunk; bg < 0: no work for this wave
+  int len;        // the group's cache length
+};
+// The chunk of wave v among one window of batches (lane l holds len_l, the cache length of
+// batch b0 + l), whose chunks start at `base`; false when it lies past the window.
+__device__ __forceinline__ bool decode_find(const DecodeArgs& a, int chunk, int v, int b0, int len_l,
+                                            int& base, DecodeWork& w) {
+  const int lane = threadIdx.x & 63;
+  const int per = (len_l + chunk - 1) / chunk;   // chunks per group of batch b0 + lane
+  int incl = per * a.Hkv;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  const int tot = __shfl(incl, kWave - 1);
+  if (v >= base + tot) {
+    base += tot;
+    return false;
+  }
+  // the first batch whose chunks end past v
+  const int hit = __builtin_ctzll(__ballot(base + incl > v));
+  const int per_h = __shfl(per, hit);
+  const int local = v - (base + __shfl(incl, hit) - per_h * a.Hkv);
+  w.chunk = chunk;
+  w.bg = uniform((b0 + hit) * a.Hkv + local / per_h);
+  w.s = uniform(local % per_h);
+  w.len = uniform(__shfl(len_l, hit));
+  return true;
+}
+__device__ __forceinline__ DecodeWork decode_work(const DecodeArgs& a, int v) {
+  const int lane = threadIdx.x & 63;
+  DecodeWork w{0, -1, 0, 0};
+  int base = 0;
+  if (a.B <= kWave) {   // one load of the lengths serves both the size and the search
+    const int len_l = lane < a.B ? cache_len(a, lane) : 0;
+    w.chunk = decode_chunk_of(a, (long long)wave_sum_int(len_l) * a.Hkv);
+    decode_find(a, w.chunk, v, 0, len_l, base, w);
+    return w;
+  }
+  w.chunk = decode_chunk(a);
+  for (int b0 = 0; b0 < a.B; b0 += kWave) {
+    const int b = b0 + lane;
+    if (decode_find(a, w.chunk, v, b0, b < a.B ? cache_len(a, b) : 0, base, w)) break;
+  }
+  return w;
 }
 
 // Blocks of 32 keys stream through a ring of three register sets, two blocks ahead of the math:
@@ -80,13 +172,12 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a) {
   constexpr int CPR = D / 8, PER = 32 * CPR / kWave;
   __shared__ __attribute__((aligned(16))) bf16 k_lds[kWaves][32 * D];
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int bg = blockIdx.x / a.wg_per_group;
-  const int s = (blockIdx.x % a.wg_per_group) * kWaves + wave;
+  const DecodeWork work = decode_work(a, blockIdx.x * kWaves + wave);
+  if (work.bg < 0) return;   // whole wave: no barrier in this kernel
+  const int chunk = uniform(work.chunk), bg = uniform(work.bg), s = uniform(work.s), len = uniform(work.len);
   const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int len = cache_len(a, b);
-  const int k0 = s * a.chunk;
-  if (s >= a.S || k0 >= len) return;   // whole wave: no barrier in this kernel
-  const int nkeys = min(a.chunk, len - k0), nb = (nkeys + 31) / 32;
+  const int k0 = s * chunk;
+  const int nkeys = min(chunk, len - k0), nb = (nkeys + 31) / 32;
 
   // B operand: query row r = lane % 32 of the group (rows past R repeat the last one)
   const int r = lane & 31, rr = min(r, a.R - 1);
@@ -102,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a) {
   // a block; rows past the chunk's keys read as zeros), stored swizzled into this wave's LDS
   // tile, from which the A fragments are read (the previous block's reads have returned: their
   // results fed the products, and a wave's LDS operations execute in order)
-  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(a.k + ((size_t)bg * a.Nk + k0) * D, nkeys, D);
+  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(uniform_ptr(a.k + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
   u32x4 ring[3][PER];
   auto load = [&](int slot, int t) {
 #pragma unroll
@@ -112,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a) {
   bf16* ktile = k_lds[wave];
   // this chunk's scores, [block][R rows][2 lane halves][16]; padded rows store past the end
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      a.scores + ((size_t)bg * a.S + s) * a.chunk * a.R, (short)0, uniform(nb * 32 * a.R * 4), kBufferWord3);
+      uniform_ptr(a.scores + ((size_t)bg * a.nk32 + k0) * a.R), (short)0, uniform(nb * 32 * a.R * 4), kBufferWord3);
   const int s_off = r < a.R ? (r * 2 + (lane >> 5)) * 64 : 0x40000000;
   float mx = -INFINITY;
   load(0, 0);
@@ -152,19 +243,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ __attribute__((aligned(16))) bf16 v_lds[kWaves][TILE];
 
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int bg = blockIdx.x / a.wg_per_group;
-  const int s = (blockIdx.x % a.wg_per_group) * kWaves + wave;
-  const int b = bg / a.Hkv;
-  const int len = cache_len(a, b);
-  const int k0 = s * a.chunk;
-  if (s >= a.S || k0 >= len) return;
-  const int nkeys = min(a.chunk, len - k0), nb = (nkeys + 31) / 32;
+  const DecodeWork work = decode_work(a, blockIdx.x * kWaves + wave);
+  if (work.bg < 0) return;
+  const int chunk = uniform(work.chunk), bg = uniform(work.bg), s = uniform(work.s), len = uniform(work.len);
+  const int k0 = s * chunk;
+  const int nkeys = min(chunk, len - k0), nb = (nkeys + 31) / 32;
   const int r = lane & 31;
   const bool live = r < a.R;
 
   // V rows: coalesced 16-byte loads into a register ring (lane l takes chunks l, l + 64, ... of
   // a block), then stored swizzled into this wave's LDS tile and read transposed
-  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(a.v + ((size_t)bg * a.Nk + k0) * D, nkeys, D);
+  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(uniform_ptr(a.v + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
   u32x4 ring[3][PER];
   auto load = [&](int slot, int t) {
 #pragma unroll
@@ -177,7 +266,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // the row max over every chunk of the group that holds keys: lanes r and r + 32 take the even
   // and odd chunks, eight loads in flight per round
-  const int nlive = (len + a.chunk - 1) / a.chunk;
+  const int nlive = (len + chunk - 1) / chunk;
   float m = -INFINITY;
   if (live) {
     const float* pm = a.pmax + (size_t)bg * a.S * a.R + r;
@@ -197,7 +286,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // this chunk's scores as the first kernel stored them; padded rows (kd = +inf, so phi = 0
   // whatever they read) and blocks past the chunk read zeros
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      a.scores + ((size_t)bg * a.S + s) * a.chunk * a.R, (short)0, uniform(nb * 32 * a.R * 4), kBufferWord3);
+      uniform_ptr(a.scores + ((size_t)bg * a.nk32 + k0) * a.R), (short)0, uniform(nb * 32 * a.R * 4), kBufferWord3);
   const int s_off = live ? (r * 2 + (lane >> 5)) * 64 : 0x40000000;
   auto load_scores = [&](int t) {
     f32x16 v;
@@ -263,7 +352,8 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) 
   const int bg = blockIdx.x;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int len = cache_len(a, b);
-  const int nlive = (len + a.chunk - 1) / a.chunk;
+  const int chunk = decode_chunk(a);
+  const int nlive = (len + chunk - 1) / chunk;
   for (int e = threadIdx.x; e < a.R * D; e += kThreads) {
     const int r = e / D, d = e % D;
     float acc = 0.0f, l = 0.0f;
@@ -284,26 +374,34 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) 
   }
 }
 
-// Measured on the B=16, Hq=32, Hkv=8 decode step (caches of 16384 and of mixed lengths): about
-// 1024 waves in all beat 2048-8192 by 3-10%, the per-wave start-up (Q fragments, the first two
-// blocks' latency) outweighing the finer load balance.
-constexpr int64_t kDecodeWaves = 1024;
+// The keys per wave come from the cache lengths at run time (decode_chunk): the total over about
+// kDecodeTarget waves.  Measured on the B=16, Hq=32, Hkv=8 decode step (caches of 16384 and of
+// mixed lengths), about 1024 waves in all beat 2048-8192 by 3-10%, the per-wave start-up (Q
+// fragments, the first two blocks' latency) outweighing the finer load balance.  The plan bounds
+// the size: at most the chunk that spreads full caches over that many waves, at least a quarter
+// of it (and kDecodeMinChunk keys), which bounds the partial-result slots per group.
 constexpr int64_t kDecodeMinChunk = 64;
+constexpr int64_t kDecodeShrink = 4;
 
 DecodePlan decode_plan(int64_t B, int64_t Hkv, int64_t Nk, int64_t R, int64_t D) {
-  // about kDecodeWaves waves over the chip, at least kDecodeMinChunk keys per wave
   const int64_t groups = B * Hkv;
-  int64_t chunk = (groups * Nk + kDecodeWaves - 1) / kDecodeWaves;
-  chunk = ((chunk + 31) / 32) * 32;
-  chunk = chunk < kDecodeMinChunk ? kDecodeMinChunk : chunk;
-  const int64_t nk32 = ((Nk + 31) / 32) * 32;
-  if (chunk > nk32) chunk = nk32 > 0 ? nk32 : 32;
+  auto up32 = [](int64_t x) { return (x + 31) / 32 * 32; };
+  const int64_t nk32 = up32(Nk);
+  int64_t cmax = up32((groups * Nk + kDecodeTarget - 1) / kDecodeTarget);
+  cmax = cmax < kDecodeMinChunk ? kDecodeMinChunk : cmax;
+  if (cmax > nk32) cmax = nk32 > 0 ? nk32 : 32;
+  int64_t cmin = up32((cmax + kDecodeShrink - 1) / kDecodeShrink);
+  cmin = cmin < kDecodeMinChunk ? kDecodeMinChunk : cmin;
+  if (cmin > cmax) cmin = cmax;
   DecodePlan p;
-  p.chunk = chunk;
-  p.S = (Nk + chunk - 1) / chunk;
+  p.chunk_min = cmin;
+  p.chunk_max = cmax;
+  p.S = (Nk + cmin - 1) / cmin;
+  // the waves full caches need; shorter ones take at most as many chunks (decode_chunk)
+  p.waves = groups * ((Nk + cmax - 1) / cmax);
   const int64_t rows = groups * p.S * R;
   auto round256 = [](size_t n) { return (n + 255) / 256 * 256; };   // every region 16-byte aligned
-  p.scores_bytes = round256((size_t)(rows * chunk) * sizeof(float));
+  p.scores_bytes = round256((size_t)(groups * nk32 * R) * sizeof(float));
   p.pmax_bytes = round256((size_t)rows * sizeof(float));
   p.psum_bytes = round256((size_t)rows * sizeof(float));
   p.pacc_bytes = round256((size_t)(rows * D) * sizeof(float));
@@ -328,19 +426,22 @@ static hipError_t launch_decode_typed(const DecodeProblem& p, const DecodePlan& 
   a.psum = reinterpret_cast<float*>(w + plan.scores_bytes + plan.pmax_bytes);
   a.pacc = reinterpret_cast<float*>(w + plan.scores_bytes + plan.pmax_bytes + plan.psum_bytes);
   a.gmax = reinterpret_cast<float*>(w + plan.scores_bytes + plan.pmax_bytes + plan.psum_bytes + plan.pacc_bytes);
+  a.B = p.B;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.Nq = p.Nq;
   a.Nk = p.Nk;
   a.rep = p.Hq / p.Hkv;
   a.R = a.rep * p.Nq;
-  a.chunk = (int)plan.chunk;
+  a.nk32 = (p.Nk + 31) / 32 * 32;
+  a.chunk_min = (int)plan.chunk_min;
+  a.chunk_max = (int)plan.chunk_max;
   a.S = (int)plan.S;
-  a.wg_per_group = (a.S + kWaves - 1) / kWaves;
+  a.waves = (int)plan.waves;
   a.causal = p.causal;
   a.c = p.scale / 16.0f;
   const int groups = p.B * p.Hkv;
-  const dim3 grid(groups * a.wg_per_group), block(kThreads);
+  const dim3 grid((a.waves + kWaves - 1) / kWaves), block(kThreads);
   hipLaunchKernelGGL((decode_scores_kernel<D>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

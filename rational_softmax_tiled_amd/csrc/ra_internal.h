@@ -63,10 +63,11 @@ struct DecodeProblem {
   int causal;
   float scale;
 };
-// Keys per wave, chunks per (batch, K/V head) group and the workspace carve-up (a function of
-// the sizes only, so the size query and the launch agree).
+// The bounds of the keys per wave (the launch picks the size inside them from the actual cache
+// lengths), the most chunks a (batch, K/V head) group can take, the waves launched and the
+// workspace carve-up: a function of the sizes only, so the size query and the launch agree.
 struct DecodePlan {
-  int64_t chunk, S;
+  int64_t chunk_min, chunk_max, S, waves;
   size_t scores_bytes, pmax_bytes, psum_bytes, pacc_bytes, gmax_bytes, bytes;
 };
 DecodePlan decode_plan(int64_t B, int64_t Hkv, int64_t Nk, int64_t R, int64_t D);
