@@ -63,6 +63,11 @@ CASES = [
     (2, 16, 16, 2, 700, 64, "bottom_right", "rand"),    # R = 2, no grouping
     (1, 8, 2, 1, 5000, 128, "none", "rand"),            # 79 chunks of 64 keys per group
     (1, 4, 1, 1, 40000, 64, "bottom_right", "full"),    # 625 chunks
+    # the keys per wave follow the actual lengths: more than 64 batches (the lengths are read in
+    # windows of 64), and lengths short enough that the chunk shrinks below its bound
+    (130, 4, 2, 1, 96, 64, "bottom_right", "rand"),
+    (8, 8, 2, 1, 16384, 128, "bottom_right", "rand"),   # chunk between 64 and 256 keys
+    (96, 2, 1, 1, 4096, 64, "none", "rand"),            # both: 96 batches, chunk 96..384
 ]
 
 
