@@ -78,6 +78,16 @@ __device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int la
   keep_rows(s, -kNoBound, min(Nk - lb, qrow + coff + 1 - lb));
 }
 
+// Keeps the entries of 32-key block sb of a 64-key tile whose key bit is set in keep (bit l: key
+// l of the tile) and sets the others to -inf.  Entry i of a lane is key 8 (i/4) + 4 (lane/32) +
+// i%4 of the block.
+__device__ __forceinline__ void keep_keys(f32x16& s, unsigned long long keep, int sb, int lane) {
+  const unsigned w = (unsigned)(keep >> (32 * sb)) >> (4 * (lane >> 5));
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (!((w >> (8 * (i >> 2) + (i & 3))) & 1u)) s[i] = -INFINITY;
+}
+
 // S^T block (32 keys x 32 query rows) of key sub-block sb of the staged (swizzled) K tile.
 template <typename T, int D>
 __device__ __forceinline__ f32x16 score_block(const T* k_tile, const typename Ty<T>::frag* qf, int sb,
@@ -120,7 +130,13 @@ __device__ __forceinline__ void score_pair(const bf16* k_tile, const bf16x8* qf,
 
 // Every launch takes the causal form: key j is allowed for query row i iff j <= i + coff, with
 // coff = 0 (top-left), Nk - Nq (bottom-right) or Nk (not causal: every key allowed).
-template <typename T, int D, int BN, bool COUNT, bool WRITE_O, bool MASKED>
+// KEYPAD: a boolean mask that depends on the key only (the same for every query row and head:
+// key padding).  Its bytes reach LDS with each pass-1 K tile, so the kernel keeps the four-stage
+// K ring and the interleaved pass-2 path of the unmasked kernel (MASKED is false): pass 1 turns a
+// tile's 64 mask bytes into 64 keep bits, drops a tile with none (its maximum stays -inf, so
+// pass 2 skips it too) and masks a partial one; pass 2 masks the partial tiles again from the
+// recorded bits and runs full tiles on the interleaved path.
+template <typename T, int D, int BN, bool COUNT, bool WRITE_O, bool MASKED, bool KEYPAD = false>
 // bf16: two waves per SIMD (at most 256 VGPRs), the second wave fills the first one's waits.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void attn_fwd_kernel(FwdArgs a) {
   using frag_t = typename Ty<T>::frag;
@@ -138,6 +154,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   __shared__ __attribute__((aligned(16))) T v_lds[WRITE_O ? 2 : 1][WRITE_O ? V_ELEMS : 8];
   __shared__ float tmax_lds[kWaves][kMaxTiles];
   __shared__ float kmin_lds[kWaves];
+  static_assert(!KEYPAD || (sizeof(T) == 2 && WRITE_O && !MASKED && BN == kWave), "key padding path");
+  __shared__ __attribute__((aligned(16))) unsigned mstage_lds[KEYPAD ? 4 : 1][KEYPAD ? kWave : 1];
+  __shared__ unsigned long long keep_lds[KEYPAD ? kMaxTiles : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -194,6 +213,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     if constexpr (sizeof(T) == 2) wait_vmem();
     else kreg.store(dst, tid);
   };
+  // KEYPAD: wave 0 copies tile kt's 64 mask bytes (lanes 0-15; the other lanes' dwords are not
+  // read) into the stage of its K tile
+  u32x4 m_rsrc = {};
+  if constexpr (KEYPAD) m_rsrc = dma_rsrc(static_cast<const char*>(a.mask.ptr) + (size_t)b * a.mask.sb, a.Nk);
+  auto m_issue = [&](int kt, int stage) {
+    if constexpr (KEYPAD)
+      if (wave == 0) lds_dma_at<4>(m_rsrc, lds_addr(mstage_lds[stage]), lane * 4, kt * BN);
+  };
   float mx = -INFINITY;
   // bf16 with V buffers: pass 1 streams K through four LDS stages (the V buffers are idle until
   // pass 2), three tiles ahead of the math.  Only without a mask: the mask loads are vector
@@ -203,6 +230,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   // Stage s of the K ring sits at a fixed LDS address, so with the stage a compile-time constant
   // every fragment read is a loop-invariant lane address plus an immediate offset.
   constexpr int kStages = DEEP ? 4 : 2;
+  // every copy of the n youngest tiles may still be in flight (wave 0 of KEYPAD copies one more
+  // per tile)
+  auto wait_younger = [&](auto n_c) {
+    constexpr int n = decltype(n_c)::value;
+    if (KEYPAD && wave == 0) wait_vmem_n<n * (kCopies + 1)>();
+    else wait_vmem_n<n * kCopies>();
+  };
   auto k_stage = [&](auto S) -> T* {
     constexpr int st = decltype(S)::value;
     if constexpr (st < 2) return k_lds[st];
@@ -210,11 +244,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   };
   if constexpr (DEEP) {
     k_issue(0, k_stage(std::integral_constant<int, 0>{}));
-    if (nt > 1) k_issue(1, k_stage(std::integral_constant<int, 1>{}));
-    if (nt > 2) k_issue(2, k_stage(std::integral_constant<int, 2>{}));
+    m_issue(0, 0);
+    if (nt > 1) {
+      k_issue(1, k_stage(std::integral_constant<int, 1>{}));
+      m_issue(1, 1);
+    }
+    if (nt > 2) {
+      k_issue(2, k_stage(std::integral_constant<int, 2>{}));
+      m_issue(2, 2);
+    }
     // tile 0 landed; the copies of tiles 1 and 2 may stay in flight
-    if (nt >= 3) wait_vmem_n<2 * kCopies>();
-    else if (nt == 2) wait_vmem_n<kCopies>();
+    if (nt >= 3) wait_younger(std::integral_constant<int, 2>{});
+    else if (nt == 2) wait_younger(std::integral_constant<int, 1>{});
     else wait_vmem();
   } else if (nt > 0) {
     k_issue(0, k_lds[0]);
@@ -227,10 +268,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     // the stage receiving tile kt + kStages - 1 was last read in step kt - 1, which every wave
     // has left (barrier at the end of each step)
     constexpr int st_in = (st + kStages - 1) % kStages;
-    if (kt + kStages - 1 < nt) k_issue(kt + kStages - 1, k_stage(std::integral_constant<int, st_in>{}));
+    if (kt + kStages - 1 < nt) {
+      k_issue(kt + kStages - 1, k_stage(std::integral_constant<int, st_in>{}));
+      m_issue(kt + kStages - 1, st_in);
+    }
     const T* kt_lds = k_stage(S);
     float tl = -INFINITY;
-    if (kt < nt_w) {
+    unsigned long long keep = ~0ull;   // KEYPAD: bit l set when key kt BN + l is kept
+    if constexpr (KEYPAD) {
+      keep = __ballot(reinterpret_cast<const unsigned char*>(mstage_lds[st])[lane] != 0);
+      if (wave == 0 && lane == 0) keep_lds[kt] = keep;
+    }
+    if (kt < nt_w && keep != 0) {
       if constexpr (sizeof(T) == 2 && SB == 2) {
         f32x16 sc[2];
         score_pair<D>(kt_lds, qf, frow, fcol, sc[0], sc[1]);
@@ -238,6 +287,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         for (int sb = 0; sb < 2; ++sb) {
           const int key0 = kt * BN + sb * 32;
           if (needs_mask(key0)) mask_block<MASKED>(sc[sb], key0, qrow, lane, a.Nk, a.coff, ms);
+          if constexpr (KEYPAD)
+            if (keep != ~0ull) keep_keys(sc[sb], keep, sb, lane);
 #pragma unroll
           for (int i = 0; i < 16; ++i) tl = fmaxf(tl, sc[sb][i]);
         }
@@ -259,8 +310,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     }
     if constexpr (DEEP) {
       // tile kt + 1 landed; the copies issued after it (tiles kt + 2, kt + 3) may stay in flight
-      if (kt + 3 < nt) wait_vmem_n<2 * kCopies>();
-      else if (kt + 2 < nt) wait_vmem_n<kCopies>();
+      if (kt + 3 < nt) wait_younger(std::integral_constant<int, 2>{});
+      else if (kt + 2 < nt) wait_younger(std::integral_constant<int, 1>{});
       else if (kt + 1 < nt) wait_vmem();
     } else {
       if (kt + 1 < nt) k_land(k_stage(std::integral_constant<int, (st + 1) % kStages>{}));
@@ -334,6 +385,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   // read is a loop-invariant lane address plus an immediate offset)
   auto p2_step = [&](auto BUF) {
     constexpr int buf = decltype(BUF)::value;
+    // KEYPAD: a tile with every key kept takes the interleaved path (a uniform flag, read first)
+    bool keys_full = true;
+    if constexpr (KEYPAD) keys_full = uniform(keep_lds[cur] == ~0ull ? 1 : 0) != 0;
     int nxt = cur + 1;
     while (nxt < nt && wg_skips(nxt)) ++nxt;
     nxt = uniform(nxt);
@@ -353,7 +407,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       // own VALU work overlaps its own MFMAs (issue is in order): S1 products run under the phi
       // math of block 0, the P.V products of block 0 under the phi math of block 1, and LDS
       // reads run ahead of the products that consume them.
-      if (!done && !needs_mask(cur * BN + 32)) {
+      if (!done && !needs_mask(cur * BN + 32) && keys_full) {
         constexpr int NV = 2 * DB;            // P.V products (and V fragments) per 32-key block
         constexpr int EB = 16 / KC;           // phi elements per S1 product (stage B)
         constexpr int EC = 16 / NV;           // phi elements per P.V0 product (stage C)
@@ -429,6 +483,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       for (int sb = 0; sb < SB; ++sb) {
         const int key0 = cur * BN + sb * 32;
         if (needs_mask(key0)) mask_block<MASKED>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
+        if constexpr (KEYPAD) {
+          const unsigned long long keep = keep_lds[cur];
+          if (keep != ~0ull) keep_keys(s[sb], keep, sb, lane);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[sb][i] = ra_phi(s[sb][i], a.c, kd);
 #pragma unroll
@@ -522,7 +580,15 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   a.coff = p.coff;
   a.mask = mask_args(p);
   dim3 grid(a.total_wg), block(kThreads);
-  if (p.mask_kind != kMaskNone) {
+  // a boolean key padding mask ([B, Nk] broadcast over heads and rows, keys contiguous, every
+  // sample's row 4-byte aligned for the dword copies) with the output: the four-stage path
+  const bool keypad = sizeof(T) == 2 && o != nullptr && !counters && p.mask_kind == kMaskBool && p.msq == 0 &&
+                      p.msh == 0 && p.msk == 1 && p.msb % 4 == 0 &&
+                      reinterpret_cast<unsigned long long>(p.mask) % 4 == 0 && (p.Nk + BN - 1) / BN <= kMaxTiles;
+  if (keypad) {
+    if constexpr (sizeof(T) == 2 && BN == kWave)
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, true>), grid, block, 0, stream, a);
+  } else if (p.mask_kind != kMaskNone) {
     if (o == nullptr) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true>), grid, block, 0, stream, a);
   } else if (o == nullptr) {   // statistics only (m, l), for a backward without saved stats

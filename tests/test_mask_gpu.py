@@ -170,6 +170,10 @@ MASK_CASES = [
     ("keypad", 2, 4, 2, 96, 200, 64, "none", "bf16"),
     ("keypad", 3, 2, 1, 130, 130, 128, "top_left", "bf16"),
     ("keypad", 2, 2, 2, 65, 190, 64, "bottom_right", "f32"),
+    # bf16 key padding with 4-byte aligned rows (Nk % 4 == 0) runs the forward whose K ring also
+    # carries the mask bytes: scattered padding (partial tiles), GQA, both alignments, D = 128
+    ("keypad", 2, 4, 2, 96, 200, 128, "bottom_right", "bf16"),
+    ("keypad", 3, 8, 2, 150, 260, 128, "top_left", "bf16"),
     ("shared2d", 1, 4, 4, 127, 127, 128, "top_left", "bf16"),
     ("shared2d", 2, 2, 1, 50, 90, 64, "none", "f32"),
     ("full_bool", 2, 6, 3, 70, 150, 128, "none", "bf16"),
@@ -197,6 +201,26 @@ def test_masked_parity(gpu_lib, case):
     for n in ("o", "dq", "dk", "dv"):
         assert np.isfinite(res[n]).all(), n
     print(f"{case}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("causal", ["none", "top_left", "bottom_right"])
+def test_key_padding_lengths(gpu_lib, causal):
+    """Key padding from per-sample lengths (contiguous kept prefixes, one empty sample): whole
+    padded tiles are dropped in both forward passes, the tile holding the boundary is masked
+    entry by entry; a sample with no key gives o = 0, dk = dv = 0."""
+    import torch
+    import rational_softmax_tiled_amd as ra
+    B, Hq, Hkv, Nq, Nk, D = 3, 4, 2, 192, 200, 128
+    lens = np.array([200, 70, 0])
+    keep = np.arange(Nk)[None, :] < lens[:, None]
+    inp = rand_inputs(B, Hq, Hkv, Nq, Nk, D, "bf16", seed=41)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    mask = (torch.from_numpy(keep).cuda(), ra.RA_MASK_BOOL, (Nk, 0, 0, 1))
+    res = run(gpu_lib, inp, causal, scale, "bf16", mask=mask)
+    check(res, inp, causal, scale, "bf16", mask_np=keep[:, None, None, :], what=f"lengths {causal}")
+    assert (res["o"][2] == 0).all() and (res["dk"][2] == 0).all() and (res["dv"][2] == 0).all()
+    for n in ("o", "dq", "dk", "dv"):
+        assert np.isfinite(res[n]).all(), n
 
 
 def test_masked_backward_without_stats_is_identical(gpu_lib):
