@@ -470,11 +470,15 @@ __device__ __forceinline__ float ra_grad_only(float s, float c16, float kd, floa
   return fmaf(dp, il, -cil) * ((w * w) * q);
 }
 
-template <int D, bool CAUSAL, bool MASKED>
+// KEYPAD (with MASKED false): a boolean key padding mask.  Wave 0 copies each tile's 64 mask bytes
+// with its K and V tiles; the 64 keep bits drop whole padded blocks and mask the partial ones.
+template <int D, bool CAUSAL, bool MASKED, bool KEYPAD = false>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int BN = 64, KC = D / 16, SB = BN / 32, DB = D / 32;
+  static_assert(!(KEYPAD && MASKED), "key padding runs the unmasked paths");
   __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * D];
   __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * D];
+  __shared__ __attribute__((aligned(16))) unsigned m_lds[KEYPAD ? 2 : 1][KEYPAD ? kWave : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_remap(blockIdx.x, a.total_wg);
@@ -504,10 +508,17 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const int lane_off = dma_lane_offset<D, kWaves>(wave, lane);
   const unsigned k_m0[2] = {lds_addr(k_lds[0]), lds_addr(k_lds[1])};
   const unsigned v_m0[2] = {lds_addr(v_lds[0]), lds_addr(v_lds[1])};
+  u32x4 m_rsrc = {};
+  if constexpr (KEYPAD) m_rsrc = dma_rsrc(static_cast<const char*>(a.mask.ptr) + (size_t)b * a.mask.sb, a.Nk);
+  auto m_issue = [&](int kt, int slot) {   // the tile's 64 mask bytes (lanes 0-15)
+    if constexpr (KEYPAD)
+      if (wave == 0) lds_dma_at<4>(m_rsrc, lds_addr(m_lds[slot]), lane * 4, kt * BN);
+  };
   // tile 0 is in flight while the row terms are prepared
   if (nt > 0) {
     dma_tile_at<D, BN>(k_rsrc, 0, k_m0[0], lane_off, wave);
     dma_tile_at<D, BN>(v_rsrc, 0, v_m0[0], lane_off, wave);
+    m_issue(0, 0);
   }
   const bf16* qp = static_cast<const bf16*>(a.q) + (head + qrow) * D;
   const bf16* dop = static_cast<const bf16*>(a.d_o) + (head + qrow) * D;
@@ -544,10 +555,14 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
     if (kt + 1 < nt) {
       dma_tile_at<D, BN>(k_rsrc, (kt + 1) * BN * D * 2, k_m0[buf ^ 1], lane_off, wave);
       dma_tile_at<D, BN>(v_rsrc, (kt + 1) * BN * D * 2, v_m0[buf ^ 1], lane_off, wave);
+      m_issue(kt + 1, buf ^ 1);
     }
+    unsigned long long keep = ~0ull;   // KEYPAD: bit l set when key kt BN + l is kept
+    if constexpr (KEYPAD) keep = __ballot(reinterpret_cast<const unsigned char*>(m_lds[buf])[lane] != 0);
     if (kt < nt_w) {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
+        if (KEYPAD && ((keep >> (32 * sb)) & 0xffffffffull) == 0) continue;   // all padding
         f32x16 s = {}, dp = {};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) mma(s, swz_frag<bf16, D>(k_lds[buf], sb * 32 + frow, 16 * kc + fcol), qf[kc]);
@@ -564,6 +579,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
           const int lb = key0 + 4 * (lane >> 5);
           keep_rows(s, -kNoBound, min(a.Nk - lb, CAUSAL ? qrow + a.coff + 1 - lb : kNoBound));
         }
+        if constexpr (KEYPAD)
+          if (keep != ~0ull) keep_keys(s, keep, sb, lane);
         float lm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) lm = fmaxf(lm, s[i]);
@@ -635,7 +652,10 @@ constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * kWave;
 constexpr int kDkdvRows = 64;   // query rows per step (32 per half of the workgroup)
 
-template <int D, bool CAUSAL, bool MASKED>
+// KEYPAD (with MASKED false): a boolean mask that depends on the key only (key padding).  A lane
+// owns one key for the whole kernel, so the mask is one keep flag per lane, read once; the
+// kernel keeps the unmasked paths, and a wave whose keys are all padding computes nothing.
+template <int D, bool CAUSAL, bool MASKED, bool KEYPAD = false>
 __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int KC = D / 16, DB = D / 32, QT = kDkdvRows, HR = QT / 2, NW = kDkdvWaves;
   constexpr int HTILE = HR * D;           // elements of one half-tile (32 rows of Q or dO)
@@ -718,9 +738,17 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
     }
   };
   // does this wave's 32 x 32 block of the tile at query row i0 hold any allowed score?
+  static_assert(!(KEYPAD && MASKED), "key padding runs the unmasked paths");
+  bool key_kept = true, keys_all = true, keys_none = false;
+  if constexpr (KEYPAD) {
+    const unsigned char* mrow = static_cast<const unsigned char*>(a.mask.ptr) + (size_t)b * a.mask.sb;
+    key_kept = active && key < a.Nk && mrow[key] != 0;
+    keys_all = !__any(!key_kept);
+    keys_none = !__any(key_kept);
+  }
   auto block_live = [&](const Cursor& c) {
     const int i0 = c.qt * QT + HR * half;
-    return active && i0 < a.Nq && !(CAUSAL && i0 + 31 + a.coff < j0);
+    return active && !keys_none && i0 < a.Nq && !(CAUSAL && i0 + 31 + a.coff < j0);
   };
   // explicit mask elements of this wave's block (read ahead of the products)
   auto mask_load = [&](const Cursor& c, unsigned (&mv)[16]) {
@@ -780,6 +808,12 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
       // (causal) and key < Nk
       const int lb = 4 * (lane >> 5);
       keep_rows(s, (CAUSAL ? key - a.coff - i0 : -kNoBound) - lb, key >= a.Nk ? -kNoBound : a.Nq - i0 - lb);
+    }
+    if constexpr (KEYPAD) {
+      if (!keys_all) {   // a padded key: its whole column of the block goes
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = key_kept ? s[i] : -INFINITY;
+      }
     }
     const float* st = &st_lds[slot][0][HR * half];
 #pragma unroll
@@ -993,8 +1027,14 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   const dim3 kblock(kBf16 ? kDkdvThreads : kThreads);
   // the masked kernels are the causal ones (coff = Nk when there is no causality)
   const bool masked = p.mask_kind != kMaskNone;
+  // a boolean key padding mask ([B, Nk] broadcast over heads and rows, keys contiguous, every
+  // sample's row 4-byte aligned for the dword copies): the unmasked kernels with keep bits
+  const bool keypad = kBf16 && p.mask_kind == kMaskBool && p.msq == 0 && p.msh == 0 && p.msk == 1 &&
+                      p.msb % 4 == 0 && reinterpret_cast<unsigned long long>(p.mask) % 4 == 0;
   if (phases & kBwdDq) {
-    if (masked) {
+    if (keypad) {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, true>), qgrid, block, 0, stream, a);
+    } else if (masked) {
       if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, true>), qgrid, block, 0, stream, a);
       else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, true>), qgrid, block, 0, stream, a);
     } else if (p.causal) {
@@ -1008,7 +1048,9 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
     if (e != hipSuccess) return e;
   }
   if (phases & kBwdDkdv) {
-    if (masked) {
+    if (keypad) {
+      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, false, true>), kgrid, kblock, 0, stream, a);
+    } else if (masked) {
       if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, true>), kgrid, kblock, 0, stream, a);
       else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true, true>), kgrid, kblock, 0, stream, a);
     } else if (p.causal) {

@@ -88,6 +88,16 @@ __device__ __forceinline__ void keep_rows(f32x16& s, int lo, int hi) {
   }
 }
 
+// Keeps the entries of 32-key block sb of a 64-key tile whose key bit is set in keep (bit l: key
+// l of the tile) and sets the others to -inf.  Entry i of a lane is key 8 (i/4) + 4 (lane/32) +
+// i%4 of the block.
+__device__ __forceinline__ void keep_keys(f32x16& s, unsigned long long keep, int sb, int lane) {
+  const unsigned w = (unsigned)(keep >> (32 * sb)) >> (4 * (lane >> 5));
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (!((w >> (8 * (i >> 2) + (i & 3))) & 1u)) s[i] = -INFINITY;
+}
+
 // Eight accumulator values (elements 8*ks .. 8*ks+7) as the B fragment of the next product.
 __device__ __forceinline__ bf16x8 pack_frag_bf16(const f32x16& s, int ks) {
   bf16x8 r;

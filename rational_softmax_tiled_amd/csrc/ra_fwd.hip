@@ -78,16 +78,6 @@ __device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int la
   keep_rows(s, -kNoBound, min(Nk - lb, qrow + coff + 1 - lb));
 }
 
-// Keeps the entries of 32-key block sb of a 64-key tile whose key bit is set in keep (bit l: key
-// l of the tile) and sets the others to -inf.  Entry i of a lane is key 8 (i/4) + 4 (lane/32) +
-// i%4 of the block.
-__device__ __forceinline__ void keep_keys(f32x16& s, unsigned long long keep, int sb, int lane) {
-  const unsigned w = (unsigned)(keep >> (32 * sb)) >> (4 * (lane >> 5));
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (!((w >> (8 * (i >> 2) + (i & 3))) & 1u)) s[i] = -INFINITY;
-}
-
 // S^T block (32 keys x 32 query rows) of key sub-block sb of the staged (swizzled) K tile.
 template <typename T, int D>
 __device__ __forceinline__ f32x16 score_block(const T* k_tile, const typename Ty<T>::frag* qf, int sb,
