@@ -48,12 +48,12 @@ MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("7ec132e6cbc4fde158bb0918667f3d4f76fbe83238282e31a0d59b3acdaf2406",
-                        263372.8, 135184.4),
-    "attn_bwd_dq_bf16_kernel": ("203558b8a601047e73706c682a815eef3855493e6d4829c56f7a226db2df863f",
-                                437374.7, 143455.9),
-    "attn_bwd_dkdv_bf16_kernel": ("203558b8a601047e73706c682a815eef3855493e6d4829c56f7a226db2df863f",
-                                  267527.0, 262145.8),
+    "attn_fwd_kernel": ("5191ac9713841e501c5ee88fc3313d0c516b3e2b02b8545f115dda5e5ce62863",
+                        264250.1, 135189.8),
+    "attn_bwd_dq_bf16_kernel": ("9b3a2dbb18ee6b36d70d6c4f61ee3603c2d3caf4f48283efa1afbd9614afda05",
+                                435292.8, 143457.0),
+    "attn_bwd_dkdv_bf16_kernel": ("9b3a2dbb18ee6b36d70d6c4f61ee3603c2d3caf4f48283efa1afbd9614afda05",
+                                  267503.8, 262144.0),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],
