@@ -299,7 +299,7 @@ def ra_attention_fwd(q, k, v, causal, scale, q_positions=None, heads=None, mask=
     return o, m, l, a
 
 
-def ra_attention_bwd(q, k, v, do, causal, scale, groups=None, mask=None):
+def ra_attention_bwd(q, k, v, do, causal, scale, groups=None, mask=None, argmax=None):
     """Gradients (dQ, dK, dV) of L = sum(O * dO) for ra_attention_fwd.
 
     Follows the chain rule in the forward's order: dP = dO V^T; the softmax
@@ -308,6 +308,13 @@ def ra_attention_bwd(q, k, v, do, causal, scale, groups=None, mask=None):
     a K/V head.  ``groups`` restricts the work to a list of (b, g) K/V groups
     (all their query heads are processed).  ``causal`` and ``mask`` as in
     ra_attention_fwd (the mask gets no gradient).
+
+    ``argmax``: optional int array [B, Hq, Nq]; where an entry is >= 0 the
+    row-max term R_i goes to that key instead of the lowest key attaining the
+    max.  The function is not differentiable where two scores tie for the
+    max; a parity check whose scores carry rounding error uses this to take
+    the gradient on the side of the other near-tied candidate.  Delta is
+    still measured from the true row max.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -326,6 +333,8 @@ def ra_attention_bwd(q, k, v, do, causal, scale, groups=None, mask=None):
         for h in range(g * rep, (g + 1) * rep):
             s, allowed_bh = _scores(q[b, h], k[b, g], scale, allowed, mask, b, h, (B, Hq, Nq, Nk))
             _, a, delta, phi = _row_stats(s, allowed_bh)
+            if argmax is not None:
+                a = np.where(argmax[b, h] >= 0, argmax[b, h], a)
             lb = phi.sum(axis=-1)
             with np.errstate(invalid="ignore", divide="ignore"):
                 p = np.where(lb[:, None] > 0, phi / lb[:, None], 0.0)

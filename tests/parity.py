@@ -1,0 +1,204 @@
+"""Parity of whole full-size launches against the oracle: every (batch, head) of a forward and
+every (batch, K/V head) group of a backward, element by element.
+
+The oracle runs one head (forward) or one group (backward) at a time on host threads: heads are
+independent, NumPy releases the GIL inside its matrix products and element-wise loops, and BLAS
+is held to one thread per worker.
+
+Tolerances (per output tensor, over the whole launch): bf16 max|gpu - oracle| / max|oracle|
+<= 2e-2; fp32 max-abs 1e-5 (gradients: relative to max|oracle| when that exceeds 1).
+
+Near ties of the row max (the reading of argmax ties): the backward puts the row-max term R_i at
+the lowest key attaining the max.  Where the oracle's best score and another allowed score of a
+row differ by less than the sum of their fp32 score error bounds, the GPU's fp32 scores may order
+them the other way.  For such rows the checker accepts the gradient of either candidate: it
+infers the GPU's choice per row from dQ (row-local) and compares every tensor with the oracle
+run with that choice (the oracle's ``argmax`` override).  Two keys with bit-identical rows tie
+exactly in both precisions, so the lowest index is required there.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+
+import numpy as np
+
+import oracle
+from helpers import U32
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+
+
+def n_workers() -> int:
+    """Host threads for the oracle: the cores granted to one GPU (16), or fewer if absent."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _pool_map(fn, items):
+    try:
+        import threadpoolctl
+        limit = threadpoolctl.threadpool_limits(1)
+    except Exception:          # pragma: no cover
+        limit = None
+    try:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=n_workers()) as ex:
+            return list(ex.map(fn, items))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+
+
+class Tally:
+    """Largest absolute error and largest |oracle| of one output tensor over many pieces."""
+
+    def __init__(self, name, dtype, grad):
+        self.name, self.dtype, self.grad = name, dtype, grad
+        self.err = 0.0
+        self.ref = 0.0
+        self.where = None
+
+    def add(self, gpu, ref, where):
+        if gpu.size == 0:
+            return
+        e = float(np.abs(gpu - ref).max())
+        if e > self.err:
+            self.err, self.where = e, where
+        self.ref = max(self.ref, float(np.abs(ref).max()))
+
+    def check(self):
+        if self.dtype == "bf16":
+            r = self.err / (self.ref if self.ref > 0 else 1.0)
+            assert r <= BF16_TOL, f"{self.name}: rel-to-max err {r:.3e} (worst at {self.where})"
+            return r
+        lim = F32_TOL * (max(1.0, self.ref) if self.grad else 1.0)
+        assert self.err <= lim, f"{self.name}: max abs err {self.err:.3e} (worst at {self.where})"
+        return self.err
+
+
+def fwd_all_heads(o, stats, inp, causal, scale, dtype, heads=None):
+    """Compare o [B, Hq, Nq, D] and stats [B, Hq, Nq, 2] (raw m, l) with the oracle on every
+    (b, h) (or the given list).  Returns {name: error} (rel-to-max for bf16, abs for fp32)."""
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    B, Hq, Nq, D = q.shape
+    rep = Hq // k.shape[1]
+    todo = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
+
+    def one(bh):
+        b, h = bh
+        g = h // rep
+        ro, rm, rl, _ = oracle.ra_attention_fwd(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1],
+                                                v[b:b + 1, g:g + 1], causal, scale)
+        eo = float(np.abs(o[b, h] - ro[0, 0]).max())
+        mo = float(np.abs(ro[0, 0]).max())
+        # m: the GPU stores the raw dot-product max, the oracle the scaled one
+        gm, gl = stats[b, h, :, 0] * scale, stats[b, h, :, 1]
+        fin = np.isfinite(rm[0, 0])
+        assert (np.isfinite(gm) == fin).all(), f"m finiteness at {bh}"
+        em = float(np.max(np.abs(gm[fin] - rm[0, 0][fin]) - 1e-5 * np.abs(rm[0, 0][fin]), initial=0.0))
+        el = float(np.max(np.abs(gl - rl[0, 0]) / np.maximum(np.abs(rl[0, 0]), 1e-30), initial=0.0))
+        return bh, eo, mo, em, el
+
+    t = Tally("o", dtype, grad=False)
+    em_max = el_max = 0.0
+    for bh, eo, mo, em, el in _pool_map(one, todo):
+        if eo > t.err:
+            t.err, t.where = eo, bh
+        t.ref = max(t.ref, mo)
+        em_max, el_max = max(em_max, em), max(el_max, el)
+    err = t.check()
+    assert em_max <= 1e-4, f"row max m off by {em_max:.3e} beyond rtol 1e-5"
+    assert el_max <= (1e-5 if dtype == "f32" else 1e-2), f"sum of phi rel err {el_max:.3e}"
+    return {"o": err, "m": em_max, "l": el_max, "heads": len(todo)}
+
+
+def score_error_bound(qh, kg, scale):
+    """|fp32 score - exact score| <= gamma_D * scale * sum_d |q_d k_d| per (i, j)."""
+    D = qh.shape[-1]
+    gamma = D * U32 / (1 - D * U32)
+    return gamma * scale * (np.abs(qh) @ np.abs(kg).T)
+
+
+def near_tie_candidates(qh, kg, scale, causal, Nq, Nk):
+    """Per row of one head: the other keys whose score may order before the oracle's argmax in
+    fp32, as a dict row -> [keys] (keys with bit-identical rows to the argmax excluded)."""
+    s = scale * (qh @ kg.T)
+    off = oracle.causal_offset(causal, Nq, Nk)
+    allowed = np.ones((Nq, Nk), bool) if off is None else \
+        np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + off
+    xm = np.where(allowed, s, -np.inf)
+    a = np.argmax(xm, axis=1)
+    m = xm[np.arange(Nq), a]
+    es = score_error_bound(qh, kg, scale)
+    near = allowed & (m[:, None] - s <= es + es[np.arange(Nq), a][:, None])
+    near[np.arange(Nq), a] = False
+    out = {}
+    for i in np.nonzero(near.any(axis=1) & np.isfinite(m))[0]:
+        cands = [int(j) for j in np.nonzero(near[i])[0] if not np.array_equal(kg[j], kg[a[i]])]
+        if cands:
+            out[int(i)] = (int(a[i]), cands)
+    return out
+
+
+def bwd_all_groups(dq, dk, dv, inp, causal, scale, dtype, groups=None):
+    """Compare dq [B, Hq, Nq, D], dk, dv [B, Hkv, Nk, D] with the oracle on every (b, g) group
+    (or the given list), accepting either candidate at near ties of the row max.  Returns
+    {name: error, "near_tie_rows": n, "flipped_rows": n}."""
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    rep = Hq // Hkv
+    todo = [(b, g) for b in range(B) for g in range(Hkv)] if groups is None else list(groups)
+
+    def one(bg):
+        b, g = bg
+        hs = slice(g * rep, (g + 1) * rep)
+        args = (q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], do[b:b + 1, hs], causal, scale)
+        kg = k[b, g].astype(np.float64)
+        ties = {r: near_tie_candidates(q[b, g * rep + r].astype(np.float64), kg, scale, causal, Nq, Nk)
+                for r in range(rep)}
+        ref = oracle.ra_attention_bwd(*args)
+        n_tie = sum(len(t) for t in ties.values())
+        n_flip = 0
+        if n_tie:
+            # the GPU's choice per near-tie row, from dQ: the default or one of the alternatives
+            choice = np.full((1, rep, Nq), -1)
+            best = {(r, i): (np.abs(dq[b, g * rep + r, i] - ref[0][0, r, i]).max(), -1)
+                    for r, t in ties.items() for i in t}
+            depth = max(len(c) for t in ties.values() for _, c in t.values())
+            for n in range(depth):
+                over = np.full((1, rep, Nq), -1)
+                for r, t in ties.items():
+                    for i, (_, c) in t.items():
+                        if n < len(c):
+                            over[0, r, i] = c[n]
+                alt = oracle.ra_attention_bwd(*args, argmax=over)
+                for (r, i), (e, _) in list(best.items()):
+                    if over[0, r, i] >= 0:
+                        e2 = np.abs(dq[b, g * rep + r, i] - alt[0][0, r, i]).max()
+                        if e2 < e:
+                            best[(r, i)] = (e2, int(over[0, r, i]))
+            for (r, i), (_, j) in best.items():
+                choice[0, r, i] = j
+            n_flip = int((choice >= 0).sum())
+            if n_flip:
+                ref = oracle.ra_attention_bwd(*args, argmax=choice)
+        out = []
+        for name, gpu, r in (("dq", dq[b, hs], ref[0][0]), ("dk", dk[b, g], ref[1][0, 0]),
+                             ("dv", dv[b, g], ref[2][0, 0])):
+            out.append((name, float(np.abs(gpu - r).max()), float(np.abs(r).max())))
+        return bg, out, n_tie, n_flip
+
+    tallies = {n: Tally(n, dtype, grad=True) for n in ("dq", "dk", "dv")}
+    n_tie = n_flip = 0
+    for bg, out, nt, nf in _pool_map(one, todo):
+        n_tie += nt
+        n_flip += nf
+        for name, e, m in out:
+            t = tallies[name]
+            if e > t.err:
+                t.err, t.where = e, bg
+            t.ref = max(t.ref, m)
+    res = {n: t.check() for n, t in tallies.items()}
+    res.update(near_tie_rows=n_tie, flipped_rows=n_flip, groups=len(todo))
+    return res

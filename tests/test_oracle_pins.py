@@ -351,6 +351,43 @@ def test_bwd_max_path_term_is_needed():
     assert np.abs(dq_bad - fd).max() > 1e-3
 
 
+def test_argmax_override_is_the_gradient_from_the_other_side_of_a_tie():
+    # Where key a' is the row max by a margin delta over key a, the override argmax = a must give
+    # the gradient the default takes once a leads by delta instead (the function on a's side of
+    # the tie, where it is smooth): equal up to O(delta), and visibly different from the default
+    # gradient at the same point, which puts the row-max term on a'.
+    rng = np.random.default_rng(19)
+    B, H, N, D, i, a, a2 = 1, 1, 6, 4, 5, 1, 3
+    q, k, v = _rand_qkv(rng, B, H, H, N, N, D, sigma=0.7)
+    do = rng.normal(size=q.shape)
+    qi = q[0, 0, i]
+    w = rng.normal(size=D)
+    w -= (w @ qi) / (qi @ qi) * qi                   # q_i . w = 0
+    delta = 1e-9
+    k[0, 0, a2] = 3.0 * qi / (qi @ qi)               # s_{i,a2} = 3, the max of row i
+    k_a_below = k[0, 0, a2] + w - delta * qi / (qi @ qi)
+    k_a_above = k[0, 0, a2] + w + delta * qi / (qi @ qi)
+    x_below, x_above = k.copy(), k.copy()
+    x_below[0, 0, a], x_above[0, 0, a] = k_a_below, k_a_above
+    _, _, _, am = oracle.ra_attention_fwd(q, x_below, v, False, 1.0)
+    assert am[0, 0, i] == a2
+    assert oracle.ra_attention_fwd(q, x_above, v, False, 1.0)[3][0, 0, i] == a
+    over = np.full((B, H, N), -1)
+    over[0, 0, i] = a
+    g_over = oracle.ra_attention_bwd(q, x_below, v, do, False, 1.0, argmax=over)
+    g_above = oracle.ra_attention_bwd(q, x_above, v, do, False, 1.0)
+    g_default = oracle.ra_attention_bwd(q, x_below, v, do, False, 1.0)
+    for x, y, z in zip(g_over, g_above, g_default):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-7)
+    assert np.abs(g_over[0] - g_default[0]).max() > 1e-3    # dQ of row i moves with the argmax
+    assert np.abs(g_over[1] - g_default[1]).max() > 1e-3    # so do dK_a, dK_a2
+    # an override equal to the default argmax changes nothing
+    same = np.full((B, H, N), -1)
+    same[0, 0, i] = a2
+    for x, y in zip(oracle.ra_attention_bwd(q, x_below, v, do, False, 1.0, argmax=same), g_default):
+        np.testing.assert_array_equal(x, y)
+
+
 # ------------------------------------------------------------- masks and causal alignment
 
 def test_key_padding_equals_dropping_keys():
@@ -608,6 +645,99 @@ def test_decode_gqa_equals_mha_on_repeated_cache():
     o2 = oracle.ra_attention_decode(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), 0.5,
                                     seqlens=lens)[0]
     np.testing.assert_array_equal(o1, o2)
+
+
+def test_gqa_per_query_head_masks_match_brute_force():
+    # GQA with a different boolean mask per query head: head h attends with its own mask row and
+    # K/V head h // REP.
+    rng = np.random.default_rng(53)
+    B, Hq, Hkv, Nq, Nk, D = 1, 4, 2, 4, 7, 3
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, Nq, Nk, D, sigma=1.5)
+    mask = rng.random((B, Hq, Nq, Nk)) < 0.6
+    mask[..., 0] = True
+    o = oracle.ra_attention_fwd(q, k, v, False, 0.7, mask=mask)[0]
+    for h in range(Hq):
+        ref = _brute_attention(q[0, h].tolist(), k[0, h // 2].tolist(), v[0, h // 2].tolist(), 0.7,
+                               lambda i, j, h=h: bool(mask[0, h, i, j]))
+        np.testing.assert_allclose(o[0, h], ref, rtol=0, atol=1e-14)
+
+
+# Planted mistakes (in the oracle, on the CPU): each must make at least one pin fail.
+
+def _planted(name, replacement):
+    """Context: oracle.ra_oracle.<name> replaced by replacement(original) while inside."""
+    import contextlib
+    import oracle.ra_oracle as ro
+
+    @contextlib.contextmanager
+    def ctx():
+        orig = getattr(ro, name)
+        setattr(ro, name, replacement(orig))
+        try:
+            yield
+        finally:
+            setattr(ro, name, orig)
+    return ctx()
+
+
+def test_planted_flipped_bottom_right_offset_breaks_brute_force():
+    flip = lambda orig: (lambda causal, Nq, Nk: (lambda off: -off if off else off)(orig(causal, Nq, Nk)))
+    with _planted("causal_offset", flip):
+        with pytest.raises(AssertionError):
+            test_bottom_right_causal_brute_force(3, 7)
+        with pytest.raises(AssertionError):
+            test_bottom_right_causal_brute_force(7, 3)
+    test_bottom_right_causal_brute_force(3, 7)     # restored
+
+
+def test_planted_ignored_bias_breaks_additive_example():
+    def ignore_bias(orig):
+        def scores(qh, kg, scale, allowed, mask, b, h, shape):
+            if mask is not None and mask.dtype != np.bool_:
+                mask = None
+            return orig(qh, kg, scale, allowed, mask, b, h, shape)
+        return scores
+    with _planted("_scores", ignore_bias):
+        with pytest.raises(AssertionError):
+            test_additive_mask_worked_example()
+    test_additive_mask_worked_example()
+
+
+def test_planted_mask_of_the_kv_head_breaks_per_head_masks():
+    def kv_head(orig):
+        def scores(qh, kg, scale, allowed, mask, b, h, shape):
+            return orig(qh, kg, scale, allowed, mask, b, h // 2, shape)   # REP = 2 in the pin
+        return scores
+    with _planted("_scores", kv_head):
+        with pytest.raises(AssertionError):
+            test_gqa_per_query_head_masks_match_brute_force()
+    test_gqa_per_query_head_masks_match_brute_force()
+
+
+@pytest.mark.parametrize("mistake", ["prefix_off_by_one", "lengths_ignored"])
+def test_planted_decode_mistakes_break_decode_pins(mistake):
+    # A scratch decode that takes one key too few per sample, or ignores the lengths, must fail
+    # the prefill-continuation and brute-force pins.
+    def bad_decode(orig):
+        def decode(q, k, v, scale, seqlens=None, causal=False):
+            if mistake == "lengths_ignored":
+                return orig(q, k, v, scale, seqlens=None, causal=causal)
+            lens = np.full(q.shape[0], k.shape[2]) if seqlens is None else np.asarray(seqlens)
+            return orig(q, k, v, scale, seqlens=np.maximum(lens - 1, 0), causal=causal)
+        return decode
+    import oracle as oracle_pkg
+    import oracle.ra_oracle as ro
+    orig = ro.ra_attention_decode
+    bad = bad_decode(orig)
+    ro.ra_attention_decode, oracle_pkg.ra_attention_decode = bad, bad
+    try:
+        with pytest.raises(AssertionError):
+            test_decode_continues_the_prefill()
+        with pytest.raises(AssertionError):
+            test_decode_brute_force_and_edges()
+    finally:
+        ro.ra_attention_decode, oracle_pkg.ra_attention_decode = orig, orig
+    test_decode_continues_the_prefill()
 
 
 def test_planted_phi_exponent_error_breaks_golden():
