@@ -111,7 +111,10 @@ int ra_last_hip_error(void);
  *   query rows is skipped for them, which leaves the result bit-identical.
  *   Sizes: B*Hq*Nq == 0 -> RA_OK, nothing launched.  Nk == 0 -> o = 0 (and stats m = -inf,
  *   l = 0): a row with no allowed key yields a zero output, not NaN.
- *   Limits: Nq * D and Nk * D below 2^31, B * Hq * Nq below 2^31.
+ *   Limits (RA_ERR_TOO_LARGE otherwise): (Nq + 256) * D * elem_size and (Nk + 256) * D *
+ *   elem_size below 2^31 bytes (elem_size 2 for RA_BF16, 4 for RA_F32: the kernels form byte
+ *   offsets inside one head's matrix, tile tails included, in 32-bit integers), and
+ *   B * Hq * Nq, B * Hkv * Nk below 2^31.
  */
 int ra_attn_fwd(const void* q, const void* k, const void* v, void* o, float* stats,
                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,

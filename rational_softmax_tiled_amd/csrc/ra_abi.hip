@@ -15,6 +15,8 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kIndexLimit = (int64_t)1 << 31;
+// Rows past the end of a matrix that a tile may address (the largest tile is 256 rows).
+constexpr int64_t kTailRows = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -38,7 +40,11 @@ int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int6
   if ((Hq > 0 || Hkv > 0) && (Hkv == 0 || Hq % Hkv != 0)) return RA_ERR_GQA;
   if (D != 64 && D != 128) return RA_ERR_HEADDIM;
   if (!(scale > 0.0f) || !isfinite(scale)) return RA_ERR_SCALE;
-  if (!below_limit(Nq, D, 1) || !below_limit(Nk, D, 1)) return RA_ERR_TOO_LARGE;
+  // The kernels form byte offsets inside one head's [N, D] matrix (buffer sizes, tile offsets,
+  // including a tile tail of up to kTailRows rows past the end) in signed 32-bit integers.
+  const int64_t row_bytes = D * (dtype == RA_BF16 ? 2 : 4);
+  if (!below_limit(Nq + kTailRows, row_bytes, 1) || !below_limit(Nk + kTailRows, row_bytes, 1))
+    return RA_ERR_TOO_LARGE;
   if (!below_limit(B, Hq, Nq) || !below_limit(B, Hkv, Nk)) return RA_ERR_TOO_LARGE;
   return RA_OK;
 }

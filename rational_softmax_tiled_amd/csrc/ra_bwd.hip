@@ -1028,9 +1028,11 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   // the masked kernels are the causal ones (coff = Nk when there is no causality)
   const bool masked = p.mask_kind != kMaskNone;
   // a boolean key padding mask ([B, Nk] broadcast over heads and rows, keys contiguous, every
-  // sample's row 4-byte aligned for the dword copies): the unmasked kernels with keep bits
+  // sample's row 4-byte aligned and a whole number of dwords long for the dword copies, whose
+  // resource ends at Nk bytes): the unmasked kernels with keep bits
   const bool keypad = kBf16 && p.mask_kind == kMaskBool && p.msq == 0 && p.msh == 0 && p.msk == 1 &&
-                      p.msb % 4 == 0 && reinterpret_cast<unsigned long long>(p.mask) % 4 == 0;
+                      p.msb % 4 == 0 && p.Nk % 4 == 0 &&
+                      reinterpret_cast<unsigned long long>(p.mask) % 4 == 0;
   if (phases & kBwdDq) {
     if (keypad) {
       if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, true>), qgrid, block, 0, stream, a);

@@ -571,9 +571,10 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   a.mask = mask_args(p);
   dim3 grid(a.total_wg), block(kThreads);
   // a boolean key padding mask ([B, Nk] broadcast over heads and rows, keys contiguous, every
-  // sample's row 4-byte aligned for the dword copies) with the output: the four-stage path
+  // sample's row 4-byte aligned and a whole number of dwords long for the dword copies, whose
+  // resource ends at Nk bytes) with the output: the four-stage path
   const bool keypad = sizeof(T) == 2 && o != nullptr && !counters && p.mask_kind == kMaskBool && p.msq == 0 &&
-                      p.msh == 0 && p.msk == 1 && p.msb % 4 == 0 &&
+                      p.msh == 0 && p.msk == 1 && p.msb % 4 == 0 && p.Nk % 4 == 0 &&
                       reinterpret_cast<unsigned long long>(p.mask) % 4 == 0 && (p.Nk + BN - 1) / BN <= kMaxTiles;
   if (keypad) {
     if constexpr (sizeof(T) == 2 && BN == kWave)

@@ -75,6 +75,21 @@ def test_fwd_validation(lib):
     assert fwd(B=1 << 40, Hq=1 << 40, Hkv=1, Nq=1 << 40) == TOO_LARGE  # no int64 overflow
 
 
+@pytest.mark.parametrize("dtype,es", [(ra.RA_BF16, 2), (ra.RA_F32, 4)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_byte_offset_boundary(lib, dtype, es, D):
+    """Every byte offset inside one head's matrix, a 256-row tile tail included, fits a signed
+    32-bit int: (N + 256) * D * elem_size < 2^31 for N = Nq and N = Nk, else RA_ERR_TOO_LARGE.
+    The size query returns 0 exactly where a call would be refused (no launch needed)."""
+    n_max = (1 << 31) // (D * es) - 256 - 1          # the largest N the limit admits
+    assert (n_max + 256) * D * es < (1 << 31) <= (n_max + 257) * D * es
+    for nq, nk in ((n_max, 8), (8, n_max)):
+        assert ra.ra_attn_bwd_workspace_bytes(1, 1, 1, nq, nk, D, dtype) > 0
+    for nq, nk in ((n_max + 1, 8), (8, n_max + 1)):
+        assert ra.ra_attn_bwd_workspace_bytes(1, 1, 1, nq, nk, D, dtype) == 0
+        assert fwd(Nq=nq, Nk=nk, D=D, dtype=dtype, Hq=1) == TOO_LARGE
+
+
 def test_fwd_empty_problems_launch_nothing(lib):
     # nothing to compute: RA_OK without touching the (fake) pointers or the GPU
     assert fwd(B=0) == OK
