@@ -23,12 +23,14 @@ def rel_to_max(gpu, ref):
     return float(np.abs(gpu - ref).max() / (den if den > 0 else 1.0))
 
 
-def assert_close(gpu, ref, dtype: str, what: str = "", fp32_tol=1e-5, bf16_tol=2e-2):
-    """fp32: max-abs error <= 1e-5 (relative-to-max when |ref| exceeds 1);
-    bf16: max|gpu - ref| / max|ref| <= 2e-2."""
+def assert_close(gpu, ref, dtype: str, what: str = "", grad=False, fp32_tol=1e-5, bf16_tol=2e-2):
+    """fp32: max-abs error <= 1e-5, absolute for outputs (O, p, rotated inputs); for gradients
+    (grad=True) relative to max|ref| when that exceeds 1, since the pages fix no gradient
+    tolerance and gradient magnitudes grow with the problem.
+    bf16: max|gpu - ref| / max|ref| <= 2e-2 (outputs and gradients)."""
     err_abs = float(np.abs(gpu - ref).max()) if gpu.size else 0.0
     if dtype == "f32":
-        scale = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
+        scale = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0) if grad else 1.0
         assert err_abs <= fp32_tol * scale, f"{what}: max abs err {err_abs:.3e}"
     else:
         r = rel_to_max(gpu, ref) if gpu.size else 0.0

@@ -1,6 +1,7 @@
 """GPU parity of ra_attn_fwd (through the C ABI) against the fp64 oracle.
 
-Tolerances: fp32 inputs max-abs 1e-5; bf16 inputs max|gpu - oracle| / max|oracle| <= 2e-2.
+Tolerances: fp32 inputs max-abs 1e-5 (absolute); bf16 inputs max|gpu - oracle| / max|oracle|
+<= 2e-2.  The full-size workloads are checked on every head in test_full_parity_gpu.py.
 """
 import numpy as np
 import pytest
@@ -70,22 +71,6 @@ def test_small_workloads_full(gpu_lib, name):
     o, stats = run_fwd(gpu_lib, inp, w.causal, w.scale, w.dtype)
     err = check_against_oracle(o, stats, inp, w.causal, w.scale, w.dtype, what=name)
     print(f"{name}: max abs err {err:.3e}")
-
-
-@pytest.mark.parametrize("name", ["bf16_causal_B8_H16_N2048_D64_sigma2",
-                                  "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope",
-                                  "bf16_causal_B4_H16_N8192_D128_fwd_bwd"])
-def test_large_workloads_sampled_heads(gpu_lib, name):
-    """Full-size launch (the bench configuration); the oracle checks whole heads, sampled."""
-    w = wl.WORKLOADS[name]
-    inp = wl.make_attention_inputs(w)
-    o, stats = run_fwd(gpu_lib, inp, w.causal, w.scale, w.dtype)
-    heads = [(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2 + 1)]
-    err = check_against_oracle(o, stats, inp, w.causal, w.scale, w.dtype, heads=heads, what=name)
-    assert np.isfinite(o).all()
-    # every row of every head: output bounded by the values it averages
-    assert np.abs(o).max() <= np.abs(inp["v"]).max() * (1 + 1e-2)
-    print(f"{name}: sampled heads max abs err {err:.3e}")
 
 
 # ----------------------------------------------------------------- edge shapes
@@ -208,7 +193,13 @@ def test_zero_support_pattern_via_identity_values(gpu_lib, causal, dtype, D):
             m = sm.max(axis=1, keepdims=True)
             delta = np.where(allowed, m - s, np.inf)
             es = score_error_bound(q[b, h].astype(np.float64), k[b, h].astype(np.float64), scale)
-            band = ULP16 + es + es[np.arange(N), sm.argmax(1)][:, None] + 64 * U32 * 16
+            # phi = 0 on the GPU iff 1 + u = fma(s, -c, kd) >= 2 (c = scale / 16, kd = 1 + m c):
+            # beside the score errors of s and m, the rounding of kd and of 1 + u (half an ulp
+            # each, at most 2^-23 for values below 4) and the reciprocal's error (one ulp of 0.5,
+            # 2^-22 in units of 1 + u) move the edge by at most 2^-21 in 1 + u, 16 * 2^-21 =
+            # 8 * 2^-24 * 16 in Delta; kd < 4 needs a scaled row max below 48
+            assert np.nanmax(m) < 48
+            band = ULP16 + es + es[np.arange(N), sm.argmax(1)][:, None] + 8 * U32 * 16
             bad, mism = zero_pattern_mismatches(o[b, h], p_ora[b, h], delta, band)
             total_bad += bad
             total_mism += mism

@@ -32,7 +32,7 @@ def upstream(shape, dtype, seed):
 
 def check(dx, x, dp, dtype, what):
     ref = oracle.ra_softmax_rows_bwd(x.astype(np.float64), dp.astype(np.float64))
-    assert_close(dx, ref, dtype, what)
+    assert_close(dx, ref, dtype, what, grad=True)
     return rel_to_max(dx, ref)
 
 
@@ -106,11 +106,11 @@ def test_autograd_wrapper(gpu_lib):
     p = gpu_lib.ra_softmax(xt, dim=-1)
     p.backward(torch.from_numpy(dp).cuda())
     ref = oracle.ra_softmax_rows_bwd(x.astype(np.float64), dp.astype(np.float64))
-    assert_close(xt.grad.cpu().numpy().astype(np.float64), ref, "f32", "autograd")
+    assert_close(xt.grad.cpu().numpy().astype(np.float64), ref, "f32", "autograd", grad=True)
     # along another dimension: the same rows, transposed
     xt2 = torch.from_numpy(np.ascontiguousarray(x.T)).cuda().requires_grad_()
     gpu_lib.ra_softmax(xt2, dim=0).backward(torch.from_numpy(np.ascontiguousarray(dp.T)).cuda())
-    assert_close(xt2.grad.cpu().numpy().T.astype(np.float64), ref, "f32", "autograd dim=0")
+    assert_close(xt2.grad.cpu().numpy().T.astype(np.float64), ref, "f32", "autograd dim=0", grad=True)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
