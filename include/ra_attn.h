@@ -210,6 +210,26 @@ int ra_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_
                      int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream);
 
 /*
+ * ra_attn_bwd_noalloc -- ra_attn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight training loops, harnesses that
+ * forbid hipMalloc.  The call allocates nothing; the per-row terms ra_attn_bwd keeps in its
+ * workspace go to a fixed 64 MiB array inside the library instead, one copy per device, held from
+ * the library's first use on that device until the process ends.
+ *   Limit: ra_attn_bwd_workspace_bytes(...) <= 64 MiB, i.e. B * Hq * Nq <= 1,864,128 query rows
+ *   (36 bytes each plus 256) -> else RA_ERR_TOO_LARGE, nothing launched.
+ *   Every call on one device shares that device's array, which keeps the last call's contents:
+ *   calls that overlap on one device (on other streams or from other threads) race, and the caller
+ *   must order them (calls on one stream are ordered by the stream).
+ *   Arguments, checks, sizes and results as ra_attn_bwd (the same kernels: the outputs equal
+ *   ra_attn_bwd's bit for bit).  A failure to resolve the array's device address returns
+ *   RA_ERR_HIP.
+ */
+int ra_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* d_o, const float* stats, void* dq, void* dk, void* dv,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                        int causal, float scale, int dtype, void* stream);
+
+/*
  * ra_attn_decode_workspace_bytes -- scratch size ra_attn_decode needs for these sizes (0 when the
  * sizes are invalid for it or there is nothing to compute).  Caller-allocated, 256-byte aligned,
  * contents need not be initialised.

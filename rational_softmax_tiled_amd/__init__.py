@@ -3,6 +3,7 @@
 A thin ctypes binding over ``libra_attn.so``.  The functions named like the C entry points
 (``ra_attn_fwd``, ``ra_attn_fwd_masked``, ``ra_attn_fwd_counted``, ``ra_attn_bwd``,
 ``ra_attn_bwd_masked``, ``ra_attn_bwd_dq``, ``ra_attn_bwd_dkdv``, ``ra_attn_bwd_workspace_bytes``,
+``ra_attn_bwd_noalloc``,
 ``ra_attn_decode``, ``ra_attn_decode_workspace_bytes``, ``ra_softmax_rows``,
 ``ra_softmax_rows_bwd``, ``ra_rope_neox``) only marshal arguments: tensors
 become device pointers, a mask becomes an ``ra_mask`` descriptor, the stream becomes a
@@ -27,7 +28,8 @@ __all__ = [
     "RA_MASK_NONE", "RA_MASK_BOOL", "RA_MASK_ADD", "RaMask", "RaError", "load_library",
     "library_path", "ra_status_string", "ra_attn_fwd", "ra_attn_fwd_masked",
     "ra_attn_fwd_counted", "ra_attn_bwd", "ra_attn_bwd_masked",
-    "ra_attn_bwd_dq", "ra_attn_bwd_dkdv", "ra_attn_bwd_workspace_bytes", "ra_attn_decode",
+    "ra_attn_bwd_dq", "ra_attn_bwd_dkdv", "ra_attn_bwd_workspace_bytes", "ra_attn_bwd_noalloc",
+    "ra_attn_decode",
     "ra_attn_decode_workspace_bytes", "attn_decode", "ra_softmax_rows",
     "ra_softmax_rows_bwd", "ra_rope_neox", "ra_rope",
     "attn_fwd", "attn_bwd", "ra_attention", "ra_softmax",
@@ -110,6 +112,10 @@ def load_library():
                                      _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                      ctypes.c_float, ctypes.c_int, _vp]
     lib.ra_attn_bwd_dkdv.restype = ctypes.c_int
+    lib.ra_attn_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                        _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_int, _vp]
+    lib.ra_attn_bwd_noalloc.restype = ctypes.c_int
     lib.ra_attn_decode_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
     lib.ra_attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.ra_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64,
@@ -221,6 +227,14 @@ def ra_attn_bwd_dkdv(q, k, v, d_o, stats, dk, dv, workspace, workspace_bytes, B,
                                            _ptr(dk), _ptr(dv), _ptr(workspace),
                                            int(workspace_bytes), B, Hq, Hkv, Nq, Nk, D,
                                            int(causal), float(scale), int(dtype), _stream(stream))
+
+
+def ra_attn_bwd_noalloc(q, k, v, o, d_o, stats, dq, dk, dv, B, Hq, Hkv, Nq, Nk, D, causal, scale,
+                        dtype, stream=None) -> int:
+    return load_library().ra_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o),
+                                              _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq,
+                                              Hkv, Nq, Nk, D, int(causal), float(scale),
+                                              int(dtype), _stream(stream))
 
 
 def ra_attn_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, dtype) -> int:

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ra_attn.h"
 #include "ra_device.h"
 #include "ra_internal.h"
@@ -138,6 +140,42 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* stat
 
 }  // namespace
 
+// ---- the backward for callers that cannot allocate device memory
+// Its per-row terms live in `scratch`, a fixed array of the library's code object (one copy per
+// device, held from the code object's load on that device until the process ends).  In host code
+// `scratch` only names the host-side shadow of the array; its device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current, and only that address
+// is passed to kernels.  Every call on a device shares the device's copy: calls that overlap on
+// one device race.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once resolved
+
+// Device address of `scratch` on the current device.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) return hip_status(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* ra_status_string(int status) {
@@ -261,6 +299,25 @@ int ra_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_
                      int64_t Nk, int64_t D, int causal, float scale, int dtype, void* stream) {
   return attn_bwd_common(q, k, v, nullptr, d_o, stats, nullptr, dk, dv, workspace, workspace_bytes,
                          B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, ra::kBwdDkdv, stream);
+}
+
+// ra_attn_bwd with its workspace in `scratch` (declared above); allocates nothing.
+int ra_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* d_o, const float* stats, void* dq, void* dk, void* dv,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                        int causal, float scale, int dtype, void* stream) {
+  int st = check_sizes(B, Hq, Hkv, Nq, Nk, D, scale, dtype);   // bounds the products below
+  if (st != RA_OK) return st;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (B * Hq * Nq > 0 && B * Hkv * Nk > 0) {   // the only case that uses a workspace
+    if (ra::bwd_workspace_bytes(B, Hq, Nq) > kNoallocScratchBytes) return RA_ERR_TOO_LARGE;
+    st = scratch_address(&ws);
+    if (st != RA_OK) return st;
+    ws_bytes = kNoallocScratchBytes;
+  }
+  return attn_bwd_common(q, k, v, o, d_o, stats, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, Nq, Nk, D,
+                         causal, scale, dtype, nullptr, ra::kBwdAll, stream);
 }
 
 // Decode: the query rows of one K/V head (rep * Nq) must fit one wave's 32 MFMA columns.

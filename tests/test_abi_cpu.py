@@ -88,6 +88,24 @@ def test_byte_offset_boundary(lib, dtype, es, D):
     for nq, nk in ((n_max + 1, 8), (8, n_max + 1)):
         assert ra.ra_attn_bwd_workspace_bytes(1, 1, 1, nq, nk, D, dtype) == 0
         assert fwd(Nq=nq, Nk=nk, D=D, dtype=dtype, Hq=1) == TOO_LARGE
+        assert ra.ra_attn_bwd_noalloc(P, P, P, P, P, None, P2, P2, P2, 1, 1, 1, nq, nk, D, 1,
+                                      0.125, dtype, 0) == TOO_LARGE
+
+
+def test_noalloc_rejects_beyond_its_array(lib):
+    """ra_attn_bwd_noalloc keeps 36 bytes per query row (plus 256) in a 64 MiB array: one row
+    more than fits is refused before anything is launched or resolved."""
+    rows = ((64 << 20) - 256) // 36
+    assert ra.ra_attn_bwd_workspace_bytes(1, 1, 1, rows, 8, 64, ra.RA_BF16) <= (64 << 20)
+    assert ra.ra_attn_bwd_workspace_bytes(1, 1, 1, rows + 1, 8, 64, ra.RA_BF16) > (64 << 20)
+    call = lambda B, Hq, Nq: ra.ra_attn_bwd_noalloc(P, P, P, P, P, None, P2, P2, P2, B, Hq, 1, Nq,
+                                                    8, 64, 1, 0.125, ra.RA_BF16, 0)
+    assert call(1, 1, rows + 1) == TOO_LARGE
+    assert call(7, 1, rows // 7 + 1) == TOO_LARGE
+    # nothing to compute needs no array: RA_OK without touching the GPU
+    assert call(0, 1, rows + 1) == OK
+    assert ra.ra_attn_bwd_noalloc(P, P, P, P, P, None, P2, P2, P2, 1, 1, 1, 8, 8, 64, 1, 0.125, 9,
+                                  0) == DTYPE
 
 
 def test_fwd_empty_problems_launch_nothing(lib):
