@@ -3,31 +3,36 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode fwd_bwd|fwd] [--no-cpu]
 
 A step is one forward (ra_attn_fwd) plus one backward (ra_attn_bwd) over the causal bf16
-workload B=4, H=16, N=8192, D=128 (inputs resident in HBM before timing starts).  The
-value is counted TFLOP/s: 4*B*Hq*Nq*Nk*D for the forward, halved when causal, times 3.5 for
-forward + backward.  Prints one JSON line.
+workload B=4, H=16, N=8192, D=128 (inputs resident in HBM before timing starts).  The value is
+counted TFLOP/s: 4*B*Hq*Nq*Nk*D for the forward, halved when causal, times 3.5 for forward +
+backward.  Prints one JSON line.
 
-Also reported: the forward alone on this workload and on the grouped-query workload
-(B=4, Hq=32, Hkv=8, N=4096, D=128, host RoPE), the two backward phases (ra_attn_bwd_dq,
-ra_attn_bwd_dkdv) alone, a padded batch through the explicit-mask entry points (B=4, H=16,
-N=4096, D=128, causal, key padding mask with per-sample lengths) beside the same workload
-unmasked, the split-KV decode step (B=16, Hq=32, Hkv=8, one query row per head, caches of up to
-16384 keys with per-sample lengths; HBM GB/s of the K/V bytes the lengths require), the row
-softmax and its backward at [16384, 8192], a roofline object for the
-dominant kernel (the longest of the forward, dQ and dK/dV kernels, each timed alone with HIP
-events on the stream the library launches it on) and the fp64 oracle timed on a bounded
-sample on the host cores.
+Also reported, each timed with HIP events on the stream the library launches on (5 warm-up
+calls, then at least 20 calls and at least 1 s; median, min and mean):
+  * every attention workload's forward (fp32 B=1 H=2 N=128 D=64 non-causal; bf16 causal
+    B=2 H=12 N=128 D=64; bf16 causal B=8 H=16 N=2048 D=64 with Q, K of sigma 2; bf16 causal
+    grouped-query B=4 Hq=32 Hkv=8 N=4096 D=128 with host RoPE; the step's workload), with the
+    skipped-tile fraction from ra_attn_fwd_counted and the SHA-256 of every input buffer;
+  * the step's forward, dQ and dK/dV kernels alone (ra_attn_fwd, ra_attn_bwd_dq,
+    ra_attn_bwd_dkdv) and a roofline object for the longest of them, the dominant kernel;
+  * a structured workload whose scores fall off away from the diagonal (whole tiles skipped)
+    beside an i.i.d. workload of the same shape (nothing skipped);
+  * the grouped-query forward with the NEOX rotation on the device, a padded batch through the
+    key padding path, the split-KV decode step, the row softmax and its backward;
+  * the fp64 oracle timed on a bounded sample of each workload on the host cores.
 
 Algorithmic work per visited score element (i, j), D = head dim: forward 4*D flops (S = QK^T
 and PV); dQ phase 6*D (S, dP = dO V^T, dQ += dS K); dK/dV phase 8*D (S, dP, dV += P^T dO,
-dK += dS^T Q).  A causal launch visits B*Hq*Nq*Nk/2 elements (the counting convention of
-the headline metric).
+dK += dS^T Q).  A causal launch visits B*Hq*Nq*Nk/2 elements (the counting convention of the
+headline metric).
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import os
+import platform
 import sys
 import time
 
@@ -38,8 +43,13 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+# VALU lane operations per second without packed fp32 instructions (the library is built
+# without them): 256 CUs x 64 lanes x 2.4 GHz.  Packed fp32 doubles it (the published fp32
+# vector peak of 157.3 TFLOP/s counts packed FMAs as four flops).
+PEAK_VALU_LANE_OPS = 256 * 64 * 2.4e9
 
 MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
+GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
 
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch) on the
 # main workload, each scaled by what the counter read for a plain copy of 256 MiB read + 256
@@ -55,12 +65,16 @@ TRAFFIC = {
     "attn_bwd_dkdv_bf16_kernel": ("9b3a2dbb18ee6b36d70d6c4f61ee3603c2d3caf4f48283efa1afbd9614afda05",
                                   267503.8, 262144.0),
 }
+# VALU instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU) of the forward on a workload,
+# for its VALU-roofline fraction; valid for the recorded kernel source only.
+VALU_INSTS = {
+    # workload: (sha256 of the forward's sources, SQ_INSTS_VALU per dispatch)
+}
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],
     "attn_bwd_dq_bf16_kernel": ["ra_bwd.hip", "ra_device.h"],
     "attn_bwd_dkdv_bf16_kernel": ["ra_bwd.hip", "ra_device.h"],
 }
-GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
 
 
 def parse():
@@ -70,8 +84,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", choices=["fwd_bwd", "fwd"], default="fwd_bwd")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--cpu-heads", type=int, default=3,
-                    help="(batch, head) pairs of the workload the oracle times")
+    ap.add_argument("--min-time", type=float, default=1.0,
+                    help="seconds each secondary measurement runs at least")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -84,11 +98,11 @@ def log(msg):
 class Attn:
     """Device-resident inputs/outputs of one workload and the C-ABI calls on them."""
 
-    def __init__(self, ra, w, need_grad):
+    def __init__(self, ra, w, need_grad, inp=None):
         import torch
         import workloads as wl
         self.ra, self.w = ra, w
-        inp = wl.make_attention_inputs(w)
+        inp = wl.make_attention_inputs(w) if inp is None else inp
         self.host = inp
         dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         dev = lambda a: torch.from_numpy(a).to(dt).cuda()   # exact: values are dtype-representable
@@ -103,54 +117,66 @@ class Attn:
             self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.stream = torch.cuda.current_stream()
 
+    def _ok(self, st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {self.ra.ra_status_string(st)}")
+
     def fwd(self):
         w = self.w
-        st = self.ra.ra_attn_fwd(self.q, self.k, self.v, self.o, self.stats, w.B, w.Hq, w.Hkv,
-                                 w.Nq, w.Nk, w.D, int(w.causal), w.scale, self.code, self.stream)
-        if st != 0:
-            raise RuntimeError(f"ra_attn_fwd: {self.ra.ra_status_string(st)}")
+        self._ok(self.ra.ra_attn_fwd(self.q, self.k, self.v, self.o, self.stats, w.B, w.Hq, w.Hkv,
+                                     w.Nq, w.Nk, w.D, int(w.causal), w.scale, self.code, self.stream),
+                 "ra_attn_fwd")
+
+    def fwd_counted(self):
+        """Skipped-tile counters of one forward: (wave tiles, wave tiles skipped, workgroup
+        tiles, workgroup tiles not loaded)."""
+        import torch
+        w = self.w
+        cnt = torch.zeros(4, dtype=torch.int64, device="cuda")
+        self._ok(self.ra.ra_attn_fwd_counted(self.q, self.k, self.v, self.o, self.stats, w.B, w.Hq,
+                                             w.Hkv, w.Nq, w.Nk, w.D, int(w.causal), w.scale,
+                                             self.code, cnt, self.stream), "ra_attn_fwd_counted")
+        torch.cuda.synchronize()
+        c = [int(x) for x in cnt.cpu().numpy()]
+        return {"wave_tiles": c[0], "wave_tiles_skipped": c[1],
+                "skipped_fraction": round(c[1] / c[0], 6) if c[0] else 0.0,
+                "workgroup_tiles": c[2], "workgroup_tiles_not_loaded": c[3],
+                "not_loaded_fraction": round(c[3] / c[2], 6) if c[2] else 0.0}
 
     def bwd(self):
         w = self.w
-        st = self.ra.ra_attn_bwd(self.q, self.k, self.v, self.o, self.do, self.stats, self.dq,
-                                 self.dk, self.dv, self.ws, self.ws_bytes, w.B, w.Hq, w.Hkv, w.Nq,
-                                 w.Nk, w.D, int(w.causal), w.scale, self.code, self.stream)
-        if st != 0:
-            raise RuntimeError(f"ra_attn_bwd: {self.ra.ra_status_string(st)}")
+        self._ok(self.ra.ra_attn_bwd(self.q, self.k, self.v, self.o, self.do, self.stats, self.dq,
+                                     self.dk, self.dv, self.ws, self.ws_bytes, w.B, w.Hq, w.Hkv, w.Nq,
+                                     w.Nk, w.D, int(w.causal), w.scale, self.code, self.stream),
+                 "ra_attn_bwd")
 
     def fwd_masked(self, mask, causal=None):
         w = self.w
         cc = int(w.causal) if causal is None else causal
-        st = self.ra.ra_attn_fwd_masked(self.q, self.k, self.v, self.o, self.stats, w.B, w.Hq,
-                                        w.Hkv, w.Nq, w.Nk, w.D, cc, w.scale, self.code,
-                                        *mask, self.stream)
-        if st != 0:
-            raise RuntimeError(f"ra_attn_fwd_masked: {self.ra.ra_status_string(st)}")
+        self._ok(self.ra.ra_attn_fwd_masked(self.q, self.k, self.v, self.o, self.stats, w.B, w.Hq,
+                                            w.Hkv, w.Nq, w.Nk, w.D, cc, w.scale, self.code,
+                                            *mask, self.stream), "ra_attn_fwd_masked")
 
     def bwd_masked(self, mask):
         w = self.w
-        st = self.ra.ra_attn_bwd_masked(self.q, self.k, self.v, self.o, self.do, self.stats,
-                                        self.dq, self.dk, self.dv, self.ws, self.ws_bytes, w.B,
-                                        w.Hq, w.Hkv, w.Nq, w.Nk, w.D, int(w.causal), w.scale,
-                                        self.code, *mask, self.stream)
-        if st != 0:
-            raise RuntimeError(f"ra_attn_bwd_masked: {self.ra.ra_status_string(st)}")
+        self._ok(self.ra.ra_attn_bwd_masked(self.q, self.k, self.v, self.o, self.do, self.stats,
+                                            self.dq, self.dk, self.dv, self.ws, self.ws_bytes, w.B,
+                                            w.Hq, w.Hkv, w.Nq, w.Nk, w.D, int(w.causal), w.scale,
+                                            self.code, *mask, self.stream), "ra_attn_bwd_masked")
 
     def bwd_dq(self):
         w = self.w
-        st = self.ra.ra_attn_bwd_dq(self.q, self.k, self.v, self.o, self.do, self.stats, self.dq,
-                                    self.ws, self.ws_bytes, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D,
-                                    int(w.causal), w.scale, self.code, self.stream)
-        if st != 0:
-            raise RuntimeError(f"ra_attn_bwd_dq: {self.ra.ra_status_string(st)}")
+        self._ok(self.ra.ra_attn_bwd_dq(self.q, self.k, self.v, self.o, self.do, self.stats, self.dq,
+                                        self.ws, self.ws_bytes, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D,
+                                        int(w.causal), w.scale, self.code, self.stream),
+                 "ra_attn_bwd_dq")
 
     def bwd_dkdv(self):
         w = self.w
-        st = self.ra.ra_attn_bwd_dkdv(self.q, self.k, self.v, self.do, self.stats, self.dk, self.dv,
-                                      self.ws, self.ws_bytes, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D,
-                                      int(w.causal), w.scale, self.code, self.stream)
-        if st != 0:
-            raise RuntimeError(f"ra_attn_bwd_dkdv: {self.ra.ra_status_string(st)}")
+        self._ok(self.ra.ra_attn_bwd_dkdv(self.q, self.k, self.v, self.do, self.stats, self.dk,
+                                          self.dv, self.ws, self.ws_bytes, w.B, w.Hq, w.Hkv, w.Nq,
+                                          w.Nk, w.D, int(w.causal), w.scale, self.code, self.stream),
+                 "ra_attn_bwd_dkdv")
 
 
 def source_digest(files):
@@ -170,41 +196,102 @@ def traffic_bytes(kernel):
     return int(rec[1] * 1024 * FETCH_SCALE + rec[2] * 1024 * WRITE_SCALE)
 
 
-def time_calls(stream, fn, n):
-    """Average duration (ms) of fn() over n calls, from HIP events recorded on `stream`."""
+def timed(stream, fn, min_s, min_calls=20, warm=5):
+    """Durations of fn() from HIP events recorded on `stream` around each call: `warm` untimed
+    calls, then batches until at least min_calls calls and min_s seconds are timed."""
     import torch
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
-    for i in range(n):
-        ev[2 * i].record(stream)
+    for _ in range(warm):
         fn()
-        ev[2 * i + 1].record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]))
+    times = []
+    while len(times) < min_calls or sum(times) < 1e3 * min_s:
+        n = max(min_calls - len(times), 10)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for i in range(n):
+            ev[2 * i].record(stream)
+            fn()
+            ev[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        times += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]
+        if len(times) >= 20000:
+            break
+    t = np.asarray(times)
+    return {"median_ms": round(float(np.median(t)), 5), "min_ms": round(float(t.min()), 5),
+            "mean_ms": round(float(t.mean()), 5), "calls": int(t.size)}
 
 
-def cpu_baseline(w, heads, mode):
-    """The fp64 oracle on `heads` (batch, head) pairs of workload w (bounded sample)."""
-    import oracle
+def tflops(flops, ms):
+    return flops / (ms * 1e-3) / 1e12
+
+
+def environment():
+    import torch
+    dev = torch.cuda.get_device_properties(0)
+    env = {"device": dev.name, "arch": getattr(dev, "gcnArchName", None),
+           "compute_units": dev.multi_processor_count, "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None), "rocm": None, "sclk_mhz": None,
+           "host": platform.node(), "host_cpus": os.cpu_count()}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            env["rocm"] = fh.read().strip()
+    except OSError:
+        pass
+    # shader clock levels of the card (the one marked * is current); max = the part's peak
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            levels = open(path).read().split("\n")
+        except OSError:
+            continue
+        mhz = [int(l.split(":")[1].strip().split("Mhz")[0]) for l in levels if "Mhz" in l]
+        cur = [int(l.split(":")[1].strip().split("Mhz")[0]) for l in levels if "*" in l]
+        if mhz:
+            env["sclk_mhz"] = {"max": max(mhz), "current": cur[0] if cur else None}
+            break
+    return env
+
+
+def cpu_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = None, None
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+        for d in threadpoolctl.threadpool_info():
+            if d.get("user_api") == "blas":
+                blas = f"{d.get('internal_api')} {d.get('version')}"
+                threads = d.get("num_threads")
+                break
     except Exception:                      # pragma: no cover
-        cores = os.cpu_count() or 1
-    import workloads as wl
-    sub = wl.AttnWorkload(w.name + "_sample", w.dtype, w.causal, 1, heads, heads, w.Nq, w.Nk,
-                          w.D, seed=w.seed, with_grad=True)
-    inp = wl.make_attention_inputs(sub)
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas": blas,
+            "blas_threads": threads}
+
+
+def oracle_time(w, inp, heads, with_bwd):
+    """Wall time of the fp64 oracle on the first `heads` (batch 0) query heads of workload w
+    (with their K/V heads), forward or forward + backward, and the counted TFLOP/s."""
+    import oracle
+    rep = w.Hq // w.Hkv
+    nkv = (heads + rep - 1) // rep
+    q, k, v = inp["q"][:1, :heads], inp["k"][:1, :nkv], inp["v"][:1, :nkv]
+    reps = 0
     t0 = time.perf_counter()
-    oracle.ra_attention_fwd(inp["q"], inp["k"], inp["v"], w.causal, w.scale)
-    if mode == "fwd_bwd":
-        oracle.ra_attention_bwd(inp["q"], inp["k"], inp["v"], inp["do"], w.causal, w.scale)
-    dt = time.perf_counter() - t0
-    flops = sub.counted_flops_fwd_bwd() if mode == "fwd_bwd" else sub.counted_flops_fwd()
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.Hq} (batch, head) pairs of {w.name}, "
-                      f"{'forward+backward' if mode == 'fwd_bwd' else 'forward'}, fp64 NumPy, "
-                      f"{dt:.1f} s", "seconds": dt}
+    while True:          # small samples are repeated until a measurable time has passed
+        oracle.ra_attention_fwd(q, k, v, w.causal, w.scale)
+        if with_bwd:
+            oracle.ra_attention_bwd(q, k, v, inp["do"][:1, :heads], w.causal, w.scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 0.25:
+            break
+    f = w.counted_flops_fwd() * heads / (w.B * w.Hq) * (3.5 if with_bwd else 1.0)
+    return dt / reps, f * reps / dt / 1e12
 
 
 def main():
@@ -217,8 +304,10 @@ def main():
     import rational_softmax_tiled_amd as ra
     import workloads as wl
     ra.load_library()
-    dev = torch.cuda.get_device_properties(0)
-    log(f"device {dev.name} CUs={dev.multi_processor_count} arch={getattr(dev, 'gcnArchName', '?')}")
+    env = environment()
+    log(f"device {env['device']} CUs={env['compute_units']} arch={env['arch']} rocm={env['rocm']} "
+        f"sclk={env['sclk_mhz']}")
+    min_s = args.min_time
 
     if args.copy_calibration:
         # a plain copy kernel of known size: 256 MiB read + 256 MiB written
@@ -230,10 +319,14 @@ def main():
         log("copy calibration: 268435456 bytes read, 268435456 bytes written")
         del src, dst
 
-    w = wl.WORKLOADS[MAIN]
     need_grad = args.mode == "fwd_bwd"
+    cpu_samples = {}            # workload -> (inputs, heads, with_bwd) for the oracle leg
+
+    # ---- the step (the headline measurement)
+    w = wl.WORKLOADS[MAIN]
     log(f"generating {w.name}")
-    main_run = Attn(ra, w, need_grad)
+    main_inp = wl.make_attention_inputs(w)
+    main_run = Attn(ra, w, need_grad, inp=main_inp)
     stream = main_run.stream
 
     def step():
@@ -255,77 +348,118 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
     flops_step = w.counted_flops_fwd_bwd() if need_grad else w.counted_flops_fwd()
-    value = flops_step / (ms_step * 1e-3) / 1e12
+    value = tflops(flops_step, ms_step)
     log(f"step {ms_step:.3f} ms ({wall:.2f} s wall for {args.steps} steps): {value:.1f} TFLOP/s")
+    step_t = timed(stream, step, min_s, warm=0)
+    log(f"step per call: median {step_t['median_ms']:.3f} ms, min {step_t['min_ms']:.3f} ms")
 
-    # per-entry-point durations over the same kind of calls
-    n_k = max(5, args.steps)
-    fwd_ms = time_calls(stream, main_run.fwd, n_k)
-    fwd_tflops = w.counted_flops_fwd() / (fwd_ms * 1e-3) / 1e12
-    log(f"forward {fwd_ms:.3f} ms: {fwd_tflops:.1f} TFLOP/s")
+    # ---- the step's kernels alone (one launch per entry-point call)
     elems = w.B * w.Hq * w.Nq * w.Nk / (2 if w.causal else 1)   # visited score elements
-    # (name, C entry point, ms per launch, algorithmic flops per launch)
-    kernels = [("attn_fwd_kernel", "ra_attn_fwd", fwd_ms, 4 * w.D * elems)]
-    bwd_ms = dq_ms = dkdv_ms = None
+    fwd_t = timed(stream, main_run.fwd, min_s)
+    # (name, C entry point, timing, algorithmic flops per launch)
+    kernels = [("attn_fwd_kernel", "ra_attn_fwd", fwd_t, 4 * w.D * elems)]
     if need_grad:
-        bwd_ms = time_calls(stream, main_run.bwd, n_k)
-        log(f"backward {bwd_ms:.3f} ms")
-        dq_ms = time_calls(stream, main_run.bwd_dq, n_k)       # leaves the row terms in place
-        dkdv_ms = time_calls(stream, main_run.bwd_dkdv, n_k)
-        log(f"backward phases: dQ {dq_ms:.3f} ms, dK/dV {dkdv_ms:.3f} ms")
-        kernels += [("attn_bwd_dq_bf16_kernel", "ra_attn_bwd_dq", dq_ms, 6 * w.D * elems),
-                    ("attn_bwd_dkdv_bf16_kernel", "ra_attn_bwd_dkdv", dkdv_ms, 8 * w.D * elems)]
+        bwd_t = timed(stream, main_run.bwd, min_s)
+        dq_t = timed(stream, main_run.bwd_dq, min_s)        # leaves the row terms in place
+        dkdv_t = timed(stream, main_run.bwd_dkdv, min_s)
+        log(f"backward {bwd_t['median_ms']:.3f} ms: dQ {dq_t['median_ms']:.3f} ms, "
+            f"dK/dV {dkdv_t['median_ms']:.3f} ms")
+        kernels += [("attn_bwd_dq_bf16_kernel", "ra_attn_bwd_dq", dq_t, 6 * w.D * elems),
+                    ("attn_bwd_dkdv_bf16_kernel", "ra_attn_bwd_dkdv", dkdv_t, 8 * w.D * elems)]
+    main_skip = main_run.fwd_counted()
     del main_run
     torch.cuda.empty_cache()
 
-    log(f"generating {GQA}")
+    # ---- every attention workload's forward
+    configs = {}
+    for name in wl.WORKLOAD_ORDER:
+        wc = wl.WORKLOADS[name]
+        if name == MAIN:
+            inp, t = main_inp, fwd_t
+            skip = main_skip
+        else:
+            log(f"generating {name}")
+            inp = wl.make_attention_inputs(wc)
+            run = Attn(ra, wc, False, inp=inp)
+            t = timed(run.stream, run.fwd, min_s)
+            skip = run.fwd_counted()
+            del run
+            torch.cuda.empty_cache()
+        tf = tflops(wc.counted_flops_fwd(), t["median_ms"])
+        configs[name] = {
+            "pass": "fwd", "dtype": wc.dtype, "causal": wc.causal, "B": wc.B, "Hq": wc.Hq,
+            "Hkv": wc.Hkv, "N": wc.Nq, "D": wc.D, "seed": wc.seed, **t,
+            "tflops": round(tf, 3), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 5),
+            "skip": skip, "inputs_sha256": wl.storage_sha256(inp, wc.dtype)}
+        rec = VALU_INSTS.get(name)
+        if rec is not None and rec[0] == source_digest(KERNEL_SOURCES["attn_fwd_kernel"]):
+            lane_ops = rec[1] * 64
+            configs[name]["valu"] = {
+                "lane_ops_per_launch": lane_ops, "peak_lane_ops_per_s": PEAK_VALU_LANE_OPS,
+                "frac": round(lane_ops / (t["median_ms"] * 1e-3) / PEAK_VALU_LANE_OPS, 4)}
+        if name == MAIN and need_grad:
+            configs[name]["fwd_bwd"] = {**step_t, "tflops": round(tflops(flops_step, step_t["median_ms"]), 3)}
+        log(f"{name}: forward median {t['median_ms']:.4f} ms ({tf:.1f} TFLOP/s), "
+            f"skipped tiles {skip['skipped_fraction']:.4f}")
+        heads = {"fp32_noncausal_B1_H2_N128_D64": 2, "bf16_causal_B2_H12_N128_D64": 12,
+                 "bf16_causal_B8_H16_N2048_D64_sigma2": 8, GQA: 4, MAIN: 3}[name]
+        cpu_samples[name] = (wc, inp, heads, name == MAIN and need_grad)
+
+    # ---- tile skipping: the structured workload beside an i.i.d. one of the same shape
+    loc = wl.LOCAL
+    wloc = wl.AttnWorkload("bf16_causal_local_B1_H16_N2048_D64_amp4", "bf16", True, loc["B"],
+                           loc["H"], loc["H"], loc["N"], loc["N"], loc["D"], seed=loc["seed"])
+    inp_loc = wl.make_local_inputs(B=loc["B"], H=loc["H"], N=loc["N"], D=loc["D"],
+                                   amplitude=loc["amplitude"], seed=loc["seed"])
+    runl = Attn(ra, wloc, False, inp=inp_loc)
+    tl = timed(runl.stream, runl.fwd, min_s)
+    skl = runl.fwd_counted()
+    del runl
+    runi = Attn(ra, wl.LOCAL_IID, False)
+    ti = timed(runi.stream, runi.fwd, min_s)
+    ski = runi.fwd_counted()
+    del runi
+    torch.cuda.empty_cache()
+    local = {"workload": wloc.name, "inputs": "Q = K = RoPE(4 c + 0.5 e), one c per head",
+             "with_skipping": {**tl, "skip": skl},
+             "iid_same_shape": {"workload": wl.LOCAL_IID.name, **ti, "skip": ski},
+             "speedup": round(ti["median_ms"] / tl["median_ms"], 3)}
+    log(f"local workload: {tl['median_ms']:.4f} ms with {skl['skipped_fraction']:.3f} of wave tiles "
+        f"skipped; i.i.d. same shape {ti['median_ms']:.4f} ms")
+
+    # ---- grouped-query forward with the rotation on the device
     wg = wl.WORKLOADS[GQA]
     gqa = Attn(ra, wg, False)
-    for _ in range(3):
-        gqa.fwd()
-    gqa_ms = time_calls(gqa.stream, gqa.fwd, n_k)
-    gqa_tflops = wg.counted_flops_fwd() / (gqa_ms * 1e-3) / 1e12
-    log(f"GQA forward {gqa_ms:.3f} ms: {gqa_tflops:.1f} TFLOP/s")
-    # the same workload with the NEOX rotation of Q and K done on the device (in place; the
-    # inputs are then rotated again each call, which changes values but not the work)
+
     def rope_qk():
         for t, H in ((gqa.q, wg.Hq), (gqa.k, wg.Hkv)):
             st = ra.ra_rope_neox(t, t, None, wg.B * H, wg.Nq, wg.D, 10000.0, False, gqa.code, gqa.stream)
             if st != 0:
                 raise RuntimeError(f"ra_rope_neox: {ra.ra_status_string(st)}")
-    for _ in range(3):
-        rope_qk()
-    rope_ms = time_calls(gqa.stream, rope_qk, n_k)
+    rope_t = timed(gqa.stream, rope_qk, min_s)
     rope_bytes = 2 * (gqa.q.numel() + gqa.k.numel()) * gqa.q.element_size()
-    rope_gbs = rope_bytes / (rope_ms * 1e-3) / 1e9
-    log(f"GQA device RoPE on Q and K {rope_ms:.3f} ms: {rope_gbs:.0f} GB/s; forward incl. RoPE "
-        f"{gqa_ms + rope_ms:.3f} ms")
+    rope_gbs = rope_bytes / (rope_t["median_ms"] * 1e-3) / 1e9
+    gqa_ms = configs[GQA]["median_ms"]
+    log(f"GQA device RoPE on Q and K {rope_t['median_ms']:.3f} ms: {rope_gbs:.0f} GB/s; forward incl. "
+        f"RoPE {gqa_ms + rope_t['median_ms']:.3f} ms")
     del gqa
     torch.cuda.empty_cache()
 
-    # explicit-mask path: a padded batch, key padding mask [B, N] (1 = attend) on top of causal
+    # ---- explicit-mask path: a padded batch, key padding mask [B, N] (1 = attend), causal
     wp = wl.padded_batch_workload()
-    log(f"generating {wp.name}")
     pad = Attn(ra, wp, True)
     keep = torch.from_numpy(wl.padded_batch_keep(wp)).cuda()
     kpm = (keep, ra.RA_MASK_BOOL, (wp.Nk, 0, 0, 1))
-    pad_masked = lambda: (pad.fwd_masked(kpm), pad.bwd_masked(kpm))
-    pad_plain = lambda: (pad.fwd(), pad.bwd())
-    for _ in range(3):
-        pad_masked()
-        pad_plain()
-    pm_ms = time_calls(pad.stream, pad_masked, n_k)
-    pp_ms = time_calls(pad.stream, pad_plain, n_k)
-    pmf_ms = time_calls(pad.stream, lambda: pad.fwd_masked(kpm), n_k)
-    pm_tflops = wp.counted_flops_fwd_bwd() / (pm_ms * 1e-3) / 1e12
-    log(f"padded batch (key padding, causal) fwd+bwd {pm_ms:.3f} ms ({pm_tflops:.1f} TFLOP/s "
-        f"counted as the unmasked causal workload), forward {pmf_ms:.3f} ms; unmasked {pp_ms:.3f} ms")
+    pm_t = timed(pad.stream, lambda: (pad.fwd_masked(kpm), pad.bwd_masked(kpm)), min_s)
+    pp_t = timed(pad.stream, lambda: (pad.fwd(), pad.bwd()), min_s)
+    pmf_t = timed(pad.stream, lambda: pad.fwd_masked(kpm), min_s)
+    log(f"padded batch fwd+bwd {pm_t['median_ms']:.3f} ms (forward {pmf_t['median_ms']:.3f} ms); "
+        f"unmasked {pp_t['median_ms']:.3f} ms")
     del pad, keep
     torch.cuda.empty_cache()
 
-    # split-KV decode: one query row per head against caches of per-sample lengths (HBM-bound)
+    # ---- split-KV decode: one query row per head against caches of per-sample lengths
     wd = wl.decode_workload()
-    log(f"generating {wd.name}")
     dec = Attn(ra, wd, False)
     lens_np = wl.decode_seqlens(wd)
     lens = torch.from_numpy(lens_np).cuda()
@@ -338,62 +472,63 @@ def main():
                                dec.code, dec.stream)
         if st != 0:
             raise RuntimeError(f"ra_attn_decode: {ra.ra_status_string(st)}")
-    for _ in range(3):
-        decode_step()
-    dec_ms = time_calls(dec.stream, decode_step, max(20, n_k))
+    dec_t = timed(dec.stream, decode_step, min_s)
     kv_bytes = int(lens_np.astype(np.int64).sum()) * wd.Hkv * wd.D * 2 * dec.q.element_size()
-    dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
-    # the same step through the tiled forward, the cache lengths as a key padding mask
+    dec_gbs = kv_bytes / (dec_t["median_ms"] * 1e-3) / 1e9
     keep = torch.arange(wd.Nk, device="cuda")[None, :] < lens[:, None]
     kpm = (keep, ra.RA_MASK_BOOL, (wd.Nk, 0, 0, 1))
     br = ra.RA_CAUSAL_BOTTOM_RIGHT   # one query row: every key below the sample's length
-    for _ in range(2):
-        dec.fwd_masked(kpm, br)
-    decf_ms = time_calls(dec.stream, lambda: dec.fwd_masked(kpm, br), n_k)
-    log(f"decode {wd.name}: {dec_ms:.4f} ms, {dec_gbs:.0f} GB/s of K/V ({kv_bytes / 2**20:.0f} MiB); "
-        f"tiled forward with the lengths as a mask {decf_ms:.4f} ms")
+    decf_t = timed(dec.stream, lambda: dec.fwd_masked(kpm, br), min_s)
+    log(f"decode: {dec_t['median_ms']:.4f} ms, {dec_gbs:.0f} GB/s of K/V; tiled forward with the "
+        f"lengths as a mask {decf_t['median_ms']:.4f} ms")
     del dec, dws, keep
     torch.cuda.empty_cache()
 
-    # row softmax (HBM-bound): read + write once
+    # ---- row softmax and its backward (HBM-bound)
     x = torch.from_numpy(wl.make_rows(16384, 8192, seed=11)).cuda()
     p = torch.empty_like(x)
-    sm = lambda: ra.ra_softmax_rows(x, p, 16384, 8192, ra.RA_F32, stream)
-    for _ in range(3):
-        sm()
-    sm_ms = time_calls(stream, sm, n_k)
-    sm_gbs = 2 * x.numel() * 4 / (sm_ms * 1e-3) / 1e9
-    log(f"softmax rows [16384, 8192] fp32 {sm_ms:.3f} ms: {sm_gbs:.0f} GB/s")
-    # its backward (x and dp read, dx written once)
+    sm_t = timed(stream, lambda: ra.ra_softmax_rows(x, p, 16384, 8192, ra.RA_F32, stream), min_s)
+    sm_gbs = 2 * x.numel() * 4 / (sm_t["median_ms"] * 1e-3) / 1e9
     g = torch.from_numpy(np.random.default_rng(12).standard_normal((16384, 8192), dtype=np.float32)).cuda()
     dx = torch.empty_like(x)
-    smb = lambda: ra.ra_softmax_rows_bwd(x, g, dx, 16384, 8192, ra.RA_F32, stream)
-    for _ in range(3):
-        smb()
-    smb_ms = time_calls(stream, smb, n_k)
-    smb_gbs = 3 * x.numel() * 4 / (smb_ms * 1e-3) / 1e9
-    log(f"softmax rows backward [16384, 8192] fp32 {smb_ms:.3f} ms: {smb_gbs:.0f} GB/s")
-    del g, dx
+    smb_t = timed(stream, lambda: ra.ra_softmax_rows_bwd(x, g, dx, 16384, 8192, ra.RA_F32, stream), min_s)
+    smb_gbs = 3 * x.numel() * 4 / (smb_t["median_ms"] * 1e-3) / 1e9
+    log(f"softmax rows {sm_t['median_ms']:.3f} ms ({sm_gbs:.0f} GB/s), backward "
+        f"{smb_t['median_ms']:.3f} ms ({smb_gbs:.0f} GB/s)")
+    del x, p, g, dx
 
-    # dominant kernel: the longest launch of the step (one launch per entry-point call)
-    dom_name, dom_call, dom_ms, dom_flops = max(kernels, key=lambda t: t[2])
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    # ---- dominant kernel: the longest launch of the step (one launch per entry-point call)
+    dom_name, dom_call, dom_t, dom_flops = max(kernels, key=lambda t: t[2]["mean_ms"])
+    achieved = tflops(dom_flops, dom_t["mean_ms"])
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_bytes(dom_name), "kernel": f"{dom_name} ({dom_call})",
-                "avg_launch_ms": round(dom_ms, 4),
+                "avg_launch_ms": dom_t["mean_ms"], "median_launch_ms": dom_t["median_ms"],
                 "flops_per_launch": dom_flops}
-    kernel_table = {n: {"ms": round(t, 4), "tflops": round(f / (t * 1e-3) / 1e12, 2),
+    kernel_table = {n: {**t, "tflops": round(tflops(f, t["median_ms"]), 2),
                         "traffic": traffic_bytes(n),
-                        "frac_of_peak": round(f / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                        "frac_of_peak": round(tflops(f, t["median_ms"]) / PEAK_BF16_TFLOPS, 4)}
                     for n, _, t, f in kernels}
 
+    # ---- the oracle on the host cores (bounded samples)
     cpu = None
     if not args.no_cpu:
-        log("timing the fp64 oracle on a bounded sample")
-        cpu = cpu_baseline(w, args.cpu_heads, args.mode)
-        log(f"oracle: {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s on {cpu['cores']} threads")
-        cpu.pop("seconds")
+        info = cpu_info()
+        per = {}
+        for name, (wc, inp, heads, with_bwd) in cpu_samples.items():
+            dt, tf = oracle_time(wc, inp, heads, with_bwd)
+            gpu_tf = configs[name]["fwd_bwd"]["tflops"] if with_bwd else configs[name]["tflops"]
+            per[name] = {"heads": heads, "of_heads": wc.B * wc.Hq,
+                         "pass": "fwd_bwd" if with_bwd else "fwd", "seconds": round(dt, 3),
+                         "tflops": round(tf, 6), "gpu_over_oracle": round(gpu_tf / tf, 1)}
+            log(f"oracle {name}: {heads} heads in {dt:.2f} s ({tf:.5f} TFLOP/s)")
+        m = per[MAIN]
+        cpu = {"value": m["tflops"], "unit": "TFLOP/s", "cores": info["blas_threads"] or info["os_cpu_count"],
+               "kind": "oracle",
+               "sample": f"{m['heads']} of {m['of_heads']} (batch, head) pairs of {MAIN}, "
+                         f"{'forward+backward' if m['pass'] == 'fwd_bwd' else 'forward'}, fp64 NumPy "
+                         f"with the full score matrix, {m['seconds']} s; scaled by heads",
+               **info, "per_workload": per}
 
     out = {
         "metric": "ra_attention fwd & fwd+bwd TFLOP/s (bf16, causal) + % of MFMA bf16 peak",
@@ -409,29 +544,30 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "pass": args.mode, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "seq_len": w.Nq, "head_dim": w.D, "causal": w.causal, "global_batch": w.B},
+                   "seq_len": w.Nq, "head_dim": w.D, "causal": w.causal, "global_batch": w.B,
+                   "seed": w.seed},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd": {"workload": w.name, "ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),
-                "frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4)},
-        "bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
+        "step": step_t,
+        "fwd": {"workload": w.name, **fwd_t, "tflops": round(tflops(w.counted_flops_fwd(), fwd_t["median_ms"]), 2),
+                "frac_of_peak": round(tflops(w.counted_flops_fwd(), fwd_t["median_ms"]) / PEAK_BF16_TFLOPS, 4)},
+        "bwd": bwd_t if need_grad else None,
         "kernels": kernel_table,
-        "fwd_gqa": {"workload": wg.name, "ms": round(gqa_ms, 4), "tflops": round(gqa_tflops, 2),
-                    "frac_of_peak": round(gqa_tflops / PEAK_BF16_TFLOPS, 4),
-                    "device_rope_ms": round(rope_ms, 4), "device_rope_GB/s": round(rope_gbs, 1)},
+        "configs": configs,
+        "tile_skipping": local,
+        "fwd_gqa_device_rope": {"workload": wg.name, "rope": rope_t, "rope_GB/s": round(rope_gbs, 1),
+                                "fwd_plus_rope_ms": round(gqa_ms + rope_t["median_ms"], 4)},
         "masked_padded_batch": {"workload": wp.name, "lengths": list(wl.padded_batch_lengths(wp)),
                                 "mask": "key padding [B, N] bool, causal top-left",
-                                "fwd_bwd_ms": round(pm_ms, 4), "fwd_ms": round(pmf_ms, 4),
-                                "tflops_counted": round(pm_tflops, 2),
-                                "unmasked_fwd_bwd_ms": round(pp_ms, 4)},
-        "decode": {"workload": wd.name, "entry": "ra_attn_decode", "ms": round(dec_ms, 4),
-                   "kv_bytes": kv_bytes, "GB/s": round(dec_gbs, 1),
-                   "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
-                   "tiled_fwd_masked_ms": round(decf_ms, 4)},
-        "softmax_rows": {"shape": [16384, 8192], "dtype": "f32", "ms": round(sm_ms, 4),
-                         "GB/s": round(sm_gbs, 1), "frac_of_hbm_peak": round(sm_gbs / PEAK_HBM_GBS, 4)},
-        "softmax_rows_bwd": {"shape": [16384, 8192], "dtype": "f32", "ms": round(smb_ms, 4),
-                             "GB/s": round(smb_gbs, 1),
+                                "fwd_bwd": pm_t, "fwd": pmf_t, "unmasked_fwd_bwd": pp_t,
+                                "tflops_counted": round(tflops(wp.counted_flops_fwd_bwd(), pm_t["median_ms"]), 2)},
+        "decode": {"workload": wd.name, "entry": "ra_attn_decode", **dec_t, "kv_bytes": kv_bytes,
+                   "GB/s": round(dec_gbs, 1), "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+                   "tiled_fwd_masked": decf_t},
+        "softmax_rows": {"shape": [16384, 8192], "dtype": "f32", **sm_t, "GB/s": round(sm_gbs, 1),
+                         "frac_of_hbm_peak": round(sm_gbs / PEAK_HBM_GBS, 4)},
+        "softmax_rows_bwd": {"shape": [16384, 8192], "dtype": "f32", **smb_t, "GB/s": round(smb_gbs, 1),
                              "frac_of_hbm_peak": round(smb_gbs / PEAK_HBM_GBS, 4)},
+        "environment": env,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

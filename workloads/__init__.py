@@ -199,3 +199,19 @@ def make_rows(rows: int, cols: int, sigma: float = 4.0, seed: int = 11, dtype: s
 
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def storage_sha256(inp: dict, dtype: str) -> dict:
+    """SHA-256 of each input buffer as the device stores it (bf16 bits or fp32 bytes)."""
+    out = {}
+    for name, a in inp.items():
+        raw = f32_to_bf16_bits(a) if dtype == "bf16" else np.ascontiguousarray(a, dtype=np.float32)
+        out[name] = sha256(raw)
+    return out
+
+
+# The structured workload that exercises tile skipping (make_local_inputs), at the size the
+# measurements use, beside an i.i.d. workload of the same shape in which no tile skips.
+LOCAL = dict(B=1, H=16, N=2048, D=64, amplitude=4.0, seed=7)
+LOCAL_IID = AttnWorkload("bf16_causal_B1_H16_N2048_D64_iid", "bf16", True, 1, 16, 16, 2048, 2048,
+                         64, seed=8)
