@@ -134,8 +134,10 @@ int ra_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, flo
 /*
  * ra_attn_fwd_counted -- ra_attn_fwd plus tile-skip counters (diagnostics, not for timing).
  *   counters: device pointer to 4 uint64, which the call ADDS to (zero them first):
- *     [0] (wave, key-tile) pairs inside the causal range of the second pass,
- *     [1] of those, pairs skipped because every entry lies outside the support,
+ *     [0] (wave, key-tile) pairs inside the causal range of the second pass (a wave holds 32
+ *         query rows, a key tile 64 keys for bf16 and 32 for fp32),
+ *     [1] of those, pairs skipped because every entry lies outside the support (skipped by the
+ *         wave alone or by its whole workgroup),
  *     [2] (workgroup, key-tile) pairs of the second pass,
  *     [3] of those, tiles whose K/V load was skipped for the whole workgroup.
  *   Everything else as ra_attn_fwd.

@@ -360,10 +360,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   auto v_land = [&](T* dst) {
     if constexpr (!VTR) vreg.template store<PV>(dst, tid);
   };
+  // counting variant: a tile the whole workgroup drops is a skipped tile of every wave whose
+  // causal range holds it
+  auto count_dropped = [&](int lo, int hi) {
+    if (COUNT) {
+      n_wg_skip += hi - lo;
+      const int in_range = max(0, min(hi, nt_w) - lo);
+      n_wave_tiles += in_range;
+      n_wave_skip += in_range;
+    }
+  };
   int cur = 0;
   while (cur < nt && wg_skips(cur)) ++cur;
   cur = uniform(cur);   // every lane computed the same index from the same LDS values
-  if (COUNT) n_wg_skip += cur;
+  count_dropped(0, cur);
   if (cur < nt) {
     k_issue(cur, k_lds[0]);
     if constexpr (WRITE_O) v_issue(cur, v_lds[0]);
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     int nxt = cur + 1;
     while (nxt < nt && wg_skips(nxt)) ++nxt;
     nxt = uniform(nxt);
-    if (COUNT) n_wg_skip += nxt - cur - 1;
+    count_dropped(cur + 1, nxt);
     if (nxt < nt) {
       k_issue(nxt, k_lds[buf ^ 1]);
       if constexpr (WRITE_O) v_issue(nxt, v_lds[buf ^ 1]);
@@ -547,6 +557,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     }
   }
 }
+
 
 template <typename T, int D, int BN>
 static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,

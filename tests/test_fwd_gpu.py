@@ -217,6 +217,9 @@ def test_tile_skipping_structured_workload(gpu_lib):
     print(f"counters: wave tiles {cnt[0]}, skipped {cnt[1]}, wg tiles {cnt[2]}, wg skipped {cnt[3]}")
     assert cnt[1] > 0 and cnt[3] > 0
     assert cnt[1] <= cnt[0] and cnt[3] <= cnt[2]
+    # every (wave, key tile) pair inside the causal range is counted, dropped or not: a wave owns
+    # 32 query rows q0..q0+31 and sees the 64-key tiles below ceil((q0 + 32) / 64)
+    assert cnt[0] == 4 * sum(-(-(q0 + 32) // 64) for q0 in range(0, 2048, 32))
     check_against_oracle(o, stats, inp, True, 0.125, "bf16", heads=[(0, 0), (0, 3)], what="local")
     # the counting variant computes the same bits as the plain one
     o2, s2 = run_fwd(gpu_lib, inp, True, 0.125, "bf16")
