@@ -163,10 +163,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   const int last_task = min(wig * kWaves + kWaves - 1, a.tasks_per_group - 1);
   const int wg_qmax = min((last_task / a.rep) * kRowsPerWave + kRowsPerWave - 1, a.Nq - 1);
   const int key_end = max(0, min(a.Nk, wg_qmax + a.coff + 1));
-  const int nt = (key_end + BN - 1) / BN;
+  // tile counts of the workgroup and of the wave: the same in every lane of a wave, read from the
+  // first lane so that the tile loops and skip tests branch on scalar registers
+  const int nt = uniform((key_end + BN - 1) / BN);
   const int wave_qmax = min(q0 + kRowsPerWave - 1, a.Nq - 1);
   const int key_end_w = !active ? 0 : max(0, min(a.Nk, wave_qmax + a.coff + 1));
-  const int nt_w = (key_end_w + BN - 1) / BN;
+  const int nt_w = uniform((key_end_w + BN - 1) / BN);
 
   const T* qh = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h) * a.Nq * D;
   const T* kg = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Nk * D;
@@ -332,17 +334,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   __syncthreads();
 
   // A tile is skipped for a wave when every entry has 1 + u >= fma(tile max, -c, min kd) >= 2
-  // (phi = 0), and not even loaded when that holds for all four waves.
+  // (phi = 0), and not even loaded when that holds for all four waves.  The tests are evaluated
+  // for 64 tiles at once, one tile per lane, and kept as bits in scalar registers: evaluated per
+  // tile they were chains of dependent LDS reads at the head of every step.
+  float kmin_w[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) kmin_w[w] = kmin_lds[w];
   auto wave_skips = [&](int w, int kt) -> bool {
     const float tm = tmax_lds[w][kt];
-    return (tm == -INFINITY) || (fmaf(tm, -a.c, kmin_lds[w]) >= 2.0f);
+    return (tm == -INFINITY) || (fmaf(tm, -a.c, kmin_w[w]) >= 2.0f);
+  };
+  unsigned long long wg_bits = 0, my_bits = 0;   // window win: skipped by all waves / this wave
+  int win = -1;
+  auto load_window = [&](int kt) {
+    if ((kt >> 6) == win) return;
+    win = kt >> 6;
+    const int t = (kt & ~63) + lane;
+    bool all = false, mine = t >= nt_w;
+    if (t < kMaxTiles) {
+      const bool s0 = wave_skips(0, t), s1 = wave_skips(1, t), s2 = wave_skips(2, t), s3 = wave_skips(3, t);
+      all = s0 && s1 && s2 && s3;
+      mine = wave == 0 ? s0 : wave == 1 ? s1 : wave == 2 ? s2 : s3;
+    }
+    wg_bits = __ballot(all);
+    my_bits = __ballot(mine);
   };
   auto wg_skips = [&](int kt) -> bool {
-    if (kt >= kMaxTiles) return false;
-    bool all = true;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) all = all && wave_skips(w, kt);
-    return all;
+    load_window(kt);
+    return (wg_bits >> (kt & 63)) & 1ull;
   };
 
   // ---- pass 2: phi, sum(phi), O^T = V^T P^T
@@ -392,22 +411,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     while (nxt < nt && wg_skips(nxt)) ++nxt;
     nxt = uniform(nxt);
     count_dropped(cur + 1, nxt);
-    if (nxt < nt) {
-      k_issue(nxt, k_lds[buf ^ 1]);
-      if constexpr (WRITE_O) v_issue(nxt, v_lds[buf ^ 1]);
-    }
-    const bool my_skip = uniform(cur < kMaxTiles ? wave_skips(wave, cur) : cur >= nt_w);
+    load_window(cur);
+    const bool my_skip = (my_bits >> (cur & 63)) & 1ull;
     if (COUNT && cur < nt_w) {
       n_wave_tiles += 1;
       n_wave_skip += my_skip ? 1 : 0;
     }
     bool done = my_skip;
+    const bool fast = VTR && WRITE_O && SB == 2 && !done && !needs_mask(cur * BN + 32) && keys_full;
+    if (nxt < nt) {
+      k_issue(nxt, k_lds[buf ^ 1]);
+      if constexpr (WRITE_O) v_issue(nxt, v_lds[buf ^ 1]);
+    }
     if constexpr (VTR && WRITE_O && SB == 2) {
       // Unmasked tile: one straight-line block whose issue order is pinned so that the wave's
       // own VALU work overlaps its own MFMAs (issue is in order): S1 products run under the phi
       // math of block 0, the P.V products of block 0 under the phi math of block 1, and LDS
       // reads run ahead of the products that consume them.
-      if (!done && !needs_mask(cur * BN + 32) && keys_full) {
+      if (fast) {
         constexpr int NV = 2 * DB;            // P.V products (and V fragments) per 32-key block
         constexpr int EB = 16 / KC;           // phi elements per S1 product (stage B)
         constexpr int EC = 16 / NV;           // phi elements per P.V0 product (stage C)
