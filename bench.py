@@ -17,8 +17,10 @@ calls, then at least 20 calls and at least 1 s; median, min and mean):
     ra_attn_bwd_dkdv) and a roofline object for the longest of them, the dominant kernel;
   * a structured workload whose scores fall off away from the diagonal (whole tiles skipped)
     beside an i.i.d. workload of the same shape (nothing skipped);
-  * the grouped-query forward with the NEOX rotation on the device, a padded batch through the
-    key padding path, the split-KV decode step, the row softmax and its backward;
+  * the grouped-query workload with the NEOX rotation on the device: forward and backward,
+    unfused (rotation passes plus the attention) beside the fused entry points
+    (ra_attn_fwd_rope, ra_attn_bwd_rope); a padded batch through the key padding path, the
+    split-KV decode step, the row softmax and its backward;
   * the fp64 oracle timed on a bounded sample of each workload on the host cores.
 
 Algorithmic work per visited score element (i, j), D = head dim: forward 4*D flops (S = QK^T
@@ -427,22 +429,63 @@ def main():
     log(f"local workload: {tl['median_ms']:.4f} ms with {skl['skipped_fraction']:.3f} of wave tiles "
         f"skipped; i.i.d. same shape {ti['median_ms']:.4f} ms")
 
-    # ---- grouped-query forward with the rotation on the device
+    # ---- grouped-query attention with the rotation on the device: unfused (two rotation passes,
+    # then the attention) beside the fused entry points (Q rotated inside the attention kernel)
     wg = wl.WORKLOADS[GQA]
-    gqa = Attn(ra, wg, False)
+    gqa = Attn(ra, wg, True, inp=wl.make_unrotated_inputs(wg))
+    q_rot, k_rot = torch.empty_like(gqa.q), torch.empty_like(gqa.k)
+    dims = (wg.B, wg.Hq, wg.Hkv, wg.Nq, wg.Nk, wg.D)
+    theta = wg.rope_theta
+
+    def ok(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {ra.ra_status_string(st)}")
 
     def rope_qk():
-        for t, H in ((gqa.q, wg.Hq), (gqa.k, wg.Hkv)):
-            st = ra.ra_rope_neox(t, t, None, wg.B * H, wg.Nq, wg.D, 10000.0, False, gqa.code, gqa.stream)
-            if st != 0:
-                raise RuntimeError(f"ra_rope_neox: {ra.ra_status_string(st)}")
+        for x, y, H in ((gqa.q, q_rot, wg.Hq), (gqa.k, k_rot, wg.Hkv)):
+            ok(ra.ra_rope_neox(x, y, None, wg.B * H, wg.Nq, wg.D, theta, False, gqa.code, gqa.stream),
+               "ra_rope_neox")
+
+    def unfused_fwd():
+        rope_qk()
+        ok(ra.ra_attn_fwd(q_rot, k_rot, gqa.v, gqa.o, gqa.stats, *dims, 1, wg.scale, gqa.code,
+                          gqa.stream), "ra_attn_fwd")
+
+    def fused_fwd(qr=True):
+        ok(ra.ra_attn_fwd_rope(gqa.q, gqa.k, gqa.v, gqa.o, gqa.stats, q_rot if qr else None, k_rot,
+                               None, None, theta, *dims, 1, wg.scale, gqa.code, gqa.stream),
+           "ra_attn_fwd_rope")
+
+    def unfused_bwd():
+        ok(ra.ra_attn_bwd(q_rot, k_rot, gqa.v, gqa.o, gqa.do, gqa.stats, gqa.dq, gqa.dk, gqa.dv,
+                          gqa.ws, gqa.ws_bytes, *dims, 1, wg.scale, gqa.code, gqa.stream), "ra_attn_bwd")
+        for t, H in ((gqa.dq, wg.Hq), (gqa.dk, wg.Hkv)):
+            ok(ra.ra_rope_neox(t, t, None, wg.B * H, wg.Nq, wg.D, theta, True, gqa.code, gqa.stream),
+               "ra_rope_neox")
+
+    def fused_bwd():
+        ok(ra.ra_attn_bwd_rope(q_rot, k_rot, gqa.v, gqa.o, gqa.do, gqa.stats, gqa.dq, gqa.dk, gqa.dv,
+                               gqa.ws, gqa.ws_bytes, None, None, theta, *dims, 1, wg.scale, gqa.code,
+                               gqa.stream), "ra_attn_bwd_rope")
+
     rope_t = timed(gqa.stream, rope_qk, min_s)
     rope_bytes = 2 * (gqa.q.numel() + gqa.k.numel()) * gqa.q.element_size()
     rope_gbs = rope_bytes / (rope_t["median_ms"] * 1e-3) / 1e9
-    gqa_ms = configs[GQA]["median_ms"]
-    log(f"GQA device RoPE on Q and K {rope_t['median_ms']:.3f} ms: {rope_gbs:.0f} GB/s; forward incl. "
-        f"RoPE {gqa_ms + rope_t['median_ms']:.3f} ms")
-    del gqa
+    unf_t = timed(gqa.stream, unfused_fwd, min_s)
+    fus_t = timed(gqa.stream, fused_fwd, min_s)
+    fus_nq_t = timed(gqa.stream, lambda: fused_fwd(False), min_s)
+    fused_fwd()
+    unfb_t = timed(gqa.stream, unfused_bwd, min_s)
+    fusb_t = timed(gqa.stream, fused_bwd, min_s)
+    log(f"GQA RoPE: rotation of Q and K {rope_t['median_ms']:.3f} ms ({rope_gbs:.0f} GB/s); forward "
+        f"unfused {unf_t['median_ms']:.3f} ms, fused {fus_t['median_ms']:.3f} ms (without q_rot "
+        f"{fus_nq_t['median_ms']:.3f}); backward unfused {unfb_t['median_ms']:.3f} ms, fused "
+        f"{fusb_t['median_ms']:.3f} ms")
+    rope_out = {"workload": wg.name, "inputs": "Q, K unrotated; theta 10000, positions 0..N-1",
+                "rotation_q_k": rope_t, "rotation_GB/s": round(rope_gbs, 1),
+                "fwd_unfused": unf_t, "fwd_fused": fus_t, "fwd_fused_without_q_rot": fus_nq_t,
+                "bwd_unfused": unfb_t, "bwd_fused": fusb_t}
+    del gqa, q_rot, k_rot
     torch.cuda.empty_cache()
 
     # ---- explicit-mask path: a padded batch, key padding mask [B, N] (1 = attend), causal
@@ -554,8 +597,7 @@ def main():
         "kernels": kernel_table,
         "configs": configs,
         "tile_skipping": local,
-        "fwd_gqa_device_rope": {"workload": wg.name, "rope": rope_t, "rope_GB/s": round(rope_gbs, 1),
-                                "fwd_plus_rope_ms": round(gqa_ms + rope_t["median_ms"], 4)},
+        "gqa_device_rope": rope_out,
         "masked_padded_batch": {"workload": wp.name, "lengths": list(wl.padded_batch_lengths(wp)),
                                 "mask": "key padding [B, N] bool, causal top-left",
                                 "fwd_bwd": pm_t, "fwd": pmf_t, "unmasked_fwd_bwd": pp_t,

@@ -300,13 +300,62 @@ int ra_softmax_rows_bwd(const void* x, const void* dp, void* dx, int64_t rows, i
  *   position p_n of row n and pair j < D/2, with angle = p_n * theta^(-2j/D):
  *     y[n, j] = x[n, j] cos - x[n, j + D/2] sin,  y[n, j + D/2] = x[n, j + D/2] cos + x[n, j] sin.
  *   inverse != 0 rotates by -angle: the transpose, which maps dL/dy to dL/dx.
- *   positions: device int32 [N], or NULL for 0..N-1.  Angles are formed in fp64; the products
- *   run in fp32 and round once to dtype.  y may be x (in place); other overlaps are not allowed.
+ *   positions: device int32 [N], or NULL for 0..N-1.  The angle is formed and reduced to
+ *   [-pi, pi] in fp64; its cosine and sine, and the products, run in fp32, and the result rounds
+ *   once to dtype.  y may be x (in place); other overlaps are not allowed.
  *   Errors: D odd -> RA_ERR_HEADDIM; theta not finite or <= 0 -> RA_ERR_SCALE; N * D >= 2^31
  *   -> RA_ERR_TOO_LARGE; mats, N or D == 0 -> RA_OK, nothing launched.
  */
 int ra_rope_neox(const void* x, void* y, const int32_t* positions, int64_t mats, int64_t N,
                  int64_t D, double theta, int inverse, int dtype, void* stream);
+
+/*
+ * ra_attn_fwd_rope -- ra_attn_fwd on queries and keys rotated by the NEOX rotary embedding,
+ * with the query rotation done inside the attention kernel as its rows are loaded.
+ *   Source: nurl page, section "Layers" (nn_rope applied to the queries and keys ahead of the
+ *   attention core), "Primitives" page, section "Attention and transformers" (split-halves
+ *   pairing), Ra-Family page, section 3, item ra_attention.
+ *   Result: bit-identical to ra_rope_neox(q -> q_rot), ra_rope_neox(k -> k_rot), then
+ *   ra_attn_fwd(q_rot, k_rot, v): the query rows the kernel multiplies are the bf16 rows
+ *   ra_rope_neox would produce.
+ *   q: [B, Hq, Nq, D] and k: [B, Hkv, Nk, D], unrotated.  k_rot: caller's [B, Hkv, Nk, D] buffer
+ *   that receives the rotated keys (one rotation pass over K before the attention kernel); it
+ *   may be k itself (k is then overwritten).  q_rot: optional [B, Hq, Nq, D] (NULL to skip)
+ *   that receives the rotated queries, for ra_attn_bwd_rope; it must not overlap q.
+ *   q_positions: device int32 [Nq], k_positions: int32 [Nk], or NULL for 0..N-1, shared by
+ *   every batch and head; they set the rotation only (the causal mode still compares row and
+ *   key indices).  theta: the base of the frequency schedule theta^(-2j/D).
+ *   o, stats, causal, scale: as ra_attn_fwd, on the rotated rows.
+ *   dtype: RA_BF16 only (RA_ERR_DTYPE otherwise).  No mask.  theta not finite or <= 0 ->
+ *   RA_ERR_SCALE.  Sizes, limits and the other errors as ra_attn_fwd; k_rot NULL with Nk > 0
+ *   -> RA_ERR_NULLPTR.  Nk == 0: o = 0, stats (-inf, 0), and q_rot is still written.
+ */
+int ra_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* stats,
+                     void* q_rot, void* k_rot, const int32_t* q_positions,
+                     const int32_t* k_positions, double theta, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype,
+                     void* stream);
+
+/*
+ * ra_attn_bwd_rope -- the backward of ra_attn_fwd_rope: the gradients with respect to the
+ * UNROTATED q and k, and v.
+ *   Source: as ra_attn_fwd_rope; the rotation is orthogonal, so the gradient of a rotated row
+ *   maps back by the rotation with the negative angle.
+ *   q_rot, k_rot: the rotated rows ra_attn_fwd_rope wrote (q_rot requested there).  v, o, d_o,
+ *   stats (nullable: recomputed), workspace, workspace_bytes (ra_attn_bwd_workspace_bytes),
+ *   causal, scale: as ra_attn_bwd.  q_positions, k_positions, theta: those of the forward.
+ *   dq [B, Hq, Nq, D], dk [B, Hkv, Nk, D]: rotated back inside the kernels' epilogues (each
+ *   element is the fp32 accumulator rotated by the negative angle, rounded once to bf16);
+ *   dv as ra_attn_bwd.
+ *   dtype: RA_BF16 only.  Errors as ra_attn_bwd, plus RA_ERR_DTYPE and RA_ERR_SCALE as
+ *   ra_attn_fwd_rope.
+ */
+int ra_attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const void* o,
+                     const void* d_o, const float* stats, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, const int32_t* q_positions,
+                     const int32_t* k_positions, double theta, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype,
+                     void* stream);
 
 #ifdef __cplusplus
 }

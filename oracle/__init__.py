@@ -10,6 +10,8 @@ from .ra_oracle import (  # noqa: F401
     ra_attention_bwd,
     ra_attention_decode,
     ra_attention_fwd,
+    ra_attention_rope_bwd,
+    ra_attention_rope_fwd,
     ra_phi,
     ra_softmax_rows,
     ra_softmax_rows_bwd,

@@ -61,6 +61,9 @@ __all__ = [
     "ra_attention_fwd",
     "ra_attention_bwd",
     "ra_attention_decode",
+    "ra_attention_rope_fwd",
+    "ra_attention_rope_bwd",
+    "rope_neox",
 ]
 
 # Delta at which phi reaches exactly zero (the compact support edge, u = 1).
@@ -344,3 +347,31 @@ def ra_attention_bwd(q, k, v, do, causal, scale, groups=None, mask=None, argmax=
             dk[b, g] += scale * (ds.T @ q[b, h])
             dv[b, g] += p.T @ do[b, h]
     return dq, dk, dv
+
+
+def ra_attention_rope_fwd(q, k, v, causal, scale, theta, q_rope_positions=None,
+                          k_rope_positions=None):
+    """Attention on rotated queries and keys: O = ra_attention(rope(Q), rope(K), V).
+
+    The nurl page, section "Layers", applies nn_rope to the queries and keys of
+    a head before the attention core; the "Primitives" page, section "Attention
+    and transformers", gives the split-halves pairing.  The rotation positions
+    (default 0..N-1) are independent of the causal test, which uses row and key
+    indices as in ra_attention_fwd.  Returns (O, m, l, a) as ra_attention_fwd.
+    """
+    qr = rope_neox(q, theta, q_rope_positions)
+    kr = rope_neox(k, theta, k_rope_positions)
+    return ra_attention_fwd(qr, kr, v, causal, scale)
+
+
+def ra_attention_rope_bwd(q, k, v, do, causal, scale, theta, q_rope_positions=None,
+                          k_rope_positions=None, groups=None, argmax=None):
+    """Gradients (dQ, dK, dV) of L = sum(O * dO) for ra_attention_rope_fwd, with respect to the
+    UNROTATED q and k: the attention gradients of the rotated inputs, each mapped back by the
+    transpose of its rotation (the rotation by the negative angle).  ``groups`` and ``argmax``
+    as in ra_attention_bwd."""
+    qr = rope_neox(q, theta, q_rope_positions)
+    kr = rope_neox(k, theta, k_rope_positions)
+    dqr, dkr, dv = ra_attention_bwd(qr, kr, v, do, causal, scale, groups=groups, argmax=argmax)
+    return (rope_neox(dqr, theta, q_rope_positions, inverse=True),
+            rope_neox(dkr, theta, k_rope_positions, inverse=True), dv)

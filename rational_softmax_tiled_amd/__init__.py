@@ -31,8 +31,9 @@ __all__ = [
     "ra_attn_bwd_dq", "ra_attn_bwd_dkdv", "ra_attn_bwd_workspace_bytes", "ra_attn_bwd_noalloc",
     "ra_attn_decode",
     "ra_attn_decode_workspace_bytes", "attn_decode", "ra_softmax_rows",
-    "ra_softmax_rows_bwd", "ra_rope_neox", "ra_rope",
-    "attn_fwd", "attn_bwd", "ra_attention", "ra_softmax",
+    "ra_softmax_rows_bwd", "ra_rope_neox", "ra_rope", "ra_attn_fwd_rope", "ra_attn_bwd_rope",
+    "attn_fwd", "attn_bwd", "attn_fwd_rope", "attn_bwd_rope", "ra_attention", "ra_attention_rope",
+    "ra_softmax",
 ]
 
 RA_F32 = 0
@@ -129,6 +130,15 @@ def load_library():
     lib.ra_rope_neox.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int,
                                  ctypes.c_int, _vp]
     lib.ra_rope_neox.restype = ctypes.c_int
+    lib.ra_attn_fwd_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_double,
+                                     _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                     ctypes.c_float, ctypes.c_int, _vp]
+    lib.ra_attn_fwd_rope.restype = ctypes.c_int
+    lib.ra_attn_bwd_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp, _vp, ctypes.c_double, _i64, _i64, _i64,
+                                     _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                     _vp]
+    lib.ra_attn_bwd_rope.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -498,6 +508,114 @@ def ra_rope(x, theta: float = 10000.0, positions=None, inverse: bool = False):
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("ra_rope supports float32 and bfloat16")
     return _RopeFn.get().apply(x, float(theta), positions, bool(inverse))
+
+
+def ra_attn_fwd_rope(q, k, v, o, stats, q_rot, k_rot, q_positions, k_positions, theta, B, Hq, Hkv,
+                     Nq, Nk, D, causal, scale, dtype, stream=None) -> int:
+    return load_library().ra_attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(stats),
+                                           _ptr(q_rot), _ptr(k_rot), _ptr(q_positions),
+                                           _ptr(k_positions), float(theta), B, Hq, Hkv, Nq, Nk, D,
+                                           int(causal), float(scale), int(dtype), _stream(stream))
+
+
+def ra_attn_bwd_rope(q_rot, k_rot, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes,
+                     q_positions, k_positions, theta, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype,
+                     stream=None) -> int:
+    return load_library().ra_attn_bwd_rope(_ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(o), _ptr(d_o),
+                                           _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv),
+                                           _ptr(workspace), workspace_bytes, _ptr(q_positions),
+                                           _ptr(k_positions), float(theta), B, Hq, Hkv, Nq, Nk, D,
+                                           int(causal), float(scale), int(dtype), _stream(stream))
+
+
+def _positions(p, n, device):
+    import torch
+    if p is None:
+        return None
+    t = torch.as_tensor(p, dtype=torch.int32, device=device).contiguous()
+    if t.numel() != n:
+        raise ValueError(f"positions must have {n} entries")
+    return t
+
+
+def attn_fwd_rope(q, k, v, causal, theta: float = 10000.0, scale: Optional[float] = None,
+                  q_positions=None, k_positions=None, with_rotated: bool = True):
+    """Allocate O, stats, the rotated keys (and queries) and run ra_attn_fwd_rope on the current
+    stream.  Returns (o, stats, q_rot or None, k_rot)."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, D = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    stats = torch.empty((B, Hq, Nq, 2), dtype=torch.float32, device=q.device)
+    q_rot = torch.empty_like(q) if with_rotated else None
+    k_rot = torch.empty_like(k)
+    qp, kp = _positions(q_positions, Nq, q.device), _positions(k_positions, Nk, q.device)
+    _check(ra_attn_fwd_rope(q, k, v, o, stats, q_rot, k_rot, qp, kp, theta, B, Hq, Hkv, Nq, Nk, D,
+                            causal_code(causal), scale, _dtype_code(q)), "ra_attn_fwd_rope")
+    return o, stats, q_rot, k_rot
+
+
+def attn_bwd_rope(q_rot, k_rot, v, o, d_o, stats, causal, theta: float = 10000.0,
+                  scale: Optional[float] = None, q_positions=None, k_positions=None):
+    """Allocate dQ, dK, dV and a workspace and run ra_attn_bwd_rope on the current stream: the
+    gradients with respect to the unrotated q and k."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, D = _shapes(q_rot, k_rot, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    d_o = d_o.contiguous()
+    dq, dk, dv = torch.empty_like(q_rot), torch.empty_like(k_rot), torch.empty_like(v)
+    code = _dtype_code(q_rot)
+    nbytes = ra_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, code)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q_rot.device)
+    qp, kp = _positions(q_positions, Nq, q_rot.device), _positions(k_positions, Nk, q_rot.device)
+    _check(ra_attn_bwd_rope(q_rot, k_rot, v, o, d_o, stats, dq, dk, dv, ws, nbytes, qp, kp, theta,
+                            B, Hq, Hkv, Nq, Nk, D, causal_code(causal), scale, code),
+           "ra_attn_bwd_rope")
+    return dq, dk, dv
+
+
+class _RopeAttentionFn:
+    _cls = None
+
+    @classmethod
+    def get(cls):
+        if cls._cls is None:
+            import torch
+
+            class Fn(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, q, k, v, causal, theta, scale, q_positions, k_positions):
+                    o, stats, q_rot, k_rot = attn_fwd_rope(q, k, v, causal, theta, scale,
+                                                           q_positions, k_positions)
+                    ctx.save_for_backward(q_rot, k_rot, v, o, stats)
+                    ctx.args = (causal, theta, scale, q_positions, k_positions)
+                    return o
+
+                @staticmethod
+                def backward(ctx, d_o):
+                    q_rot, k_rot, v, o, stats = ctx.saved_tensors
+                    causal, theta, scale, qp, kp = ctx.args
+                    dq, dk, dv = attn_bwd_rope(q_rot, k_rot, v, o, d_o, stats, causal, theta, scale,
+                                               qp, kp)
+                    return dq, dk, dv, None, None, None, None, None
+
+            cls._cls = Fn
+        return cls._cls
+
+
+def ra_attention_rope(q, k, v, is_causal=False, theta: float = 10000.0,
+                      scale: Optional[float] = None, q_positions=None, k_positions=None):
+    """ra_attention on q and k rotated by the NEOX rotary embedding (ra_rope), the query rotation
+    fused into the attention kernel.  q, k unrotated, bf16, shapes and causal modes as
+    ra_attention; positions default to 0..N-1.  Differentiable in q, k and v (the gradients
+    are with respect to the unrotated q and k)."""
+    import torch
+    if q.dtype != torch.bfloat16:
+        raise TypeError("ra_attention_rope supports bfloat16")
+    D = q.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    return _RopeAttentionFn.get().apply(q, k, v, causal_code(is_causal), float(theta), scale,
+                                        q_positions, k_positions)
 
 
 def _softmax_rows_2d(x):

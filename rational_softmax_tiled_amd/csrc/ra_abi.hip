@@ -233,7 +233,8 @@ static int attn_bwd_common(const void* q, const void* k, const void* v, const vo
                            const void* d_o, const float* stats, void* dq, void* dk, void* dv,
                            const void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq,
                            int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
-                           int dtype, const ra_mask* mask, int phases, void* stream) {
+                           int dtype, const ra_mask* mask, int phases, void* stream,
+                           const ra::RopeArgs* rope = nullptr) {
   int st = check_sizes(B, Hq, Hkv, Nq, Nk, D, scale, dtype);
   if (st != RA_OK) return st;
   st = check_mask(mask, causal, B, Hq, Nq, Nk, dtype);
@@ -264,6 +265,12 @@ static int attn_bwd_common(const void* q, const void* k, const void* v, const vo
     return st;
   }
   ra::AttnProblem p = make_problem(q, k, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, mask);
+  if (rope != nullptr) {
+    p.rope = true;
+    p.rope_theta = rope->theta;
+    p.q_pos = rope->q_pos;
+    p.k_pos = rope->k_pos;
+  }
   ra::BwdWorkspace ws = ra::bwd_workspace_layout(const_cast<void*>(workspace), B, Hq, Nq);
   return hip_status(ra::launch_attn_bwd(p, o, d_o, stats, dq, dk, dv, ws, phases, s));
 }
@@ -318,6 +325,68 @@ int ra_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void*
   }
   return attn_bwd_common(q, k, v, o, d_o, stats, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, Nq, Nk, D,
                          causal, scale, dtype, nullptr, ra::kBwdAll, stream);
+}
+
+// ---- attention with the NEOX rotary embedding fused in
+static int check_rope(double theta, int dtype, const int32_t* q_positions, const int32_t* k_positions) {
+  if (dtype != RA_BF16) return RA_ERR_DTYPE;
+  if (!(theta > 0.0) || !isfinite(theta)) return RA_ERR_SCALE;
+  if ((q_positions != nullptr && !aligned(q_positions, 4)) || (k_positions != nullptr && !aligned(k_positions, 4)))
+    return RA_ERR_ALIGN;
+  return RA_OK;
+}
+
+int ra_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* stats, void* q_rot,
+                     void* k_rot, const int32_t* q_positions, const int32_t* k_positions, double theta,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                     float scale, int dtype, void* stream) {
+  int st = check_sizes(B, Hq, Hkv, Nq, Nk, D, scale, dtype);
+  if (st != RA_OK) return st;
+  st = check_mask(nullptr, causal, B, Hq, Nq, Nk, dtype);
+  if (st != RA_OK) return st;
+  st = check_rope(theta, dtype, q_positions, k_positions);
+  if (st != RA_OK) return st;
+  const int64_t rows = B * Hq * Nq;
+  if (rows == 0) return RA_OK;
+  if (q == nullptr || o == nullptr) return RA_ERR_NULLPTR;
+  if (Nk > 0 && (k == nullptr || v == nullptr || k_rot == nullptr)) return RA_ERR_NULLPTR;
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q_rot, 16) ||
+      !aligned(k_rot, 16))
+    return RA_ERR_ALIGN;
+  if (stats != nullptr && !aligned(stats, 4)) return RA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (Nk == 0) {   // no key: o = 0; the rotated queries are still produced when asked for
+    st = fill_zero(o, (size_t)rows * D, dtype, s);
+    if (st == RA_OK && stats != nullptr)
+      st = hip_status(ra::launch_fill_pairs(stats, -INFINITY, 0.0f, (size_t)rows, s));
+    if (st == RA_OK && q_rot != nullptr)
+      st = hip_status(ra::launch_rope_neox(q, q_rot, q_positions, B * Hq, Nq, D, theta, false, true, s));
+    return st;
+  }
+  // K once, by the standalone rotation, into k_rot; Q in the attention kernel, on load
+  st = hip_status(ra::launch_rope_neox(k, k_rot, k_positions, B * Hkv, Nk, D, theta, false, true, s));
+  if (st != RA_OK) return st;
+  ra::AttnProblem p = make_problem(q, k_rot, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr);
+  p.rope = true;
+  p.rope_theta = theta;
+  p.q_pos = q_positions;
+  p.q_rot = q_rot;
+  return hip_status(ra::launch_attn_fwd(p, o, stats, nullptr, s));
+}
+
+int ra_attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const void* o,
+                     const void* d_o, const float* stats, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, const int32_t* q_positions, const int32_t* k_positions,
+                     double theta, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                     int causal, float scale, int dtype, void* stream) {
+  int st = check_rope(theta, dtype, q_positions, k_positions);
+  if (st != RA_OK) return st;
+  ra::RopeArgs rope;
+  rope.theta = theta;
+  rope.q_pos = q_positions;
+  rope.k_pos = k_positions;
+  return attn_bwd_common(q_rot, k_rot, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes, B, Hq,
+                         Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, ra::kBwdAll, stream, &rope);
 }
 
 // Decode: the query rows of one K/V head (rep * Nq) must fit one wave's 32 MFMA columns.

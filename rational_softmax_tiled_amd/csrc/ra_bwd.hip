@@ -73,7 +73,49 @@ struct BwdArgs {
   float scale, c16;                              // c16 = scale / 16
   int coff;        // causal diagonal: key j allowed for query row i iff j <= i + coff
   MaskArgs mask;   // explicit mask (MASKED kernels)
+  // ROPE kernels: q and k hold the rotated rows, and dQ, dK are turned back by the inverse rotation
+  // before they are stored (rows at q_pos, keys at k_pos; nullable: 0..N-1)
+  const int* q_pos;
+  const int* k_pos;
+  double log2_theta;
 };
+
+// Stores the channels a lane holds of one dQ or dK row (row pointer at channel 0) after turning
+// them back by the inverse rotary embedding: element 4 r4 + e of acc[db] is channel
+// db*32 + 8 r4 + 4 (lane/32) + e, so channel j < D/2 and its pair j + D/2 (acc[db + DB/2]) lie in
+// the same lane.  The value turned is s * (acc + radd * add), as store_quad_scaled forms it;
+// add[db][r4][e] holds the matching addend.  cs(pr, j) gives (cos, sin) of the inverse turn of
+// pair pr = (db * 4 + r4) * 4 + e of the lane, channel j.
+template <int D, typename CS>
+__device__ __forceinline__ void store_row_unrotated(bf16* row, const f32x16* acc, float s,
+                                                    const float (*add)[4][4], float radd, CS&& cs,
+                                                    int lane) {
+  constexpr int DB = D / 32;
+#pragma unroll
+  for (int db = 0; db < DB / 2; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
+      bf16x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x1 = s * fmaf(radd, add[db][r4][e], acc[db][4 * r4 + e]);
+        const float x2 = s * fmaf(radd, add[db + DB / 2][r4][e], acc[db + DB / 2][4 * r4 + e]);
+        const f32x2 v = cs((db * 4 + r4) * 4 + e, d0 + e);
+        float y1, y2;
+        rope_pair(x1, x2, v[0], v[1], y1, y2);
+        lo[e] = (bf16)y1;
+        hi[e] = (bf16)y2;
+      }
+      *reinterpret_cast<bf16x4*>(row + d0) = lo;
+      *reinterpret_cast<bf16x4*>(row + d0 + D / 2) = hi;
+    }
+}
+
+// Channel of pair pr = (db * 4 + r4) * 4 + e of a lane in store_row_unrotated.
+__device__ __forceinline__ int unrot_channel(int pr, int lane) {
+  return (pr >> 4) * 32 + 8 * ((pr >> 2) & 3) + 4 * (lane >> 5) + (pr & 3);
+}
 
 // Row statistics of a row with no allowed key (m = -inf) are mapped so that every entry lands
 // off the support: t = m - s = +inf, 1 + u = +inf.  The argmax test compares with NaN instead,
@@ -472,15 +514,20 @@ __device__ __forceinline__ float ra_grad_only(float s, float c16, float kd, floa
 
 // KEYPAD (with MASKED false): a boolean key padding mask.  Wave 0 copies each tile's 64 mask bytes
 // with its K and V tiles; the 64 keep bits drop whole padded blocks and mask the partial ones.
-template <int D, bool CAUSAL, bool MASKED, bool KEYPAD = false>
+template <int D, bool CAUSAL, bool MASKED, bool KEYPAD = false, bool ROPE = false>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int BN = 64, KC = D / 16, SB = BN / 32, DB = D / 32;
   static_assert(!(KEYPAD && MASKED), "key padding runs the unmasked paths");
   __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * D];
   __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * D];
   __shared__ __attribute__((aligned(16))) unsigned m_lds[KEYPAD ? 2 : 1][KEYPAD ? kWave : 1];
+  __shared__ double rate_lds[ROPE ? D / 2 : 1];   // ROPE: theta^(-2j/D) per pair j
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (ROPE) {
+    if (tid < D / 2) rate_lds[tid] = rope_rate(tid, D, a.log2_theta);
+    __syncthreads();
+  }
   const int logical = xcd_remap(blockIdx.x, a.total_wg);
   const int bg = logical / a.wg_per_group;
   int wig = logical % a.wg_per_group;
@@ -607,21 +654,65 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 
   const float R = -(rsum + __shfl_xor(rsum, 32));
   amax = min(amax, __shfl_xor(amax, 32));
+  // ROPE: the (cos, sin) pairs of the inverse turn, [pair][lane], in the K/V buffers (idle after
+  // the loop).  When the four waves hold the same rows (rep a multiple of four) they split one
+  // table; otherwise each wave fills its own.  Rolled loops, so that the angles' code is not
+  // repeated per pair.
+  const f32x2* cs_tab = nullptr;
+  if constexpr (ROPE) {
+    constexpr int NP = D / 4;
+    static_assert(2 * NP * kWave * sizeof(f32x2) <= sizeof(k_lds) &&
+                  2 * NP * kWave * sizeof(f32x2) <= sizeof(v_lds), "cos/sin tables fit the K/V buffers");
+    f32x2* tab = reinterpret_cast<f32x2*>(&k_lds[0][0]);
+    const double pos = a.q_pos != nullptr ? (double)a.q_pos[qrow] : (double)qrow;
+    if (a.rep % kWaves == 0) {
+      constexpr int PW = NP / kWaves;
+#pragma unroll 2
+      for (int i = 0; i < PW; ++i) {
+        const int pr = wave * PW + i;
+        float c, sn;
+        rope_cs(pos, rate_lds[unrot_channel(pr, lane)], true, c, sn);
+        tab[pr * kWave + lane] = f32x2{c, sn};
+      }
+      __syncthreads();
+    } else {   // waves 0, 1 in the K buffers, 2, 3 in the V buffers
+      tab = reinterpret_cast<f32x2*>(wave < 2 ? &k_lds[0][0] : &v_lds[0][0]) + (wave & 1) * NP * kWave;
+#pragma unroll 2
+      for (int pr = 0; pr < NP; ++pr) {
+        float c, sn;
+        rope_cs(pos, rate_lds[unrot_channel(pr, lane)], true, c, sn);
+        tab[pr * kWave + lane] = f32x2{c, sn};
+      }
+    }
+    cs_tab = tab;
+  }
   if (active && qi < a.Nq) {
     bf16* dqrow = static_cast<bf16*>(a.dq) + (head + qi) * D;
     const bool has_max = amax < a.Nk;
     const bf16* krow = kg + (size_t)(has_max ? amax : 0) * D;
     const float radd = has_max ? R : 0.0f;
+    if constexpr (ROPE) {
+      float kv[DB][4][4];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
-        float kv[4];
+        for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kv[e] = (float)krow[d0 + e];
-        store_quad_scaled<bf16>(dqrow + d0, acc[db], 4 * r4, a.scale, kv, radd);
-      }
+          for (int e = 0; e < 4; ++e) kv[db][r4][e] = (float)krow[db * 32 + 8 * r4 + 4 * (lane >> 5) + e];
+      store_row_unrotated<D>(dqrow, acc, a.scale, kv, radd,
+                             [&](int pr, int) { return cs_tab[pr * kWave + lane]; }, lane);
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
+          float kv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kv[e] = (float)krow[d0 + e];
+          store_quad_scaled<bf16>(dqrow + d0, acc[db], 4 * r4, a.scale, kv, radd);
+        }
+    }
     if (lane < 32) {
       a.c[head + qi] = cval;
       a.r[head + qi] = R;
@@ -655,7 +746,7 @@ constexpr int kDkdvRows = 64;   // query rows per step (32 per half of the workg
 // KEYPAD (with MASKED false): a boolean mask that depends on the key only (key padding).  A lane
 // owns one key for the whole kernel, so the mask is one keep flag per lane, read once; the
 // kernel keeps the unmasked paths, and a wave whose keys are all padding computes nothing.
-template <int D, bool CAUSAL, bool MASKED, bool KEYPAD = false>
+template <int D, bool CAUSAL, bool MASKED, bool KEYPAD = false, bool ROPE = false>
 __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int KC = D / 16, DB = D / 32, QT = kDkdvRows, HR = QT / 2, NW = kDkdvWaves;
   constexpr int HTILE = HR * D;           // elements of one half-tile (32 rows of Q or dO)
@@ -667,6 +758,11 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
                 "partial sums must fit in the tile buffers");
   // per-row terms of a tile [slot][term][row]: 1 + c16*m, 1/l, c/l, R, argmax (int bits)
   __shared__ __attribute__((aligned(16))) float st_lds[3][5][QT];
+  __shared__ double rate_lds[ROPE ? D / 2 : 1];   // ROPE: theta^(-2j/D) per pair j
+  if constexpr (ROPE) {
+    if (threadIdx.x < D / 2) rate_lds[threadIdx.x] = rope_rate(threadIdx.x, D, a.log2_theta);
+    __syncthreads();
+  }
   bf16* const k_lds = smem;
   bf16* const v_lds = smem + KV;
   auto q_up = [&](int slot) { return smem + 2 * KV + slot * HTILE; };
@@ -973,6 +1069,23 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
     const size_t kvbase = (size_t)(b * a.Hkv + g) * a.Nk;
     bf16* dkrow = static_cast<bf16*>(a.dk) + (kvbase + key) * D;
     bf16* dvrow = static_cast<bf16*>(a.dv) + (kvbase + key) * D;
+    if constexpr (ROPE) {
+      float ak[DB][4][4];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 pk = part[slot(0, db, i4)];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ak[db][i4][e] = pk[e];
+        }
+      const double pos = a.k_pos != nullptr ? (double)a.k_pos[key] : (double)key;
+      store_row_unrotated<D>(dkrow, acc_dk, a.scale, ak, 1.0f, [&](int, int j) {
+        float c, sn;
+        rope_cs(pos, rate_lds[j], true, c, sn);
+        return f32x2{c, sn};
+      }, lane);
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -982,7 +1095,7 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
         const f32x4 pv = part[slot(1, db, i4)];
         const float ak[4] = {pk[0], pk[1], pk[2], pk[3]};
         const float av[4] = {pv[0], pv[1], pv[2], pv[3]};
-        store_quad_scaled<bf16>(dkrow + d0, acc_dk[db], 4 * i4, a.scale, ak, 1.0f);
+        if constexpr (!ROPE) store_quad_scaled<bf16>(dkrow + d0, acc_dk[db], 4 * i4, a.scale, ak, 1.0f);
         store_quad_scaled<bf16>(dvrow + d0, acc_dv[db], 4 * i4, 1.0f, av, 1.0f);
       }
   }
@@ -1022,6 +1135,9 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   a.c16 = p.scale / 16.0f;
   a.coff = p.coff;
   a.mask = mask_args(p);
+  a.q_pos = p.q_pos;
+  a.k_pos = p.k_pos;
+  a.log2_theta = p.rope ? log2(p.rope_theta) : 0.0;
   constexpr bool kBf16 = sizeof(T) == 2;
   const dim3 qgrid(a.total_wg), kgrid(a.total_kwg), block(kThreads);
   const dim3 kblock(kBf16 ? kDkdvThreads : kThreads);
@@ -1033,6 +1149,21 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   const bool keypad = kBf16 && p.mask_kind == kMaskBool && p.msq == 0 && p.msh == 0 && p.msk == 1 &&
                       p.msb % 4 == 0 && p.Nk % 4 == 0 &&
                       reinterpret_cast<unsigned long long>(p.mask) % 4 == 0;
+  if (p.rope) {   // bf16, no explicit mask: the host checks both
+    if constexpr (kBf16) {
+      if (phases & kBwdDq) {
+        if (p.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, false, true>), qgrid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, false, false, true>), qgrid, block, 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      if (phases & kBwdDkdv) {
+        if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, false, false, true>), kgrid, kblock, 0, stream, a);
+        else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, false, false, true>), kgrid, kblock, 0, stream, a);
+      }
+    }
+    return hipGetLastError();
+  }
   if (phases & kBwdDq) {
     if (keypad) {
       if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, true>), qgrid, block, 0, stream, a);
@@ -1071,7 +1202,9 @@ hipError_t launch_attn_bwd(const AttnProblem& p, const void* o, const void* d_o,
                            const BwdWorkspace& ws, int phases, hipStream_t stream) {
   if (stats == nullptr) {
     if (phases & kBwdDq) {   // recompute (m, l) with the forward's statistics-only variant
-      const hipError_t e = launch_attn_fwd(p, nullptr, ws.stats, nullptr, stream);
+      AttnProblem ps = p;
+      ps.rope = false;       // with the rotary embedding q and k already hold the rotated rows
+      const hipError_t e = launch_attn_fwd(ps, nullptr, ws.stats, nullptr, stream);
       if (e != hipSuccess) return e;
     }
     stats = ws.stats;

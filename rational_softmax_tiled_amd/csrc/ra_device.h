@@ -162,7 +162,43 @@ __device__ __forceinline__ float ra_grad_t(float t, float c16, float dpc, float 
   return dpc * ((q6 * q) * (r * r));
 }
 
+// ---------------------------------------------------------------- NEOX rotary embedding
+// Split halves ("Primitives" page, section "Attention and transformers", RoPE; the nurl page,
+// section "Layers", nn_rope): channel j < D/2 of a row at position pos pairs with j + D/2 and
+// turns by pos * theta^(-2j/D) (the frequency schedule the pages leave open).  The rate
+// theta^(-2j/D) is formed in fp64 from log2(theta) (computed once on the host); kernels keep the
+// D/2 rates in a small table.  The angle is formed and reduced to [-pi, pi] in fp64 (large
+// positions lose the phase in fp32); its cos and sin are then evaluated in fp32.  Every kernel
+// that rotates uses these helpers, so a rotation fused into another kernel is bit-identical to
+// the standalone one.
+__device__ __forceinline__ double rope_rate(int j, int D, double log2_theta) {
+  return exp2((double)(-2 * j) / (double)D * log2_theta);
+}
+__device__ __forceinline__ void rope_cs(double pos, double rate, bool inverse, float& c, float& s) {
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  const double ang = pos * rate;
+  const double red = fma(-kTwoPi, rint(ang * (1.0 / kTwoPi)), ang);
+  float sf, cf;
+  sincosf((float)red, &sf, &cf);
+  c = cf;
+  s = inverse ? -sf : sf;
+}
+// (x_j, x_{j+D/2}) -> (x_j c - x_{j+D/2} s, x_j s + x_{j+D/2} c), in fp32 with fixed contractions
+__device__ __forceinline__ void rope_pair(float x1, float x2, float c, float s, float& y1, float& y2) {
+  y1 = fmaf(x1, c, -(x2 * s));
+  y2 = fmaf(x1, s, x2 * c);
+}
+
 // ---------------------------------------------------------------- wave / block helpers
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, unrolled at compile time
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

@@ -43,6 +43,11 @@ struct FwdArgs {
   float c;               // scale / 16
   int coff;              // causal diagonal: key j allowed for query row i iff j <= i + coff
   MaskArgs mask;         // explicit mask (MASKED kernels)
+  // ROPE kernels: Q is rotated (NEOX) as its fragments are loaded; row i sits at position
+  // q_pos[i] (nullable: i); the rotated rows go to q_rot when it is non-null
+  const int* q_pos;
+  double log2_theta;
+  void* q_rot;
 };
 
 constexpr int kMaxTiles = 512;   // key tiles with a recorded maximum (skip test); beyond: no skip
@@ -126,7 +131,11 @@ __device__ __forceinline__ void score_pair(const bf16* k_tile, const bf16x8* qf,
 // tile's 64 mask bytes into 64 keep bits, drops a tile with none (its maximum stays -inf, so
 // pass 2 skips it too) and masks a partial one; pass 2 masks the partial tiles again from the
 // recorded bits and runs full tiles on the interleaved path.
-template <typename T, int D, int BN, bool COUNT, bool WRITE_O, bool MASKED, bool KEYPAD = false>
+// ROPE: q holds the rows before the rotary embedding; each wave rotates its Q fragments once, on
+// load (the pair of channel j, j + D/2 lies in fragments kc, kc + KC/2 of the same lane), and may
+// store them (q_rot) for a backward pass.
+template <typename T, int D, int BN, bool COUNT, bool WRITE_O, bool MASKED, bool KEYPAD = false,
+          bool ROPE = false>
 // bf16: two waves per SIMD (at most 256 VGPRs), the second wave fills the first one's waits.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void attn_fwd_kernel(FwdArgs a) {
   using frag_t = typename Ty<T>::frag;
@@ -145,8 +154,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   __shared__ float tmax_lds[kWaves][kMaxTiles];
   __shared__ float kmin_lds[kWaves];
   static_assert(!KEYPAD || (sizeof(T) == 2 && WRITE_O && !MASKED && BN == kWave), "key padding path");
+  static_assert(!ROPE || (sizeof(T) == 2 && WRITE_O && !MASKED && !KEYPAD && !COUNT), "rotary path");
   __shared__ __attribute__((aligned(16))) unsigned mstage_lds[KEYPAD ? 4 : 1][KEYPAD ? kWave : 1];
   __shared__ unsigned long long keep_lds[KEYPAD ? kMaxTiles : 1];
+  __shared__ double rate_lds[ROPE ? D / 2 : 1];   // ROPE: theta^(-2j/D) per pair j
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -180,9 +191,80 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   frag_t qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) qf[kc] = load_frag(qh + (size_t)qrow * D + 16 * kc + 8 * (lane >> 5));
+  // ROPE: the row's position and, in wave 0, the table of rates theta^(-2j/D)
+  int rope_pos = 0;
+  if constexpr (ROPE) {
+    rope_pos = a.q_pos != nullptr ? a.q_pos[qrow] : qrow;
+    if (tid < D / 2) rate_lds[tid] = rope_rate(tid, D, a.log2_theta);
+  }
   // settle these loads here: otherwise the compiler waits for them (vmcnt) inside the tile loops,
   // where the count would also cover the tile prefetch in flight
   wait_vmem();
+  if constexpr (ROPE) {
+    asm volatile("" : "+v"(rope_pos));   // landed: no wait after the copies below
+    __syncthreads();                     // the rate table is written
+  }
+
+  // ROPE: turn the Q fragments by the NEOX rotary embedding.  Channel j < D/2 and its partner
+  // j + D/2 sit in fragments kc and kc + KC/2 of the same lane (element j % 8), so the rotation is
+  // lane-local.  The (cos, sin) pairs go through LDS, stage 3 of pass 1 (free until its first
+  // step), so that the angle loops stay rolled while the fragments are indexed statically.  When
+  // the four waves hold the same query rows (rep a multiple of four) they split one table;
+  // otherwise each wave fills its own, one fragment pair at a time.  Runs while pass 1's first
+  // tiles are in flight; q_rot, when given, receives the rotated rows.
+  auto rope_rotate = [&]() {
+    if constexpr (ROPE) {
+      constexpr int NP = D / 4;   // pairs per lane
+      constexpr int STAGE = (int)sizeof(v_lds[0]);
+      // pairs per chunk of the per-wave tables: the four tables share stage 3
+      constexpr int CH = STAGE / (kWaves * kWave * (int)sizeof(f32x2)) < 8
+                             ? STAGE / (kWaves * kWave * (int)sizeof(f32x2)) : 8;
+      static_assert(NP * kWave * (int)sizeof(f32x2) <= STAGE && CH >= 1 && 8 % CH == 0,
+                    "cos/sin tables fit stage 3");
+      f32x2* tab = reinterpret_cast<f32x2*>(v_lds[1]);
+      const double pos = (double)rope_pos;
+      auto angle = [&](int pr) {   // pair pr of the lane: channel 16 (pr / 8) + 8 (lane / 32) + pr % 8
+        float c, sn;
+        rope_cs(pos, rate_lds[16 * (pr >> 3) + 8 * (lane >> 5) + (pr & 7)], false, c, sn);
+        return f32x2{c, sn};
+      };
+      // pairs p0 .. p0 + n - 1 (within one fragment pair) from t: [pair - p0][lane]
+      auto turn = [&](auto p0_c, auto n_c, const f32x2* t) {
+        constexpr int p0 = decltype(p0_c)::value, n = decltype(n_c)::value, kc = p0 / 8;
+#pragma unroll
+        for (int e = 0; e < n; ++e) {
+          const f32x2 v = t[e * kWave + lane];
+          float y1, y2;
+          rope_pair((float)qf[kc][p0 % 8 + e], (float)qf[kc + KC / 2][p0 % 8 + e], v[0], v[1], y1, y2);
+          qf[kc][p0 % 8 + e] = (T)y1;
+          qf[kc + KC / 2][p0 % 8 + e] = (T)y2;
+        }
+      };
+      if (a.rep % kWaves == 0) {
+        constexpr int PW = NP / kWaves;
+#pragma unroll 2
+        for (int i = 0; i < PW; ++i) tab[(wave * PW + i) * kWave + lane] = angle(wave * PW + i);
+        __syncthreads();
+        static_for<NP / 8>([&](auto kc) {
+          constexpr int p0 = decltype(kc)::value * 8;
+          turn(std::integral_constant<int, p0>{}, std::integral_constant<int, 8>{}, tab + p0 * kWave);
+        });
+      } else {
+        f32x2* own = tab + wave * CH * kWave;
+        static_for<NP / CH>([&](auto c) {
+          constexpr int p0 = decltype(c)::value * CH;
+#pragma unroll 2
+          for (int e = 0; e < CH; ++e) own[e * kWave + lane] = angle(p0 + e);
+          turn(std::integral_constant<int, p0>{}, std::integral_constant<int, CH>{}, own);
+        });
+      }
+      if (a.q_rot != nullptr && active && qi < a.Nq) {
+        T* qr = static_cast<T*>(a.q_rot) + ((size_t)(b * a.Hq + h) * a.Nq + qi) * D + 8 * (lane >> 5);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) *reinterpret_cast<frag_t*>(qr + 16 * kc) = qf[kc];
+      }
+    }
+  };
 
   const int frow = lane & 31;           // A-fragment row inside a 32-row block
   const int fcol = 8 * (lane >> 5);     // A-fragment column offset
@@ -245,6 +327,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       k_issue(2, k_stage(std::integral_constant<int, 2>{}));
       m_issue(2, 2);
     }
+    if constexpr (ROPE) rope_rotate();
     // tile 0 landed; the copies of tiles 1 and 2 may stay in flight
     if (nt >= 3) wait_younger(std::integral_constant<int, 2>{});
     else if (nt == 2) wait_younger(std::integral_constant<int, 1>{});
@@ -601,6 +684,9 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   a.c = p.scale / 16.0f;
   a.coff = p.coff;
   a.mask = mask_args(p);
+  a.q_pos = p.q_pos;
+  a.log2_theta = p.rope ? log2(p.rope_theta) : 0.0;
+  a.q_rot = p.q_rot;
   dim3 grid(a.total_wg), block(kThreads);
   // a boolean key padding mask ([B, Nk] broadcast over heads and rows, keys contiguous, every
   // sample's row 4-byte aligned and a whole number of dwords long for the dword copies, whose
@@ -608,7 +694,12 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   const bool keypad = sizeof(T) == 2 && o != nullptr && !counters && p.mask_kind == kMaskBool && p.msq == 0 &&
                       p.msh == 0 && p.msk == 1 && p.msb % 4 == 0 && p.Nk % 4 == 0 &&
                       reinterpret_cast<unsigned long long>(p.mask) % 4 == 0 && (p.Nk + BN - 1) / BN <= kMaxTiles;
-  if (keypad) {
+  if (p.rope) {   // bf16 only; the host rejects masks and counters with the rotary embedding
+    if (sizeof(T) != 2 || o == nullptr || counters != nullptr || p.mask_kind != kMaskNone)
+      return hipErrorInvalidValue;
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, false, true>), grid, block, 0, stream, a);
+  } else if (keypad) {
     if constexpr (sizeof(T) == 2 && BN == kWave)
       hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, true>), grid, block, 0, stream, a);
   } else if (p.mask_kind != kMaskNone) {

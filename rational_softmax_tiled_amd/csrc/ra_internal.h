@@ -22,6 +22,21 @@ struct AttnProblem {
   int mask_kind;
   long long msb, msh;
   int msq, msk, mask_bytes;
+  // NEOX rotary embedding fused into the kernels (rope): the forward rotates Q on load (rows at
+  // q_pos, nullable: 0..Nq-1) and writes the rotated rows to q_rot when non-null; the backward
+  // turns dQ and dK back (keys at k_pos, nullable: 0..Nk-1)
+  bool rope = false;
+  double rope_theta = 0.0;
+  const int* q_pos = nullptr;
+  const int* k_pos = nullptr;
+  void* q_rot = nullptr;
+};
+
+// The rotary embedding of the fused entry points (theta, positions of query rows and keys).
+struct RopeArgs {
+  double theta;
+  const int* q_pos;
+  const int* k_pos;
 };
 
 // Forward: o (and stats when non-null); counters non-null selects the counting variant;

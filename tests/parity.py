@@ -112,6 +112,63 @@ def fwd_all_heads(o, stats, inp, causal, scale, dtype, heads=None):
     return {"o": err, "m": em_max, "l": el_max, "heads": len(todo)}
 
 
+def fwd_rope_all_heads(o, stats, inp, causal, scale, theta, q_positions=None, k_positions=None,
+                       heads=None):
+    """fwd_all_heads for attention on rotated rows: inp holds the UNROTATED bf16 q and k.  O is
+    compared with the exact function (ra_attention_rope_fwd).  The GPU scores the rotated rows
+    rounded to bf16, so m and l are held to bounds derived from rope_score_bound per row:
+    |m~ - m| <= t_i = max_j b_ij over the allowed keys, and, with |delta Delta_ij| <= b_ij + t_i
+    and |phi'| <= phi^(7/8) (phi decreasing in Delta),
+    |l~ - l| <= sum_j (b_ij + t_i) phi(max(Delta_ij - b_ij - t_i, 0))^(7/8); each plus the fp32
+    margins of fwd_all_heads."""
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    B, Hq, Nq, D = q.shape
+    Nk = k.shape[2]
+    rep = Hq // k.shape[1]
+    todo = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
+    off = oracle.causal_offset(causal, Nq, Nk)
+    allowed = np.ones((Nq, Nk), bool) if off is None else \
+        np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + off
+
+    def one(bh):
+        b, h = bh
+        g = h // rep
+        ro, rm, rl, _ = oracle.ra_attention_rope_fwd(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1],
+                                                     v[b:b + 1, g:g + 1], causal, scale, theta,
+                                                     q_positions, k_positions)
+        qh = oracle.rope_neox(q[b, h].astype(np.float64), theta, q_positions)
+        kg = oracle.rope_neox(k[b, g].astype(np.float64), theta, k_positions)
+        bnd = np.where(allowed, rope_score_bound(qh, kg, scale), 0.0)
+        t = bnd.max(axis=1)
+        s = scale * (qh @ kg.T)
+        m0 = rm[0, 0]
+        fin = np.isfinite(m0)
+        delta = np.where(allowed & fin[:, None], m0[:, None] - s, np.inf)
+        w = bnd + t[:, None]
+        lb = (w * oracle.ra_phi(np.maximum(delta - w, 0.0)) ** 0.875).sum(axis=1)
+        gm, gl = stats[b, h, :, 0] * scale, stats[b, h, :, 1]
+        assert (np.isfinite(gm) == fin).all(), f"m finiteness at {bh}"
+        em = np.abs(gm[fin] - m0[fin]) - t[fin] - 1e-5 * np.abs(m0[fin])
+        el = np.abs(gl - rl[0, 0]) - lb - 1e-5 * np.abs(rl[0, 0])
+        return (bh, float(np.abs(o[b, h] - ro[0, 0]).max()), float(np.abs(ro[0, 0]).max()),
+                float(np.max(em, initial=-np.inf)), float(np.max(el, initial=-np.inf)),
+                float(t.max(initial=0.0)))
+
+    tal = Tally("o", "bf16", grad=False)
+    em_max = el_max = -np.inf
+    t_max = 0.0
+    for bh, eo, mo, em, el, tm in _pool_map(one, todo):
+        if eo > tal.err:
+            tal.err, tal.where = eo, bh
+        tal.ref = max(tal.ref, mo)
+        em_max, el_max, t_max = max(em_max, em), max(el_max, el), max(t_max, tm)
+    err = tal.check()
+    assert em_max <= 1e-4, f"row max m beyond its rounding bound by {em_max:.3e}"
+    assert el_max <= 0.0, f"sum of phi beyond its rounding bound by {el_max:.3e}"
+    return {"o": err, "m_excess": em_max, "l_excess": el_max, "score_bound": t_max,
+            "heads": len(todo)}
+
+
 def score_error_bound(qh, kg, scale):
     """|fp32 score - exact score| <= gamma_D * scale * sum_d |q_d k_d| per (i, j)."""
     D = qh.shape[-1]
@@ -119,9 +176,28 @@ def score_error_bound(qh, kg, scale):
     return gamma * scale * (np.abs(qh) @ np.abs(kg).T)
 
 
-def near_tie_candidates(qh, kg, scale, causal, Nq, Nk):
+def rope_score_bound(qh, kg, scale):
+    """|GPU score - exact score| per (i, j) when the GPU multiplies the rotated rows rounded to
+    bf16 (qh, kg: the exactly rotated rows of one head).  Each rotated element is the fp32
+    rotation (error below 2^-20 times its pair's norm n) rounded to bf16 (relative 2^-8), so
+    |delta q_d| <= e A_d with e = 2^-8, A = |q| + 2^-12 n; then |q~.k~ - q.k| <=
+    (2e + e^2) A_q . A_k, plus the fp32 dot product of the rounded rows, gamma_D (1 + e)^2
+    A_q . A_k."""
+    D = qh.shape[-1]
+    e = 2.0 ** -8
+    gamma = D * U32 / (1 - D * U32)
+
+    def amp(x):
+        h = D // 2
+        n = np.sqrt(x[:, :h] ** 2 + x[:, h:] ** 2)
+        return np.abs(x) + 2.0 ** -12 * np.concatenate([n, n], axis=1)
+    return scale * (2 * e + e * e + gamma * (1 + e) ** 2) * (amp(qh) @ amp(kg).T)
+
+
+def near_tie_candidates(qh, kg, scale, causal, Nq, Nk, es=None):
     """Per row of one head: the other keys whose score may order before the oracle's argmax in
-    fp32, as a dict row -> [keys] (keys with bit-identical rows to the argmax excluded)."""
+    fp32, as a dict row -> [keys] (keys with bit-identical rows to the argmax excluded).  ``es``:
+    the per-entry score error bound (default: fp32 scoring of the given rows)."""
     s = scale * (qh @ kg.T)
     off = oracle.causal_offset(causal, Nq, Nk)
     allowed = np.ones((Nq, Nk), bool) if off is None else \
@@ -129,7 +205,8 @@ def near_tie_candidates(qh, kg, scale, causal, Nq, Nk):
     xm = np.where(allowed, s, -np.inf)
     a = np.argmax(xm, axis=1)
     m = xm[np.arange(Nq), a]
-    es = score_error_bound(qh, kg, scale)
+    if es is None:
+        es = score_error_bound(qh, kg, scale)
     near = allowed & (m[:, None] - s <= es + es[np.arange(Nq), a][:, None])
     near[np.arange(Nq), a] = False
     out = {}
@@ -140,9 +217,11 @@ def near_tie_candidates(qh, kg, scale, causal, Nq, Nk):
     return out
 
 
-def bwd_all_groups(dq, dk, dv, inp, causal, scale, dtype, groups=None):
+def bwd_all_groups(dq, dk, dv, inp, causal, scale, dtype, groups=None, rope=None):
     """Compare dq [B, Hq, Nq, D], dk, dv [B, Hkv, Nk, D] with the oracle on every (b, g) group
-    (or the given list), accepting either candidate at near ties of the row max.  Returns
+    (or the given list), accepting either candidate at near ties of the row max.  ``rope``:
+    None, or {"theta", "q_positions", "k_positions"}: q and k are unrotated, the oracle is
+    ra_attention_rope_bwd and near ties are taken within rope_score_bound.  Returns
     {name: error, "near_tie_rows": n, "flipped_rows": n}."""
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
     B, Hq, Nq, D = q.shape
@@ -150,14 +229,26 @@ def bwd_all_groups(dq, dk, dv, inp, causal, scale, dtype, groups=None):
     rep = Hq // Hkv
     todo = [(b, g) for b in range(B) for g in range(Hkv)] if groups is None else list(groups)
 
+    def bwd(*args, argmax=None):
+        if rope is None:
+            return oracle.ra_attention_bwd(*args, argmax=argmax)
+        return oracle.ra_attention_rope_bwd(*args, rope["theta"], rope["q_positions"],
+                                            rope["k_positions"], argmax=argmax)
+
     def one(bg):
         b, g = bg
         hs = slice(g * rep, (g + 1) * rep)
         args = (q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], do[b:b + 1, hs], causal, scale)
         kg = k[b, g].astype(np.float64)
-        ties = {r: near_tie_candidates(q[b, g * rep + r].astype(np.float64), kg, scale, causal, Nq, Nk)
-                for r in range(rep)}
-        ref = oracle.ra_attention_bwd(*args)
+        qg = [q[b, g * rep + r].astype(np.float64) for r in range(rep)]
+        if rope is not None:
+            kg = oracle.rope_neox(kg, rope["theta"], rope["k_positions"])
+            qg = [oracle.rope_neox(x, rope["theta"], rope["q_positions"]) for x in qg]
+        ties = {}
+        for r in range(rep):
+            es = None if rope is None else rope_score_bound(qg[r], kg, scale)
+            ties[r] = near_tie_candidates(qg[r], kg, scale, causal, Nq, Nk, es)
+        ref = bwd(*args)
         n_tie = sum(len(t) for t in ties.values())
         n_flip = 0
         if n_tie:
@@ -172,7 +263,7 @@ def bwd_all_groups(dq, dk, dv, inp, causal, scale, dtype, groups=None):
                     for i, (_, c) in t.items():
                         if n < len(c):
                             over[0, r, i] = c[n]
-                alt = oracle.ra_attention_bwd(*args, argmax=over)
+                alt = bwd(*args, argmax=over)
                 for (r, i), (e, _) in list(best.items()):
                     if over[0, r, i] >= 0:
                         e2 = np.abs(dq[b, g * rep + r, i] - alt[0][0, r, i]).max()
@@ -182,7 +273,7 @@ def bwd_all_groups(dq, dk, dv, inp, causal, scale, dtype, groups=None):
                 choice[0, r, i] = j
             n_flip = int((choice >= 0).sum())
             if n_flip:
-                ref = oracle.ra_attention_bwd(*args, argmax=choice)
+                ref = bwd(*args, argmax=choice)
         out = []
         for name, gpu, r in (("dq", dq[b, hs], ref[0][0]), ("dk", dk[b, g], ref[1][0, 0]),
                              ("dv", dv[b, g], ref[2][0, 0])):

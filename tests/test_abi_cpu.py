@@ -212,6 +212,48 @@ def test_rope_validation(lib):
     assert f(None, None, None, 2, 0, 64, 10000.0, 0, ra.RA_F32, 0) == OK
 
 
+def fwd_rope(B=1, Hq=2, Hkv=1, Nq=8, Nk=8, D=64, causal=1, scale=0.125, dtype=ra.RA_BF16,
+             q=P, k=P, v=P, o=P2, q_rot=None, k_rot=P2, qp=None, kp=None, theta=10000.0):
+    return ra.ra_attn_fwd_rope(q, k, v, o, None, q_rot, k_rot, qp, kp, theta, B, Hq, Hkv, Nq, Nk,
+                               D, causal, scale, dtype, 0)
+
+
+def test_fwd_rope_validation(lib):
+    assert fwd_rope(dtype=ra.RA_F32) == DTYPE
+    assert fwd_rope(dtype=7) == DTYPE
+    assert fwd_rope(Hq=3, Hkv=2) == GQA
+    assert fwd_rope(D=96) == HEADDIM
+    assert fwd_rope(causal=5) == MASK
+    for th in (0.0, -1.0, math.inf, math.nan):
+        assert fwd_rope(theta=th) == SCALE
+    assert fwd_rope(scale=0.0) == SCALE
+    assert fwd_rope(q=None) == NULLPTR
+    assert fwd_rope(o=None) == NULLPTR
+    assert fwd_rope(k_rot=None) == NULLPTR
+    assert fwd_rope(q_rot=P2 + 2) == ALIGN
+    assert fwd_rope(k_rot=P2 + 8) == ALIGN
+    assert fwd_rope(qp=P + 2) == ALIGN
+    assert fwd_rope(kp=P + 1) == ALIGN
+    assert fwd_rope(Nq=1 << 25, D=128) == TOO_LARGE
+    assert fwd_rope(B=0) == OK
+    assert fwd_rope(Nq=0, q=None, o=None, k_rot=None) == OK
+
+
+def test_bwd_rope_validation(lib):
+    def f(dtype=ra.RA_BF16, theta=10000.0, ws=P2, ws_bytes=1 << 30, dq=P2, qp=None, B=1, D=64):
+        return ra.ra_attn_bwd_rope(P, P, P, P, P, None, dq, P2, P2, ws, ws_bytes, qp, None, theta,
+                                   B, 2, 1, 8, 8, D, 1, 0.125, dtype, 0)
+    assert f(dtype=ra.RA_F32) == DTYPE
+    assert f(theta=0.0) == SCALE
+    assert f(theta=math.nan) == SCALE
+    assert f(qp=P + 2) == ALIGN
+    assert f(dq=None) == NULLPTR
+    assert f(dq=P2 + 2) == ALIGN
+    assert f(ws=None) == WORKSPACE
+    assert f(D=80) == HEADDIM
+    assert f(B=0) == OK
+
+
 def test_product_path_has_no_fallback():
     # The binding must not reach the oracle or any CPU implementation.
     import rational_softmax_tiled_amd

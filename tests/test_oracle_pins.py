@@ -827,3 +827,55 @@ def test_rope_matches_the_host_input_generator():
     rng = np.random.default_rng(34)
     x = rng.normal(size=(2, 64, 32)).astype(np.float32)
     np.testing.assert_allclose(wl.neox_rope(x, 10000.0), oracle.rope_neox(x, 10000.0), atol=2e-5)
+
+
+# ------------------------------------------------------------- attention on rotated Q and K
+
+@pytest.mark.parametrize("causal", [False, "bottom_right"])
+def test_rope_attention_bwd_matches_central_differences(causal):
+    """The gradients with respect to the unrotated q and k (positions given, distinct per side)
+    against central differences of the composed forward."""
+    B, Hq, Hkv, Nq, Nk, D = 1, 2, 1, 3, 5, 4
+    rng = np.random.default_rng(35)
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, Nq, Nk, D, sigma=1.5)
+    do = rng.normal(size=q.shape)
+    qp, kp = np.array([7, 2, 40]), np.array([3, 11, 0, 25, 9])
+    args = (causal, 0.8, 100.0)
+    dq, dk, dv = oracle.ra_attention_rope_bwd(q, k, v, do, *args, q_rope_positions=qp,
+                                              k_rope_positions=kp)
+
+    def loss(qq, kk, vv):
+        o = oracle.ra_attention_rope_fwd(qq, kk, vv, *args, q_rope_positions=qp, k_rope_positions=kp)[0]
+        return float((o * do).sum())
+
+    np.testing.assert_allclose(dq, _fd_grad(lambda z: loss(z, k, v), q), rtol=0, atol=3e-8)
+    np.testing.assert_allclose(dk, _fd_grad(lambda z: loss(q, z, v), k), rtol=0, atol=3e-8)
+    np.testing.assert_allclose(dv, _fd_grad(lambda z: loss(q, k, z), v), rtol=0, atol=3e-8)
+
+
+def test_rope_attention_at_position_zero_is_plain_attention():
+    rng = np.random.default_rng(36)
+    q, k, v = _rand_qkv(rng, 1, 2, 2, 4, 6, 8)
+    zq, zk = np.zeros(4, int), np.zeros(6, int)
+    o = oracle.ra_attention_rope_fwd(q, k, v, True, 0.5, 10000.0, zq, zk)[0]
+    np.testing.assert_array_equal(o, oracle.ra_attention_fwd(q, k, v, True, 0.5)[0])
+
+
+def test_rope_attention_depends_on_relative_positions_only():
+    """The same shift of every query and key position leaves the output unchanged."""
+    rng = np.random.default_rng(37)
+    q, k, v = _rand_qkv(rng, 1, 2, 1, 5, 5, 8, sigma=2.0)
+    base = oracle.ra_attention_rope_fwd(q, k, v, True, 0.6, 500.0)[0]
+    shifted = oracle.ra_attention_rope_fwd(q, k, v, True, 0.6, 500.0, np.arange(5) + 1234,
+                                           np.arange(5) + 1234)[0]
+    np.testing.assert_allclose(shifted, base, rtol=0, atol=1e-10)
+
+
+def test_planted_forward_rotation_of_the_gradient_breaks_the_rope_pin():
+    # Mapping dQ and dK back with the forward rotation instead of its transpose must fail.
+    def no_inverse(orig):
+        return lambda x, theta, positions=None, inverse=False: orig(x, theta, positions)
+    with _planted("rope_neox", no_inverse):
+        with pytest.raises(AssertionError):
+            test_rope_attention_bwd_matches_central_differences(False)
+    test_rope_attention_bwd_matches_central_differences(False)

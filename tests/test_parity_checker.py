@@ -6,6 +6,7 @@ import pytest
 
 import oracle
 import parity
+import workloads as wl
 
 
 def near_tie_problem(exact=False):
@@ -75,3 +76,50 @@ def test_rejects_planted_gradient_and_output_mistakes():
     o_bad[0, 1, 2, 3] += 2e-5                       # beyond the absolute fp32 bound
     with pytest.raises(AssertionError):
         parity.fwd_all_heads(o_bad, stats, inp, False, 0.35, "f32")
+
+
+# ------------------------------------------------------------- attention on rotated rows
+
+def _rope_problem():
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, N, D = 1, 4, 2, 40, 16
+    r = lambda *s: wl.round_to_dtype(rng.standard_normal(s, dtype=np.float32), "bf16")
+    inp = {"q": r(B, Hq, N, D), "k": r(B, Hkv, N, D), "v": r(B, Hkv, N, D), "do": r(B, Hq, N, D)}
+    rope = {"theta": 500.0, "q_positions": np.arange(N) + 3, "k_positions": np.arange(N) + 3}
+    return inp, rope
+
+
+def _rounded_rotation(inp, rope):
+    """The arithmetic the GPU performs, on the oracle: rotated rows rounded to bf16."""
+    qr = wl.round_to_dtype(oracle.rope_neox(inp["q"], rope["theta"], rope["q_positions"]), "bf16")
+    kr = wl.round_to_dtype(oracle.rope_neox(inp["k"], rope["theta"], rope["k_positions"]), "bf16")
+    return qr, kr
+
+
+def test_rope_checker_accepts_rounded_rotated_rows():
+    inp, rope = _rope_problem()
+    qr, kr = _rounded_rotation(inp, rope)
+    o, m, l, _ = oracle.ra_attention_fwd(qr, kr, inp["v"], True, 0.25)
+    stats = np.stack([m / 0.25, l], axis=-1)
+    parity.fwd_rope_all_heads(o, stats, inp, True, 0.25, rope["theta"], rope["q_positions"],
+                              rope["k_positions"])
+    dqr, dkr, dv = oracle.ra_attention_bwd(qr, kr, inp["v"], inp["do"], True, 0.25)
+    dq = oracle.rope_neox(dqr, rope["theta"], rope["q_positions"], inverse=True)
+    dk = oracle.rope_neox(dkr, rope["theta"], rope["k_positions"], inverse=True)
+    parity.bwd_all_groups(dq, dk, dv, inp, True, 0.25, "bf16", rope=rope)
+
+
+def test_rope_checker_rejects_planted_mistakes():
+    inp, rope = _rope_problem()
+    qr, kr = _rounded_rotation(inp, rope)
+    # keys left unrotated: the output moves beyond the bf16 tolerance or the stats bounds
+    o, m, l, _ = oracle.ra_attention_fwd(qr, inp["k"], inp["v"], True, 0.25)
+    with pytest.raises(AssertionError):
+        parity.fwd_rope_all_heads(o, np.stack([m / 0.25, l], axis=-1), inp, True, 0.25,
+                                  rope["theta"], rope["q_positions"], rope["k_positions"])
+    # gradients rotated forward instead of back
+    dqr, dkr, dv = oracle.ra_attention_bwd(qr, kr, inp["v"], inp["do"], True, 0.25)
+    dq = oracle.rope_neox(dqr, rope["theta"], rope["q_positions"])
+    dk = oracle.rope_neox(dkr, rope["theta"], rope["k_positions"], inverse=True)
+    with pytest.raises(AssertionError):
+        parity.bwd_all_groups(dq, dk, dv, inp, True, 0.25, "bf16", rope=rope)

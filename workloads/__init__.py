@@ -175,6 +175,23 @@ def make_attention_inputs(w: AttnWorkload, seed: Optional[int] = None) -> dict:
     return out
 
 
+def make_unrotated_inputs(w: AttnWorkload, seed: Optional[int] = None) -> dict:
+    """The draws of make_attention_inputs for a workload with a rotary embedding, with Q and K
+    left unrotated (for the kernels that rotate them on the device), each rounded to the
+    storage dtype; dO as a seeded N(0, 1) draw when the workload has none."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    shp_q = (w.B, w.Hq, w.Nq, w.D)
+    shp_k = (w.B, w.Hkv, w.Nk, w.D)
+    q = rng.standard_normal(shp_q, dtype=np.float32) * np.float32(w.sigma_qk)
+    k = rng.standard_normal(shp_k, dtype=np.float32) * np.float32(w.sigma_qk)
+    v = rng.standard_normal(shp_k, dtype=np.float32) * np.float32(w.sigma_v)
+    out = {"q": round_to_dtype(q, w.dtype), "k": round_to_dtype(k, w.dtype),
+           "v": round_to_dtype(v, w.dtype)}
+    do = rng.standard_normal(shp_q, dtype=np.float32)
+    out["do"] = round_to_dtype(do, w.dtype)
+    return out
+
+
 def make_local_inputs(B=1, H=16, N=2048, D=64, amplitude=4.0, seed=7, dtype="bf16"):
     """Structured causal workload whose scores fall off sharply away from the
     diagonal, so whole tiles leave the compact support.  Q = K = RoPE(a*c + 0.5*e)
