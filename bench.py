@@ -227,6 +227,40 @@ def timed(stream, fn, min_s, min_calls=20, warm=5):
             "mean_ms": round(float(t.mean()), 5), "calls": int(t.size)}
 
 
+def timed_graph(run, fn, calls=64, reps=20):
+    """Per-call duration of fn() with no launch overhead: `calls` calls captured in one HIP
+    graph on a side stream (run.stream pointed at it during capture), replayed `reps` times
+    between HIP events.  Median and min over the replays, divided by `calls`."""
+    import torch
+    keep = run.stream
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run.stream = side
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.stream = torch.cuda.current_stream()
+        for _ in range(calls):
+            fn()
+    run.stream = keep
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b) / calls)
+    t = np.asarray(times)
+    return {"median_ms": round(float(np.median(t)), 5), "min_ms": round(float(t.min()), 5),
+            "calls_per_graph": calls, "replays": reps}
+
+
 def tflops(flops, ms):
     return flops / (ms * 1e-3) / 1e12
 
@@ -389,6 +423,8 @@ def main():
             inp = wl.make_attention_inputs(wc)
             run = Attn(ra, wc, False, inp=inp)
             t = timed(run.stream, run.fwd, min_s)
+            if t["median_ms"] < 0.1:   # launch-bound: the kernel's own time from a HIP graph
+                t = {**t, "graph": timed_graph(run, run.fwd)}
             skip = run.fwd_counted()
             del run
             torch.cuda.empty_cache()
@@ -407,7 +443,8 @@ def main():
         if name == MAIN and need_grad:
             configs[name]["fwd_bwd"] = {**step_t, "tflops": round(tflops(flops_step, step_t["median_ms"]), 3)}
         log(f"{name}: forward median {t['median_ms']:.4f} ms ({tf:.1f} TFLOP/s), "
-            f"skipped tiles {skip['skipped_fraction']:.4f}")
+            f"skipped tiles {skip['skipped_fraction']:.4f}"
+            + (f"; in a HIP graph {t['graph']['median_ms']:.4f} ms per call" if "graph" in t else ""))
         heads = {"fp32_noncausal_B1_H2_N128_D64": 2, "bf16_causal_B2_H12_N128_D64": 12,
                  "bf16_causal_B8_H16_N2048_D64_sigma2": 8, GQA: 4, MAIN: 3}[name]
         cpu_samples[name] = (wc, inp, heads, name == MAIN and need_grad)
@@ -521,14 +558,17 @@ def main():
         if st != 0:
             raise RuntimeError(f"ra_attn_decode: {ra.ra_status_string(st)}")
     dec_t = timed(dec.stream, decode_step, min_s)
+    dec_t["graph"] = timed_graph(dec, decode_step, calls=32)   # the three kernels, no launch gaps
     kv_bytes = int(lens_np.astype(np.int64).sum()) * wd.Hkv * wd.D * 2 * dec.q.element_size()
     dec_gbs = kv_bytes / (dec_t["median_ms"] * 1e-3) / 1e9
+    dec_t["graph"]["GB/s"] = round(kv_bytes / (dec_t["graph"]["median_ms"] * 1e-3) / 1e9, 1)
     keep = torch.arange(wd.Nk, device="cuda")[None, :] < lens[:, None]
     kpm = (keep, ra.RA_MASK_BOOL, (wd.Nk, 0, 0, 1))
     br = ra.RA_CAUSAL_BOTTOM_RIGHT   # one query row: every key below the sample's length
     decf_t = timed(dec.stream, lambda: dec.fwd_masked(kpm, br), min_s)
-    log(f"decode: {dec_t['median_ms']:.4f} ms, {dec_gbs:.0f} GB/s of K/V; tiled forward with the "
-        f"lengths as a mask {decf_t['median_ms']:.4f} ms")
+    log(f"decode: {dec_t['median_ms']:.4f} ms, {dec_gbs:.0f} GB/s of K/V (in a HIP graph "
+        f"{dec_t['graph']['median_ms']:.4f} ms, {dec_t['graph']['GB/s']:.0f} GB/s); tiled forward "
+        f"with the lengths as a mask {decf_t['median_ms']:.4f} ms")
     del dec, dws, keep
     torch.cuda.empty_cache()
 
