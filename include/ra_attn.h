@@ -321,7 +321,8 @@ int ra_rope_neox(const void* x, void* y, const int32_t* positions, int64_t mats,
  *   q: [B, Hq, Nq, D] and k: [B, Hkv, Nk, D], unrotated.  k_rot: caller's [B, Hkv, Nk, D] buffer
  *   that receives the rotated keys (one rotation pass over K before the attention kernel); it
  *   may be k itself (k is then overwritten).  q_rot: optional [B, Hq, Nq, D] (NULL to skip)
- *   that receives the rotated queries, for ra_attn_bwd_rope; it must not overlap q.
+ *   that receives the rotated queries, for ra_attn_bwd_rope.  q_rot and k_rot must not
+ *   overlap q, v, o or stats (k_rot may be k, see above).
  *   q_positions: device int32 [Nq], k_positions: int32 [Nk], or NULL for 0..N-1, shared by
  *   every batch and head; they set the rotation only (the causal mode still compares row and
  *   key indices).  theta: the base of the frequency schedule theta^(-2j/D).
