@@ -9,8 +9,9 @@ the C ABI.
   oracle of attention on rotated rows: O within the bf16 tolerance of the exact function, m and l
   within bounds derived from the bf16 rounding of the rotated rows (tests/parity.py).
 * The backward against the oracle's gradient with respect to the unrotated rows (near ties of the
-  row max within the same rounding bound accepted either way), and, at the full grouped-query
-  size, against the unfused chain (ra_attn_bwd on the rotated rows, then the inverse rotation).
+  row max within the same rounding bound accepted either way), on small cases and on every
+  (batch, K/V head) group of the grouped-query workload, and, at that size, against the unfused
+  chain (ra_attn_bwd on the rotated rows, then the inverse rotation).
 """
 import numpy as np
 import pytest
@@ -219,3 +220,22 @@ def test_grouped_query_backward_against_the_unfused_chain(gpu_lib):
         excess = np.abs(a - b) - 1.01 * 2.0 ** -7 * _pair_norm(b) - 1e-30
         print(f"{name}: max |fused - chain| {np.abs(a - b).max():.3e}, max |chain| {np.abs(b).max():.3e}")
         assert excess.max() <= 0, f"{name}: beyond two bf16 roundings by {excess.max():.3e}"
+
+
+def test_grouped_query_backward_every_group(gpu_lib):
+    """The fused backward of the grouped-query workload against the oracle's gradient with
+    respect to the unrotated rows, on every (batch, K/V head) group; near ties of the row max
+    within the rounding bound of the rotated rows are taken either way (tests/parity.py)."""
+    w = wl.WORKLOADS[GQA]
+    inp = wl.make_unrotated_inputs(w)
+    dims = (w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D)
+    qt, kt, vt, dot = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    print(f"fused backward {GQA}: every group", flush=True)
+    o, stats, q_rot, k_rot = fused_fwd(gpu_lib, qt, kt, vt, dims, 1, w.scale, w.rope_theta, None, None)
+    dq, dk, dv = fused_bwd(gpu_lib, q_rot, k_rot, vt, o, dot, stats, dims, 1, w.scale, w.rope_theta,
+                           None, None)
+    import torch
+    torch.cuda.synchronize()
+    res = parity.bwd_all_groups(to_np(dq), to_np(dk), to_np(dv), inp, True, w.scale, "bf16",
+                                rope={"theta": w.rope_theta, "q_positions": None, "k_positions": None})
+    print(f"{GQA} fused backward: {res}")
