@@ -327,7 +327,8 @@ int ra_rope_neox(const void* x, void* y, const int32_t* positions, int64_t mats,
  *   every batch and head; they set the rotation only (the causal mode still compares row and
  *   key indices).  theta: the base of the frequency schedule theta^(-2j/D).
  *   o, stats, causal, scale: as ra_attn_fwd, on the rotated rows.
- *   dtype: RA_BF16 only (RA_ERR_DTYPE otherwise).  No mask.  theta not finite or <= 0 ->
+ *   dtype: RA_BF16 or RA_F32 (for fp32 the rotated rows are the fp32 rows ra_rope_neox gives).
+ *   No mask.  theta not finite or <= 0 ->
  *   RA_ERR_SCALE.  Sizes, limits and the other errors as ra_attn_fwd; k_rot NULL with Nk > 0
  *   -> RA_ERR_NULLPTR.  Nk == 0: o = 0, stats (-inf, 0), and q_rot is still written.
  */
@@ -346,10 +347,9 @@ int ra_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float
  *   stats (nullable: recomputed), workspace, workspace_bytes (ra_attn_bwd_workspace_bytes),
  *   causal, scale: as ra_attn_bwd.  q_positions, k_positions, theta: those of the forward.
  *   dq [B, Hq, Nq, D], dk [B, Hkv, Nk, D]: rotated back inside the kernels' epilogues (each
- *   element is the fp32 accumulator rotated by the negative angle, rounded once to bf16);
+ *   element is the fp32 accumulator rotated by the negative angle, rounded once to the dtype);
  *   dv as ra_attn_bwd.
- *   dtype: RA_BF16 only.  Errors as ra_attn_bwd, plus RA_ERR_DTYPE and RA_ERR_SCALE as
- *   ra_attn_fwd_rope.
+ *   dtype: RA_BF16 or RA_F32.  Errors as ra_attn_bwd, plus RA_ERR_SCALE as ra_attn_fwd_rope.
  */
 int ra_attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const void* o,
                      const void* d_o, const float* stats, void* dq, void* dk, void* dv,

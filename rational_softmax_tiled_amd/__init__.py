@@ -606,12 +606,12 @@ class _RopeAttentionFn:
 def ra_attention_rope(q, k, v, is_causal=False, theta: float = 10000.0,
                       scale: Optional[float] = None, q_positions=None, k_positions=None):
     """ra_attention on q and k rotated by the NEOX rotary embedding (ra_rope), the query rotation
-    fused into the attention kernel.  q, k unrotated, bf16, shapes and causal modes as
+    fused into the attention kernel.  q, k unrotated, bf16 or fp32, shapes and causal modes as
     ra_attention; positions default to 0..N-1.  Differentiable in q, k and v (the gradients
     are with respect to the unrotated q and k)."""
     import torch
-    if q.dtype != torch.bfloat16:
-        raise TypeError("ra_attention_rope supports bfloat16")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("ra_attention_rope supports bfloat16 and float32")
     D = q.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     return _RopeAttentionFn.get().apply(q, k, v, causal_code(is_causal), float(theta), scale,

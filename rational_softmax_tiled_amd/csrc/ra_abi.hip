@@ -329,7 +329,7 @@ int ra_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void*
 
 // ---- attention with the NEOX rotary embedding fused in
 static int check_rope(double theta, int dtype, const int32_t* q_positions, const int32_t* k_positions) {
-  if (dtype != RA_BF16) return RA_ERR_DTYPE;
+  if (dtype != RA_BF16 && dtype != RA_F32) return RA_ERR_DTYPE;
   if (!(theta > 0.0) || !isfinite(theta)) return RA_ERR_SCALE;
   if ((q_positions != nullptr && !aligned(q_positions, 4)) || (k_positions != nullptr && !aligned(k_positions, 4)))
     return RA_ERR_ALIGN;
@@ -360,11 +360,11 @@ int ra_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float
     if (st == RA_OK && stats != nullptr)
       st = hip_status(ra::launch_fill_pairs(stats, -INFINITY, 0.0f, (size_t)rows, s));
     if (st == RA_OK && q_rot != nullptr)
-      st = hip_status(ra::launch_rope_neox(q, q_rot, q_positions, B * Hq, Nq, D, theta, false, true, s));
+      st = hip_status(ra::launch_rope_neox(q, q_rot, q_positions, B * Hq, Nq, D, theta, false, dtype == RA_BF16, s));
     return st;
   }
   // K once, by the standalone rotation, into k_rot; Q in the attention kernel, on load
-  st = hip_status(ra::launch_rope_neox(k, k_rot, k_positions, B * Hkv, Nk, D, theta, false, true, s));
+  st = hip_status(ra::launch_rope_neox(k, k_rot, k_positions, B * Hkv, Nk, D, theta, false, dtype == RA_BF16, s));
   if (st != RA_OK) return st;
   ra::AttnProblem p = make_problem(q, k_rot, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr);
   p.rope = true;

@@ -86,17 +86,18 @@ struct BwdArgs {
 // the same lane.  The value turned is s * (acc + radd * add), as store_quad_scaled forms it;
 // add[db][r4][e] holds the matching addend.  cs(pr, j) gives (cos, sin) of the inverse turn of
 // pair pr = (db * 4 + r4) * 4 + e of the lane, channel j.
-template <int D, typename CS>
-__device__ __forceinline__ void store_row_unrotated(bf16* row, const f32x16* acc, float s,
+template <typename T, int D, typename CS>
+__device__ __forceinline__ void store_row_unrotated(T* row, const f32x16* acc, float s,
                                                     const float (*add)[4][4], float radd, CS&& cs,
                                                     int lane) {
   constexpr int DB = D / 32;
+  using quad_t = typename Ty<T>::quad;
 #pragma unroll
   for (int db = 0; db < DB / 2; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
-      bf16x4 lo, hi;
+      quad_t lo, hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x1 = s * fmaf(radd, add[db][r4][e], acc[db][4 * r4 + e]);
@@ -104,11 +105,11 @@ __device__ __forceinline__ void store_row_unrotated(bf16* row, const f32x16* acc
         const f32x2 v = cs((db * 4 + r4) * 4 + e, d0 + e);
         float y1, y2;
         rope_pair(x1, x2, v[0], v[1], y1, y2);
-        lo[e] = (bf16)y1;
-        hi[e] = (bf16)y2;
+        lo[e] = (T)y1;
+        hi[e] = (T)y2;
       }
-      *reinterpret_cast<bf16x4*>(row + d0) = lo;
-      *reinterpret_cast<bf16x4*>(row + d0 + D / 2) = hi;
+      *reinterpret_cast<quad_t*>(row + d0) = lo;
+      *reinterpret_cast<quad_t*>(row + d0 + D / 2) = hi;
     }
 }
 
@@ -167,7 +168,9 @@ template <> __device__ __forceinline__ f32x8 pack_frag<float>(const f32x16& s, i
 
 // ------------------------------------------------------------------ query-parallel: dQ, R, a
 
-template <typename T, int D, int BN, bool CAUSAL, bool MASKED>
+// ROPE: q and k hold the rotated rows; dQ is turned back by the inverse rotation before it is
+// stored (the angles formed per lane in the epilogue).
+template <typename T, int D, int BN, bool CAUSAL, bool MASKED, bool ROPE = false>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
   using frag_t = typename Ty<T>::frag;
   constexpr int PAD = 16 / sizeof(T);
@@ -178,8 +181,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T k_lds[BN * PK];
   __shared__ __attribute__((aligned(16))) T v_lds[BN * PK];
   __shared__ __attribute__((aligned(16))) T kt_lds[D * PT];
+  __shared__ double rate_lds[ROPE ? D / 2 : 1];   // ROPE: theta^(-2j/D) per pair j
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (ROPE) {
+    if (tid < D / 2) rate_lds[tid] = rope_rate(tid, D, a.log2_theta);
+    __syncthreads();
+  }
   const int logical = xcd_remap(blockIdx.x, a.total_wg);
   const int bg = logical / a.wg_per_group;
   int wig = logical % a.wg_per_group;
@@ -287,16 +295,32 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
     const bool has_max = amax < a.Nk;
     const T* krow = kg + (size_t)(has_max ? amax : 0) * D;
     const float radd = has_max ? R : 0.0f;
+    if constexpr (ROPE) {
+      float kv[DB][4][4];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
-        float kv[4];
+        for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kv[e] = to_f(krow[d0 + e]);
-        store_quad_scaled<T>(dqrow + d0, acc[db], 4 * r4, a.scale, kv, radd);
-      }
+          for (int e = 0; e < 4; ++e) kv[db][r4][e] = to_f(krow[db * 32 + 8 * r4 + 4 * (lane >> 5) + e]);
+      const double pos = a.q_pos != nullptr ? (double)a.q_pos[qi] : (double)qi;
+      store_row_unrotated<T, D>(dqrow, acc, a.scale, kv, radd, [&](int, int j) {
+        float c, sn;
+        rope_cs(pos, rate_lds[j], true, c, sn);
+        return f32x2{c, sn};
+      }, lane);
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
+          float kv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kv[e] = to_f(krow[d0 + e]);
+          store_quad_scaled<T>(dqrow + d0, acc[db], 4 * r4, a.scale, kv, radd);
+        }
+    }
     if (lane < 32) {
       a.c[head + qi] = cval;
       a.r[head + qi] = R;
@@ -310,7 +334,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ key-parallel: dK, dV
 
-template <typename T, int D, bool CAUSAL, bool MASKED>
+// ROPE: dK is turned back by the inverse rotation before it is stored.
+template <typename T, int D, bool CAUSAL, bool MASKED, bool ROPE = false>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
   using frag_t = typename Ty<T>::frag;
   constexpr int PAD = 16 / sizeof(T);
@@ -331,8 +356,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float st_cil[kQTile];
   __shared__ __attribute__((aligned(16))) float st_r[kQTile];
   __shared__ __attribute__((aligned(16))) int st_a[kQTile];
+  __shared__ double rate_lds[ROPE ? D / 2 : 1];   // ROPE: theta^(-2j/D) per pair j
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (ROPE) {
+    if (tid < D / 2) rate_lds[tid] = rope_rate(tid, D, a.log2_theta);
+    __syncthreads();
+  }
   const int logical = xcd_remap(blockIdx.x, a.total_kwg);
   const int bg = logical / a.kwg_per_group;
   const int kb = logical % a.kwg_per_group;   // low key blocks (most causal work) first
@@ -469,12 +499,21 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
     T* dkrow = static_cast<T*>(a.dk) + (kvbase + key) * D;
     T* dvrow = static_cast<T*>(a.dv) + (kvbase + key) * D;
     const float zero4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (ROPE) {
+      const float zero[DB][4][4] = {};
+      const double pos = a.k_pos != nullptr ? (double)a.k_pos[key] : (double)key;
+      store_row_unrotated<T, D>(dkrow, acc_dk, a.scale, zero, 0.0f, [&](int, int j) {
+        float c, sn;
+        rope_cs(pos, rate_lds[j], true, c, sn);
+        return f32x2{c, sn};
+      }, lane);
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = db * 32 + 8 * r4 + 4 * (lane >> 5);
-        store_quad_scaled<T>(dkrow + d0, acc_dk[db], 4 * r4, a.scale, zero4, 0.0f);
+        if constexpr (!ROPE) store_quad_scaled<T>(dkrow + d0, acc_dk[db], 4 * r4, a.scale, zero4, 0.0f);
         store_quad_scaled<T>(dvrow + d0, acc_dv[db], 4 * r4, 1.0f, zero4, 0.0f);
       }
   }
@@ -699,7 +738,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
         for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
           for (int e = 0; e < 4; ++e) kv[db][r4][e] = (float)krow[db * 32 + 8 * r4 + 4 * (lane >> 5) + e];
-      store_row_unrotated<D>(dqrow, acc, a.scale, kv, radd,
+      store_row_unrotated<bf16, D>(dqrow, acc, a.scale, kv, radd,
                              [&](int pr, int) { return cs_tab[pr * kWave + lane]; }, lane);
     } else {
 #pragma unroll
@@ -1080,7 +1119,7 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
           for (int e = 0; e < 4; ++e) ak[db][i4][e] = pk[e];
         }
       const double pos = a.k_pos != nullptr ? (double)a.k_pos[key] : (double)key;
-      store_row_unrotated<D>(dkrow, acc_dk, a.scale, ak, 1.0f, [&](int, int j) {
+      store_row_unrotated<bf16, D>(dkrow, acc_dk, a.scale, ak, 1.0f, [&](int, int j) {
         float c, sn;
         rope_cs(pos, rate_lds[j], true, c, sn);
         return f32x2{c, sn};
@@ -1149,17 +1188,26 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   const bool keypad = kBf16 && p.mask_kind == kMaskBool && p.msq == 0 && p.msh == 0 && p.msk == 1 &&
                       p.msb % 4 == 0 && p.Nk % 4 == 0 &&
                       reinterpret_cast<unsigned long long>(p.mask) % 4 == 0;
-  if (p.rope) {   // bf16, no explicit mask: the host checks both
-    if constexpr (kBf16) {
-      if (phases & kBwdDq) {
+  if (p.rope) {   // no explicit mask: the host checks it
+    if (masked) return hipErrorInvalidValue;
+    if (phases & kBwdDq) {
+      if constexpr (kBf16) {
         if (p.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, false, true>), qgrid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, false, false, true>), qgrid, block, 0, stream, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+      } else {
+        if (p.causal) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, false, true>), qgrid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false, false, true>), qgrid, block, 0, stream, a);
       }
-      if (phases & kBwdDkdv) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (phases & kBwdDkdv) {
+      if constexpr (kBf16) {
         if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, false, false, true>), kgrid, kblock, 0, stream, a);
         else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, false, false, true>), kgrid, kblock, 0, stream, a);
+      } else {
+        if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true, false, true>), kgrid, kblock, 0, stream, a);
+        else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false, false, true>), kgrid, kblock, 0, stream, a);
       }
     }
     return hipGetLastError();

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   __shared__ float tmax_lds[kWaves][kMaxTiles];
   __shared__ float kmin_lds[kWaves];
   static_assert(!KEYPAD || (sizeof(T) == 2 && WRITE_O && !MASKED && BN == kWave), "key padding path");
-  static_assert(!ROPE || (sizeof(T) == 2 && WRITE_O && !MASKED && !KEYPAD && !COUNT), "rotary path");
+  static_assert(!ROPE || (WRITE_O && !MASKED && !KEYPAD && !COUNT), "rotary path");
   __shared__ __attribute__((aligned(16))) unsigned mstage_lds[KEYPAD ? 4 : 1][KEYPAD ? kWave : 1];
   __shared__ unsigned long long keep_lds[KEYPAD ? kMaxTiles : 1];
   __shared__ double rate_lds[ROPE ? D / 2 : 1];   // ROPE: theta^(-2j/D) per pair j
@@ -207,11 +207,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 
   // ROPE: turn the Q fragments by the NEOX rotary embedding.  Channel j < D/2 and its partner
   // j + D/2 sit in fragments kc and kc + KC/2 of the same lane (element j % 8), so the rotation is
-  // lane-local.  The (cos, sin) pairs go through LDS, stage 3 of pass 1 (free until its first
-  // step), so that the angle loops stay rolled while the fragments are indexed statically.  When
+  // lane-local.  The (cos, sin) pairs go through LDS, the second V buffer (stage 3 of the bf16
+  // K ring, free until pass 1's first step; for fp32 idle until pass 2), so that the angle loops
+  // stay rolled while the fragments are indexed statically.  When
   // the four waves hold the same query rows (rep a multiple of four) they split one table;
-  // otherwise each wave fills its own, one fragment pair at a time.  Runs while pass 1's first
-  // tiles are in flight; q_rot, when given, receives the rotated rows.
+  // otherwise each wave fills its own, one fragment pair at a time.  For bf16 it runs while pass
+  // 1's first tiles are in flight; q_rot, when given, receives the rotated rows.
   auto rope_rotate = [&]() {
     if constexpr (ROPE) {
       constexpr int NP = D / 4;   // pairs per lane
@@ -332,9 +333,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     if (nt >= 3) wait_younger(std::integral_constant<int, 2>{});
     else if (nt == 2) wait_younger(std::integral_constant<int, 1>{});
     else wait_vmem();
-  } else if (nt > 0) {
-    k_issue(0, k_lds[0]);
-    k_land(k_lds[0]);
+  } else {
+    if constexpr (ROPE) rope_rotate();
+    if (nt > 0) {
+      k_issue(0, k_lds[0]);
+      k_land(k_lds[0]);
+    }
   }
   __syncthreads();
   // one step of pass 1 on tile kt, held in stage S
@@ -694,11 +698,9 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   const bool keypad = sizeof(T) == 2 && o != nullptr && !counters && p.mask_kind == kMaskBool && p.msq == 0 &&
                       p.msh == 0 && p.msk == 1 && p.msb % 4 == 0 && p.Nk % 4 == 0 &&
                       reinterpret_cast<unsigned long long>(p.mask) % 4 == 0 && (p.Nk + BN - 1) / BN <= kMaxTiles;
-  if (p.rope) {   // bf16 only; the host rejects masks and counters with the rotary embedding
-    if (sizeof(T) != 2 || o == nullptr || counters != nullptr || p.mask_kind != kMaskNone)
-      return hipErrorInvalidValue;
-    if constexpr (sizeof(T) == 2)
-      hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, false, true>), grid, block, 0, stream, a);
+  if (p.rope) {   // the host rejects masks and counters with the rotary embedding
+    if (o == nullptr || counters != nullptr || p.mask_kind != kMaskNone) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, false, true>), grid, block, 0, stream, a);
   } else if (keypad) {
     if constexpr (sizeof(T) == 2 && BN == kWave)
       hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, true>), grid, block, 0, stream, a);

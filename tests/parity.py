@@ -113,10 +113,10 @@ def fwd_all_heads(o, stats, inp, causal, scale, dtype, heads=None):
 
 
 def fwd_rope_all_heads(o, stats, inp, causal, scale, theta, q_positions=None, k_positions=None,
-                       heads=None):
-    """fwd_all_heads for attention on rotated rows: inp holds the UNROTATED bf16 q and k.  O is
+                       heads=None, dtype="bf16"):
+    """fwd_all_heads for attention on rotated rows: inp holds the UNROTATED q and k.  O is
     compared with the exact function (ra_attention_rope_fwd).  The GPU scores the rotated rows
-    rounded to bf16, so m and l are held to bounds derived from rope_score_bound per row:
+    in the dtype, so m and l are held to bounds derived from rope_score_bound per row:
     |m~ - m| <= t_i = max_j b_ij over the allowed keys, and, with |delta Delta_ij| <= b_ij + t_i
     and |phi'| <= phi^(7/8) (phi decreasing in Delta),
     |l~ - l| <= sum_j (b_ij + t_i) phi(max(Delta_ij - b_ij - t_i, 0))^(7/8); each plus the fp32
@@ -138,7 +138,7 @@ def fwd_rope_all_heads(o, stats, inp, causal, scale, theta, q_positions=None, k_
                                                      q_positions, k_positions)
         qh = oracle.rope_neox(q[b, h].astype(np.float64), theta, q_positions)
         kg = oracle.rope_neox(k[b, g].astype(np.float64), theta, k_positions)
-        bnd = np.where(allowed, rope_score_bound(qh, kg, scale), 0.0)
+        bnd = np.where(allowed, rope_score_bound(qh, kg, scale, dtype), 0.0)
         t = bnd.max(axis=1)
         s = scale * (qh @ kg.T)
         m0 = rm[0, 0]
@@ -154,7 +154,7 @@ def fwd_rope_all_heads(o, stats, inp, causal, scale, theta, q_positions=None, k_
                 float(np.max(em, initial=-np.inf)), float(np.max(el, initial=-np.inf)),
                 float(t.max(initial=0.0)))
 
-    tal = Tally("o", "bf16", grad=False)
+    tal = Tally("o", dtype, grad=False)
     em_max = el_max = -np.inf
     t_max = 0.0
     for bh, eo, mo, em, el, tm in _pool_map(one, todo):
@@ -176,22 +176,23 @@ def score_error_bound(qh, kg, scale):
     return gamma * scale * (np.abs(qh) @ np.abs(kg).T)
 
 
-def rope_score_bound(qh, kg, scale):
-    """|GPU score - exact score| per (i, j) when the GPU multiplies the rotated rows rounded to
-    bf16 (qh, kg: the exactly rotated rows of one head).  Each rotated element is the fp32
-    rotation (error below 2^-20 times its pair's norm n) rounded to bf16 (relative 2^-8), so
-    |delta q_d| <= e A_d with e = 2^-8, A = |q| + 2^-12 n; then |q~.k~ - q.k| <=
-    (2e + e^2) A_q . A_k, plus the fp32 dot product of the rounded rows, gamma_D (1 + e)^2
-    A_q . A_k."""
+def rope_score_bound(qh, kg, scale, dtype="bf16"):
+    """|GPU score - exact score| per (i, j) when the GPU multiplies rotated rows (qh, kg: the
+    exactly rotated rows of one head).  Each rotated element is the fp32 rotation, within
+    2^-20 times its pair's norm n, then rounded to the dtype (bf16: relative 2^-8; fp32: 2^-24),
+    so |delta q_d| <= E_d = e |q_d| + 1.004 * 2^-20 n_d.  Then |q~.k~ - q.k| <= E_q.|k| + |q|.E_k
+    + E_q.E_k, plus the fp32 dot product of the rotated rows, gamma_D (|q| + E_q).(|k| + E_k)."""
     D = qh.shape[-1]
-    e = 2.0 ** -8
+    e = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
     gamma = D * U32 / (1 - D * U32)
 
-    def amp(x):
+    def err(x):
         h = D // 2
         n = np.sqrt(x[:, :h] ** 2 + x[:, h:] ** 2)
-        return np.abs(x) + 2.0 ** -12 * np.concatenate([n, n], axis=1)
-    return scale * (2 * e + e * e + gamma * (1 + e) ** 2) * (amp(qh) @ amp(kg).T)
+        return e * np.abs(x) + 1.004 * 2.0 ** -20 * np.concatenate([n, n], axis=1)
+    eq, ek = err(qh), err(kg)
+    aq, ak = np.abs(qh), np.abs(kg)
+    return scale * (eq @ ak.T + aq @ ek.T + eq @ ek.T + gamma * ((aq + eq) @ (ak + ek).T))
 
 
 def near_tie_candidates(qh, kg, scale, causal, Nq, Nk, es=None):
@@ -246,7 +247,7 @@ def bwd_all_groups(dq, dk, dv, inp, causal, scale, dtype, groups=None, rope=None
             qg = [oracle.rope_neox(x, rope["theta"], rope["q_positions"]) for x in qg]
         ties = {}
         for r in range(rep):
-            es = None if rope is None else rope_score_bound(qg[r], kg, scale)
+            es = None if rope is None else rope_score_bound(qg[r], kg, scale, dtype)
             ties[r] = near_tie_candidates(qg[r], kg, scale, causal, Nq, Nk, es)
         ref = bwd(*args)
         n_tie = sum(len(t) for t in ties.values())

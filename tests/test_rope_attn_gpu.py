@@ -37,11 +37,16 @@ def _dev_pos(p):
     return None if p is None else torch.as_tensor(p, dtype=torch.int32, device="cuda")
 
 
-def _inputs(B, Hq, Hkv, Nq, Nk, D, seed, sigma=1.0):
+def _inputs(B, Hq, Hkv, Nq, Nk, D, seed, sigma=1.0, dtype="bf16"):
     rng = np.random.default_rng(seed)
-    r = lambda *s, sg=1.0: wl.round_to_dtype(rng.standard_normal(s, dtype=np.float32) * np.float32(sg), "bf16")
+    r = lambda *s, sg=1.0: wl.round_to_dtype(rng.standard_normal(s, dtype=np.float32) * np.float32(sg), dtype)
     return {"q": r(B, Hq, Nq, D, sg=sigma), "k": r(B, Hkv, Nk, D, sg=sigma), "v": r(B, Hkv, Nk, D),
             "do": r(B, Hq, Nq, D)}
+
+
+def _code(ra, t):
+    import torch
+    return ra.RA_BF16 if t.dtype == torch.bfloat16 else ra.RA_F32
 
 
 def fused_fwd(ra, qt, kt, vt, dims, causal, scale, theta, qp, kp, with_qrot=True):
@@ -52,7 +57,7 @@ def fused_fwd(ra, qt, kt, vt, dims, causal, scale, theta, qp, kp, with_qrot=True
     q_rot = torch.empty_like(qt) if with_qrot else None
     k_rot = torch.empty_like(kt)
     st = ra.ra_attn_fwd_rope(qt, kt, vt, o, stats, q_rot, k_rot, _dev_pos(qp), _dev_pos(kp), theta,
-                             B, Hq, Hkv, Nq, Nk, D, causal, scale, ra.RA_BF16)
+                             B, Hq, Hkv, Nq, Nk, D, causal, scale, _code(ra, qt))
     assert st == 0, ra.ra_status_string(st)
     return o, stats, q_rot, k_rot
 
@@ -61,11 +66,11 @@ def chain_fwd(ra, qt, kt, vt, dims, causal, scale, theta, qp, kp):
     import torch
     B, Hq, Hkv, Nq, Nk, D = dims
     qr, kr = torch.empty_like(qt), torch.empty_like(kt)
-    assert ra.ra_rope_neox(qt, qr, _dev_pos(qp), B * Hq, Nq, D, theta, False, ra.RA_BF16) == 0
-    assert ra.ra_rope_neox(kt, kr, _dev_pos(kp), B * Hkv, Nk, D, theta, False, ra.RA_BF16) == 0
+    assert ra.ra_rope_neox(qt, qr, _dev_pos(qp), B * Hq, Nq, D, theta, False, _code(ra, qt)) == 0
+    assert ra.ra_rope_neox(kt, kr, _dev_pos(kp), B * Hkv, Nk, D, theta, False, _code(ra, qt)) == 0
     o = torch.empty_like(qt)
     stats = torch.empty((B, Hq, Nq, 2), dtype=torch.float32, device="cuda")
-    st = ra.ra_attn_fwd(qr, kr, vt, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, ra.RA_BF16)
+    st = ra.ra_attn_fwd(qr, kr, vt, o, stats, B, Hq, Hkv, Nq, Nk, D, causal, scale, _code(ra, qt))
     assert st == 0, ra.ra_status_string(st)
     return o, stats, qr, kr
 
@@ -74,44 +79,49 @@ def fused_bwd(ra, q_rot, k_rot, vt, o, dot, stats, dims, causal, scale, theta, q
     import torch
     B, Hq, Hkv, Nq, Nk, D = dims
     dq, dk, dv = torch.empty_like(q_rot), torch.empty_like(k_rot), torch.empty_like(vt)
-    nbytes = ra.ra_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, ra.RA_BF16)
+    nbytes = ra.ra_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, _code(ra, q_rot))
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     st = ra.ra_attn_bwd_rope(q_rot, k_rot, vt, o, dot, stats, dq, dk, dv, ws, nbytes, _dev_pos(qp),
-                             _dev_pos(kp), theta, B, Hq, Hkv, Nq, Nk, D, causal, scale, ra.RA_BF16)
+                             _dev_pos(kp), theta, B, Hq, Hkv, Nq, Nk, D, causal, scale, _code(ra, q_rot))
     assert st == 0, ra.ra_status_string(st)
     return dq, dk, dv
 
 
-def rotation_bound_check(gpu, x, theta, positions, what):
-    """|gpu - exact| <= 2^-8 |exact| + 2^-19 n per element (n: the norm of its pair)."""
+def rotation_bound_check(gpu, x, theta, positions, what, dtype="bf16"):
+    """|gpu - exact| <= e |exact| + 2^-19 n per element (n: the norm of its pair; e = 2^-8 for
+    bf16, 2^-24 for fp32)."""
     ex = oracle.rope_neox(x, theta, positions)
     h = ex.shape[-1] // 2
     n = np.sqrt(ex[..., :h] ** 2 + ex[..., h:] ** 2)
     n = np.concatenate([n, n], axis=-1)
-    excess = np.abs(gpu - ex) - (2.0 ** -8 * np.abs(ex) + 2.0 ** -19 * n)
+    e = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+    excess = np.abs(gpu - ex) - (e * np.abs(ex) + 2.0 ** -19 * n)
     assert excess.max() <= 0, f"{what}: rotation beyond one bf16 rounding by {excess.max():.3e}"
 
 
 CASES = [
-    # (B, Hq, Hkv, Nq, Nk, D, causal, positions, theta)
-    (1, 2, 1, 200, 200, 64, 1, None, 10000.0),
-    (2, 4, 2, 333, 333, 128, 1, "random", 500000.0),
-    (1, 4, 4, 70, 1000, 128, 2, "random", 10000.0),
-    (1, 2, 2, 129, 77, 64, 0, None, 10000.0),
-    (1, 8, 2, 1, 300, 128, 2, None, 10000.0),
-    (1, 2, 1, 64, 64, 128, 1, "random", 100.0),
+    # (B, Hq, Hkv, Nq, Nk, D, causal, positions, theta, dtype)
+    (1, 2, 1, 200, 200, 64, 1, None, 10000.0, "bf16"),
+    (2, 4, 2, 333, 333, 128, 1, "random", 500000.0, "bf16"),
+    (1, 4, 4, 70, 1000, 128, 2, "random", 10000.0, "bf16"),
+    (1, 2, 2, 129, 77, 64, 0, None, 10000.0, "bf16"),
+    (1, 8, 2, 1, 300, 128, 2, None, 10000.0, "bf16"),
+    (1, 2, 1, 64, 64, 128, 1, "random", 100.0, "bf16"),
+    (1, 2, 1, 100, 100, 64, 1, "random", 10000.0, "f32"),
+    (1, 8, 2, 70, 130, 128, 2, None, 500000.0, "f32"),
+    (1, 3, 3, 45, 33, 64, 0, None, 10000.0, "f32"),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
 def test_fused_forward_equals_the_unfused_chain(gpu_lib, case):
     import torch
-    B, Hq, Hkv, Nq, Nk, D, causal, pk, theta = case
+    B, Hq, Hkv, Nq, Nk, D, causal, pk, theta, dt = case
     dims = (B, Hq, Hkv, Nq, Nk, D)
-    inp = _inputs(B, Hq, Hkv, Nq, Nk, D, seed=Nq + Nk + D)
+    inp = _inputs(B, Hq, Hkv, Nq, Nk, D, seed=Nq + Nk + D, dtype=dt)
     qp, kp = _positions(pk, Nq, 1), _positions(pk, Nk, 2)
     scale = float(np.float32(1 / np.sqrt(D)))
-    qt, kt, vt = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    qt, kt, vt = (to_dev(inp[n], dt) for n in ("q", "k", "v"))
     print(f"fused forward {case}", flush=True)
     o, stats, q_rot, k_rot = fused_fwd(gpu_lib, qt, kt, vt, dims, causal, scale, theta, qp, kp)
     o2 = fused_fwd(gpu_lib, qt, kt, vt, dims, causal, scale, theta, qp, kp, with_qrot=False)[0]
@@ -120,22 +130,28 @@ def test_fused_forward_equals_the_unfused_chain(gpu_lib, case):
     assert torch.equal(q_rot, qr) and torch.equal(k_rot, kr)
     assert torch.equal(o, ro) and torch.equal(o2, ro)
     assert torch.equal(stats, rstats)
-    rotation_bound_check(to_np(q_rot), inp["q"], theta, qp, "q_rot")
-    rotation_bound_check(to_np(k_rot), inp["k"], theta, kp, "k_rot")
+    rotation_bound_check(to_np(q_rot), inp["q"], theta, qp, "q_rot", dt)
+    rotation_bound_check(to_np(k_rot), inp["k"], theta, kp, "k_rot", dt)
+    if dt == "f32":   # fp32: the whole output against the exact function at fp32's bound
+        oc = {0: False, 1: True, 2: "bottom_right"}[causal]
+        res = parity.fwd_rope_all_heads(to_np(o), stats.cpu().numpy().astype(np.float64), inp, oc,
+                                        scale, theta, qp, kp, dtype="f32")
+        print(f"{case}: {res}")
 
 
-def test_no_keys_still_writes_the_rotated_queries(gpu_lib):
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_no_keys_still_writes_the_rotated_queries(gpu_lib, dt):
     import torch
-    inp = _inputs(1, 2, 1, 37, 0, 64, seed=3)
-    qt = to_dev(inp["q"], "bf16")
-    kt = vt = torch.empty((1, 1, 0, 64), dtype=torch.bfloat16, device="cuda")
+    inp = _inputs(1, 2, 1, 37, 0, 64, seed=3, dtype=dt)
+    qt = to_dev(inp["q"], dt)
+    kt = vt = torch.empty((1, 1, 0, 64), dtype=qt.dtype, device="cuda")
     o, stats, q_rot, _ = fused_fwd(gpu_lib, qt, kt, vt, (1, 2, 1, 37, 0, 64), 0, 0.125, 10000.0,
                                    None, None)
     torch.cuda.synchronize()
     assert (to_np(o) == 0).all()
     s = stats.cpu().numpy()
     assert np.isneginf(s[..., 0]).all() and (s[..., 1] == 0).all()
-    rotation_bound_check(to_np(q_rot), inp["q"], 10000.0, None, "q_rot")
+    rotation_bound_check(to_np(q_rot), inp["q"], 10000.0, None, "q_rot", dt)
 
 
 def test_grouped_query_workload_every_head(gpu_lib):
@@ -154,25 +170,27 @@ def test_grouped_query_workload_every_head(gpu_lib):
 
 
 BWD_CASES = [
-    # (B, Hq, Hkv, Nq, Nk, D, causal, positions, theta)
-    (1, 4, 2, 300, 300, 128, 1, "shifted", 10000.0),
-    (2, 2, 1, 200, 520, 64, 2, "random", 500000.0),
-    (1, 2, 2, 150, 90, 64, 0, None, 10000.0),
+    # (B, Hq, Hkv, Nq, Nk, D, causal, positions, theta, dtype)
+    (1, 4, 2, 300, 300, 128, 1, "shifted", 10000.0, "bf16"),
+    (2, 2, 1, 200, 520, 64, 2, "random", 500000.0, "bf16"),
+    (1, 2, 2, 150, 90, 64, 0, None, 10000.0, "bf16"),
+    (1, 2, 1, 96, 96, 64, 1, "shifted", 10000.0, "f32"),
+    (1, 4, 2, 64, 150, 128, 2, "random", 500000.0, "f32"),
 ]
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=[str(c) for c in BWD_CASES])
 def test_fused_backward_against_the_oracle(gpu_lib, case):
     import torch
-    B, Hq, Hkv, Nq, Nk, D, causal, pk, theta = case
+    B, Hq, Hkv, Nq, Nk, D, causal, pk, theta, dt = case
     dims = (B, Hq, Hkv, Nq, Nk, D)
-    inp = _inputs(B, Hq, Hkv, Nq, Nk, D, seed=7 * Nq + Nk)
+    inp = _inputs(B, Hq, Hkv, Nq, Nk, D, seed=7 * Nq + Nk, dtype=dt)
     if pk == "shifted":
         qp, kp = np.arange(Nq, dtype=np.int32) + 17, np.arange(Nk, dtype=np.int32) + 17
     else:
         qp, kp = _positions(pk, Nq, 5), _positions(pk, Nk, 6)
     scale = float(np.float32(1 / np.sqrt(D)))
-    qt, kt, vt, dot = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    qt, kt, vt, dot = (to_dev(inp[n], dt) for n in ("q", "k", "v", "do"))
     print(f"fused backward {case}", flush=True)
     o, stats, q_rot, k_rot = fused_fwd(gpu_lib, qt, kt, vt, dims, causal, scale, theta, qp, kp)
     dq, dk, dv = fused_bwd(gpu_lib, q_rot, k_rot, vt, o, dot, stats, dims, causal, scale, theta, qp, kp)
@@ -182,7 +200,7 @@ def test_fused_backward_against_the_oracle(gpu_lib, case):
     # without the saved statistics the backward recomputes them from the rotated rows
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
     oc = {0: False, 1: True, 2: "bottom_right"}[causal]
-    res = parity.bwd_all_groups(to_np(dq), to_np(dk), to_np(dv), inp, oc, scale, "bf16",
+    res = parity.bwd_all_groups(to_np(dq), to_np(dk), to_np(dv), inp, oc, scale, dt,
                                 rope={"theta": theta, "q_positions": qp, "k_positions": kp})
     print(f"{case}: {res}")
 
