@@ -495,7 +495,7 @@ def main():
 
     def fused_fwd(qr=True):
         ok(ra.ra_attn_fwd_rope(gqa.q, gqa.k, gqa.v, gqa.o, gqa.stats, q_rot if qr else None, k_rot,
-                               None, None, theta, *dims, 1, wg.scale, gqa.code, gqa.stream),
+                               None, None, theta, *dims, 1, wg.scale, gqa.code, stream=gqa.stream),
            "ra_attn_fwd_rope")
 
     def unfused_bwd():
@@ -508,7 +508,7 @@ def main():
     def fused_bwd():
         ok(ra.ra_attn_bwd_rope(q_rot, k_rot, gqa.v, gqa.o, gqa.do, gqa.stats, gqa.dq, gqa.dk, gqa.dv,
                                gqa.ws, gqa.ws_bytes, None, None, theta, *dims, 1, wg.scale, gqa.code,
-                               gqa.stream), "ra_attn_bwd_rope")
+                               stream=gqa.stream), "ra_attn_bwd_rope")
 
     rope_t = timed(gqa.stream, rope_qk, min_s)
     rope_bytes = 2 * (gqa.q.numel() + gqa.k.numel()) * gqa.q.element_size()

@@ -326,9 +326,10 @@ int ra_rope_neox(const void* x, void* y, const int32_t* positions, int64_t mats,
  *   q_positions: device int32 [Nq], k_positions: int32 [Nk], or NULL for 0..N-1, shared by
  *   every batch and head; they set the rotation only (the causal mode still compares row and
  *   key indices).  theta: the base of the frequency schedule theta^(-2j/D).
- *   o, stats, causal, scale: as ra_attn_fwd, on the rotated rows.
+ *   o, stats, causal, scale: as ra_attn_fwd, on the rotated rows.  mask: an explicit mask as
+ *   in ra_attn_fwd_masked (NULL = none), with its checks.
  *   dtype: RA_BF16 or RA_F32 (for fp32 the rotated rows are the fp32 rows ra_rope_neox gives).
- *   No mask.  theta not finite or <= 0 ->
+ *   theta not finite or <= 0 ->
  *   RA_ERR_SCALE.  Sizes, limits and the other errors as ra_attn_fwd; k_rot NULL with Nk > 0
  *   -> RA_ERR_NULLPTR.  Nk == 0: o = 0, stats (-inf, 0), and q_rot is still written.
  */
@@ -336,7 +337,7 @@ int ra_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float
                      void* q_rot, void* k_rot, const int32_t* q_positions,
                      const int32_t* k_positions, double theta, int64_t B, int64_t Hq, int64_t Hkv,
                      int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype,
-                     void* stream);
+                     const ra_mask* mask, void* stream);
 
 /*
  * ra_attn_bwd_rope -- the backward of ra_attn_fwd_rope: the gradients with respect to the
@@ -345,7 +346,8 @@ int ra_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float
  *   maps back by the rotation with the negative angle.
  *   q_rot, k_rot: the rotated rows ra_attn_fwd_rope wrote (q_rot requested there).  v, o, d_o,
  *   stats (nullable: recomputed), workspace, workspace_bytes (ra_attn_bwd_workspace_bytes),
- *   causal, scale: as ra_attn_bwd.  q_positions, k_positions, theta: those of the forward.
+ *   causal, scale: as ra_attn_bwd; mask as ra_attn_bwd_masked (NULL = none).  q_positions,
+ *   k_positions, theta: those of the forward.
  *   dq [B, Hq, Nq, D], dk [B, Hkv, Nk, D]: rotated back inside the kernels' epilogues (each
  *   element is the fp32 accumulator rotated by the negative angle, rounded once to the dtype);
  *   dv as ra_attn_bwd.
@@ -356,7 +358,7 @@ int ra_attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const 
                      void* workspace, size_t workspace_bytes, const int32_t* q_positions,
                      const int32_t* k_positions, double theta, int64_t B, int64_t Hq, int64_t Hkv,
                      int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, int dtype,
-                     void* stream);
+                     const ra_mask* mask, void* stream);
 
 #ifdef __cplusplus
 }

@@ -350,28 +350,30 @@ def ra_attention_bwd(q, k, v, do, causal, scale, groups=None, mask=None, argmax=
 
 
 def ra_attention_rope_fwd(q, k, v, causal, scale, theta, q_rope_positions=None,
-                          k_rope_positions=None):
+                          k_rope_positions=None, mask=None):
     """Attention on rotated queries and keys: O = ra_attention(rope(Q), rope(K), V).
 
     The nurl page, section "Layers", applies nn_rope to the queries and keys of
     a head before the attention core; the "Primitives" page, section "Attention
     and transformers", gives the split-halves pairing.  The rotation positions
     (default 0..N-1) are independent of the causal test, which uses row and key
-    indices as in ra_attention_fwd.  Returns (O, m, l, a) as ra_attention_fwd.
+    indices as in ra_attention_fwd, and so does ``mask`` (as in ra_attention_fwd).  Returns
+    (O, m, l, a) as ra_attention_fwd.
     """
     qr = rope_neox(q, theta, q_rope_positions)
     kr = rope_neox(k, theta, k_rope_positions)
-    return ra_attention_fwd(qr, kr, v, causal, scale)
+    return ra_attention_fwd(qr, kr, v, causal, scale, mask=mask)
 
 
 def ra_attention_rope_bwd(q, k, v, do, causal, scale, theta, q_rope_positions=None,
-                          k_rope_positions=None, groups=None, argmax=None):
+                          k_rope_positions=None, groups=None, argmax=None, mask=None):
     """Gradients (dQ, dK, dV) of L = sum(O * dO) for ra_attention_rope_fwd, with respect to the
     UNROTATED q and k: the attention gradients of the rotated inputs, each mapped back by the
-    transpose of its rotation (the rotation by the negative angle).  ``groups`` and ``argmax``
-    as in ra_attention_bwd."""
+    transpose of its rotation (the rotation by the negative angle).  ``groups``, ``argmax`` and
+    ``mask`` as in ra_attention_bwd."""
     qr = rope_neox(q, theta, q_rope_positions)
     kr = rope_neox(k, theta, k_rope_positions)
-    dqr, dkr, dv = ra_attention_bwd(qr, kr, v, do, causal, scale, groups=groups, argmax=argmax)
+    dqr, dkr, dv = ra_attention_bwd(qr, kr, v, do, causal, scale, groups=groups, argmax=argmax,
+                                    mask=mask)
     return (rope_neox(dqr, theta, q_rope_positions, inverse=True),
             rope_neox(dkr, theta, k_rope_positions, inverse=True), dv)

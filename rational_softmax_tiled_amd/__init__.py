@@ -132,12 +132,12 @@ def load_library():
     lib.ra_rope_neox.restype = ctypes.c_int
     lib.ra_attn_fwd_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_double,
                                      _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
-                                     ctypes.c_float, ctypes.c_int, _vp]
+                                     ctypes.c_float, ctypes.c_int, _mp, _vp]
     lib.ra_attn_fwd_rope.restype = ctypes.c_int
     lib.ra_attn_bwd_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      ctypes.c_size_t, _vp, _vp, ctypes.c_double, _i64, _i64, _i64,
                                      _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
-                                     _vp]
+                                     _mp, _vp]
     lib.ra_attn_bwd_rope.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -511,21 +511,30 @@ def ra_rope(x, theta: float = 10000.0, positions=None, inverse: bool = False):
 
 
 def ra_attn_fwd_rope(q, k, v, o, stats, q_rot, k_rot, q_positions, k_positions, theta, B, Hq, Hkv,
-                     Nq, Nk, D, causal, scale, dtype, stream=None) -> int:
+                     Nq, Nk, D, causal, scale, dtype, mask=None, mask_kind=RA_MASK_NONE,
+                     mask_strides=(0, 0, 0, 0), stream=None) -> int:
+    """ra_attn_fwd_rope; ``mask``, ``mask_kind``, ``mask_strides`` as ra_attn_fwd_masked (none by
+    default)."""
     return load_library().ra_attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(stats),
                                            _ptr(q_rot), _ptr(k_rot), _ptr(q_positions),
                                            _ptr(k_positions), float(theta), B, Hq, Hkv, Nq, Nk, D,
-                                           int(causal), float(scale), int(dtype), _stream(stream))
+                                           int(causal), float(scale), int(dtype),
+                                           _mask_struct(mask, mask_kind, mask_strides),
+                                           _stream(stream))
 
 
 def ra_attn_bwd_rope(q_rot, k_rot, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes,
                      q_positions, k_positions, theta, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype,
+                     mask=None, mask_kind=RA_MASK_NONE, mask_strides=(0, 0, 0, 0),
                      stream=None) -> int:
+    """ra_attn_bwd_rope; the mask arguments as ra_attn_fwd_rope."""
     return load_library().ra_attn_bwd_rope(_ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(o), _ptr(d_o),
                                            _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv),
                                            _ptr(workspace), workspace_bytes, _ptr(q_positions),
                                            _ptr(k_positions), float(theta), B, Hq, Hkv, Nq, Nk, D,
-                                           int(causal), float(scale), int(dtype), _stream(stream))
+                                           int(causal), float(scale), int(dtype),
+                                           _mask_struct(mask, mask_kind, mask_strides),
+                                           _stream(stream))
 
 
 def _positions(p, n, device):
@@ -539,9 +548,9 @@ def _positions(p, n, device):
 
 
 def attn_fwd_rope(q, k, v, causal, theta: float = 10000.0, scale: Optional[float] = None,
-                  q_positions=None, k_positions=None, with_rotated: bool = True):
+                  q_positions=None, k_positions=None, with_rotated: bool = True, mask=None):
     """Allocate O, stats, the rotated keys (and queries) and run ra_attn_fwd_rope on the current
-    stream.  Returns (o, stats, q_rot or None, k_rot)."""
+    stream (``mask``: a mask_descriptor or None).  Returns (o, stats, q_rot or None, k_rot)."""
     import torch
     B, Hq, Hkv, Nq, Nk, D = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
@@ -551,12 +560,13 @@ def attn_fwd_rope(q, k, v, causal, theta: float = 10000.0, scale: Optional[float
     k_rot = torch.empty_like(k)
     qp, kp = _positions(q_positions, Nq, q.device), _positions(k_positions, Nk, q.device)
     _check(ra_attn_fwd_rope(q, k, v, o, stats, q_rot, k_rot, qp, kp, theta, B, Hq, Hkv, Nq, Nk, D,
-                            causal_code(causal), scale, _dtype_code(q)), "ra_attn_fwd_rope")
+                            causal_code(causal), scale, _dtype_code(q), *(mask or ())),
+           "ra_attn_fwd_rope")
     return o, stats, q_rot, k_rot
 
 
 def attn_bwd_rope(q_rot, k_rot, v, o, d_o, stats, causal, theta: float = 10000.0,
-                  scale: Optional[float] = None, q_positions=None, k_positions=None):
+                  scale: Optional[float] = None, q_positions=None, k_positions=None, mask=None):
     """Allocate dQ, dK, dV and a workspace and run ra_attn_bwd_rope on the current stream: the
     gradients with respect to the unrotated q and k."""
     import torch
@@ -569,7 +579,7 @@ def attn_bwd_rope(q_rot, k_rot, v, o, d_o, stats, causal, theta: float = 10000.0
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q_rot.device)
     qp, kp = _positions(q_positions, Nq, q_rot.device), _positions(k_positions, Nk, q_rot.device)
     _check(ra_attn_bwd_rope(q_rot, k_rot, v, o, d_o, stats, dq, dk, dv, ws, nbytes, qp, kp, theta,
-                            B, Hq, Hkv, Nq, Nk, D, causal_code(causal), scale, code),
+                            B, Hq, Hkv, Nq, Nk, D, causal_code(causal), scale, code, *(mask or ())),
            "ra_attn_bwd_rope")
     return dq, dk, dv
 
@@ -584,38 +594,43 @@ class _RopeAttentionFn:
 
             class Fn(torch.autograd.Function):
                 @staticmethod
-                def forward(ctx, q, k, v, causal, theta, scale, q_positions, k_positions):
+                def forward(ctx, q, k, v, causal, theta, scale, q_positions, k_positions, mask):
                     o, stats, q_rot, k_rot = attn_fwd_rope(q, k, v, causal, theta, scale,
-                                                           q_positions, k_positions)
+                                                           q_positions, k_positions, mask=mask)
                     ctx.save_for_backward(q_rot, k_rot, v, o, stats)
-                    ctx.args = (causal, theta, scale, q_positions, k_positions)
+                    ctx.args = (causal, theta, scale, q_positions, k_positions, mask)
                     return o
 
                 @staticmethod
                 def backward(ctx, d_o):
                     q_rot, k_rot, v, o, stats = ctx.saved_tensors
-                    causal, theta, scale, qp, kp = ctx.args
+                    causal, theta, scale, qp, kp, mask = ctx.args
                     dq, dk, dv = attn_bwd_rope(q_rot, k_rot, v, o, d_o, stats, causal, theta, scale,
-                                               qp, kp)
-                    return dq, dk, dv, None, None, None, None, None
+                                               qp, kp, mask=mask)
+                    return dq, dk, dv, None, None, None, None, None, None
 
             cls._cls = Fn
         return cls._cls
 
 
 def ra_attention_rope(q, k, v, is_causal=False, theta: float = 10000.0,
-                      scale: Optional[float] = None, q_positions=None, k_positions=None):
+                      scale: Optional[float] = None, q_positions=None, k_positions=None,
+                      attn_mask=None, key_padding_mask=None):
     """ra_attention on q and k rotated by the NEOX rotary embedding (ra_rope), the query rotation
-    fused into the attention kernel.  q, k unrotated, bf16 or fp32, shapes and causal modes as
-    ra_attention; positions default to 0..N-1.  Differentiable in q, k and v (the gradients
-    are with respect to the unrotated q and k)."""
+    fused into the attention kernel.  q, k unrotated, bf16 or fp32, shapes, causal modes and
+    masks as ra_attention; positions default to 0..N-1.  Differentiable in q, k and v (the
+    gradients are with respect to the unrotated q and k)."""
     import torch
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("ra_attention_rope supports bfloat16 and float32")
+    for m in (attn_mask, key_padding_mask):
+        if m is not None and getattr(m, "requires_grad", False):
+            raise ValueError("ra_attention_rope computes no gradient for a mask; detach it")
     D = q.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    mask = mask_descriptor(q, k, attn_mask, key_padding_mask)
     return _RopeAttentionFn.get().apply(q, k, v, causal_code(is_causal), float(theta), scale,
-                                        q_positions, k_positions)
+                                        q_positions, k_positions, mask)
 
 
 def _softmax_rows_2d(x):

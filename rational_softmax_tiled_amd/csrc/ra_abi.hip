@@ -339,10 +339,10 @@ static int check_rope(double theta, int dtype, const int32_t* q_positions, const
 int ra_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* stats, void* q_rot,
                      void* k_rot, const int32_t* q_positions, const int32_t* k_positions, double theta,
                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal,
-                     float scale, int dtype, void* stream) {
+                     float scale, int dtype, const ra_mask* mask, void* stream) {
   int st = check_sizes(B, Hq, Hkv, Nq, Nk, D, scale, dtype);
   if (st != RA_OK) return st;
-  st = check_mask(nullptr, causal, B, Hq, Nq, Nk, dtype);
+  st = check_mask(mask, causal, B, Hq, Nq, Nk, dtype);
   if (st != RA_OK) return st;
   st = check_rope(theta, dtype, q_positions, k_positions);
   if (st != RA_OK) return st;
@@ -366,7 +366,7 @@ int ra_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float
   // K once, by the standalone rotation, into k_rot; Q in the attention kernel, on load
   st = hip_status(ra::launch_rope_neox(k, k_rot, k_positions, B * Hkv, Nk, D, theta, false, dtype == RA_BF16, s));
   if (st != RA_OK) return st;
-  ra::AttnProblem p = make_problem(q, k_rot, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, nullptr);
+  ra::AttnProblem p = make_problem(q, k_rot, v, B, Hq, Hkv, Nq, Nk, D, causal, scale, dtype, mask);
   p.rope = true;
   p.rope_theta = theta;
   p.q_pos = q_positions;
@@ -378,7 +378,7 @@ int ra_attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const 
                      const void* d_o, const float* stats, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, const int32_t* q_positions, const int32_t* k_positions,
                      double theta, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
-                     int causal, float scale, int dtype, void* stream) {
+                     int causal, float scale, int dtype, const ra_mask* mask, void* stream) {
   int st = check_rope(theta, dtype, q_positions, k_positions);
   if (st != RA_OK) return st;
   ra::RopeArgs rope;
@@ -386,7 +386,7 @@ int ra_attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const 
   rope.q_pos = q_positions;
   rope.k_pos = k_positions;
   return attn_bwd_common(q_rot, k_rot, v, o, d_o, stats, dq, dk, dv, workspace, workspace_bytes, B, Hq,
-                         Hkv, Nq, Nk, D, causal, scale, dtype, nullptr, ra::kBwdAll, stream, &rope);
+                         Hkv, Nq, Nk, D, causal, scale, dtype, mask, ra::kBwdAll, stream, &rope);
 }
 
 // Decode: the query rows of one K/V head (rep * Nq) must fit one wave's 32 MFMA columns.

@@ -1188,14 +1188,16 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   const bool keypad = kBf16 && p.mask_kind == kMaskBool && p.msq == 0 && p.msh == 0 && p.msk == 1 &&
                       p.msb % 4 == 0 && p.Nk % 4 == 0 &&
                       reinterpret_cast<unsigned long long>(p.mask) % 4 == 0;
-  if (p.rope) {   // no explicit mask: the host checks it
-    if (masked) return hipErrorInvalidValue;
+  if (p.rope) {   // the same kernel choice as below, each with the epilogue turn
     if (phases & kBwdDq) {
       if constexpr (kBf16) {
-        if (p.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, false, true>), qgrid, block, 0, stream, a);
+        if (keypad) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, true, true>), qgrid, block, 0, stream, a);
+        else if (masked) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, true, false, true>), qgrid, block, 0, stream, a);
+        else if (p.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, false, true>), qgrid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, false, false, true>), qgrid, block, 0, stream, a);
       } else {
-        if (p.causal) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, false, true>), qgrid, block, 0, stream, a);
+        if (masked) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, true, true>), qgrid, block, 0, stream, a);
+        else if (p.causal) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, false, true>), qgrid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, false, false, true>), qgrid, block, 0, stream, a);
       }
       const hipError_t e = hipGetLastError();
@@ -1203,10 +1205,13 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
     }
     if (phases & kBwdDkdv) {
       if constexpr (kBf16) {
-        if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, false, false, true>), kgrid, kblock, 0, stream, a);
+        if (keypad) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, false, true, true>), kgrid, kblock, 0, stream, a);
+        else if (masked) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, true, false, true>), kgrid, kblock, 0, stream, a);
+        else if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, false, false, true>), kgrid, kblock, 0, stream, a);
         else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, false, false, true>), kgrid, kblock, 0, stream, a);
       } else {
-        if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true, false, true>), kgrid, kblock, 0, stream, a);
+        if (masked) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true, true, true>), kgrid, kblock, 0, stream, a);
+        else if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true, false, true>), kgrid, kblock, 0, stream, a);
         else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false, false, true>), kgrid, kblock, 0, stream, a);
       }
     }

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   __shared__ float tmax_lds[kWaves][kMaxTiles];
   __shared__ float kmin_lds[kWaves];
   static_assert(!KEYPAD || (sizeof(T) == 2 && WRITE_O && !MASKED && BN == kWave), "key padding path");
-  static_assert(!ROPE || (WRITE_O && !MASKED && !KEYPAD && !COUNT), "rotary path");
+  static_assert(!ROPE || (WRITE_O && !COUNT), "rotary path");
   __shared__ __attribute__((aligned(16))) unsigned mstage_lds[KEYPAD ? 4 : 1][KEYPAD ? kWave : 1];
   __shared__ unsigned long long keep_lds[KEYPAD ? kMaxTiles : 1];
   __shared__ double rate_lds[ROPE ? D / 2 : 1];   // ROPE: theta^(-2j/D) per pair j
@@ -698,9 +698,16 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   const bool keypad = sizeof(T) == 2 && o != nullptr && !counters && p.mask_kind == kMaskBool && p.msq == 0 &&
                       p.msh == 0 && p.msk == 1 && p.msb % 4 == 0 && p.Nk % 4 == 0 &&
                       reinterpret_cast<unsigned long long>(p.mask) % 4 == 0 && (p.Nk + BN - 1) / BN <= kMaxTiles;
-  if (p.rope) {   // the host rejects masks and counters with the rotary embedding
-    if (o == nullptr || counters != nullptr || p.mask_kind != kMaskNone) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, false, true>), grid, block, 0, stream, a);
+  if (p.rope) {   // always with an output; the host rejects counters with the rotary embedding
+    if (o == nullptr || counters != nullptr) return hipErrorInvalidValue;
+    if (keypad) {
+      if constexpr (sizeof(T) == 2 && BN == kWave)
+        hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, true, true>), grid, block, 0, stream, a);
+    } else if (p.mask_kind != kMaskNone) {
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true, false, true>), grid, block, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, false, true>), grid, block, 0, stream, a);
+    }
   } else if (keypad) {
     if constexpr (sizeof(T) == 2 && BN == kWave)
       hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, true>), grid, block, 0, stream, a);

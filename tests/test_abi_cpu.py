@@ -215,7 +215,7 @@ def test_rope_validation(lib):
 def fwd_rope(B=1, Hq=2, Hkv=1, Nq=8, Nk=8, D=64, causal=1, scale=0.125, dtype=ra.RA_BF16,
              q=P, k=P, v=P, o=P2, q_rot=None, k_rot=P2, qp=None, kp=None, theta=10000.0):
     return ra.ra_attn_fwd_rope(q, k, v, o, None, q_rot, k_rot, qp, kp, theta, B, Hq, Hkv, Nq, Nk,
-                               D, causal, scale, dtype, 0)
+                               D, causal, scale, dtype, stream=0)
 
 
 def test_fwd_rope_validation(lib):
@@ -236,12 +236,18 @@ def test_fwd_rope_validation(lib):
     assert fwd_rope(Nq=1 << 25, D=128) == TOO_LARGE
     assert fwd_rope(B=0) == OK
     assert fwd_rope(Nq=0, q=None, o=None, k_rot=None) == OK
+    bad = ra.ra_attn_fwd_rope(P, P, P, P2, None, None, P2, None, None, 10000.0, 1, 2, 1, 8, 8, 64, 1,
+                              0.125, ra.RA_BF16, P + 1, ra.RA_MASK_ADD, (8, 0, 0, 1), stream=0)
+    assert bad == ALIGN          # the mask's checks apply (a bf16 additive mask: 2-byte aligned)
+    bad = ra.ra_attn_fwd_rope(P, P, P, P2, None, None, P2, None, None, 10000.0, 1, 2, 1, 8, 8, 64, 1,
+                              0.125, ra.RA_BF16, P, 9, (8, 0, 0, 1), stream=0)
+    assert bad == MASK
 
 
 def test_bwd_rope_validation(lib):
     def f(dtype=ra.RA_BF16, theta=10000.0, ws=P2, ws_bytes=1 << 30, dq=P2, qp=None, B=1, D=64):
         return ra.ra_attn_bwd_rope(P, P, P, P, P, None, dq, P2, P2, ws, ws_bytes, qp, None, theta,
-                                   B, 2, 1, 8, 8, D, 1, 0.125, dtype, 0)
+                                   B, 2, 1, 8, 8, D, 1, 0.125, dtype, stream=0)
     assert f(dtype=5) == DTYPE
     assert f(theta=0.0) == SCALE
     assert f(theta=math.nan) == SCALE

@@ -257,3 +257,68 @@ def test_grouped_query_backward_every_group(gpu_lib):
     res = parity.bwd_all_groups(to_np(dq), to_np(dk), to_np(dv), inp, True, w.scale, "bf16",
                                 rope={"theta": w.rope_theta, "q_positions": None, "k_positions": None})
     print(f"{GQA} fused backward: {res}")
+
+
+MASK_CASES = [
+    # (B, Hq, Hkv, Nq, Nk, D, causal, mask layout, dtype)
+    (2, 8, 2, 200, 256, 128, 2, "keypad", "bf16"),          # key padding fast path
+    (2, 4, 2, 130, 130, 64, 1, "keypad", "bf16"),           # Nk % 4 != 0: the general masked kernels
+    (1, 4, 2, 100, 140, 128, 0, "head_bias", "bf16"),       # additive, per query head, -inf entries
+    (1, 2, 1, 77, 90, 64, 2, "full_bool", "f32"),
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[str(c) for c in MASK_CASES])
+def test_masked_rotary_attention_equals_the_unfused_chain(gpu_lib, case):
+    """With an explicit mask: the fused forward equals the rotation passes followed by
+    ra_attn_fwd_masked bit for bit, and O matches the oracle; the fused backward matches
+    ra_attn_bwd_masked on the rotated rows followed by the inverse rotation (dV bit for bit; dQ
+    and dK within two roundings of the dtype)."""
+    import torch
+    from test_mask_gpu import make_mask
+    ra = gpu_lib
+    B, Hq, Hkv, Nq, Nk, D, causal, layout, dt = case
+    dims = (B, Hq, Hkv, Nq, Nk, D)
+    theta = 10000.0
+    inp = _inputs(B, Hq, Hkv, Nq, Nk, D, seed=Nq * 3 + Nk, dtype=dt)
+    mask_np, t, kind, strides = make_mask(layout, B, Hq, Nq, Nk, dt, seed=Nq + Nk)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    code = ra.RA_BF16 if dt == "bf16" else ra.RA_F32
+    qt, kt, vt, dot = (to_dev(inp[n], dt) for n in ("q", "k", "v", "do"))
+    print(f"masked rotary {case}", flush=True)
+    o = torch.empty_like(qt)
+    stats = torch.empty((B, Hq, Nq, 2), dtype=torch.float32, device="cuda")
+    q_rot, k_rot = torch.empty_like(qt), torch.empty_like(kt)
+    assert ra.ra_attn_fwd_rope(qt, kt, vt, o, stats, q_rot, k_rot, None, None, theta, *dims, causal,
+                               scale, code, t, kind, strides) == 0
+    qr, kr = torch.empty_like(qt), torch.empty_like(kt)
+    assert ra.ra_rope_neox(qt, qr, None, B * Hq, Nq, D, theta, False, code) == 0
+    assert ra.ra_rope_neox(kt, kr, None, B * Hkv, Nk, D, theta, False, code) == 0
+    ro, rstats = torch.empty_like(qt), torch.empty_like(stats)
+    assert ra.ra_attn_fwd_masked(qr, kr, vt, ro, rstats, *dims, causal, scale, code, t, kind,
+                                 strides) == 0
+    nbytes = ra.ra_attn_bwd_workspace_bytes(*dims, code)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(qt), torch.empty_like(kt), torch.empty_like(vt)
+    assert ra.ra_attn_bwd_rope(q_rot, k_rot, vt, o, dot, stats, dq, dk, dv, ws, nbytes, None, None,
+                               theta, *dims, causal, scale, code, t, kind, strides) == 0
+    cq, ck, cv = torch.empty_like(qt), torch.empty_like(kt), torch.empty_like(vt)
+    assert ra.ra_attn_bwd_masked(qr, kr, vt, ro, dot, rstats, cq, ck, cv, ws, nbytes, *dims, causal,
+                                 scale, code, t, kind, strides) == 0
+    for x, H, N in ((cq, Hq, Nq), (ck, Hkv, Nk)):
+        assert ra.ra_rope_neox(x, x, None, B * H, N, D, theta, True, code) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(q_rot, qr) and torch.equal(k_rot, kr)
+    assert torch.equal(o, ro) and torch.equal(stats, rstats)
+    assert torch.equal(dv, cv)
+    e = 2.0 ** -8 if dt == "bf16" else 2.0 ** -23
+    for name, a, b in (("dq", dq, cq), ("dk", dk, ck)):
+        a, b = to_np(a), to_np(b)
+        excess = np.abs(a - b) - 1.01 * 2 * e * _pair_norm(b)
+        assert excess.max() <= 0, f"{name}: beyond two roundings by {excess.max():.3e}"
+    oc = {0: False, 1: True, 2: "bottom_right"}[causal]
+    ref = oracle.ra_attention_rope_fwd(inp["q"], inp["k"], inp["v"], oc, scale, theta,
+                                       mask=mask_np)[0]
+    from helpers import assert_close
+    err = assert_close(to_np(o), ref, dt, "masked rotary O")
+    print(f"{case}: O err {err:.3e}")
