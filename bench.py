@@ -60,22 +60,22 @@ GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("01c20e25172cd9f5b2bc208ff46eee8f30dbd985626fd2d9330d8112cb3e1954",
-                        287088.9, 135180.6),
-    "attn_bwd_dq_bf16_kernel": ("cb42533549dfa1500a0c1d8ffbdd881be4e6736968647266669b3242397564e5",
-                                436562.9, 143480.8),
-    "attn_bwd_dkdv_bf16_kernel": ("cb42533549dfa1500a0c1d8ffbdd881be4e6736968647266669b3242397564e5",
-                                  267505.9, 262144.6),
+    "attn_fwd_kernel": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4",
+                        286919.0, 135180.3),
+    "attn_bwd_dq_bf16_kernel": ("35abd4981b02a7ecb962a224ba6e600d60f0a7149361755916ac13d939542362",
+                                437059.0, 143467.8),
+    "attn_bwd_dkdv_bf16_kernel": ("35abd4981b02a7ecb962a224ba6e600d60f0a7149361755916ac13d939542362",
+                                  267525.0, 262145.2),
 }
 # VALU instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU) of the forward on a workload,
 # for its VALU-roofline fraction; valid for the recorded kernel source only.
 VALU_INSTS = {
     # workload: (sha256 of the forward's sources, SQ_INSTS_VALU per dispatch)
-    "fp32_noncausal_B1_H2_N128_D64": ("01c20e25172cd9f5b2bc208ff46eee8f30dbd985626fd2d9330d8112cb3e1954", 11560),
-    "bf16_causal_B2_H12_N128_D64": ("01c20e25172cd9f5b2bc208ff46eee8f30dbd985626fd2d9330d8112cb3e1954", 101160),
-    "bf16_causal_B8_H16_N2048_D64_sigma2": ("01c20e25172cd9f5b2bc208ff46eee8f30dbd985626fd2d9330d8112cb3e1954", 45893632),
-    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("01c20e25172cd9f5b2bc208ff46eee8f30dbd985626fd2d9330d8112cb3e1954", 189317120),
-    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("01c20e25172cd9f5b2bc208ff46eee8f30dbd985626fd2d9330d8112cb3e1954", 364273664),
+    "fp32_noncausal_B1_H2_N128_D64": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 11560),
+    "bf16_causal_B2_H12_N128_D64": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 101160),
+    "bf16_causal_B8_H16_N2048_D64_sigma2": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 45893632),
+    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 189317120),
+    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 364273664),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],
