@@ -528,6 +528,21 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdArgs a) {
 
 // Direct gradient and probability of one entry: with d = 1 + u = fma(s, -c, kd),
 // q = clamp(2/d - 1), p = q^8 * il and G = (dP * il - c * il) * q^7 / d^2.
+// Fragment reads at an LDS byte address (a register plus an immediate offset in the instruction):
+// a row fragment (16 bytes), and a transposed fragment from its two 8-byte halves (rows 0-7 and
+// 8-15 of its 16-row block, as tr_frag reads them).
+__device__ __forceinline__ bf16x8 lds_frag_at(unsigned addr) {
+  typedef __attribute__((address_space(3))) const bf16x8 lds_frag_t;
+  return *reinterpret_cast<lds_frag_t*>((size_t)addr);
+}
+__device__ __forceinline__ bf16x8 lds_tr_frag_at(unsigned a1, unsigned a2) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a1);
+  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a2);
+  const short8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ float ra_grad(float s, float c16, float kd, float dp, float il, float cil,
                                          float* p) {
   const float d = fmaf(s, -c16, kd);
@@ -893,14 +908,52 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
     }
   };
 
+  // Q/dO half-tiles are addressed from the half's slot-0 Q tile hb: Q of slot t at byte offset
+  // qo = t HTB, dO at doo.  The unmasked kernels read them through QdoAddr: the LDS address of
+  // every fragment this lane reads from hb, one opaque register each, to which the slot, the matrix
+  // and the second 16-row block add immediate offsets (all below 64 KiB).  With the slot in a
+  // register instead, each fragment read cost two address instructions per step, and with the
+  // slots' absolute addresses as constants (above 64 KiB, too large for an immediate) the
+  // compiler kept one register per slot and spilled.
+  constexpr unsigned HTB = HTILE * 2;
+  struct QdoAddr {
+    unsigned row[KC];      // row fragment kc: row frow, 16-byte chunk 2 kc + lane / 32
+    unsigned tr[2 * DB];   // transposed fragment db: rows 0-7 [2 db] and 8-15 [2 db + 1]
+  };
+  auto qdo_addr = [&](const bf16* hb) {
+    QdoAddr ad;
+    const unsigned b0 = lds_addr(hb);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int trow = 4 * (g4 >> 1) + (l16 >> 2);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      ad.row[kc] = b0 + 2u * swz_off<bf16, D>(frow, 2 * kc + (lane >> 5));
+      asm volatile("" : "+v"(ad.row[kc]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 32 * db + 16 * (g4 & 1) + 4 * (l16 & 3);
+      ad.tr[2 * db] = b0 + 2u * (swz_off<bf16, D>(trow, col >> 3) + (col & 7));
+      ad.tr[2 * db + 1] = b0 + 2u * (swz_off<bf16, D>(trow + 8, col >> 3) + (col & 7));
+      asm volatile("" : "+v"(ad.tr[2 * db]));
+      asm volatile("" : "+v"(ad.tr[2 * db + 1]));
+    }
+    return ad;
+  };
+  // the second 16-row block of a transposed read: swz(r + 16) = swz(r), so it is an offset
+  static_assert(swz<bf16, D>(5) == swz<bf16, D>(21) && swz<bf16, D>(14) == swz<bf16, D>(30),
+                "16-row block offset");
+
   // S^T and dP^T of this wave's block: lane = key, registers = the half-tile's 32 query rows
   // S and dP run as two independent chains with their four operand reads pinned two products
   // ahead (left alone, the compiler read each operand just before its product, so every product
   // waited out an LDS latency)
-  auto products_sdp = [&](const bf16* qt_, const bf16* dot_, f32x16& s, f32x16& dp) {
+  auto products_sdp = [&](const bf16* hb, const QdoAddr& ad, unsigned qo, unsigned doo, f32x16& s, f32x16& dp) {
     s = f32x16{};
     dp = f32x16{};
     if constexpr (MASKED) {   // no registers to spare for the read-ahead
+      const bf16* qt_ = hb + qo / 2;
+      const bf16* dot_ = hb + doo / 2;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
         mma(s, swz_frag<bf16, D>(qt_, frow, 16 * kc + fcol), swz_frag<bf16, D>(k_lds, kr, 16 * kc + fcol));
@@ -912,9 +965,9 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
     bf16x8 qa[KC], ka[KC], da[KC], va[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      qa[kc] = swz_frag<bf16, D>(qt_, frow, 16 * kc + fcol);
+      qa[kc] = lds_frag_at(ad.row[kc] + qo);
       ka[kc] = swz_frag<bf16, D>(k_lds, kr, 16 * kc + fcol);
-      da[kc] = swz_frag<bf16, D>(dot_, frow, 16 * kc + fcol);
+      da[kc] = lds_frag_at(ad.row[kc] + doo);
       va[kc] = swz_frag<bf16, D>(v_lds, kr, 16 * kc + fcol);
     }
 #pragma unroll
@@ -999,8 +1052,11 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
     acc_dv[db] = f32x16{};
   }
   // dV^T += dO^T P^T, dK^T += Q^T G^T over the half-tile's 32 rows
-  auto products_dkdv = [&](const f32x16& s, const f32x16& dp, const bf16* qt_, const bf16* dot_) {
+  auto products_dkdv = [&](const f32x16& s, const f32x16& dp, const bf16* hb, const QdoAddr& ad, unsigned qo,
+                           unsigned doo) {
     if constexpr (MASKED) {
+      const bf16* qt_ = hb + qo / 2;
+      const bf16* dot_ = hb + doo / 2;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 pf = pack_frag_bf16(s, ks);
@@ -1023,8 +1079,10 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
     }
 #pragma unroll
     for (int c = 0; c < NP; ++c) {
-      ta[c] = tr_frag<D>(dot_, 16 * (c / DB), (c % DB) * 32, lane);
-      tb[c] = tr_frag<D>(qt_, 16 * (c / DB), (c % DB) * 32, lane);
+      const unsigned blk = (c / DB) * 16 * D * 2;   // second 16-row block
+      const int db = c % DB;
+      ta[c] = lds_tr_frag_at(ad.tr[2 * db] + doo + blk, ad.tr[2 * db + 1] + doo + blk);
+      tb[c] = lds_tr_frag_at(ad.tr[2 * db] + qo + blk, ad.tr[2 * db + 1] + qo + blk);
     }
 #pragma unroll
     for (int c = 0; c < NP; ++c) {
@@ -1049,44 +1107,71 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
   wait_vmem();
   __syncthreads();
 
+  // The unmasked kernels unroll the loops over the slots, so that every slot offset is an
+  // immediate; the masked ones keep them rolled (no registers to spare).
   if (half == 0) {
+    const bf16* hb = q_up(0);   // Q slots 0, 1, then dO slots 0, 1
+    QdoAddr ad{};
+    if constexpr (!MASKED) ad = qdo_addr(hb);
     Cursor cur = first, nxt = advance(first);   // steps st and st + 1
-    for (int st = 0; st <= steps; ++st) {
+    auto up_step = [&](int st, int par) {       // par = st & 1: the Q/dO slot of tile st
       // the next tile's copies go out first: their buffers were last read before the barrier
       // that ended step st - 1, and they have the whole step to land
-      if (st + 1 < steps) issue(nxt, (st + 1) & 1);
+      if (st + 1 < steps) issue(nxt, par ^ 1);
       if (st < steps && block_live(cur)) {
         f32x16 s, dp;
         unsigned mv[16];
         mask_load(cur, mv);
-        products_sdp(q_up(st & 1), do_up(st & 1), s, dp);
+        products_sdp(hb, ad, par * HTB, (2 + par) * HTB, s, dp);
         derivative(s, dp, mv, cur.qt * QT, cur.slot3);
-        products_dkdv(s, dp, q_up(st & 1), do_up(st & 1));
+        products_dkdv(s, dp, hb, ad, par * HTB, (2 + par) * HTB);
       }
       wait_vmem();
       __syncthreads();
       cur = nxt;
       nxt = advance(nxt);
+    };
+    if constexpr (MASKED) {
+      for (int st = 0; st <= steps; ++st) up_step(st, st & 1);
+    } else {
+      for (int st = 0; st <= steps; st += 2) {
+        up_step(st, 0);
+        if (st + 1 <= steps) up_step(st + 1, 1);
+      }
     }
   } else {
+    const bf16* hb = q_lo(0);   // Q slots 0-2, then dO slots 0-2
+    QdoAddr ad{};
+    if constexpr (!MASKED) ad = qdo_addr(hb);
     f32x16 s = {}, dp = {};
     unsigned mv[16];
     bool carried = false;   // s, dp (and mv) hold S, dP (and the mask block) of tile st - 1
     Cursor prev = first, cur = first;
-    for (int st = 0; st <= steps; ++st) {
+    auto lo_step = [&](int st, int sp, int sc) {   // sp, sc: slots of tiles st - 1 and st
       if (carried) {
-        derivative(s, dp, mv, prev.qt * QT + HR, prev.slot3);
-        products_dkdv(s, dp, q_lo(prev.slot3), do_lo(prev.slot3));
+        derivative(s, dp, mv, prev.qt * QT + HR, sp);
+        products_dkdv(s, dp, hb, ad, sp * HTB, (3 + sp) * HTB);
       }
       carried = st < steps && block_live(cur);
       if (carried) {
         mask_load(cur, mv);
-        products_sdp(q_lo(cur.slot3), do_lo(cur.slot3), s, dp);
+        products_sdp(hb, ad, sc * HTB, (3 + sc) * HTB, s, dp);
       }
       wait_vmem();
       __syncthreads();
       prev = cur;
       cur = advance(cur);
+    };
+    if constexpr (MASKED) {
+      for (int st = 0; st <= steps; ++st) lo_step(st, prev.slot3, cur.slot3);
+    } else {   // tile st sits in slot st % 3
+      for (int st = 0; st <= steps; st += 3) {
+        lo_step(st, 2, 0);
+        if (st + 1 > steps) break;
+        lo_step(st + 1, 0, 1);
+        if (st + 2 > steps) break;
+        lo_step(st + 2, 1, 2);
+      }
     }
   }
 
