@@ -572,8 +572,11 @@ template <int D, bool CAUSAL, bool MASKED, bool KEYPAD = false, bool ROPE = fals
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int BN = 64, KC = D / 16, SB = BN / 32, DB = D / 32;
   static_assert(!(KEYPAD && MASKED), "key padding runs the unmasked paths");
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * D];
+  // the K and V tiles, two buffers each, in one array (K0, K1, V0, V1): every buffer then lies at
+  // a constant offset below 64 KiB from the first, an immediate of the LDS read instructions
+  __shared__ __attribute__((aligned(16))) bf16 kv_lds[4][BN * D];
+  bf16 (*const k_lds)[BN * D] = kv_lds;
+  bf16 (*const v_lds)[BN * D] = kv_lds + 2;
   __shared__ __attribute__((aligned(16))) unsigned m_lds[KEYPAD ? 2 : 1][KEYPAD ? kWave : 1];
   __shared__ double rate_lds[ROPE ? D / 2 : 1];   // ROPE: theta^(-2j/D) per pair j
 
@@ -648,62 +651,108 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float rsum = 0.0f;
   int amax = INT_MAX;
+
+  // Fragment reads.  The unmasked kernels address them from the first buffer: one opaque register
+  // per fragment this lane reads, to which the buffer, the 32-key block and the 16-row block add
+  // immediate offsets (swz(r + 16) = swz(r)), and their tile loop is unrolled over the two buffers.
+  // With the buffer in a register, every read cost address instructions in each step.  The masked
+  // kernels keep the rolled loop: they have no registers to spare.
+  constexpr unsigned TB = BN * D * 2;   // bytes of one tile buffer
+  static_assert(swz<bf16, D>(5) == swz<bf16, D>(21) && swz<bf16, D>(14) == swz<bf16, D>(62),
+                "16-row block offsets");
+  unsigned ad_row[KC] = {}, ad_tr[2 * DB] = {};
+  if constexpr (!MASKED) {
+    const unsigned b0 = lds_addr(kv_lds);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int trow = 4 * (g4 >> 1) + (l16 >> 2);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      ad_row[kc] = b0 + 2u * swz_off<bf16, D>(frow, 2 * kc + (lane >> 5));
+      asm volatile("" : "+v"(ad_row[kc]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 32 * db + 16 * (g4 & 1) + 4 * (l16 & 3);
+      ad_tr[2 * db] = b0 + 2u * (swz_off<bf16, D>(trow, col >> 3) + (col & 7));
+      ad_tr[2 * db + 1] = b0 + 2u * (swz_off<bf16, D>(trow + 8, col >> 3) + (col & 7));
+      asm volatile("" : "+v"(ad_tr[2 * db]));
+      asm volatile("" : "+v"(ad_tr[2 * db + 1]));
+    }
+  }
+  auto k_row = [&](int buf, int sb, int kc) -> bf16x8 {   // K rows sb 32 + frow (A of S^T)
+    if constexpr (MASKED) return swz_frag<bf16, D>(k_lds[buf], sb * 32 + frow, 16 * kc + fcol);
+    else return lds_frag_at(ad_row[kc] + buf * TB + sb * 32 * D * 2);
+  };
+  auto v_row = [&](int buf, int sb, int kc) -> bf16x8 {
+    if constexpr (MASKED) return swz_frag<bf16, D>(v_lds[buf], sb * 32 + frow, 16 * kc + fcol);
+    else return lds_frag_at(ad_row[kc] + (2 + buf) * TB + sb * 32 * D * 2);
+  };
+  auto k_tr = [&](int buf, int k0, int db) -> bf16x8 {     // K^T rows k0 .. k0 + 15, columns 32 db
+    if constexpr (MASKED) return tr_frag<D>(k_lds[buf], k0, db * 32, lane);
+    else return lds_tr_frag_at(ad_tr[2 * db] + buf * TB + k0 * D * 2, ad_tr[2 * db + 1] + buf * TB + k0 * D * 2);
+  };
   wait_vmem();
   __syncthreads();
 
-  for (int kt = 0; kt < nt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nt) {
-      dma_tile_at<D, BN>(k_rsrc, (kt + 1) * BN * D * 2, k_m0[buf ^ 1], lane_off, wave);
-      dma_tile_at<D, BN>(v_rsrc, (kt + 1) * BN * D * 2, v_m0[buf ^ 1], lane_off, wave);
-      m_issue(kt + 1, buf ^ 1);
-    }
-    unsigned long long keep = ~0ull;   // KEYPAD: bit l set when key kt BN + l is kept
-    if constexpr (KEYPAD) keep = __ballot(reinterpret_cast<const unsigned char*>(m_lds[buf])[lane] != 0);
-    if (kt < nt_w) {
+  constexpr int U = MASKED ? 1 : 2;   // tiles per iteration
+  for (int kt0 = 0; kt0 < nt; kt0 += U) {
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-        if (KEYPAD && ((keep >> (32 * sb)) & 0xffffffffull) == 0) continue;   // all padding
-        f32x16 s = {}, dp = {};
+    for (int u = 0; u < U; ++u) {
+      const int kt = kt0 + u;
+      if (U > 1 && kt >= nt) break;
+      const int buf = U > 1 ? u : kt & 1;
+      if (kt + 1 < nt) {
+        dma_tile_at<D, BN>(k_rsrc, (kt + 1) * BN * D * 2, k_m0[buf ^ 1], lane_off, wave);
+        dma_tile_at<D, BN>(v_rsrc, (kt + 1) * BN * D * 2, v_m0[buf ^ 1], lane_off, wave);
+        m_issue(kt + 1, buf ^ 1);
+      }
+      unsigned long long keep = ~0ull;   // KEYPAD: bit l set when key kt BN + l is kept
+      if constexpr (KEYPAD) keep = __ballot(reinterpret_cast<const unsigned char*>(m_lds[buf])[lane] != 0);
+      if (kt < nt_w) {
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) mma(s, swz_frag<bf16, D>(k_lds[buf], sb * 32 + frow, 16 * kc + fcol), qf[kc]);
+        for (int sb = 0; sb < SB; ++sb) {
+          if (KEYPAD && ((keep >> (32 * sb)) & 0xffffffffull) == 0) continue;   // all padding
+          f32x16 s = {}, dp = {};
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) mma(dp, swz_frag<bf16, D>(v_lds[buf], sb * 32 + frow, 16 * kc + fcol), df[kc]);
-        const int key0 = kt * BN + sb * 32;
-        if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
-          if constexpr (MASKED) {
-            unsigned mv[16];
-            ms.load(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk, ms.sk);
+          for (int kc = 0; kc < KC; ++kc) mma(s, k_row(buf, sb, kc), qf[kc]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
+          for (int kc = 0; kc < KC; ++kc) mma(dp, v_row(buf, sb, kc), df[kc]);
+          const int key0 = kt * BN + sb * 32;
+          if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
+            if constexpr (MASKED) {
+              unsigned mv[16];
+              ms.load(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk, ms.sk);
+#pragma unroll
+              for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
+            }
+            const int lb = key0 + 4 * (lane >> 5);
+            keep_rows(s, -kNoBound, min(a.Nk - lb, CAUSAL ? qrow + a.coff + 1 - lb : kNoBound));
           }
-          const int lb = key0 + 4 * (lane >> 5);
-          keep_rows(s, -kNoBound, min(a.Nk - lb, CAUSAL ? qrow + a.coff + 1 - lb : kNoBound));
-        }
-        if constexpr (KEYPAD)
-          if (keep != ~0ull) keep_keys(s, keep, sb, lane);
-        float lm = -INFINITY;
+          if constexpr (KEYPAD)
+            if (keep != ~0ull) keep_keys(s, keep, sb, lane);
+          float lm = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) lm = fmaxf(lm, s[i]);
-        if (__any(lm == mprobe)) {
+          for (int i = 0; i < 16; ++i) lm = fmaxf(lm, s[i]);
+          if (__any(lm == mprobe)) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (s[i] == mprobe) amax = min(amax, key0 + acc_row(i, lane));
-        }
+            for (int i = 0; i < 16; ++i)
+              if (s[i] == mprobe) amax = min(amax, key0 + acc_row(i, lane));
+          }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = ra_grad_only(s[i], a.c16, kd, dp[i], il, cil);
+          for (int i = 0; i < 16; ++i) s[i] = ra_grad_only(s[i], a.c16, kd, dp[i], il, cil);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 gf = pack_frag_bf16(s, ks);
-          rsum = frag_sum(gf, rsum);
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 gf = pack_frag_bf16(s, ks);
+            rsum = frag_sum(gf, rsum);
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-            mma(acc[db], tr_frag<D>(k_lds[buf], sb * 32 + 16 * ks, db * 32, lane), gf);
+            for (int db = 0; db < DB; ++db)
+              mma(acc[db], k_tr(buf, sb * 32 + 16 * ks, db), gf);
+          }
         }
       }
+      wait_vmem();
+      __syncthreads();
     }
-    wait_vmem();
-    __syncthreads();
   }
 
   const float R = -(rsum + __shfl_xor(rsum, 32));
@@ -715,8 +764,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const f32x2* cs_tab = nullptr;
   if constexpr (ROPE) {
     constexpr int NP = D / 4;
-    static_assert(2 * NP * kWave * sizeof(f32x2) <= sizeof(k_lds) &&
-                  2 * NP * kWave * sizeof(f32x2) <= sizeof(v_lds), "cos/sin tables fit the K/V buffers");
+    static_assert(2 * NP * kWave * sizeof(f32x2) <= 2 * BN * D * sizeof(bf16), "cos/sin tables fit the K/V buffers");
     f32x2* tab = reinterpret_cast<f32x2*>(&k_lds[0][0]);
     const double pos = a.q_pos != nullptr ? (double)a.q_pos[qrow] : (double)qrow;
     if (a.rep % kWaves == 0) {
