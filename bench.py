@@ -62,10 +62,10 @@ TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "attn_fwd_kernel": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4",
                         286919.0, 135180.3),
-    "attn_bwd_dq_bf16_kernel": ("35abd4981b02a7ecb962a224ba6e600d60f0a7149361755916ac13d939542362",
-                                437059.0, 143467.8),
-    "attn_bwd_dkdv_bf16_kernel": ("35abd4981b02a7ecb962a224ba6e600d60f0a7149361755916ac13d939542362",
-                                  267525.0, 262145.2),
+    "attn_bwd_dq_bf16_kernel": ("4888bbf23626a18c854ac0fbb5b2983c12a701c4761ec81dc531e6c6da6849ea",
+                                441266.4, 143463.7),
+    "attn_bwd_dkdv_bf16_kernel": ("4888bbf23626a18c854ac0fbb5b2983c12a701c4761ec81dc531e6c6da6849ea",
+                                  272491.0, 274299.0),
 }
 # VALU instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU) of the forward on a workload,
 # for its VALU-roofline fraction; valid for the recorded kernel source only.
