@@ -20,7 +20,7 @@ calls, then at least 20 calls and at least 1 s; median, min and mean):
   * the grouped-query workload with the NEOX rotation on the device: forward and backward,
     unfused (rotation passes plus the attention) beside the fused entry points
     (ra_attn_fwd_rope, ra_attn_bwd_rope); a padded batch through the key padding path, the
-    split-KV decode step, the row softmax and its backward;
+    split-KV decode step, the row softmax and its backward (fp32 and bf16);
   * the fp64 oracle timed on a bounded sample of each workload on the host cores.
 
 Algorithmic work per visited score element (i, j), D = head dim: forward 4*D flops (S = QK^T
@@ -583,7 +583,24 @@ def main():
     smb_gbs = 3 * x.numel() * 4 / (smb_t["median_ms"] * 1e-3) / 1e9
     log(f"softmax rows {sm_t['median_ms']:.3f} ms ({sm_gbs:.0f} GB/s), backward "
         f"{smb_t['median_ms']:.3f} ms ({smb_gbs:.0f} GB/s)")
-    del x, p, g, dx
+    # the same rows in bf16 (the values rounded to bf16), half the bytes per element
+    xh = torch.from_numpy(wl.make_rows(16384, 8192, seed=11, dtype="bf16")).cuda().to(torch.bfloat16)
+    gh = g.to(torch.bfloat16)
+    ph, dxh = torch.empty_like(xh), torch.empty_like(xh)
+    smh_t = timed(stream, lambda: ra.ra_softmax_rows(xh, ph, 16384, 8192, ra.RA_BF16, stream), min_s)
+    smh_gbs = 2 * xh.numel() * 2 / (smh_t["median_ms"] * 1e-3) / 1e9
+    smbh_t = timed(stream, lambda: ra.ra_softmax_rows_bwd(xh, gh, dxh, 16384, 8192, ra.RA_BF16, stream), min_s)
+    smbh_gbs = 3 * xh.numel() * 2 / (smbh_t["median_ms"] * 1e-3) / 1e9
+    log(f"softmax rows bf16 {smh_t['median_ms']:.3f} ms ({smh_gbs:.0f} GB/s), backward "
+        f"{smbh_t['median_ms']:.3f} ms ({smbh_gbs:.0f} GB/s)")
+    del x, p, g, dx, xh, gh, ph, dxh
+    # reference for the HBM-bound kernels: torch's device copy of 1 GiB (read, then written)
+    src = torch.empty(256 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    cp_t = timed(stream, lambda: dst.copy_(src), min_s)
+    cp_gbs = 2 * src.numel() * 4 / (cp_t["median_ms"] * 1e-3) / 1e9
+    log(f"device copy of 1 GiB {cp_t['median_ms']:.3f} ms ({cp_gbs:.0f} GB/s)")
+    del src, dst
 
     # ---- dominant kernel: the longest launch of the step (one launch per entry-point call)
     dom_name, dom_call, dom_t, dom_flops = max(kernels, key=lambda t: t[2]["mean_ms"])
@@ -654,6 +671,12 @@ def main():
                          "frac_of_hbm_peak": round(sm_gbs / PEAK_HBM_GBS, 4)},
         "softmax_rows_bwd": {"shape": [16384, 8192], "dtype": "f32", **smb_t, "GB/s": round(smb_gbs, 1),
                              "frac_of_hbm_peak": round(smb_gbs / PEAK_HBM_GBS, 4)},
+        "softmax_rows_bf16": {"shape": [16384, 8192], "dtype": "bf16", **smh_t, "GB/s": round(smh_gbs, 1),
+                              "frac_of_hbm_peak": round(smh_gbs / PEAK_HBM_GBS, 4)},
+        "softmax_rows_bwd_bf16": {"shape": [16384, 8192], "dtype": "bf16", **smbh_t,
+                                  "GB/s": round(smbh_gbs, 1), "frac_of_hbm_peak": round(smbh_gbs / PEAK_HBM_GBS, 4)},
+        "hbm_copy_reference": {"what": "torch device copy, 1 GiB read + 1 GiB written", **cp_t,
+                               "GB/s": round(cp_gbs, 1), "frac_of_hbm_peak": round(cp_gbs / PEAK_HBM_GBS, 4)},
         "environment": env,
         "roofline": roofline,
         "cpu_baseline": cpu,
