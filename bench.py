@@ -45,10 +45,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
-# VALU lane operations per second without packed fp32 instructions (the library is built
-# without them): 256 CUs x 64 lanes x 2.4 GHz.  Packed fp32 doubles it (the published fp32
-# vector peak of 157.3 TFLOP/s counts packed FMAs as four flops).
-PEAK_VALU_LANE_OPS = 256 * 64 * 2.4e9
+# VALU lane operations per second: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz, the published fp32
+# vector peak of 157.3 TFLOP/s counted as FMAs of two flops.  Without packed fp32 instructions
+# (the library is built without them) one wave issues a 64-lane instruction about every 4
+# cycles, but two waves on one SIMD each keep that rate (measured with plain FMAs), so a SIMD
+# with two waves reaches 32 lanes per cycle.
+PEAK_VALU_LANE_OPS = 256 * 4 * 32 * 2.4e9
 
 MAIN = "bf16_causal_B4_H16_N8192_D128_fwd_bwd"
 GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
