@@ -65,10 +65,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_neox_kernel(const T* x, T* 
   for (int i = 0; i < V; ++i) rope_cs(pos, rope_rate(j0 + i, D, log2_theta), inverse, c[i], s[i]);
   const int64_t m0 = (int64_t)blockIdx.y * mats_per_thread;
   const int64_t m1 = min(mats, m0 + mats_per_thread);
-  for (int64_t m = m0; m < m1; ++m) {
-    const size_t base = ((size_t)m * N + n) * D + j0;
-    const vec_t a = *reinterpret_cast<const vec_t*>(x + base);
-    const vec_t b = *reinterpret_cast<const vec_t*>(x + base + half);
+  auto turn = [&](const vec_t& a, const vec_t& b, size_t base) {
     vec_t ya, yb;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
@@ -79,6 +76,25 @@ __global__ __launch_bounds__(kRopeThreads) void rope_neox_kernel(const T* x, T* 
     }
     *reinterpret_cast<vec_t*>(y + base) = ya;
     *reinterpret_cast<vec_t*>(y + base + half) = yb;
+  };
+  // four matrices at a time: their eight loads go out together (one matrix at a time left two
+  // loads in flight per thread; measured 2.5% slower)
+  constexpr int U = 4;
+  int64_t m = m0;
+  for (; m + U <= m1; m += U) {
+    vec_t a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t base = ((size_t)(m + u) * N + n) * D + j0;
+      a[u] = *reinterpret_cast<const vec_t*>(x + base);
+      b[u] = *reinterpret_cast<const vec_t*>(x + base + half);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) turn(a[u], b[u], ((size_t)(m + u) * N + n) * D + j0);
+  }
+  for (; m < m1; ++m) {
+    const size_t base = ((size_t)m * N + n) * D + j0;
+    turn(*reinterpret_cast<const vec_t*>(x + base), *reinterpret_cast<const vec_t*>(x + base + half), base);
   }
 }
 
