@@ -19,7 +19,8 @@ calls, then at least 20 calls and at least 1 s; median, min and mean):
     beside an i.i.d. workload of the same shape (nothing skipped);
   * the grouped-query workload with the NEOX rotation on the device: forward and backward,
     unfused (rotation passes plus the attention) beside the fused entry points
-    (ra_attn_fwd_rope, ra_attn_bwd_rope); a padded batch through the key padding path, the
+    (ra_attn_fwd_rope, ra_attn_bwd_rope); a padded batch through the key padding path, packed
+    documents through the general explicit-mask path, the
     split-KV decode step, the row softmax and its backward (fp32 and bf16);
   * the fp64 oracle timed on a bounded sample of each workload on the host cores.
 
@@ -58,26 +59,27 @@ GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch) on the
 # main workload, each scaled by what the counter read for a plain copy of 256 MiB read + 256
 # MiB written (FETCH_SIZE counted half the bytes read: x2; WRITE_SIZE all of them: x1).  Valid
-# only for the kernel source the counters were taken on (sha256 of the files listed).
+# only for the kernel source the counters were taken on (sha256 of the files listed; moved on to
+# a later source only when the kernels' gfx950 assembly is unchanged).
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4",
+    "attn_fwd_kernel": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235",
                         286919.0, 135180.3),
-    "attn_bwd_dq_bf16_kernel": ("4888bbf23626a18c854ac0fbb5b2983c12a701c4761ec81dc531e6c6da6849ea",
+    "attn_bwd_dq_bf16_kernel": ("6042e34915d927ed74e3856872d97b39a6b29f24361d8be53d4de06ee92223a6",
                                 441266.4, 143463.7),
-    "attn_bwd_dkdv_bf16_kernel": ("4888bbf23626a18c854ac0fbb5b2983c12a701c4761ec81dc531e6c6da6849ea",
+    "attn_bwd_dkdv_bf16_kernel": ("6042e34915d927ed74e3856872d97b39a6b29f24361d8be53d4de06ee92223a6",
                                   272491.0, 274299.0),
 }
 # VALU instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU) of the forward on a workload,
 # for its VALU-roofline fraction; valid for the recorded kernel source only.
 VALU_INSTS = {
     # workload: (sha256 of the forward's sources, SQ_INSTS_VALU per dispatch)
-    "fp32_noncausal_B1_H2_N128_D64": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 11560),
-    "bf16_causal_B2_H12_N128_D64": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 101160),
-    "bf16_causal_B8_H16_N2048_D64_sigma2": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 45893632),
-    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 189317120),
-    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("07a0671fb738b2f7478f9187348a29eb3f1720ff04159d5faa408148642c3db4", 364273664),
+    "fp32_noncausal_B1_H2_N128_D64": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 11560),
+    "bf16_causal_B2_H12_N128_D64": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 101160),
+    "bf16_causal_B8_H16_N2048_D64_sigma2": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 45893632),
+    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 189317120),
+    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 364273664),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],
@@ -545,6 +547,26 @@ def main():
     del pad, keep
     torch.cuda.empty_cache()
 
+    # ---- general explicit mask: packed documents, one [B, N, N] boolean mask over all heads
+    wdoc = wl.documents_workload()
+    doc = Attn(ra, wdoc, True)
+    dkeep = wl.documents_keep(wdoc)
+    dmask = (torch.from_numpy(dkeep).cuda(), ra.RA_MASK_BOOL, (wdoc.Nq * wdoc.Nk, 0, wdoc.Nk, 1))
+    # visited entries: the causal ones the mask keeps
+    doc_entries = float(np.tril(dkeep).sum()) * wdoc.Hq
+    dm_t = timed(doc.stream, lambda: doc.fwd_masked(dmask), min_s)
+    dmb_t = timed(doc.stream, lambda: (doc.fwd_masked(dmask), doc.bwd_masked(dmask)), min_s)
+    dc_t = timed(doc.stream, lambda: doc.fwd(), min_s)
+    log(f"packed documents: masked forward {dm_t['median_ms']:.3f} ms, fwd+bwd {dmb_t['median_ms']:.3f} ms; "
+        f"causal forward without the mask {dc_t['median_ms']:.3f} ms")
+    doc_out = {"workload": wdoc.name, "mask": "[B, N, N] bool (same document), causal top-left",
+               "kept_causal_entries": int(doc_entries),
+               "kept_fraction_of_causal": round(doc_entries / (wdoc.B * wdoc.Hq * wdoc.Nq * (wdoc.Nq + 1) / 2), 4),
+               "fwd": dm_t, "fwd_bwd": dmb_t, "unmasked_causal_fwd": dc_t,
+               "fwd_tflops_on_kept_entries": round(4 * wdoc.D * doc_entries / (dm_t["median_ms"] * 1e-3) / 1e12, 2)}
+    del doc, dkeep, dmask
+    torch.cuda.empty_cache()
+
     # ---- split-KV decode: one query row per head against caches of per-sample lengths
     wd = wl.decode_workload()
     dec = Attn(ra, wd, False)
@@ -666,6 +688,7 @@ def main():
                                 "mask": "key padding [B, N] bool, causal top-left",
                                 "fwd_bwd": pm_t, "fwd": pmf_t, "unmasked_fwd_bwd": pp_t,
                                 "tflops_counted": round(tflops(wp.counted_flops_fwd_bwd(), pm_t["median_ms"]), 2)},
+        "masked_documents": doc_out,
         "decode": {"workload": wd.name, "entry": "ra_attn_decode", **dec_t, "kv_bytes": kv_bytes,
                    "GB/s": round(dec_gbs, 1), "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
                    "tiled_fwd_masked": decf_t},

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdArgs a) {
       if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
         if constexpr (MASKED) {
           unsigned mv[16];
-          ms.load(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk, ms.sk);
+          ms.load_keys(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
 #pragma unroll
           for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
         }
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
           if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
             if constexpr (MASKED) {
               unsigned mv[16];
-              ms.load(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk, ms.sk);
+              ms.load_keys(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
 #pragma unroll
               for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
             }

@@ -627,6 +627,9 @@ struct MaskArgs {
   int bytes;             // bytes of one (b, h) slice, tails included
   int kind;
   float inv_scale;       // 1 / scale
+  // keys contiguous (sk = 1), every row and slice start a multiple of 4 elements, Nk a multiple of
+  // 4 and the mask 4-byte aligned: a boolean mask's runs of 4 keys load as one dword (never past Nk)
+  int packed;
 };
 
 inline MaskArgs mask_args(const AttnProblem& p) {
@@ -639,6 +642,8 @@ inline MaskArgs mask_args(const AttnProblem& p) {
   m.bytes = p.mask_bytes;
   m.kind = p.mask_kind;
   m.inv_scale = 1.0f / p.scale;
+  m.packed = p.mask_kind == kMaskBool && p.msk == 1 && p.msq % 4 == 0 && p.msb % 4 == 0 && p.msh % 4 == 0 &&
+             p.Nk % 4 == 0 && reinterpret_cast<unsigned long long>(p.mask) % 4 == 0;
   return m;
 }
 
@@ -656,6 +661,7 @@ struct MaskSlice {
   __amdgpu_buffer_rsrc_t r;
   int sq, sk, kind;
   float inv_scale;
+  bool packed;
 
   __device__ __forceinline__ MaskSlice(const MaskArgs& m, int b, int h) {
     const int es = m.kind == kMaskBool ? 1 : (int)sizeof(T);
@@ -669,6 +675,7 @@ struct MaskSlice {
     sk = m.sk * es;
     kind = m.kind;
     inv_scale = m.inv_scale;
+    packed = __builtin_amdgcn_readfirstlane(m.packed) != 0;
   }
 
   // raw values of the 16 elements of a lane (bool: the byte; additive: the bits as fp32).
@@ -688,6 +695,30 @@ struct MaskSlice {
       for (int i = 0; i < 16; ++i)
         v[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, uniform((8 * (i >> 2) + (i & 3)) * step), 0);
     }
+  }
+
+  // load() along keys (step = sk): a boolean mask with a packed layout reads each run of four keys
+  // as one 4-byte load instead of four byte loads (one row per lane, so the per-element loads
+  // touched a cache line per lane each)
+  __device__ __forceinline__ void load_keys(unsigned (&v)[16], int voff) const {
+    if (packed && kind == kMaskBool) {
+      unsigned w[4];
+      load_words(w, voff);
+      expand_words(w, v);
+    } else {
+      load(v, voff, sk);
+    }
+  }
+  // the packed boolean layout's four runs as words (byte e of word j: element 4 j + e)
+  __device__ __forceinline__ void load_words(unsigned (&w)[4], int voff) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, uniform(8 * j), 0);
+  }
+  static __device__ __forceinline__ void expand_words(const unsigned (&w)[4], unsigned (&v)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * j + e] = (w[j] >> (8 * e)) & 0xffu;
   }
 
   // load() along query rows, where a zero stride (a mask broadcast over rows, as key padding is)

@@ -67,20 +67,49 @@ __device__ __forceinline__ void store_quad<float>(float* dst, f32x16 acc, int ba
   *reinterpret_cast<f32x4*>(dst) = v;
 }
 
-// Mask entries of a 32x32 S^T block (keys on the accumulator rows, query row qrow on the lane):
-// the explicit mask first, then key >= Nk or key > qrow + coff (coff = Nk: no causal limit).
+// Raw explicit-mask values: does one leave its score as it is (boolean: kept; additive: a zero
+// bias), and does one keep its entry at all (boolean: kept; additive: anything but -inf)?
+__device__ __forceinline__ bool mask_identity(int kind, unsigned v) {
+  return kind == kMaskBool ? v != 0u : (v << 1) == 0u;
+}
+__device__ __forceinline__ bool mask_alive(int kind, unsigned v) {
+  return kind == kMaskBool ? v != 0u : v != 0xff800000u;
+}
+
+// The explicit-mask values of a 32x32 S^T block (keys on the accumulator rows, query row qrow on
+// the lane), one per entry of the lane.
+template <typename T>
+__device__ __forceinline__ void load_mask_block(const MaskSlice<T>& ms, unsigned (&mv)[16], int key0, int qrow,
+                                                int lane) {
+  ms.load_keys(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
+}
+
+// Mask entries of a 32x32 S^T block: the explicit mask values mv first (MASKED), then key >= Nk or
+// key > qrow + coff (coff = Nk: no causal limit).  With `ident`, also reports (the same in every
+// lane) whether the explicit mask left every entry of the block as it was.
 template <bool MASKED, typename T>
-__device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int lane, int Nk, int coff,
-                                           const MaskSlice<T>& ms) {
+__device__ __forceinline__ void apply_mask_block(f32x16& s, const unsigned (&mv)[16], int key0, int qrow, int lane,
+                                                 int Nk, int coff, const MaskSlice<T>& ms, bool* ident = nullptr) {
   if constexpr (MASKED) {
-    unsigned mv[16];
-    ms.load(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk, ms.sk);
+    bool all = true;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
+    for (int i = 0; i < 16; ++i) {
+      all = all && mask_identity(ms.kind, mv[i]);
+      s[i] = ms.apply(s[i], mv[i]);
+    }
+    if (ident != nullptr) *ident = !__any(!all);
   }
   // key = key0 + 4 (lane >> 5) + r is kept iff key < Nk and key <= qrow + coff
   const int lb = key0 + 4 * (lane >> 5);
   keep_rows(s, -kNoBound, min(Nk - lb, qrow + coff + 1 - lb));
+}
+
+template <bool MASKED, typename T>
+__device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int lane, int Nk, int coff,
+                                           const MaskSlice<T>& ms, bool* ident = nullptr) {
+  unsigned mv[16] = {};
+  if constexpr (MASKED) load_mask_block(ms, mv, key0, qrow, lane);
+  apply_mask_block<MASKED>(s, mv, key0, qrow, lane, Nk, coff, ms, ident);
 }
 
 // S^T block (32 keys x 32 query rows) of key sub-block sb of the staged (swizzled) K tile.
@@ -157,6 +186,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   static_assert(!ROPE || (WRITE_O && !COUNT), "rotary path");
   __shared__ __attribute__((aligned(16))) unsigned mstage_lds[KEYPAD ? 4 : 1][KEYPAD ? kWave : 1];
   __shared__ unsigned long long keep_lds[KEYPAD ? kMaxTiles : 1];
+  // MASKED: per wave and key tile, 1 when the explicit mask keeps every entry of the wave's block
+  // as it is (recorded in pass 1); pass 2 then treats the tile as unmasked
+  __shared__ unsigned char mfree_lds[MASKED ? kWaves : 1][MASKED ? kMaxTiles : 1];
   __shared__ double rate_lds[ROPE ? D / 2 : 1];   // ROPE: theta^(-2j/D) per pair j
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -271,6 +303,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   const int fcol = 8 * (lane >> 5);     // A-fragment column offset
 
   auto needs_mask = [&](int key0) { return MASKED || key0 + 31 > q0 + a.coff || key0 + 32 > a.Nk; };
+  auto at_edge = [&](int key0) { return key0 + 31 > q0 + a.coff || key0 + 32 > a.Nk; };
   const MaskSlice<T> ms(a.mask, b, h);
 
   // ---- pass 1: row max of the raw dot products (K tiles double-buffered through LDS)
@@ -358,14 +391,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       keep = __ballot(reinterpret_cast<const unsigned char*>(mstage_lds[st])[lane] != 0);
       if (wave == 0 && lane == 0) keep_lds[kt] = keep;
     }
-    if (kt < nt_w && keep != 0) {
+    // MASKED with a boolean mask in the packed layout: the tile's mask words are read before its
+    // products (four per block), and a tile whose mask keeps none of the wave's entries is
+    // dropped without them (its maximum stays -inf, so pass 2 skips it too).  mfree records
+    // whether the mask leaves both blocks of the tile as they are.
+    bool mfree = true, alive = true;
+    const bool mpack = MASKED && ms.packed && ms.kind == kMaskBool;
+    unsigned mw[SB][4];
+    if constexpr (MASKED) {
+      if (mpack && kt < nt_w) {
+        unsigned any = 0;
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+          ms.load_words(mw[sb], qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) any |= mw[sb][j];
+        }
+        alive = __any(any != 0u);
+      }
+    }
+    // the block's mask, from the words read above or loaded now
+    auto p1_mask = [&](f32x16& sc, int sb, int key0, bool& id) {
+      if (MASKED && mpack) {
+        unsigned mv[16];
+        MaskSlice<T>::expand_words(mw[sb], mv);
+        apply_mask_block<MASKED>(sc, mv, key0, qrow, lane, a.Nk, a.coff, ms, &id);
+      } else {
+        mask_block<MASKED>(sc, key0, qrow, lane, a.Nk, a.coff, ms, &id);
+      }
+    };
+    if (kt < nt_w && keep != 0 && alive) {
       if constexpr (sizeof(T) == 2 && SB == 2) {
         f32x16 sc[2];
         score_pair<D>(kt_lds, qf, frow, fcol, sc[0], sc[1]);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
           const int key0 = kt * BN + sb * 32;
-          if (needs_mask(key0)) mask_block<MASKED>(sc[sb], key0, qrow, lane, a.Nk, a.coff, ms);
+          bool id = true;
+          if (needs_mask(key0)) p1_mask(sc[sb], sb, key0, id);
+          mfree = mfree && id;
           if constexpr (KEYPAD)
             if (keep != ~0ull) keep_keys(sc[sb], keep, sb, lane);
 #pragma unroll
@@ -376,7 +440,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         for (int sb = 0; sb < SB; ++sb) {
           f32x16 sc = score_block<T, D>(kt_lds, qf, sb, frow, fcol);
           const int key0 = kt * BN + sb * 32;
-          if (needs_mask(key0)) mask_block<MASKED>(sc, key0, qrow, lane, a.Nk, a.coff, ms);
+          bool id = true;
+          if (needs_mask(key0)) p1_mask(sc, sb, key0, id);
+          mfree = mfree && id;
 #pragma unroll
           for (int i = 0; i < 16; ++i) tl = fmaxf(tl, sc[i]);
         }
@@ -386,6 +452,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     if (kt < kMaxTiles) {
       const float wm = wave_max_lane63(tl);
       if (lane == 63) tmax_lds[wave][kt] = wm;
+      if (MASKED && lane == 0) mfree_lds[MASKED ? wave : 0][MASKED ? kt : 0] = mfree ? 1 : 0;
     }
     if constexpr (DEEP) {
       // tile kt + 1 landed; the copies issued after it (tiles kt + 2, kt + 3) may stay in flight
@@ -505,7 +572,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       n_wave_skip += my_skip ? 1 : 0;
     }
     bool done = my_skip;
-    const bool fast = VTR && WRITE_O && SB == 2 && !done && !needs_mask(cur * BN + 32) && keys_full;
+    // MASKED: a tile whose explicit mask pass 1 found to keep every entry of the wave's blocks as
+    // they are runs as an unmasked one (no mask reads; the interleaved path when away from edges)
+    bool mfree = false;
+    if constexpr (MASKED) mfree = cur < kMaxTiles && uniform((int)mfree_lds[wave][cur]) != 0;
+    const bool fast = VTR && WRITE_O && SB == 2 && !done && !(MASKED && !mfree) && !at_edge(cur * BN + 32) &&
+                      keys_full;
     if (nxt < nt) {
       k_issue(nxt, k_lds[buf ^ 1]);
       if constexpr (WRITE_O) v_issue(nxt, v_lds[buf ^ 1]);
@@ -590,7 +662,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         const int key0 = cur * BN + sb * 32;
-        if (needs_mask(key0)) mask_block<MASKED>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
+        if (MASKED && !mfree) mask_block<MASKED>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
+        else if (at_edge(key0)) mask_block<false>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
         if constexpr (KEYPAD) {
           const unsigned long long keep = keep_lds[cur];
           if (keep != ~0ull) keep_keys(s[sb], keep, sb, lane);

@@ -61,7 +61,15 @@ def make_mask(layout, B, Hq, Nq, Nk, dtype, seed):
         keep_t = rng.random((Nk, Nq)) < 0.7
         t = torch.from_numpy(keep_t).cuda()
         return keep_t.T, t, ra.RA_MASK_BOOL, (0, 0, 1, Nq)
-    if layout == "head_bias":                     # additive [1, Hq, Nq, Nk] with -inf entries
+    if layout in ("documents", "documents_add"):  # packed documents, [B, N, N] over all heads
+        assert Nq == Nk
+        ids = wl.document_ids(B, Nq, seed, 40, 200)
+        keep = ids[:, :, None] == ids[:, None, :]
+        if layout == "documents":
+            t = torch.from_numpy(keep).cuda()
+            return keep[:, None], t, ra.RA_MASK_BOOL, (Nq * Nk, 0, Nk, 1)
+        bias = np.where(keep, 0.0, -np.inf)[:, None].astype(np.float32)   # the same as 0 / -inf
+    elif layout == "head_bias":                   # additive [1, Hq, Nq, Nk] with -inf entries
         bias = rng.normal(0, 2, size=(1, Hq, Nq, Nk)).astype(np.float32)
         bias[rng.random(bias.shape) < 0.1] = -np.inf
     elif layout == "alibi":                       # additive -slope_h |i - j|
@@ -197,6 +205,13 @@ MASK_CASES = [
     ("alibi", 1, 8, 2, 160, 160, 128, "top_left", "bf16"),
     ("alibi", 1, 4, 4, 50, 120, 64, "bottom_right", "f32"),
     ("key_bias", 3, 2, 1, 75, 140, 128, "none", "bf16"),
+    # packed documents: whole tiles kept (run as unmasked ones), partial ones at the documents'
+    # edges and tiles the mask drops entirely (no products in either pass)
+    ("documents", 2, 4, 2, 300, 300, 128, "top_left", "bf16"),
+    ("documents", 1, 4, 4, 260, 260, 64, "none", "bf16"),
+    ("documents", 1, 2, 2, 200, 200, 128, "top_left", "f32"),
+    ("documents_add", 2, 2, 1, 300, 300, 128, "top_left", "bf16"),
+    ("documents_add", 1, 2, 2, 170, 170, 64, "none", "f32"),
     ("key_bias", 2, 2, 2, 40, 40, 64, "top_left", "f32"),
 ]
 
@@ -346,3 +361,24 @@ def test_padded_batch_full_size_sampled_heads(gpu_lib):
     # keys past a sample's length take no part: their dk, dv are exactly zero
     for b, n in enumerate(lengths):
         assert (res["dk"][b, :, n:] == 0).all() and (res["dv"][b, :, n:] == 0).all()
+
+
+# ----------------------------------------------------------------- masks that change nothing
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_identity_masks_equal_the_unmasked_forward(gpu_lib, dtype, D):
+    """An all-true boolean mask and an all-zero additive one leave every score as it is: the masked
+    forward (whose tiles pass 1 finds unmasked then run as unmasked ones) gives the unmasked
+    forward's bits."""
+    import torch
+    ra = gpu_lib
+    B, Hq, Hkv, N = 2, 4, 2, 333
+    inp = rand_inputs(B, Hq, Hkv, N, N, D, dtype, seed=41)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    ref = run(ra, inp, "top_left", scale, dtype, bwd=False)
+    ones = torch.ones((N, N), dtype=torch.bool, device="cuda")
+    zeros = torch.zeros((N, N), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+    for mask in ((ones, ra.RA_MASK_BOOL, (0, 0, N, 1)), (zeros, ra.RA_MASK_ADD, (0, 0, N, 1))):
+        got = run(ra, inp, "top_left", scale, dtype, mask=mask, bwd=False)
+        np.testing.assert_array_equal(got["o"], ref["o"])
+        np.testing.assert_array_equal(got["stats"], ref["stats"])

@@ -46,3 +46,14 @@ def test_workload_flop_counts():
     assert w.counted_flops_fwd() == pytest.approx(549.76e9, rel=1e-4)
     w5 = wl.WORKLOADS["bf16_causal_B4_H16_N8192_D128_fwd_bwd"]
     assert w5.counted_flops_fwd_bwd() == pytest.approx(3848.3e9, rel=1e-4)
+
+
+def test_document_ids_are_contiguous_runs_of_bounded_length():
+    ids = wl.document_ids(3, 1000, seed=5, lo=40, hi=200)
+    for row in ids:
+        assert row[0] == 0 and (np.diff(row) >= 0).all() and (np.diff(row) <= 1).all()
+        lengths = np.bincount(row)
+        assert (lengths[:-1] >= 40).all() and (lengths <= 200).all()
+    keep = wl.documents_keep()
+    assert keep.shape == (4, 4096, 4096) and keep.dtype == bool
+    assert (keep == keep.transpose(0, 2, 1)).all() and keep[:, np.arange(4096), np.arange(4096)].all()

@@ -108,6 +108,40 @@ def decode_seqlens(w: AttnWorkload = DECODE) -> np.ndarray:
     return rng.integers(w.Nk // 4, w.Nk + 1, size=w.B).astype(np.int32)
 
 
+# Packed documents for the general explicit-mask path: each sample of N tokens holds several
+# documents back to back, and a token attends to the tokens of its own document only (with the
+# causal limit).  The mask is one [B, N, N] boolean array broadcast over heads; document lengths
+# are drawn from [N/16, N/2] with their own seeded generator, the last one cut at N.  Most of its
+# 64-key tiles are either wholly inside a document or wholly outside.
+DOCUMENTS = AttnWorkload("bf16_causal_documents_B4_H16_N4096_D128", "bf16", True, 4, 16, 16,
+                         4096, 4096, 128, seed=8, with_grad=True)
+
+
+def documents_workload() -> AttnWorkload:
+    return DOCUMENTS
+
+
+def document_ids(B: int, N: int, seed: int, lo: int, hi: int) -> np.ndarray:
+    """int32 [B, N]: the document of every token, documents of lengths drawn from [lo, hi]."""
+    rng = np.random.default_rng(seed)
+    ids = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        pos, d = 0, 0
+        while pos < N:
+            n = int(rng.integers(lo, hi + 1))
+            ids[b, pos:pos + n] = d
+            pos, d = pos + n, d + 1
+    return ids
+
+
+def documents_keep(w: AttnWorkload = DOCUMENTS) -> np.ndarray:
+    """The [B, N, N] boolean mask of the documents workload: True where query and key share a
+    document."""
+    assert w.Nq == w.Nk
+    ids = document_ids(w.B, w.Nq, w.seed + 2000, w.Nq // 16, w.Nq // 2)
+    return ids[:, :, None] == ids[:, None, :]
+
+
 def padded_batch_keep(w: AttnWorkload = PADDED_BATCH) -> np.ndarray:
     """The [B, Nk] boolean key padding mask: True where key j < length of sample b."""
     return np.arange(w.Nk)[None, :] < np.asarray(padded_batch_lengths(w))[:, None]
