@@ -64,22 +64,22 @@ GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235",
+    "attn_fwd_kernel": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083",
                         286919.0, 135180.3),
-    "attn_bwd_dq_bf16_kernel": ("6042e34915d927ed74e3856872d97b39a6b29f24361d8be53d4de06ee92223a6",
+    "attn_bwd_dq_bf16_kernel": ("8a182001426cf273ebaa4452bc1995406367434e662d0b11abdf22ab5aa951db",
                                 441266.4, 143463.7),
-    "attn_bwd_dkdv_bf16_kernel": ("6042e34915d927ed74e3856872d97b39a6b29f24361d8be53d4de06ee92223a6",
+    "attn_bwd_dkdv_bf16_kernel": ("8a182001426cf273ebaa4452bc1995406367434e662d0b11abdf22ab5aa951db",
                                   272491.0, 274299.0),
 }
 # VALU instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU) of the forward on a workload,
 # for its VALU-roofline fraction; valid for the recorded kernel source only.
 VALU_INSTS = {
     # workload: (sha256 of the forward's sources, SQ_INSTS_VALU per dispatch)
-    "fp32_noncausal_B1_H2_N128_D64": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 11560),
-    "bf16_causal_B2_H12_N128_D64": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 101160),
-    "bf16_causal_B8_H16_N2048_D64_sigma2": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 45893632),
-    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 189317120),
-    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("34f2ec7e0b2db482c0ae204ceef746cef4c4b4a0fb95d4e65a2e3a503215f235", 364273664),
+    "fp32_noncausal_B1_H2_N128_D64": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 11560),
+    "bf16_causal_B2_H12_N128_D64": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 101160),
+    "bf16_causal_B8_H16_N2048_D64_sigma2": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 45893632),
+    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 189317120),
+    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 364273664),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],

@@ -645,6 +645,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const float kd = m == -INFINITY ? INFINITY : fmaf(m, a.c16, 1.0f);
   const float mprobe = argmax_probe(m);
   const MaskSlice<bf16> ms(a.mask, b, h);
+  const bool mpack = MASKED && ms.packed && ms.kind == kMaskBool;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -712,16 +713,26 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
           if (KEYPAD && ((keep >> (32 * sb)) & 0xffffffffull) == 0) continue;   // all padding
+          // MASKED with a boolean mask in the packed layout: the block's mask words are read
+          // before its products and tested after them (a wait before them would also wait for
+          // the next tile's copies, issued earlier in the step), and a block the mask empties for
+          // every row of the wave stops there (its entries add nothing to dQ, R or the argmax)
+          unsigned mw[4];
+          if constexpr (MASKED)
+            if (mpack) ms.load_words(mw, qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
           f32x16 s = {}, dp = {};
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) mma(s, k_row(buf, sb, kc), qf[kc]);
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) mma(dp, v_row(buf, sb, kc), df[kc]);
+          if constexpr (MASKED)
+            if (mpack && !__any((mw[0] | mw[1] | mw[2] | mw[3]) != 0u)) continue;
           const int key0 = kt * BN + sb * 32;
           if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
             if constexpr (MASKED) {
               unsigned mv[16];
-              ms.load_keys(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
+              if (mpack) MaskSlice<bf16>::expand_words(mw, mv);
+              else ms.load_keys(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
 #pragma unroll
               for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
             }
@@ -955,6 +966,17 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
       ms.load_rows(mv, key * ms.sk + (c.qt * QT + HR * half + 4 * (lane >> 5)) * ms.sq, ms.sq);
     }
   };
+  // does the mask keep any entry of the wave's block?  A block it empties adds nothing to dK or
+  // dV: the lower half skips all of its work, the upper half the work after its S/dP products (a
+  // wait before them would also wait for the next tile's copies, which it issues at the start of
+  // the step)
+  auto mask_keeps_any = [&](const unsigned (&mv)[16]) {
+    if constexpr (!MASKED) return true;
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) any = any || mask_alive(a.mask.kind, mv[i]);
+    return __any(any) != 0;
+  };
 
   // Q/dO half-tiles are addressed from the half's slot-0 Q tile hb: Q of slot t at byte offset
   // qo = t HTB, dO at doo.  The unmasked kernels read them through QdoAddr: the LDS address of
@@ -1171,8 +1193,10 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
         unsigned mv[16];
         mask_load(cur, mv);
         products_sdp(hb, ad, par * HTB, (2 + par) * HTB, s, dp);
-        derivative(s, dp, mv, cur.qt * QT, cur.slot3);
-        products_dkdv(s, dp, hb, ad, par * HTB, (2 + par) * HTB);
+        if (mask_keeps_any(mv)) {
+          derivative(s, dp, mv, cur.qt * QT, cur.slot3);
+          products_dkdv(s, dp, hb, ad, par * HTB, (2 + par) * HTB);
+        }
       }
       wait_vmem();
       __syncthreads();
@@ -1203,7 +1227,8 @@ __global__ __launch_bounds__(kDkdvThreads) void attn_bwd_dkdv_bf16_kernel(BwdArg
       carried = st < steps && block_live(cur);
       if (carried) {
         mask_load(cur, mv);
-        products_sdp(hb, ad, sc * HTB, (3 + sc) * HTB, s, dp);
+        carried = mask_keeps_any(mv);
+        if (carried) products_sdp(hb, ad, sc * HTB, (3 + sc) * HTB, s, dp);
       }
       wait_vmem();
       __syncthreads();

@@ -647,6 +647,11 @@ inline MaskArgs mask_args(const AttnProblem& p) {
   return m;
 }
 
+// Does a raw mask value keep its entry at all (boolean: kept; additive: anything but -inf)?
+__device__ __forceinline__ bool mask_alive(int kind, unsigned v) {
+  return kind == kMaskBool ? v != 0u : v != 0xff800000u;
+}
+
 // A score with its mask element applied (v as MaskSlice::load returns it).
 __device__ __forceinline__ float mask_value(int kind, float inv_scale, float s, unsigned v) {
   return kind == kMaskBool ? (v != 0u ? s : -INFINITY) : fmaf(__uint_as_float(v), inv_scale, s);

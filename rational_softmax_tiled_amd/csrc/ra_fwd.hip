@@ -67,13 +67,9 @@ __device__ __forceinline__ void store_quad<float>(float* dst, f32x16 acc, int ba
   *reinterpret_cast<f32x4*>(dst) = v;
 }
 
-// Raw explicit-mask values: does one leave its score as it is (boolean: kept; additive: a zero
-// bias), and does one keep its entry at all (boolean: kept; additive: anything but -inf)?
+// Does a raw explicit-mask value leave its score as it is (boolean: kept; additive: a zero bias)?
 __device__ __forceinline__ bool mask_identity(int kind, unsigned v) {
   return kind == kMaskBool ? v != 0u : (v << 1) == 0u;
-}
-__device__ __forceinline__ bool mask_alive(int kind, unsigned v) {
-  return kind == kMaskBool ? v != 0u : v != 0xff800000u;
 }
 
 // The explicit-mask values of a 32x32 S^T block (keys on the accumulator rows, query row qrow on
@@ -330,6 +326,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       if (wave == 0) lds_dma_at<4>(m_rsrc, lds_addr(mstage_lds[stage]), lane * 4, kt * BN);
   };
   float mx = -INFINITY;
+  // MASKED with a boolean mask in the packed layout: pass 1 reads each tile's mask words one step
+  // ahead (they land with the step's copies, so deciding on them waits for nothing), drops a tile
+  // the mask empties for every row of the wave before its products, and applies the words to the
+  // tiles it computes.  (A wait for words loaded in the same step would also wait for the step's
+  // K copy, issued before them, which counts in the same in-order counter.)
+  const bool mpack = MASKED && ms.packed && ms.kind == kMaskBool;
+  unsigned mw_next[SB][4];
+  auto load_tile_words = [&](int kt, unsigned (&w)[SB][4]) {
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) ms.load_words(w[sb], qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
+  };
   // bf16 with V buffers: pass 1 streams K through four LDS stages (the V buffers are idle until
   // pass 2), three tiles ahead of the math.  Only without a mask: the mask loads are vector
   // loads too, and the counted waits below assume the copies are the only ones in flight.
@@ -370,6 +377,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     if constexpr (ROPE) rope_rotate();
     if (nt > 0) {
       k_issue(0, k_lds[0]);
+      if (mpack && nt_w > 0) load_tile_words(0, mw_next);
       k_land(k_lds[0]);
     }
   }
@@ -377,6 +385,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   // one step of pass 1 on tile kt, held in stage S
   auto p1_step = [&](int kt, auto S) {
     constexpr int st = decltype(S)::value;
+    // MASKED, packed: tile kt's words (read in the previous step) decide before anything is issued
+    bool alive = true;
+    unsigned mw[SB][4];
+    if constexpr (MASKED) {
+      if (mpack && kt < nt_w) {
+        unsigned any = 0;
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            mw[sb][j] = mw_next[sb][j];
+            any |= mw[sb][j];
+          }
+        alive = __any(any != 0u);
+      }
+    }
     // the stage receiving tile kt + kStages - 1 was last read in step kt - 1, which every wave
     // has left (barrier at the end of each step)
     constexpr int st_in = (st + kStages - 1) % kStages;
@@ -384,6 +408,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       k_issue(kt + kStages - 1, k_stage(std::integral_constant<int, st_in>{}));
       m_issue(kt + kStages - 1, st_in);
     }
+    if (MASKED && mpack && kt + 1 < nt_w) load_tile_words(kt + 1, mw_next);
     const T* kt_lds = k_stage(S);
     float tl = -INFINITY;
     unsigned long long keep = ~0ull;   // KEYPAD: bit l set when key kt BN + l is kept
@@ -391,26 +416,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       keep = __ballot(reinterpret_cast<const unsigned char*>(mstage_lds[st])[lane] != 0);
       if (wave == 0 && lane == 0) keep_lds[kt] = keep;
     }
-    // MASKED with a boolean mask in the packed layout: the tile's mask words are read before its
-    // products (four per block), and a tile whose mask keeps none of the wave's entries is
-    // dropped without them (its maximum stays -inf, so pass 2 skips it too).  mfree records
-    // whether the mask leaves both blocks of the tile as they are.
-    bool mfree = true, alive = true;
-    const bool mpack = MASKED && ms.packed && ms.kind == kMaskBool;
-    unsigned mw[SB][4];
-    if constexpr (MASKED) {
-      if (mpack && kt < nt_w) {
-        unsigned any = 0;
-#pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-          ms.load_words(mw[sb], qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) any |= mw[sb][j];
-        }
-        alive = __any(any != 0u);
-      }
-    }
-    // the block's mask, from the words read above or loaded now
+    bool mfree = true;   // MASKED: the mask leaves both blocks of the tile as they are
+    // the block's mask, from the words read one step ahead or loaded now
     auto p1_mask = [&](f32x16& sc, int sb, int key0, bool& id) {
       if (MASKED && mpack) {
         unsigned mv[16];
