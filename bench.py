@@ -595,6 +595,25 @@ def main():
         f"with the lengths as a mask {decf_t['median_ms']:.4f} ms")
     del dec, dws, keep
     torch.cuda.empty_cache()
+    # the same step with fp32 caches (twice the bytes per key)
+    wd32 = wl.decode_workload("f32")
+    dec32 = Attn(ra, wd32, False)
+    dws32_bytes = ra.ra_attn_decode_workspace_bytes(wd32.B, wd32.Hq, wd32.Hkv, wd32.Nq, wd32.Nk,
+                                                    wd32.D, dec32.code)
+    dws32 = torch.empty(dws32_bytes, dtype=torch.uint8, device="cuda")
+
+    def decode_step_f32():
+        st = ra.ra_attn_decode(dec32.q, dec32.k, dec32.v, dec32.o, None, lens, dws32, dws32_bytes,
+                               wd32.B, wd32.Hq, wd32.Hkv, wd32.Nq, wd32.Nk, wd32.D,
+                               ra.RA_CAUSAL_BOTTOM_RIGHT, wd32.scale, dec32.code, dec32.stream)
+        if st != 0:
+            raise RuntimeError(f"ra_attn_decode: {ra.ra_status_string(st)}")
+    dec32_t = timed(dec32.stream, decode_step_f32, min_s)
+    kv32_bytes = int(lens_np.astype(np.int64).sum()) * wd32.Hkv * wd32.D * 2 * 4
+    dec32_gbs = kv32_bytes / (dec32_t["median_ms"] * 1e-3) / 1e9
+    log(f"decode fp32: {dec32_t['median_ms']:.4f} ms, {dec32_gbs:.0f} GB/s of K/V")
+    del dec32, dws32
+    torch.cuda.empty_cache()
 
     # ---- row softmax and its backward (HBM-bound)
     x = torch.from_numpy(wl.make_rows(16384, 8192, seed=11)).cuda()
@@ -691,7 +710,10 @@ def main():
         "masked_documents": doc_out,
         "decode": {"workload": wd.name, "entry": "ra_attn_decode", **dec_t, "kv_bytes": kv_bytes,
                    "GB/s": round(dec_gbs, 1), "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
-                   "tiled_fwd_masked": decf_t},
+                   "tiled_fwd_masked": decf_t,
+                   "f32": {"workload": wd32.name, **dec32_t, "kv_bytes": kv32_bytes,
+                           "GB/s": round(dec32_gbs, 1),
+                           "frac_of_hbm_peak": round(dec32_gbs / PEAK_HBM_GBS, 4)}},
         "softmax_rows": {"shape": [16384, 8192], "dtype": "f32", **sm_t, "GB/s": round(sm_gbs, 1),
                          "frac_of_hbm_peak": round(sm_gbs / PEAK_HBM_GBS, 4)},
         "softmax_rows_bwd": {"shape": [16384, 8192], "dtype": "f32", **smb_t, "GB/s": round(smb_gbs, 1),

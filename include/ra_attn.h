@@ -254,8 +254,9 @@ size_t ra_attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_
  *   keys j <= seqlens[b] - Nq + i).  stats (optional) as ra_attn_fwd.  Equivalent to
  *   ra_attn_fwd on each sample's cache prefix; a sample with seqlens[b] = 0 (or a row with no
  *   allowed key) gives o = 0.
- *   Restrictions: dtype RA_BF16 only (RA_ERR_DTYPE otherwise); (Hq / Hkv) * Nq <= 32, the query
- *   rows of one K/V head (RA_ERR_SHAPE otherwise; use ra_attn_fwd for longer query blocks).
+ *   dtype RA_BF16 (bf16 products) or RA_F32 (fp32 products), as ra_attn_fwd; fp32 sums either way.
+ *   Restrictions: (Hq / Hkv) * Nq <= 32, the query rows of one K/V head (RA_ERR_SHAPE otherwise;
+ *   use ra_attn_fwd for longer query blocks).
  *   Forward only.  Deterministic.  Other checks, sizes and limits as ra_attn_fwd; workspace at
  *   least ra_attn_decode_workspace_bytes(...) bytes, 256-byte aligned (RA_ERR_WORKSPACE,
  *   RA_ERR_ALIGN).

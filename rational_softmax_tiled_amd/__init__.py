@@ -302,7 +302,7 @@ def _shapes(q, k, v):
 
 def attn_decode(q, k_cache, v_cache, seqlens=None, causal=False, scale: Optional[float] = None,
                 with_stats: bool = False):
-    """Decode step: q [B, Hq, Nq, D] (bf16, (Hq / Hkv) * Nq <= 32) against the caches
+    """Decode step: q [B, Hq, Nq, D] (bf16 or fp32, (Hq / Hkv) * Nq <= 32) against the caches
     k_cache, v_cache [B, Hkv, Nk, D], sample b using its first seqlens[b] keys (int32 device
     tensor [B], or None for all).  ``causal``: see causal_code ("bottom_right": query i is
     position seqlens[b] - Nq + i).  Allocates O (and stats) and a workspace; runs

@@ -394,7 +394,6 @@ static int check_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t 
                         int causal, float scale, int dtype) {
   int st = check_sizes(B, Hq, Hkv, Nq, Nk, D, scale, dtype);
   if (st != RA_OK) return st;
-  if (dtype != RA_BF16) return RA_ERR_DTYPE;
   if (causal != RA_CAUSAL_NONE && causal != RA_CAUSAL_TOP_LEFT && causal != RA_CAUSAL_BOTTOM_RIGHT)
     return RA_ERR_MASK;
   if (Hkv > 0 && (Hq / Hkv) * Nq > 32) return RA_ERR_SHAPE;
@@ -446,6 +445,7 @@ int ra_attn_decode(const void* q, const void* k, const void* v, void* o, float* 
   p.D = (int)D;
   p.causal = causal;
   p.scale = scale;
+  p.bf16 = dtype == RA_BF16;
   return hip_status(ra::launch_attn_decode(p, workspace, s));
 }
 

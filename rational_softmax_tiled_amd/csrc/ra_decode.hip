@@ -16,6 +16,10 @@
 // K and V are each read from HBM once; the scores (R x 4 bytes per key) and partials are small
 // beside them.  Decode is memory-bound: a wave's 32 query columns are padded past R, and that
 // idle matrix-core and vector work hides under the K/V streams.
+// bf16 and fp32 share the split and the first and last kernels; the fp32 scores take fp32
+// products (eight 32x32x2 per 16 columns) with twice the bytes per block, so their register ring
+// holds two blocks instead of three, and the fp32 P.V reads V straight into the product's
+// operand layout (below) instead of through LDS.
 #include <type_traits>
 
 #include "ra_device.h"
@@ -24,10 +28,10 @@
 namespace ra {
 
 struct DecodeArgs {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  bf16* o;
+  const void* q;        // [B, Hq, Nq, D] of the attention dtype, as k, v and o
+  const void* k;
+  const void* v;
+  void* o;
   float* stats;
   const int* seqlens;   // [B] cache lengths (nullptr: all Nk)
   float* scores;        // [groups][nk32 / 32][R][2][16] raw dot products, by 32-key block
@@ -168,12 +172,26 @@ __device__ __forceinline__ void ring3(int nb, F&& step) {
     step(std::integral_constant<int, 2>{}, t + 2);
   }
 }
+// The same with two register sets, one block ahead (fp32: a block is twice the bytes, so the
+// data in flight per wave stays that of the bf16 ring).
+template <typename F>
+__device__ __forceinline__ void ring2(int nb, F&& step) {
+  for (int t = 0; t < nb; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 >= nb) break;
+    step(std::integral_constant<int, 1>{}, t + 1);
+  }
+}
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a) {
+template <typename T, int D>
+__device__ __forceinline__ void decode_scores(const DecodeArgs& a) {
   constexpr int KC = D / 16;
-  constexpr int CPR = D / 8, PER = 32 * CPR / kWave;
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[kWaves][32 * D];
+  constexpr int CPR = D * (int)sizeof(T) / 16, PER = 32 * CPR / kWave;
+  // register ring slots: bf16 three, two blocks ahead of the math; fp32 (a block is twice the
+  // bytes, and the Q fragments take 64 registers at D = 128) one, refilled with the next block as
+  // soon as this one is in LDS, so one block is in flight under the products
+  constexpr int NS = sizeof(T) == 2 ? 3 : 1;
+  __shared__ __attribute__((aligned(16))) T k_lds[kWaves][32 * D];
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const DecodeWork work = decode_work(a, blockIdx.x * kWaves + wave);
   if (work.bg < 0) return;   // whole wave: no barrier in this kernel
@@ -185,9 +203,9 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a) {
   // B operand: query row r = lane % 32 of the group (rows past R repeat the last one)
   const int r = lane & 31, rr = min(r, a.R - 1);
   const int h = g * a.rep + rr / a.Nq;
-  const bf16* qrow = a.q + ((size_t)(b * a.Hq + h) * a.Nq + rr % a.Nq) * D;
+  const T* qrow = static_cast<const T*>(a.q) + ((size_t)(b * a.Hq + h) * a.Nq + rr % a.Nq) * D;
   const int fcol = 8 * (lane >> 5);
-  bf16x8 qf[KC];
+  typename Ty<T>::frag qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) qf[kc] = load_frag(qrow + 16 * kc + fcol);
   const int lim = key_limit(a, len, rr);
@@ -196,34 +214,35 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a) {
   // a block; rows past the chunk's keys read as zeros), stored swizzled into this wave's LDS
   // tile, from which the A fragments are read (the previous block's reads have returned: their
   // results fed the products, and a wave's LDS operations execute in order)
-  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(uniform_ptr(a.k + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
-  u32x4 ring[3][PER];
+  const __amdgpu_buffer_rsrc_t kr =
+      tile_rsrc(uniform_ptr(static_cast<const T*>(a.k) + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
+  u32x4 ring[NS][PER];
   auto load = [&](int slot, int t) {
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-      ring[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(kr, (j * kWave + lane) * 16, uniform(t * 32 * D * 2), kStreamOnce);
+      ring[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(kr, (j * kWave + lane) * 16,
+                                                            uniform(t * 32 * D * (int)sizeof(T)), kStreamOnce);
   };
-  bf16* ktile = k_lds[wave];
+  T* ktile = k_lds[wave];
   // this chunk's scores, [block][R rows][2 lane halves][16]; padded rows store past the end
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(a.scores + ((size_t)bg * a.nk32 + k0) * a.R), (short)0, uniform(nb * 32 * a.R * 4), kBufferWord3);
   const int s_off = r < a.R ? (r * 2 + (lane >> 5)) * 64 : 0x40000000;
   float mx = -INFINITY;
-  load(0, 0);
-  load(1, 1);
-  ring3(nb, [&](auto slot_c, int t) {
+  auto step = [&](auto slot_c, int t) {
     constexpr int slot = decltype(slot_c)::value;
-    load((slot + 2) % 3, t + 2);
+    if constexpr (NS > 1) load((slot + NS - 1) % NS, t + NS - 1);
     // S^T = K Q^T: keys on the accumulator rows, query row r on the lane
     f32x16 sacc = {};
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int c = j * kWave + lane, row = c / CPR, cc = c % CPR;
-      *reinterpret_cast<u32x4*>(ktile + swz_off<bf16, D>(row, cc)) = ring[slot][j];
+      *reinterpret_cast<u32x4*>(ktile + swz_off<T, D>(row, cc)) = ring[slot][j];
     }
+    if constexpr (NS == 1) load(0, t + 1);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) mma(sacc, swz_frag<bf16, D>(ktile, lane & 31, 16 * kc + fcol), qf[kc]);
+    for (int kc = 0; kc < KC; ++kc) mma(sacc, swz_frag<T, D>(ktile, lane & 31, 16 * kc + fcol), qf[kc]);
     // key k0 + 32 t + 4 (lane >> 5) + row offset is kept iff it is <= lim (which is < len)
     keep_rows(sacc, -kNoBound, lim + 1 - (k0 + 32 * t + 4 * (lane >> 5)));
 #pragma unroll
@@ -233,13 +252,72 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a) {
       __builtin_amdgcn_raw_buffer_store_b128(
           __builtin_bit_cast(u32x4, f32x4{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]}),
           sr, s_off + 16 * q4, uniform(t * 32 * a.R * 4), 0);
-  });
+  };
+#pragma unroll
+  for (int t = 0; t < (NS > 1 ? NS - 1 : 1); ++t) load(t, t);
+  if constexpr (NS == 3) ring3(nb, step);
+  else for (int t = 0; t < nb; ++t) step(std::integral_constant<int, 0>{}, t);
   mx = fmaxf(mx, __shfl_xor(mx, 32));   // lanes l and l + 32 hold the same row
   if (lane < a.R) a.pmax[((size_t)bg * a.S + s) * a.R + lane] = mx;
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_pv_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a) {
+  decode_scores<bf16, D>(a);
+}
+// fp32: the Q fragments take 64 registers at D = 128 and each ring slot 64 more
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_scores_f32_kernel(DecodeArgs a) {
+  decode_scores<float, D>(a);
+}
+
+// The row max of query row r (lanes r and r + 32) over every chunk of the group that holds keys:
+// the two lanes take the even and odd chunks, eight loads in flight per round.  The wave of
+// chunk 0 records it for the stats.
+__device__ __forceinline__ float decode_row_max(const DecodeArgs& a, int bg, int s, int nlive, int lane, bool live) {
+  float m = -INFINITY;
+  if (live) {
+    const float* pm = a.pmax + (size_t)bg * a.S * a.R + (lane & 31);
+    for (int s2 = lane >> 5; s2 < nlive; s2 += 16) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = s2 + 2 * j < nlive ? pm[(size_t)(s2 + 2 * j) * a.R] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, x[j]);
+    }
+  }
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (s == 0 && lane < a.R) a.gmax[(size_t)bg * a.R + lane] = m;
+  return m;
+}
+
+// A chunk's scores as the first kernel stored them, block by block, in its lane layout; padded
+// rows and blocks past the chunk read zeros.
+struct ChunkScores {
+  __amdgpu_buffer_rsrc_t sr;
+  int s_off, stride;
+  __device__ __forceinline__ ChunkScores(const DecodeArgs& a, int bg, int k0, int nb, int lane, bool live) {
+    sr = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.scores + ((size_t)bg * a.nk32 + k0) * a.R), (short)0,
+                                           uniform(nb * 32 * a.R * 4), kBufferWord3);
+    s_off = live ? ((lane & 31) * 2 + (lane >> 5)) * 64 : 0x40000000;
+    stride = 32 * a.R * 4;
+  }
+  __device__ __forceinline__ f32x16 load(int t) const {
+    f32x16 v;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, s_off + 16 * q4, uniform(t * stride), 0));
+      v[4 * q4] = x[0];
+      v[4 * q4 + 1] = x[1];
+      v[4 * q4 + 2] = x[2];
+      v[4 * q4 + 3] = x[3];
+    }
+    return v;
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void decode_pv_bf16(const DecodeArgs& a) {
   constexpr int DB = D / 32, TILE = 32 * D;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int PER = 32 * CPR / kWave;   // chunks of a 32-row tile per lane
@@ -256,7 +334,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // V rows: coalesced 16-byte loads into a register ring (lane l takes chunks l, l + 64, ... of
   // a block), then stored swizzled into this wave's LDS tile and read transposed
-  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(uniform_ptr(a.v + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
+  const __amdgpu_buffer_rsrc_t vr =
+      tile_rsrc(uniform_ptr(static_cast<const bf16*>(a.v) + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
   u32x4 ring[3][PER];
   auto load = [&](int slot, int t) {
 #pragma unroll
@@ -267,43 +346,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   load(0, 0);
   load(1, 1);
 
-  // the row max over every chunk of the group that holds keys: lanes r and r + 32 take the even
-  // and odd chunks, eight loads in flight per round
-  const int nlive = (len + chunk - 1) / chunk;
-  float m = -INFINITY;
-  if (live) {
-    const float* pm = a.pmax + (size_t)bg * a.S * a.R + r;
-    for (int s2 = lane >> 5; s2 < nlive; s2 += 16) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = s2 + 2 * j < nlive ? pm[(size_t)(s2 + 2 * j) * a.R] : -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, x[j]);
-    }
-  }
-  m = fmaxf(m, __shfl_xor(m, 32));
-  if (s == 0 && lane < a.R) a.gmax[(size_t)bg * a.R + lane] = m;
+  const float m = decode_row_max(a, bg, s, (len + chunk - 1) / chunk, lane, live);
   // 1 + u = fma(s, -c, kd); a row with no allowed key (m = -inf) takes kd = +inf: phi = 0
   const float kd = m == -INFINITY ? INFINITY : fmaf(m, a.c, 1.0f);
 
-  // this chunk's scores as the first kernel stored them; padded rows (kd = +inf, so phi = 0
-  // whatever they read) and blocks past the chunk read zeros
-  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(a.scores + ((size_t)bg * a.nk32 + k0) * a.R), (short)0, uniform(nb * 32 * a.R * 4), kBufferWord3);
-  const int s_off = live ? (r * 2 + (lane >> 5)) * 64 : 0x40000000;
-  auto load_scores = [&](int t) {
-    f32x16 v;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, s_off + 16 * q4, uniform(t * 32 * a.R * 4), 0));
-      v[4 * q4] = x[0];
-      v[4 * q4 + 1] = x[1];
-      v[4 * q4 + 2] = x[2];
-      v[4 * q4 + 3] = x[3];
-    }
-    return v;
-  };
-  f32x16 sv = load_scores(0);
+  const ChunkScores sc(a, bg, k0, nb, lane, live);
+  f32x16 sv = sc.load(0);
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
@@ -311,7 +359,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   ring3(nb, [&](auto slot_c, int t) {
     constexpr int slot = decltype(slot_c)::value;
     load((slot + 2) % 3, t + 2);
-    const f32x16 sn = load_scores(t + 1);
+    const f32x16 sn = sc.load(t + 1);
     // this wave's LDS tile takes block t (the previous block's transposed reads have returned:
     // their results fed the products; a wave's LDS operations execute in order)
 #pragma unroll
@@ -348,15 +396,108 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           f32x4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
 }
 
+// fp32 P.V as O = P V (fp32 products): the A operand is P as phi leaves it (lane (r, h) holds
+// keys 16 ks + 8 (j / 4) + 4 h + j % 4 of row r in element 8 ks + j), and the B operand V is read
+// from HBM straight into that layout: lane (n, h) loads, for each of those 16 keys, the D / 32
+// consecutive values at columns (D / 32) n ...; product block db takes column (D / 32) n + db on
+// lane n.  One 16-byte (D = 128) or 8-byte (D = 64) load per key serves every column block, and
+// the 32 lanes of a half read a key's whole row.
+template <int D>
+__device__ __forceinline__ void decode_pv_f32(const DecodeArgs& a) {
+  constexpr int DB = D / 32;
+  static_assert(DB == 2 || DB == 4, "D = 64 or 128");
+  using vec = std::conditional_t<DB == 4, f32x4, f32x2>;
+
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const DecodeWork work = decode_work(a, blockIdx.x * kWaves + wave);
+  if (work.bg < 0) return;
+  const int chunk = uniform(work.chunk), bg = uniform(work.bg), s = uniform(work.s), len = uniform(work.len);
+  const int k0 = s * chunk;
+  const int nkeys = min(chunk, len - k0), nb = (nkeys + 31) / 32;
+  const bool live = (lane & 31) < a.R;
+
+  // keys past the chunk read zeros (and meet phi = 0)
+  const __amdgpu_buffer_rsrc_t vr =
+      tile_rsrc(uniform_ptr(static_cast<const float*>(a.v) + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
+  const int voff = (4 * (lane >> 5) * D + DB * (lane & 31)) * 4;
+  vec ring[2][16];
+  auto load = [&](int slot, int t) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = 16 * (e >> 3) + 8 * ((e & 7) >> 2) + (e & 3);
+      if constexpr (DB == 4)
+        ring[slot][e] = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, uniform(t * 32 * D * 4) + key * D * 4, kStreamOnce));
+      else
+        ring[slot][e] = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b64(vr, voff, uniform(t * 32 * D * 4) + key * D * 4, kStreamOnce));
+    }
+  };
+  load(0, 0);
+
+  const float m = decode_row_max(a, bg, s, (len + chunk - 1) / chunk, lane, live);
+  const float kd = m == -INFINITY ? INFINITY : fmaf(m, a.c, 1.0f);
+
+  const ChunkScores sc(a, bg, k0, nb, lane, live);
+  f32x16 sv = sc.load(0);
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float lsum = 0.0f;
+  ring2(nb, [&](auto slot_c, int t) {
+    constexpr int slot = decltype(slot_c)::value;
+    load(slot ^ 1, t + 1);
+    const f32x16 sn = sc.load(t + 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sv[i] = ra_phi(sv[i], a.c, kd);
+      lsum += sv[i];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const f32x8 pf = pack_frag_f32(sv, ks);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f32x8 vf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vf[j] = ring[slot][8 * ks + j][db];
+        mma(oacc[db], pf, vf);
+      }
+    }
+    sv = sn;
+  });
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const size_t row0 = ((size_t)bg * a.S + s) * a.R;
+  if (lane < a.R) a.psum[row0 + lane] = ltot;
+  // O block db: lane (n, h) holds rows acc_row(i, lane) of column (D / 32) n + db
+  float* dst = a.pacc + row0 * D + DB * (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = acc_row(i, lane);
+    vec x;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) x[db] = oacc[db][i];
+    if (r < a.R) *reinterpret_cast<vec*>(dst + (size_t)r * D) = x;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_pv_kernel(DecodeArgs a) {
+  decode_pv_bf16<D>(a);
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_pv_f32_kernel(DecodeArgs a) {
+  decode_pv_f32<D>(a);
+}
+
 // One workgroup per group: O = (sum of the chunks' partial P.V) / (sum of their phi sums), in
 // chunk order; stats (m, l) as ra_attn_fwd writes them.
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) {
+template <typename T, int D>
+__device__ __forceinline__ void decode_combine(const DecodeArgs& a) {
   const int bg = blockIdx.x;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int len = cache_len(a, b);
   const int chunk = decode_chunk(a);
   const int nlive = (len + chunk - 1) / chunk;
+  T* o = static_cast<T*>(a.o);
   for (int e = threadIdx.x; e < a.R * D; e += kThreads) {
     const int r = e / D, d = e % D;
     float acc = 0.0f, l = 0.0f;
@@ -369,12 +510,20 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) 
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const int h = g * a.rep + r / a.Nq, i = r % a.Nq;
     const size_t orow = (size_t)(b * a.Hq + h) * a.Nq + i;
-    a.o[orow * D + d] = (bf16)(acc * inv);
+    o[orow * D + d] = (T)(acc * inv);
     if (d == 0 && a.stats != nullptr) {
       a.stats[orow * 2] = nlive > 0 ? a.gmax[(size_t)bg * a.R + r] : -INFINITY;
       a.stats[orow * 2 + 1] = l;
     }
   }
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) {
+  decode_combine<bf16, D>(a);
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_combine_f32_kernel(DecodeArgs a) {
+  decode_combine<float, D>(a);
 }
 
 // The keys per wave come from the cache lengths at run time (decode_chunk): the total over about
@@ -413,14 +562,15 @@ DecodePlan decode_plan(int64_t B, int64_t Hkv, int64_t Nk, int64_t R, int64_t D)
   return p;
 }
 
-template <int D>
+template <typename T, int D>
 static hipError_t launch_decode_typed(const DecodeProblem& p, const DecodePlan& plan, void* ws,
                                       hipStream_t stream) {
+  constexpr bool kBf16 = sizeof(T) == 2;
   DecodeArgs a;
-  a.q = static_cast<const bf16*>(p.q);
-  a.k = static_cast<const bf16*>(p.k);
-  a.v = static_cast<const bf16*>(p.v);
-  a.o = static_cast<bf16*>(p.o);
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.o = p.o;
   a.stats = p.stats;
   a.seqlens = p.seqlens;
   char* w = static_cast<char*>(ws);
@@ -445,20 +595,27 @@ static hipError_t launch_decode_typed(const DecodeProblem& p, const DecodePlan& 
   a.c = p.scale / 16.0f;
   const int groups = p.B * p.Hkv;
   const dim3 grid((a.waves + kWaves - 1) / kWaves), block(kThreads);
-  hipLaunchKernelGGL((decode_scores_kernel<D>), grid, block, 0, stream, a);
+  if constexpr (kBf16) hipLaunchKernelGGL((decode_scores_kernel<D>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((decode_scores_f32_kernel<D>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_pv_kernel<D>), grid, block, 0, stream, a);
+  if constexpr (kBf16) hipLaunchKernelGGL((decode_pv_kernel<D>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((decode_pv_f32_kernel<D>), grid, block, 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(groups), block, 0, stream, a);
+  if constexpr (kBf16) hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(groups), block, 0, stream, a);
+  else hipLaunchKernelGGL((decode_combine_f32_kernel<D>), dim3(groups), block, 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_decode(const DecodeProblem& p, void* workspace, hipStream_t stream) {
   const DecodePlan plan = decode_plan(p.B, p.Hkv, p.Nk, (int64_t)(p.Hq / p.Hkv) * p.Nq, p.D);
-  if (p.D == 64) return launch_decode_typed<64>(p, plan, workspace, stream);
-  return launch_decode_typed<128>(p, plan, workspace, stream);
+  if (p.bf16) {
+    if (p.D == 64) return launch_decode_typed<bf16, 64>(p, plan, workspace, stream);
+    return launch_decode_typed<bf16, 128>(p, plan, workspace, stream);
+  }
+  if (p.D == 64) return launch_decode_typed<float, 64>(p, plan, workspace, stream);
+  return launch_decode_typed<float, 128>(p, plan, workspace, stream);
 }
 
 }  // namespace ra

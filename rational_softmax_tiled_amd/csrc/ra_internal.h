@@ -64,7 +64,7 @@ hipError_t launch_attn_bwd(const AttnProblem& p, const void* o, const void* d_o,
                            const float* stats, void* dq, void* dk, void* dv,
                            const BwdWorkspace& ws, int phases, hipStream_t stream);
 
-// Split-KV decode (bf16): R = (Hq / Hkv) * Nq <= 32 query rows per K/V head against caches of
+// Split-KV decode (bf16 or fp32): R = (Hq / Hkv) * Nq <= 32 query rows per K/V head against caches of
 // Nk rows, sample b using its first seqlens[b] (nullable: all).  causal: 0, 1 top-left,
 // 2 bottom-right per sample.
 struct DecodeProblem {
@@ -77,6 +77,7 @@ struct DecodeProblem {
   int B, Hq, Hkv, Nq, Nk, D;
   int causal;
   float scale;
+  bool bf16;
 };
 // The bounds of the keys per wave (the launch picks the size inside them from the actual cache
 // lengths), the most chunks a (batch, K/V head) group can take, the waves launched and the

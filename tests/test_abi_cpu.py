@@ -327,7 +327,7 @@ def dec(B=1, Hq=8, Hkv=2, Nq=1, Nk=100, D=128, causal=2, dtype=ra.RA_BF16, ws=P2
 
 
 def test_decode_validation(lib):
-    assert dec(dtype=ra.RA_F32) == DTYPE
+    assert dec(dtype=7) == DTYPE
     assert dec(Hq=8, Hkv=2, Nq=9) == SHAPE          # 4 * 9 = 36 query rows per K/V head > 32
     assert dec(Hq=64, Hkv=1, Nq=1) == SHAPE
     assert dec(Hq=3, Hkv=2) == GQA
@@ -346,7 +346,8 @@ def test_decode_validation(lib):
 def test_decode_workspace_size(lib):
     f = ra.ra_attn_decode_workspace_bytes
     assert f(16, 32, 8, 1, 16384, 128, ra.RA_BF16) > 16 * 8 * 16384 * 4 * 4   # scores of 4 rows
-    assert f(16, 32, 8, 1, 16384, 128, ra.RA_F32) == 0
+    assert f(16, 32, 8, 1, 16384, 128, ra.RA_F32) == f(16, 32, 8, 1, 16384, 128, ra.RA_BF16)
+    assert f(16, 32, 8, 1, 16384, 128, 7) == 0
     assert f(1, 8, 2, 9, 100, 128, ra.RA_BF16) == 0
     assert f(0, 8, 2, 1, 100, 128, ra.RA_BF16) == 0
     assert f(1, 8, 2, 1, 100, 64, ra.RA_BF16) < f(1, 8, 2, 1, 10000, 64, ra.RA_BF16)

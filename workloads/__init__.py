@@ -98,8 +98,13 @@ DECODE = AttnWorkload("bf16_decode_gqa_B16_Hq32_Hkv8_Nq1_Nk16384_D128", "bf16", 
                       1, 16384, 128, seed=7)
 
 
-def decode_workload() -> AttnWorkload:
-    return DECODE
+# The same decode step with fp32 caches and queries (same seed, so the same cache lengths).
+DECODE_F32 = dataclasses.replace(DECODE, name="fp32_decode_gqa_B16_Hq32_Hkv8_Nq1_Nk16384_D128",
+                                 dtype="f32")
+
+
+def decode_workload(dtype: str = "bf16") -> AttnWorkload:
+    return DECODE if dtype == "bf16" else DECODE_F32
 
 
 def decode_seqlens(w: AttnWorkload = DECODE) -> np.ndarray:
