@@ -479,6 +479,189 @@ __device__ __forceinline__ void decode_pv_f32(const DecodeArgs& a) {
   }
 }
 
+// ---- fp32 with at most 16 query rows per K/V head: 16x16x4 fp32 products, half the matrix cycles
+// of the 32-column form per key.  Product layout (16x16x4): lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; it holds D[4 (l / 16) + v][l % 16], v = 0..3.
+//
+// Scores S^T = K Q^T per 16-key half sb of a 32-key block: lane (i, g) = (l % 16, l / 16) feeds
+// key 16 sb + i, columns (D / 4) g + kc, kc = 0..D/4-1 (one product per kc), so each lane reads
+// a contiguous quarter of its key's row from LDS, and Q row l % 16 the same quarter from
+// registers.  Lane (r, g) then holds the scores of row r for keys 16 sb + 4 g + v: eight values
+// per block, stored in that order ([block][R rows][4 groups][8]).
+template <int D>
+__device__ __forceinline__ void decode_scores_f32_16(const DecodeArgs& a) {
+  constexpr int DQ = D / 4;                      // contraction columns per lane group
+  constexpr int CPR = D * 4 / 16, PER = 32 * CPR / kWave;
+  __shared__ __attribute__((aligned(16))) float k_lds[kWaves][32 * D];
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const DecodeWork work = decode_work(a, blockIdx.x * kWaves + wave);
+  if (work.bg < 0) return;   // whole wave: no barrier in this kernel
+  const int chunk = uniform(work.chunk), bg = uniform(work.bg), s = uniform(work.s), len = uniform(work.len);
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int k0 = s * chunk;
+  const int nkeys = min(chunk, len - k0), nb = (nkeys + 31) / 32;
+  const int r = lane & 15, grp = lane >> 4, rr = min(r, a.R - 1);
+  const int h = g * a.rep + rr / a.Nq;
+  const float* qrow = static_cast<const float*>(a.q) + ((size_t)(b * a.Hq + h) * a.Nq + rr % a.Nq) * D + DQ * grp;
+  float qf[DQ];
+#pragma unroll
+  for (int c = 0; c < DQ / 4; ++c) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(qrow + 4 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qf[4 * c + e] = x[e];
+  }
+  const int lim = key_limit(a, len, rr);
+
+  const __amdgpu_buffer_rsrc_t kr =
+      tile_rsrc(uniform_ptr(static_cast<const float*>(a.k) + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
+  u32x4 ring[2][PER];
+  auto load = [&](int slot, int t) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      ring[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(kr, (j * kWave + lane) * 16, uniform(t * 32 * D * 4), kStreamOnce);
+  };
+  float* ktile = k_lds[wave];
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(a.scores + ((size_t)bg * a.nk32 + k0) * a.R), (short)0, uniform(nb * 32 * a.R * 4), kBufferWord3);
+  const int s_off = r < a.R ? (r * 4 + grp) * 32 : 0x40000000;
+  float mx = -INFINITY;
+  load(0, 0);
+  ring2(nb, [&](auto slot_c, int t) {
+    constexpr int slot = decltype(slot_c)::value;
+    load(slot ^ 1, t + 1);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = j * kWave + lane, row = c / CPR, cc = c % CPR;
+      *reinterpret_cast<u32x4*>(ktile + swz_off<float, D>(row, cc)) = ring[slot][j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    f32x4 sacc[2] = {};
+#pragma unroll
+    for (int c = 0; c < DQ / 4; ++c)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(ktile + swz_off<float, D>(16 * sb + r, (DQ / 4) * grp + c));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e], qf[4 * c + e], sacc[sb], 0, 0, 0);
+      }
+    // key k0 + 32 t + 16 sb + 4 grp + v is kept iff it is <= lim (which is < len)
+    const int room = lim - (k0 + 32 * t + 4 * grp);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (16 * sb + v > room) sacc[sb][v] = -INFINITY;
+        mx = fmaxf(mx, sacc[sb][v]);
+      }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc[sb]), sr, s_off + 16 * sb,
+                                             uniform(t * 32 * a.R * 4), 0);
+  });
+  mx = fmaxf(mx, __shfl_xor(mx, 16));   // lanes r, r + 16, r + 32, r + 48 hold the same row
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (lane < a.R) a.pmax[((size_t)bg * a.S + s) * a.R + lane] = mx;
+}
+
+// P.V as O = P V with 16x16x4 fp32 products: in product kc (0..7) of a block, lane (r, g) feeds
+// P[r][key 16 (kc / 4) + 4 g + kc % 4], its own stored score kc after phi, and V[that key]
+// [column (D / 16) j + db] as B on lane (j, g), product block db taking column (D / 16) j + db:
+// one or two 16-byte loads per key serve every column block.
+template <int D>
+__device__ __forceinline__ void decode_pv_f32_16(const DecodeArgs& a) {
+  constexpr int DBL = D / 16;                 // column blocks, columns per lane
+  constexpr int NL = DBL / 4;                 // 16-byte loads per key
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const DecodeWork work = decode_work(a, blockIdx.x * kWaves + wave);
+  if (work.bg < 0) return;
+  const int chunk = uniform(work.chunk), bg = uniform(work.bg), s = uniform(work.s), len = uniform(work.len);
+  const int k0 = s * chunk;
+  const int nkeys = min(chunk, len - k0), nb = (nkeys + 31) / 32;
+  const int r = lane & 15, grp = lane >> 4;
+  const bool live = r < a.R;
+
+  const __amdgpu_buffer_rsrc_t vr =
+      tile_rsrc(uniform_ptr(static_cast<const float*>(a.v) + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
+  const int voff = (4 * grp * D + DBL * r) * 4;
+  f32x4 ring[2][8][NL];
+  auto load = [&](int slot, int t) {
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const int key = 16 * (kc >> 2) + (kc & 3);
+#pragma unroll
+      for (int n = 0; n < NL; ++n)
+        ring[slot][kc][n] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            vr, voff + 16 * n, uniform(t * 32 * D * 4) + key * D * 4, kStreamOnce));
+    }
+  };
+  load(0, 0);
+
+  // row max over the chunks: the four lanes of row r take chunks r mod 4 apart
+  float m = -INFINITY;
+  const int nlive = (len + chunk - 1) / chunk;
+  if (live) {
+    const float* pm = a.pmax + (size_t)bg * a.S * a.R + r;
+    for (int s2 = grp; s2 < nlive; s2 += 32) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = s2 + 4 * j < nlive ? pm[(size_t)(s2 + 4 * j) * a.R] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, x[j]);
+    }
+  }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (s == 0 && lane < a.R) a.gmax[(size_t)bg * a.R + lane] = m;
+  const float kd = m == -INFINITY ? INFINITY : fmaf(m, a.c, 1.0f);
+
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(a.scores + ((size_t)bg * a.nk32 + k0) * a.R), (short)0, uniform(nb * 32 * a.R * 4), kBufferWord3);
+  const int s_off = live ? (r * 4 + grp) * 32 : 0x40000000;
+  auto load_scores = [&](int t, f32x4 (&v)[2]) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      v[h2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, s_off + 16 * h2, uniform(t * 32 * a.R * 4), 0));
+  };
+  f32x4 sv[2], sn[2];
+  load_scores(0, sv);
+  f32x4 oacc[DBL];
+#pragma unroll
+  for (int db = 0; db < DBL; ++db) oacc[db] = f32x4{};
+  float lsum = 0.0f;
+  ring2(nb, [&](auto slot_c, int t) {
+    constexpr int slot = decltype(slot_c)::value;
+    load(slot ^ 1, t + 1);
+    load_scores(t + 1, sn);
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const float p = ra_phi(sv[kc >> 2][kc & 3], a.c, kd);
+      lsum += p;
+#pragma unroll
+      for (int db = 0; db < DBL; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, ring[slot][kc][db >> 2][db & 3], oacc[db], 0, 0, 0);
+    }
+    sv[0] = sn[0];
+    sv[1] = sn[1];
+  });
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  const size_t row0 = ((size_t)bg * a.S + s) * a.R;
+  if (lane < a.R) a.psum[row0 + lane] = lsum;
+  // O block db: lane (j, g) holds rows 4 g + v of column (D / 16) j + db
+  float* dst = a.pacc + row0 * D + DBL * r;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int row = 4 * grp + v;
+    if (row < a.R) {
+#pragma unroll
+      for (int n = 0; n < NL; ++n)
+        *reinterpret_cast<f32x4*>(dst + (size_t)row * D + 4 * n) =
+            f32x4{oacc[4 * n][v], oacc[4 * n + 1][v], oacc[4 * n + 2][v], oacc[4 * n + 3][v]};
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_pv_kernel(DecodeArgs a) {
   decode_pv_bf16<D>(a);
@@ -486,6 +669,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_pv_f32_kernel(DecodeArgs a) {
   decode_pv_f32<D>(a);
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_scores_f32x16_kernel(DecodeArgs a) {
+  decode_scores_f32_16<D>(a);
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_pv_f32x16_kernel(DecodeArgs a) {
+  decode_pv_f32_16<D>(a);
 }
 
 // One workgroup per group: O = (sum of the chunks' partial P.V) / (sum of their phi sums), in
@@ -595,11 +786,15 @@ static hipError_t launch_decode_typed(const DecodeProblem& p, const DecodePlan& 
   a.c = p.scale / 16.0f;
   const int groups = p.B * p.Hkv;
   const dim3 grid((a.waves + kWaves - 1) / kWaves), block(kThreads);
+  // fp32 with at most 16 rows per K/V head: the 16-column products
+  const bool narrow = !kBf16 && a.R <= 16;
   if constexpr (kBf16) hipLaunchKernelGGL((decode_scores_kernel<D>), grid, block, 0, stream, a);
+  else if (narrow) hipLaunchKernelGGL((decode_scores_f32x16_kernel<D>), grid, block, 0, stream, a);
   else hipLaunchKernelGGL((decode_scores_f32_kernel<D>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (kBf16) hipLaunchKernelGGL((decode_pv_kernel<D>), grid, block, 0, stream, a);
+  else if (narrow) hipLaunchKernelGGL((decode_pv_f32x16_kernel<D>), grid, block, 0, stream, a);
   else hipLaunchKernelGGL((decode_pv_f32_kernel<D>), grid, block, 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
