@@ -566,8 +566,9 @@ __device__ __forceinline__ void decode_scores_f32_16(const DecodeArgs& a) {
 
 // P.V as O = P V with 16x16x4 fp32 products: in product kc (0..7) of a block, lane (r, g) feeds
 // P[r][key 16 (kc / 4) + 4 g + kc % 4], its own stored score kc after phi, and V[that key]
-// [column (D / 16) j + db] as B on lane (j, g), product block db taking column (D / 16) j + db:
-// one or two 16-byte loads per key serve every column block.
+// [column 4 j + 64 (db / 4) + db % 4] as B on lane (j, g) for product block db: the 16 lanes of
+// a group read 256 contiguous bytes of a key's row per load, one or two loads per key serving
+// every column block.
 template <int D>
 __device__ __forceinline__ void decode_pv_f32_16(const DecodeArgs& a) {
   constexpr int DBL = D / 16;                 // column blocks, columns per lane
@@ -583,7 +584,7 @@ __device__ __forceinline__ void decode_pv_f32_16(const DecodeArgs& a) {
 
   const __amdgpu_buffer_rsrc_t vr =
       tile_rsrc(uniform_ptr(static_cast<const float*>(a.v) + ((size_t)bg * a.Nk + k0) * D), nkeys, D);
-  const int voff = (4 * grp * D + DBL * r) * 4;
+  const int voff = (4 * grp * D + 4 * r) * 4;
   f32x4 ring[2][8][NL];
   auto load = [&](int slot, int t) {
 #pragma unroll
@@ -592,7 +593,7 @@ __device__ __forceinline__ void decode_pv_f32_16(const DecodeArgs& a) {
 #pragma unroll
       for (int n = 0; n < NL; ++n)
         ring[slot][kc][n] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-            vr, voff + 16 * n, uniform(t * 32 * D * 4) + key * D * 4, kStreamOnce));
+            vr, voff + 256 * n, uniform(t * 32 * D * 4) + key * D * 4, kStreamOnce));
     }
   };
   load(0, 0);
@@ -648,15 +649,15 @@ __device__ __forceinline__ void decode_pv_f32_16(const DecodeArgs& a) {
   lsum += __shfl_xor(lsum, 32);
   const size_t row0 = ((size_t)bg * a.S + s) * a.R;
   if (lane < a.R) a.psum[row0 + lane] = lsum;
-  // O block db: lane (j, g) holds rows 4 g + v of column (D / 16) j + db
-  float* dst = a.pacc + row0 * D + DBL * r;
+  // O block db: lane (j, g) holds rows 4 g + v of column 4 j + 64 (db / 4) + db % 4
+  float* dst = a.pacc + row0 * D + 4 * r;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int row = 4 * grp + v;
     if (row < a.R) {
 #pragma unroll
       for (int n = 0; n < NL; ++n)
-        *reinterpret_cast<f32x4*>(dst + (size_t)row * D + 4 * n) =
+        *reinterpret_cast<f32x4*>(dst + (size_t)row * D + 64 * n) =
             f32x4{oacc[4 * n][v], oacc[4 * n + 1][v], oacc[4 * n + 2][v], oacc[4 * n + 3][v]};
     }
   }
