@@ -71,15 +71,18 @@ TRAFFIC = {
     "attn_bwd_dkdv_bf16_kernel": ("8a182001426cf273ebaa4452bc1995406367434e662d0b11abdf22ab5aa951db",
                                   272491.0, 274299.0),
 }
-# VALU instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU) of the forward on a workload,
-# for its VALU-roofline fraction; valid for the recorded kernel source only.
+# VALU and MFMA instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA, one run)
+# of the forward on a workload, for its VALU-roofline fraction; valid for the recorded kernel
+# source only.  SQ_INSTS_VALU counts the MFMA instructions too (they issue through the VALU: the
+# forward's loops hold about 283 vector and 48 matrix instructions per wave and 64-key tile at
+# D = 128, against 345 counted), so the vector lane operations are 64 x (VALU - MFMA).
 VALU_INSTS = {
-    # workload: (sha256 of the forward's sources, SQ_INSTS_VALU per dispatch)
-    "fp32_noncausal_B1_H2_N128_D64": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 11560),
-    "bf16_causal_B2_H12_N128_D64": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 101160),
-    "bf16_causal_B8_H16_N2048_D64_sigma2": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 45893632),
-    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 189317120),
-    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 364273664),
+    # workload: (sha256 of the forward's sources, SQ_INSTS_VALU, SQ_INSTS_MFMA per dispatch)
+    "fp32_noncausal_B1_H2_N128_D64": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 11560, 3072),
+    "bf16_causal_B2_H12_N128_D64": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 101160, 3456),
+    "bf16_causal_B8_H16_N2048_D64_sigma2": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 45893632, 3244032),
+    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 189317120, 25559040),
+    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 364273664, 50724864),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],
@@ -440,7 +443,7 @@ def main():
             "skip": skip, "inputs_sha256": wl.storage_sha256(inp, wc.dtype)}
         rec = VALU_INSTS.get(name)
         if rec is not None and rec[0] == source_digest(KERNEL_SOURCES["attn_fwd_kernel"]):
-            lane_ops = rec[1] * 64
+            lane_ops = (rec[1] - rec[2]) * 64
             configs[name]["valu"] = {
                 "lane_ops_per_launch": lane_ops, "peak_lane_ops_per_s": PEAK_VALU_LANE_OPS,
                 "frac": round(lane_ops / (t["median_ms"] * 1e-3) / PEAK_VALU_LANE_OPS, 4)}

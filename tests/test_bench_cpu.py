@@ -43,3 +43,10 @@ def test_traffic_is_reported_only_for_the_recorded_sources():
         else:
             assert got is None
     assert b.traffic_bytes("no_such_kernel") is None
+
+
+def test_valu_counts_leave_out_the_matrix_instructions():
+    # SQ_INSTS_VALU counts MFMA issues too; every record carries both counts, MFMA below VALU
+    b = _bench()
+    for name, (digest, valu, mfma) in b.VALU_INSTS.items():
+        assert 0 < mfma < valu, name
