@@ -418,8 +418,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     }
     bool mfree = true;   // MASKED: the mask leaves both blocks of the tile as they are
     // the block's mask, from the words read one step ahead or loaded now
+    // A block whose words hold no zero byte in any lane keeps every entry: only the causal and
+    // tail limits apply (at an edge), without the per-entry mask arithmetic.
     auto p1_mask = [&](f32x16& sc, int sb, int key0, bool& id) {
       if (MASKED && mpack) {
+        unsigned zero = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zero |= (mw[sb][j] - 0x01010101u) & ~mw[sb][j] & 0x80808080u;
+        if (!__any(zero != 0u)) {
+          id = true;
+          if (at_edge(key0)) mask_block<false>(sc, key0, qrow, lane, a.Nk, a.coff, ms);
+          return;
+        }
         unsigned mv[16];
         MaskSlice<T>::expand_words(mw[sb], mv);
         apply_mask_block<MASKED>(sc, mv, key0, qrow, lane, a.Nk, a.coff, ms, &id);
