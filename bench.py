@@ -64,11 +64,11 @@ GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083",
+    "attn_fwd_kernel": ("18d7a5960df5dcb7f2baa0cdae3199d581c09c824315ab64ecab8f0de8ba3bb2",
                         286919.0, 135180.3),
-    "attn_bwd_dq_bf16_kernel": ("8a182001426cf273ebaa4452bc1995406367434e662d0b11abdf22ab5aa951db",
+    "attn_bwd_dq_bf16_kernel": ("dc39674d0800a29268e9b7de520558738aebbdfe7132191ede1d7a6e9497b377",
                                 441266.4, 143463.7),
-    "attn_bwd_dkdv_bf16_kernel": ("8a182001426cf273ebaa4452bc1995406367434e662d0b11abdf22ab5aa951db",
+    "attn_bwd_dkdv_bf16_kernel": ("dc39674d0800a29268e9b7de520558738aebbdfe7132191ede1d7a6e9497b377",
                                   272491.0, 274299.0),
 }
 # VALU and MFMA instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA, one run)
@@ -78,11 +78,11 @@ TRAFFIC = {
 # D = 128, against 345 counted), so the vector lane operations are 64 x (VALU - MFMA).
 VALU_INSTS = {
     # workload: (sha256 of the forward's sources, SQ_INSTS_VALU, SQ_INSTS_MFMA per dispatch)
-    "fp32_noncausal_B1_H2_N128_D64": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 11560, 3072),
-    "bf16_causal_B2_H12_N128_D64": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 101160, 3456),
-    "bf16_causal_B8_H16_N2048_D64_sigma2": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 45893632, 3244032),
-    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 189317120, 25559040),
-    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("47d40999739ec9cd3bf08b420b73b860755e2c50959f150474766bf079c42083", 364273664, 50724864),
+    "fp32_noncausal_B1_H2_N128_D64": ("18d7a5960df5dcb7f2baa0cdae3199d581c09c824315ab64ecab8f0de8ba3bb2", 11560, 3072),
+    "bf16_causal_B2_H12_N128_D64": ("18d7a5960df5dcb7f2baa0cdae3199d581c09c824315ab64ecab8f0de8ba3bb2", 101160, 3456),
+    "bf16_causal_B8_H16_N2048_D64_sigma2": ("18d7a5960df5dcb7f2baa0cdae3199d581c09c824315ab64ecab8f0de8ba3bb2", 45893632, 3244032),
+    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("18d7a5960df5dcb7f2baa0cdae3199d581c09c824315ab64ecab8f0de8ba3bb2", 189317120, 25559040),
+    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("18d7a5960df5dcb7f2baa0cdae3199d581c09c824315ab64ecab8f0de8ba3bb2", 364273664, 50724864),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],

@@ -717,16 +717,20 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
           // before its products and tested after them (a wait before them would also wait for
           // the next tile's copies, issued earlier in the step), and a block the mask empties for
           // every row of the wave stops there (its entries add nothing to dQ, R or the argmax)
-          unsigned mw[4];
+          u32x4 mwp;
           if constexpr (MASKED)
-            if (mpack) ms.load_words(mw, qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
+            if (mpack) mwp = ms.load_word_pairs(qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
           f32x16 s = {}, dp = {};
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) mma(s, k_row(buf, sb, kc), qf[kc]);
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) mma(dp, v_row(buf, sb, kc), df[kc]);
+          unsigned mw[4];
           if constexpr (MASKED)
-            if (mpack && !__any((mw[0] | mw[1] | mw[2] | mw[3]) != 0u)) continue;
+            if (mpack) {
+              MaskSlice<bf16>::words_of_pairs(mwp, mw);
+              if (!__any((mw[0] | mw[1] | mw[2] | mw[3]) != 0u)) continue;
+            }
           const int key0 = kt * BN + sb * 32;
           if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
             if constexpr (MASKED) {

@@ -714,10 +714,27 @@ struct MaskSlice {
       load(v, voff, sk);
     }
   }
-  // the packed boolean layout's four runs as words (byte e of word j: element 4 j + e)
+  // the packed boolean layout's four runs as words (byte e of word j: element 4 j + e).  Lanes l
+  // and l + 32 hold the same row, at keys 8 j + 4 h + e of the block (h = l / 32): each loads
+  // its half of the row's 32 bytes (keys 16 h to 16 h + 15) in one 16-byte load
+  // (load_word_pairs, voff the offset of the lane's element 0, keys contiguous), and the pair
+  // trade the two words each needs from the other (words_of_pairs, by the whole wave, when the
+  // words are needed: the trade waits for the load).  Four 4-byte loads per lane, each touching a
+  // cache line per row, measured 0.13 ms of a masked forward that took 0.65 ms.
+  __device__ __forceinline__ u32x4 load_word_pairs(int voff) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff + 12 * ((threadIdx.x >> 5) & 1), 0, 0);
+  }
+  static __device__ __forceinline__ void words_of_pairs(const u32x4& x, unsigned (&w)[4]) {
+    const int h = (threadIdx.x >> 5) & 1;
+    const unsigned lo = __shfl_xor(h ? x[0] : x[1], 32);
+    const unsigned hi = __shfl_xor(h ? x[2] : x[3], 32);
+    w[0] = h ? lo : x[0];
+    w[1] = h ? hi : x[2];
+    w[2] = h ? x[1] : lo;
+    w[3] = h ? x[3] : hi;
+  }
   __device__ __forceinline__ void load_words(unsigned (&w)[4], int voff) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, uniform(8 * j), 0);
+    words_of_pairs(load_word_pairs(voff), w);
   }
   static __device__ __forceinline__ void expand_words(const unsigned (&w)[4], unsigned (&v)[16]) {
 #pragma unroll

@@ -332,10 +332,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   // tiles it computes.  (A wait for words loaded in the same step would also wait for the step's
   // K copy, issued before them, which counts in the same in-order counter.)
   const bool mpack = MASKED && ms.packed && ms.kind == kMaskBool;
-  unsigned mw_next[SB][4];
-  auto load_tile_words = [&](int kt, unsigned (&w)[SB][4]) {
+  u32x4 mw_next[SB];   // the words in pairs as loaded, traded when the tile's step starts
+  auto load_tile_words = [&](int kt, u32x4 (&w)[SB]) {
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) ms.load_words(w[sb], qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
+    for (int sb = 0; sb < SB; ++sb) w[sb] = ms.load_word_pairs(qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
   };
   // bf16 with V buffers: pass 1 streams K through four LDS stages (the V buffers are idle until
   // pass 2), three tiles ahead of the math.  Only without a mask: the mask loads are vector
@@ -392,12 +392,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       if (mpack && kt < nt_w) {
         unsigned any = 0;
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb)
+        for (int sb = 0; sb < SB; ++sb) {
+          MaskSlice<T>::words_of_pairs(mw_next[sb], mw[sb]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            mw[sb][j] = mw_next[sb][j];
-            any |= mw[sb][j];
-          }
+          for (int j = 0; j < 4; ++j) any |= mw[sb][j];
+        }
         alive = __any(any != 0u);
       }
     }
