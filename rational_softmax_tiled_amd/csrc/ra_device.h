@@ -628,7 +628,8 @@ struct MaskArgs {
   int kind;
   float inv_scale;       // 1 / scale
   // keys contiguous (sk = 1), every row and slice start a multiple of 4 elements, Nk a multiple of
-  // 4 and the mask 4-byte aligned: a boolean mask's runs of 4 keys load as one dword (never past Nk)
+  // 4 and the mask 4-byte aligned: a row's 32-key block loads in 16-byte pieces, half per lane of a
+  // pair (boolean masks, and additive ones of 2-byte elements; see MaskSlice)
   int packed;
 };
 
@@ -642,7 +643,7 @@ inline MaskArgs mask_args(const AttnProblem& p) {
   m.bytes = p.mask_bytes;
   m.kind = p.mask_kind;
   m.inv_scale = 1.0f / p.scale;
-  m.packed = p.mask_kind == kMaskBool && p.msk == 1 && p.msq % 4 == 0 && p.msb % 4 == 0 && p.msh % 4 == 0 &&
+  m.packed = p.mask_kind != kMaskNone && p.msk == 1 && p.msq % 4 == 0 && p.msb % 4 == 0 && p.msh % 4 == 0 &&
              p.Nk % 4 == 0 && reinterpret_cast<unsigned long long>(p.mask) % 4 == 0;
   return m;
 }
@@ -702,14 +703,34 @@ struct MaskSlice {
     }
   }
 
-  // load() along keys (step = sk): a boolean mask with a packed layout reads each run of four keys
-  // as one 4-byte load instead of four byte loads (one row per lane, so the per-element loads
-  // touched a cache line per lane each)
+  // load() along keys (step = sk) for a lane holding one query row.  In the packed layout a
+  // boolean mask's block comes as words (below); an additive mask of 2-byte elements likewise: its
+  // four runs are 8 bytes each, lanes l and l + 32 load their halves of the row's 64 bytes (keys
+  // 16 h to 16 h + 15) in two 16-byte loads and trade the 8-byte runs the other needs.  Per
+  // element, each load touched a cache line per lane.  Called by the whole wave.
   __device__ __forceinline__ void load_keys(unsigned (&v)[16], int voff) const {
     if (packed && kind == kMaskBool) {
       unsigned w[4];
       load_words(w, voff);
       expand_words(w, v);
+    } else if (sizeof(T) == 2 && packed && kind == kMaskAdd) {
+      const int h = (threadIdx.x >> 5) & 1;
+      // voff is element 0's byte offset (key0 + 4 h); the lane's half starts at key0 + 16 h
+      const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 24 * h, 0, 0);        // runs of keys +0, +4
+      const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 24 * h + 16, 0, 0);   // keys +8, +12
+      // h = 0 keeps its runs at +0 and +8 and sends +4, +12; h = 1 the other way round
+      const unsigned r0 = __shfl_xor(h ? x0[0] : x0[2], 32), r1 = __shfl_xor(h ? x0[1] : x0[3], 32);
+      const unsigned r2 = __shfl_xor(h ? x1[0] : x1[2], 32), r3 = __shfl_xor(h ? x1[1] : x1[3], 32);
+      // run j (keys 8 j + 4 h .. + 3) as two dwords of two elements each
+      const unsigned d[8] = {h ? r0 : x0[0], h ? r1 : x0[1], h ? r2 : x1[0], h ? r3 : x1[1],
+                             h ? x0[2] : r0, h ? x0[3] : r1, h ? x1[2] : r2, h ? x1[3] : r3};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned dw = d[2 * j + (e >> 1)];
+          v[4 * j + e] = (e & 1) ? (dw & 0xffff0000u) : (dw << 16);
+        }
     } else {
       load(v, voff, sk);
     }

@@ -202,6 +202,8 @@ MASK_CASES = [
     ("transposed", 1, 2, 2, 61, 61, 128, "top_left", "f32"),
     ("head_bias", 2, 4, 2, 90, 90, 128, "top_left", "bf16"),
     ("head_bias", 1, 4, 1, 64, 129, 64, "none", "f32"),
+    # bf16 bias rows of 4-element multiples: the 16-byte loads of a key block, ragged last block
+    ("head_bias", 1, 4, 2, 100, 132, 128, "bottom_right", "bf16"),
     ("alibi", 1, 8, 2, 160, 160, 128, "top_left", "bf16"),
     ("alibi", 1, 4, 4, 50, 120, 64, "bottom_right", "f32"),
     ("key_bias", 3, 2, 1, 75, 140, 128, "none", "bf16"),
