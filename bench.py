@@ -64,11 +64,11 @@ GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("9c4ffc1c6e46b5d4d00aa1ff9f3e47bb9df5b0a11171d7d81fe36f254eb7b87a",
+    "attn_fwd_kernel": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47",
                         286919.0, 135180.3),
-    "attn_bwd_dq_bf16_kernel": ("9ee20e1b0070579366cc14c237b38eaa4a7aa2b83a67d5a2ddff0d2dd3e402e0",
+    "attn_bwd_dq_bf16_kernel": ("15f19b0844a4a396ed2ded32ce669c03ed64ec46256978bfc87d56d12f3d381d",
                                 441266.4, 143463.7),
-    "attn_bwd_dkdv_bf16_kernel": ("9ee20e1b0070579366cc14c237b38eaa4a7aa2b83a67d5a2ddff0d2dd3e402e0",
+    "attn_bwd_dkdv_bf16_kernel": ("15f19b0844a4a396ed2ded32ce669c03ed64ec46256978bfc87d56d12f3d381d",
                                   272491.0, 274299.0),
 }
 # VALU and MFMA instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA, one run)
@@ -78,11 +78,11 @@ TRAFFIC = {
 # D = 128, against 345 counted), so the vector lane operations are 64 x (VALU - MFMA).
 VALU_INSTS = {
     # workload: (sha256 of the forward's sources, SQ_INSTS_VALU, SQ_INSTS_MFMA per dispatch)
-    "fp32_noncausal_B1_H2_N128_D64": ("9c4ffc1c6e46b5d4d00aa1ff9f3e47bb9df5b0a11171d7d81fe36f254eb7b87a", 11560, 3072),
-    "bf16_causal_B2_H12_N128_D64": ("9c4ffc1c6e46b5d4d00aa1ff9f3e47bb9df5b0a11171d7d81fe36f254eb7b87a", 101160, 3456),
-    "bf16_causal_B8_H16_N2048_D64_sigma2": ("9c4ffc1c6e46b5d4d00aa1ff9f3e47bb9df5b0a11171d7d81fe36f254eb7b87a", 45893632, 3244032),
-    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("9c4ffc1c6e46b5d4d00aa1ff9f3e47bb9df5b0a11171d7d81fe36f254eb7b87a", 189317120, 25559040),
-    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("9c4ffc1c6e46b5d4d00aa1ff9f3e47bb9df5b0a11171d7d81fe36f254eb7b87a", 364273664, 50724864),
+    "fp32_noncausal_B1_H2_N128_D64": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 11560, 3072),
+    "bf16_causal_B2_H12_N128_D64": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 101160, 3456),
+    "bf16_causal_B8_H16_N2048_D64_sigma2": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 45893632, 3244032),
+    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 189317120, 25559040),
+    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 364273664, 50724864),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],

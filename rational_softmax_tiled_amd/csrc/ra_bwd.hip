@@ -568,10 +568,13 @@ __device__ __forceinline__ float ra_grad_only(float s, float c16, float kd, floa
 
 // KEYPAD (with MASKED false): a boolean key padding mask.  Wave 0 copies each tile's 64 mask bytes
 // with its K and V tiles; the 64 keep bits drop whole padded blocks and mask the partial ones.
-template <int D, bool CAUSAL, bool MASKED, bool KEYPAD = false, bool ROPE = false>
+// MADD (with MASKED): the mask is additive in the packed layout, read as 16-byte runs; a variant
+// of its own, so the boolean kernel keeps its registers.
+template <int D, bool CAUSAL, bool MASKED, bool KEYPAD = false, bool ROPE = false, bool MADD = false>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int BN = 64, KC = D / 16, SB = BN / 32, DB = D / 32;
   static_assert(!(KEYPAD && MASKED), "key padding runs the unmasked paths");
+  static_assert(!MADD || MASKED, "packed additive masks: masked kernels");
   // the K and V tiles, two buffers each, in one array (K0, K1, V0, V1): every buffer then lies at
   // a constant offset below 64 KiB from the first, an immediate of the LDS read instructions
   __shared__ __attribute__((aligned(16))) bf16 kv_lds[4][BN * D];
@@ -645,7 +648,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const float kd = m == -INFINITY ? INFINITY : fmaf(m, a.c16, 1.0f);
   const float mprobe = argmax_probe(m);
   const MaskSlice<bf16> ms(a.mask, b, h);
-  const bool mpack = MASKED && ms.packed && ms.kind == kMaskBool;
+  const bool madd = MADD && ms.packed;
+  const bool mpack = MASKED && ms.packed && (MADD || ms.kind == kMaskBool);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -716,26 +720,40 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
           // MASKED with a boolean mask in the packed layout: the block's mask words are read
           // before its products and tested after them (a wait before them would also wait for
           // the next tile's copies, issued earlier in the step), and a block the mask empties for
-          // every row of the wave stops there (its entries add nothing to dQ, R or the argmax)
-          u32x4 mwp;
-          if constexpr (MASKED)
+          // every row of the wave stops there (its entries add nothing to dQ, R or the argmax).
+          // An additive mask in that layout the same way, with its elements (all -inf: empty).
+          u32x4 mwp, mwp2;
+          if constexpr (MADD) {
+            if (madd) ms.load_run_pairs(qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk, mwp, mwp2);
+          } else if constexpr (MASKED) {
             if (mpack) mwp = ms.load_word_pairs(qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
+          }
           f32x16 s = {}, dp = {};
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) mma(s, k_row(buf, sb, kc), qf[kc]);
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) mma(dp, v_row(buf, sb, kc), df[kc]);
-          unsigned mw[4];
-          if constexpr (MASKED)
+          unsigned mw[4], md[8];
+          if constexpr (MADD) {
+            if (madd) {
+              MaskSlice<bf16>::runs_of_pairs(mwp, mwp2, md);
+              unsigned kept = 0;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) kept |= MaskSlice<bf16>::kept_halves(md[j]);
+              if (!__any(kept != 0u)) continue;
+            }
+          } else if constexpr (MASKED) {
             if (mpack) {
               MaskSlice<bf16>::words_of_pairs(mwp, mw);
               if (!__any((mw[0] | mw[1] | mw[2] | mw[3]) != 0u)) continue;
             }
+          }
           const int key0 = kt * BN + sb * 32;
           if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
             if constexpr (MASKED) {
               unsigned mv[16];
-              if (mpack) MaskSlice<bf16>::expand_words(mw, mv);
+              if (MADD && madd) MaskSlice<bf16>::expand_runs(md, mv);
+              else if (!MADD && mpack) MaskSlice<bf16>::expand_words(mw, mv);
               else ms.load_keys(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
 #pragma unroll
               for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
@@ -1344,6 +1362,7 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
   const dim3 kblock(kBf16 ? kDkdvThreads : kThreads);
   // the masked kernels are the causal ones (coff = Nk when there is no causality)
   const bool masked = p.mask_kind != kMaskNone;
+  const bool madd = kBf16 && p.mask_kind == kMaskAdd && a.mask.packed;   // the packed additive dQ
   // a boolean key padding mask ([B, Nk] broadcast over heads and rows, keys contiguous, every
   // sample's row 4-byte aligned and a whole number of dwords long for the dword copies, whose
   // resource ends at Nk bytes): the unmasked kernels with keep bits
@@ -1354,6 +1373,7 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
     if (phases & kBwdDq) {
       if constexpr (kBf16) {
         if (keypad) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, true, true>), qgrid, block, 0, stream, a);
+        else if (madd) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, true, false, true, true>), qgrid, block, 0, stream, a);
         else if (masked) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, true, false, true>), qgrid, block, 0, stream, a);
         else if (p.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, false, true>), qgrid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, false, false, true>), qgrid, block, 0, stream, a);
@@ -1383,8 +1403,12 @@ static hipError_t launch_bwd_typed(const AttnProblem& p, const void* o, const vo
     if (keypad) {
       if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false, true>), qgrid, block, 0, stream, a);
     } else if (masked) {
-      if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, true>), qgrid, block, 0, stream, a);
-      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, true>), qgrid, block, 0, stream, a);
+      if constexpr (kBf16) {
+        if (madd) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, true, false, false, true>), qgrid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, true>), qgrid, block, 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, true>), qgrid, block, 0, stream, a);
+      }
     } else if (p.causal) {
       if constexpr (kBf16) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, false>), qgrid, block, 0, stream, a);
       else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, true, false>), qgrid, block, 0, stream, a);

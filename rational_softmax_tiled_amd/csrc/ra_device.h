@@ -704,33 +704,23 @@ struct MaskSlice {
   }
 
   // load() along keys (step = sk) for a lane holding one query row.  In the packed layout a
-  // boolean mask's block comes as words (below); an additive mask of 2-byte elements likewise: its
-  // four runs are 8 bytes each, lanes l and l + 32 load their halves of the row's 64 bytes (keys
-  // 16 h to 16 h + 15) in two 16-byte loads and trade the 8-byte runs the other needs.  Per
-  // element, each load touched a cache line per lane.  Called by the whole wave.
+  // boolean mask's block comes as words (below); with RUNS (kernels for additive masks of 2-byte
+  // elements in that layout), an additive one likewise: its four runs are 8 bytes each, lanes l
+  // and l + 32 load their halves of the row's 64 bytes (keys 16 h to 16 h + 15) in two 16-byte
+  // loads and trade the 8-byte runs the other needs.  Per element, each load touched a cache line
+  // per lane.  Called by the whole wave.
+  template <bool RUNS = false>
   __device__ __forceinline__ void load_keys(unsigned (&v)[16], int voff) const {
     if (packed && kind == kMaskBool) {
       unsigned w[4];
       load_words(w, voff);
       expand_words(w, v);
-    } else if (sizeof(T) == 2 && packed && kind == kMaskAdd) {
-      const int h = (threadIdx.x >> 5) & 1;
-      // voff is element 0's byte offset (key0 + 4 h); the lane's half starts at key0 + 16 h
-      const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 24 * h, 0, 0);        // runs of keys +0, +4
-      const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 24 * h + 16, 0, 0);   // keys +8, +12
-      // h = 0 keeps its runs at +0 and +8 and sends +4, +12; h = 1 the other way round
-      const unsigned r0 = __shfl_xor(h ? x0[0] : x0[2], 32), r1 = __shfl_xor(h ? x0[1] : x0[3], 32);
-      const unsigned r2 = __shfl_xor(h ? x1[0] : x1[2], 32), r3 = __shfl_xor(h ? x1[1] : x1[3], 32);
-      // run j (keys 8 j + 4 h .. + 3) as two dwords of two elements each
-      const unsigned d[8] = {h ? r0 : x0[0], h ? r1 : x0[1], h ? r2 : x1[0], h ? r3 : x1[1],
-                             h ? x0[2] : r0, h ? x0[3] : r1, h ? x1[2] : r2, h ? x1[3] : r3};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const unsigned dw = d[2 * j + (e >> 1)];
-          v[4 * j + e] = (e & 1) ? (dw & 0xffff0000u) : (dw << 16);
-        }
+    } else if (RUNS && sizeof(T) == 2 && packed && kind == kMaskAdd) {
+      u32x4 x0, x1;
+      load_run_pairs(voff, x0, x1);
+      unsigned d[8];
+      runs_of_pairs(x0, x1, d);
+      expand_runs(d, v);
     } else {
       load(v, voff, sk);
     }
@@ -762,6 +752,58 @@ struct MaskSlice {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[4 * j + e] = (w[j] >> (8 * e)) & 0xffu;
+  }
+
+  // The packed additive layout of 2-byte elements, the same way: lanes l and l + 32 load their
+  // halves of the row's 64 bytes (keys 16 h to 16 h + 15, voff the offset of the lane's element
+  // 0) in two 16-byte loads (load_run_pairs), and the trade hands each the two 8-byte runs it
+  // needs from the other (runs_of_pairs, by the whole wave; run j of the lane, keys 8 j + 4 h to
+  // 8 j + 4 h + 3, in d[2 j] and d[2 j + 1], two elements per dword, the lower key in the low half).
+  __device__ __forceinline__ void load_run_pairs(int voff, u32x4& x0, u32x4& x1) const {
+    const int o = voff + 24 * ((threadIdx.x >> 5) & 1);
+    x0 = __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);        // keys +0 to +7 of the half
+    x1 = __builtin_amdgcn_raw_buffer_load_b128(r, o + 16, 0, 0);   // keys +8 to +15
+  }
+  static __device__ __forceinline__ void runs_of_pairs(const u32x4& x0, const u32x4& x1, unsigned (&d)[8]) {
+    const int h = (threadIdx.x >> 5) & 1;
+    // h = 0 keeps the runs at +0 and +8 of its half and sends +4 and +12; h = 1 the reverse
+    const unsigned r0 = __shfl_xor(h ? x0[0] : x0[2], 32), r1 = __shfl_xor(h ? x0[1] : x0[3], 32);
+    const unsigned r2 = __shfl_xor(h ? x1[0] : x1[2], 32), r3 = __shfl_xor(h ? x1[1] : x1[3], 32);
+    d[0] = h ? r0 : x0[0];
+    d[1] = h ? r1 : x0[1];
+    d[2] = h ? r2 : x1[0];
+    d[3] = h ? r3 : x1[1];
+    d[4] = h ? x0[2] : r0;
+    d[5] = h ? x0[3] : r1;
+    d[6] = h ? x1[2] : r2;
+    d[7] = h ? x1[3] : r3;
+  }
+  // the elements as load() gives them (bf16 bits in the high half of an fp32)
+  static __device__ __forceinline__ void expand_runs(const unsigned (&d)[8], unsigned (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (i & 1) ? (d[i >> 1] & 0xffff0000u) : (d[i >> 1] << 16);
+  }
+  // Bit 15 and bit 31 of a dword of two bf16 elements: set where the element is not -inf (a kept
+  // key), and where it is neither -inf nor +-0 (a bias that changes the score).  A 16-bit lane x
+  // is nonzero iff bit 15 of ((x & 0x7fff) + 0x7fff) | x is set; the sum never carries out of it.
+  static __device__ __forceinline__ unsigned kept_halves(unsigned dw) {
+    const unsigned x = dw ^ 0xff80ff80u;
+    return (((x & 0x7fff7fffu) + 0x7fff7fffu) | x) & 0x80008000u;
+  }
+  static __device__ __forceinline__ unsigned biased_halves(unsigned dw) {
+    return ((dw & 0x7fff7fffu) + 0x7fff7fffu) & kept_halves(dw);
+  }
+  // A 0 / -inf block as the boolean words above (byte e of word j: element 4 j + e, 0x80 where
+  // kept, 0 where -inf): the bytes holding bits 15 and 31 of the two dwords' flags, by a byte
+  // permute.  ORs into `biased` where an element is neither, and then the words do not describe
+  // the block.
+  static __device__ __forceinline__ void add_words_of_runs(const unsigned (&d)[8], unsigned (&w)[4],
+                                                           unsigned& biased) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = __builtin_amdgcn_perm(kept_halves(d[2 * j + 1]), kept_halves(d[2 * j]), 0x07050301u);
+      biased |= biased_halves(d[2 * j]) | biased_halves(d[2 * j + 1]);
+    }
   }
 
   // load() along query rows, where a zero stride (a mask broadcast over rows, as key padding is)

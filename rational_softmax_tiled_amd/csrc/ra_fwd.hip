@@ -74,10 +74,10 @@ __device__ __forceinline__ bool mask_identity(int kind, unsigned v) {
 
 // The explicit-mask values of a 32x32 S^T block (keys on the accumulator rows, query row qrow on
 // the lane), one per entry of the lane.
-template <typename T>
+template <bool RUNS, typename T>
 __device__ __forceinline__ void load_mask_block(const MaskSlice<T>& ms, unsigned (&mv)[16], int key0, int qrow,
                                                 int lane) {
-  ms.load_keys(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
+  ms.template load_keys<RUNS>(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
 }
 
 // Mask entries of a 32x32 S^T block: the explicit mask values mv first (MASKED), then key >= Nk or
@@ -100,11 +100,12 @@ __device__ __forceinline__ void apply_mask_block(f32x16& s, const unsigned (&mv)
   keep_rows(s, -kNoBound, min(Nk - lb, qrow + coff + 1 - lb));
 }
 
-template <bool MASKED, typename T>
+// RUNS: an additive mask in the packed layout may come (see MaskSlice::load_keys)
+template <bool MASKED, bool RUNS = false, typename T>
 __device__ __forceinline__ void mask_block(f32x16& s, int key0, int qrow, int lane, int Nk, int coff,
                                            const MaskSlice<T>& ms, bool* ident = nullptr) {
   unsigned mv[16] = {};
-  if constexpr (MASKED) load_mask_block(ms, mv, key0, qrow, lane);
+  if constexpr (MASKED) load_mask_block<RUNS>(ms, mv, key0, qrow, lane);
   apply_mask_block<MASKED>(s, mv, key0, qrow, lane, Nk, coff, ms, ident);
 }
 
@@ -159,8 +160,10 @@ __device__ __forceinline__ void score_pair(const bf16* k_tile, const bf16x8* qf,
 // ROPE: q holds the rows before the rotary embedding; each wave rotates its Q fragments once, on
 // load (the pair of channel j, j + D/2 lies in fragments kc, kc + KC/2 of the same lane), and may
 // store them (q_rot) for a backward pass.
+// MADD (with MASKED, bf16): the mask is additive in the packed layout (see MaskSlice), read ahead
+// the way a boolean one is; a variant of its own, so the boolean kernels keep their registers.
 template <typename T, int D, int BN, bool COUNT, bool WRITE_O, bool MASKED, bool KEYPAD = false,
-          bool ROPE = false>
+          bool ROPE = false, bool MADD = false>
 // bf16: two waves per SIMD (at most 256 VGPRs), the second wave fills the first one's waits.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void attn_fwd_kernel(FwdArgs a) {
   using frag_t = typename Ty<T>::frag;
@@ -179,6 +182,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   __shared__ float tmax_lds[kWaves][kMaxTiles];
   __shared__ float kmin_lds[kWaves];
   static_assert(!KEYPAD || (sizeof(T) == 2 && WRITE_O && !MASKED && BN == kWave), "key padding path");
+  static_assert(!MADD || (sizeof(T) == 2 && MASKED), "packed additive masks: bf16 masked kernels");
   static_assert(!ROPE || (WRITE_O && !COUNT), "rotary path");
   __shared__ __attribute__((aligned(16))) unsigned mstage_lds[KEYPAD ? 4 : 1][KEYPAD ? kWave : 1];
   __shared__ unsigned long long keep_lds[KEYPAD ? kMaxTiles : 1];
@@ -330,12 +334,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   // ahead (they land with the step's copies, so deciding on them waits for nothing), drops a tile
   // the mask empties for every row of the wave before its products, and applies the words to the
   // tiles it computes.  (A wait for words loaded in the same step would also wait for the step's
-  // K copy, issued before them, which counts in the same in-order counter.)
-  const bool mpack = MASKED && ms.packed && ms.kind == kMaskBool;
-  u32x4 mw_next[SB];   // the words in pairs as loaded, traded when the tile's step starts
+  // K copy, issued before them, which counts in the same in-order counter.)  A bf16 additive mask
+  // in that layout takes the same path: its elements, read one step ahead, become boolean words
+  // (-inf drops the key, anything else keeps it), and a block holding a bias other than 0 or -inf
+  // reads its values again where they are applied.
+  const bool mpack = MASKED && ms.packed && (MADD || ms.kind == kMaskBool);
+  // the slice the words are applied as: boolean (an additive mask's words stand for 0 / -inf)
+  MaskSlice<T> mword = ms;
+  if constexpr (MADD) mword.kind = kMaskBool;
+  u32x4 mw_next[SB];    // the words in pairs as loaded (additive: keys +0 to +7 of the half),
+  u32x4 mw_next2[SB];   // traded when the tile's step starts (additive: keys +8 to +15)
   auto load_tile_words = [&](int kt, u32x4 (&w)[SB]) {
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) w[sb] = ms.load_word_pairs(qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
+    for (int sb = 0; sb < SB; ++sb) {
+      if constexpr (MADD) ms.load_run_pairs(qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk, w[sb], mw_next2[sb]);
+      else w[sb] = ms.load_word_pairs(qrow * ms.sq + (kt * BN + sb * 32 + 4 * (lane >> 5)) * ms.sk);
+    }
   };
   // bf16 with V buffers: pass 1 streams K through four LDS stages (the V buffers are idle until
   // pass 2), three tiles ahead of the math.  Only without a mask: the mask loads are vector
@@ -388,12 +402,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     // MASKED, packed: tile kt's words (read in the previous step) decide before anything is issued
     bool alive = true;
     unsigned mw[SB][4];
+    unsigned mbias = 0;   // MADD: bit sb set when block sb holds a bias other than 0 or -inf (every lane)
     if constexpr (MASKED) {
       if (mpack && kt < nt_w) {
         unsigned any = 0;
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
-          MaskSlice<T>::words_of_pairs(mw_next[sb], mw[sb]);
+          if constexpr (MADD) {
+            unsigned d[8], biased = 0;
+            MaskSlice<T>::runs_of_pairs(mw_next[sb], mw_next2[sb], d);
+            MaskSlice<T>::add_words_of_runs(d, mw[sb], biased);
+            if (__any(biased != 0u)) mbias |= 1u << sb;
+          } else {
+            MaskSlice<T>::words_of_pairs(mw_next[sb], mw[sb]);
+          }
 #pragma unroll
           for (int j = 0; j < 4; ++j) any |= mw[sb][j];
         }
@@ -420,7 +442,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     // A block whose words hold no zero byte in any lane keeps every entry: only the causal and
     // tail limits apply (at an edge), without the per-entry mask arithmetic.
     auto p1_mask = [&](f32x16& sc, int sb, int key0, bool& id) {
-      if (MASKED && mpack) {
+      if (MASKED && mpack && !(MADD && ((mbias >> sb) & 1u))) {
         unsigned zero = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) zero |= (mw[sb][j] - 0x01010101u) & ~mw[sb][j] & 0x80808080u;
@@ -431,9 +453,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         }
         unsigned mv[16];
         MaskSlice<T>::expand_words(mw[sb], mv);
-        apply_mask_block<MASKED>(sc, mv, key0, qrow, lane, a.Nk, a.coff, ms, &id);
+        apply_mask_block<MASKED>(sc, mv, key0, qrow, lane, a.Nk, a.coff, mword, &id);
       } else {
-        mask_block<MASKED>(sc, key0, qrow, lane, a.Nk, a.coff, ms, &id);
+        mask_block<MASKED, MADD>(sc, key0, qrow, lane, a.Nk, a.coff, ms, &id);
       }
     };
     if (kt < nt_w && keep != 0 && alive) {
@@ -678,7 +700,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         const int key0 = cur * BN + sb * 32;
-        if (MASKED && !mfree) mask_block<MASKED>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
+        if (MASKED && !mfree) mask_block<MASKED, MADD>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
         else if (at_edge(key0)) mask_block<false>(s[sb], key0, qrow, lane, a.Nk, a.coff, ms);
         if constexpr (KEYPAD) {
           const unsigned long long keep = keep_lds[cur];
@@ -781,6 +803,7 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
   a.log2_theta = p.rope ? log2(p.rope_theta) : 0.0;
   a.q_rot = p.q_rot;
   dim3 grid(a.total_wg), block(kThreads);
+  const bool madd = sizeof(T) == 2 && p.mask_kind == kMaskAdd && a.mask.packed;
   // a boolean key padding mask ([B, Nk] broadcast over heads and rows, keys contiguous, every
   // sample's row 4-byte aligned and a whole number of dwords long for the dword copies, whose
   // resource ends at Nk bytes) with the output: the four-stage path
@@ -793,6 +816,11 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
       if constexpr (sizeof(T) == 2 && BN == kWave)
         hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, true, true>), grid, block, 0, stream, a);
     } else if (p.mask_kind != kMaskNone) {
+      if constexpr (sizeof(T) == 2)
+        if (madd) {
+          hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true, false, true, true>), grid, block, 0, stream, a);
+          return hipGetLastError();
+        }
       hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true, false, true>), grid, block, 0, stream, a);
     } else {
       hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, false, true>), grid, block, 0, stream, a);
@@ -801,6 +829,12 @@ static hipError_t launch_typed(const AttnProblem& p, void* o, float* stats,
     if constexpr (sizeof(T) == 2 && BN == kWave)
       hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, false, true>), grid, block, 0, stream, a);
   } else if (p.mask_kind != kMaskNone) {
+    if constexpr (sizeof(T) == 2)
+      if (madd) {
+        if (o == nullptr) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, true, false, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true, false, false, true>), grid, block, 0, stream, a);
+        return hipGetLastError();
+      }
     if (o == nullptr) hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, false, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, false, true, true>), grid, block, 0, stream, a);
   } else if (o == nullptr) {   // statistics only (m, l), for a backward without saved stats

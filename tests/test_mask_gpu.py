@@ -61,7 +61,7 @@ def make_mask(layout, B, Hq, Nq, Nk, dtype, seed):
         keep_t = rng.random((Nk, Nq)) < 0.7
         t = torch.from_numpy(keep_t).cuda()
         return keep_t.T, t, ra.RA_MASK_BOOL, (0, 0, 1, Nq)
-    if layout in ("documents", "documents_add"):  # packed documents, [B, N, N] over all heads
+    if layout in ("documents", "documents_add", "documents_mixed"):  # packed documents, [B, N, N]
         assert Nq == Nk
         ids = wl.document_ids(B, Nq, seed, 40, 200)
         keep = ids[:, :, None] == ids[:, None, :]
@@ -69,6 +69,12 @@ def make_mask(layout, B, Hq, Nq, Nk, dtype, seed):
             t = torch.from_numpy(keep).cuda()
             return keep[:, None], t, ra.RA_MASK_BOOL, (Nq * Nk, 0, Nk, 1)
         bias = np.where(keep, 0.0, -np.inf)[:, None].astype(np.float32)   # the same as 0 / -inf
+        if layout == "documents_mixed":
+            # -0.0 on some kept entries (still no change), a real bias on a few (their blocks take
+            # the values, the others stay 0 / -inf)
+            u = rng.random(bias.shape)
+            bias[(u < 0.05) & (bias == 0)] = -0.0
+            bias[(u > 0.998) & (bias == 0)] = rng.normal(0, 1, size=int(((u > 0.998) & (bias == 0)).sum()))
     elif layout == "head_bias":                   # additive [1, Hq, Nq, Nk] with -inf entries
         bias = rng.normal(0, 2, size=(1, Hq, Nq, Nk)).astype(np.float32)
         bias[rng.random(bias.shape) < 0.1] = -np.inf
@@ -214,6 +220,8 @@ MASK_CASES = [
     ("documents", 1, 2, 2, 200, 200, 128, "top_left", "f32"),
     ("documents_add", 2, 2, 1, 300, 300, 128, "top_left", "bf16"),
     ("documents_add", 1, 2, 2, 170, 170, 64, "none", "f32"),
+    ("documents_mixed", 1, 4, 2, 300, 300, 128, "top_left", "bf16"),
+    ("documents_mixed", 2, 2, 2, 256, 256, 64, "none", "bf16"),
     ("key_bias", 2, 2, 2, 40, 40, 64, "top_left", "f32"),
 ]
 
