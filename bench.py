@@ -560,14 +560,22 @@ def main():
     dm_t = timed(doc.stream, lambda: doc.fwd_masked(dmask), min_s)
     dmb_t = timed(doc.stream, lambda: (doc.fwd_masked(dmask), doc.bwd_masked(dmask)), min_s)
     dc_t = timed(doc.stream, lambda: doc.fwd(), min_s)
+    # the same documents as an additive bf16 mask, 0 where kept and -inf where not
+    dadd = torch.zeros(dkeep.shape, dtype=torch.bfloat16, device="cuda")
+    dadd[~dmask[0]] = float("-inf")
+    amask = (dadd, ra.RA_MASK_ADD, dmask[2])
+    da_t = timed(doc.stream, lambda: doc.fwd_masked(amask), min_s)
+    dab_t = timed(doc.stream, lambda: (doc.fwd_masked(amask), doc.bwd_masked(amask)), min_s)
     log(f"packed documents: masked forward {dm_t['median_ms']:.3f} ms, fwd+bwd {dmb_t['median_ms']:.3f} ms; "
+        f"as a 0/-inf additive mask {da_t['median_ms']:.3f} / {dab_t['median_ms']:.3f} ms; "
         f"causal forward without the mask {dc_t['median_ms']:.3f} ms")
     doc_out = {"workload": wdoc.name, "mask": "[B, N, N] bool (same document), causal top-left",
                "kept_causal_entries": int(doc_entries),
                "kept_fraction_of_causal": round(doc_entries / (wdoc.B * wdoc.Hq * wdoc.Nq * (wdoc.Nq + 1) / 2), 4),
                "fwd": dm_t, "fwd_bwd": dmb_t, "unmasked_causal_fwd": dc_t,
+               "additive_0_neginf_bf16": {"fwd": da_t, "fwd_bwd": dab_t},
                "fwd_tflops_on_kept_entries": round(4 * wdoc.D * doc_entries / (dm_t["median_ms"] * 1e-3) / 1e12, 2)}
-    del doc, dkeep, dmask
+    del doc, dkeep, dmask, dadd, amask
     torch.cuda.empty_cache()
 
     # ---- split-KV decode: one query row per head against caches of per-sample lengths
