@@ -64,11 +64,11 @@ GQA = "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     # kernel: (sha256 of its KERNEL_SOURCES concatenated, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attn_fwd_kernel": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47",
+    "attn_fwd_kernel": ("3177d22ee600e987d71867dc1a06396f1cee3dc3bd89d4d64d0e183a1935de6d",
                         286919.0, 135180.3),
-    "attn_bwd_dq_bf16_kernel": ("15f19b0844a4a396ed2ded32ce669c03ed64ec46256978bfc87d56d12f3d381d",
+    "attn_bwd_dq_bf16_kernel": ("9c9406fdab48c334200ef155bcff02395064a245e4dddcb0a21ac4dc604f330b",
                                 441266.4, 143463.7),
-    "attn_bwd_dkdv_bf16_kernel": ("15f19b0844a4a396ed2ded32ce669c03ed64ec46256978bfc87d56d12f3d381d",
+    "attn_bwd_dkdv_bf16_kernel": ("9c9406fdab48c334200ef155bcff02395064a245e4dddcb0a21ac4dc604f330b",
                                   272491.0, 274299.0),
 }
 # VALU and MFMA instructions per dispatch (rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA, one run)
@@ -78,11 +78,11 @@ TRAFFIC = {
 # D = 128, against 345 counted), so the vector lane operations are 64 x (VALU - MFMA).
 VALU_INSTS = {
     # workload: (sha256 of the forward's sources, SQ_INSTS_VALU, SQ_INSTS_MFMA per dispatch)
-    "fp32_noncausal_B1_H2_N128_D64": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 11560, 3072),
-    "bf16_causal_B2_H12_N128_D64": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 101160, 3456),
-    "bf16_causal_B8_H16_N2048_D64_sigma2": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 45893632, 3244032),
-    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 189317120, 25559040),
-    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("6b65e50c31efb333d217dc036ad2a7cf8f04104347008d1bcff59462b708cd47", 364273664, 50724864),
+    "fp32_noncausal_B1_H2_N128_D64": ("3177d22ee600e987d71867dc1a06396f1cee3dc3bd89d4d64d0e183a1935de6d", 11560, 3072),
+    "bf16_causal_B2_H12_N128_D64": ("3177d22ee600e987d71867dc1a06396f1cee3dc3bd89d4d64d0e183a1935de6d", 101160, 3456),
+    "bf16_causal_B8_H16_N2048_D64_sigma2": ("3177d22ee600e987d71867dc1a06396f1cee3dc3bd89d4d64d0e183a1935de6d", 45893632, 3244032),
+    "bf16_causal_gqa_B4_Hq32_Hkv8_N4096_D128_rope": ("3177d22ee600e987d71867dc1a06396f1cee3dc3bd89d4d64d0e183a1935de6d", 189317120, 25559040),
+    "bf16_causal_B4_H16_N8192_D128_fwd_bwd": ("3177d22ee600e987d71867dc1a06396f1cee3dc3bd89d4d64d0e183a1935de6d", 364273664, 50724864),
 }
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["ra_fwd.hip", "ra_device.h"],

@@ -734,13 +734,14 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) mma(dp, v_row(buf, sb, kc), df[kc]);
           unsigned mw[4], md[8];
+          bool mzero = false;   // MADD: every element of the block is +-0 (the same in every lane)
           if constexpr (MADD) {
             if (madd) {
-              MaskSlice<bf16>::runs_of_pairs(mwp, mwp2, md);
-              unsigned kept = 0;
-#pragma unroll
-              for (int j = 0; j < 8; ++j) kept |= MaskSlice<bf16>::kept_halves(md[j]);
-              if (!__any(kept != 0u)) continue;
+              unsigned nz, ni;
+              MaskSlice<bf16>::run_flags(mwp, mwp2, nz, ni);
+              if (!__any(ni != 0u)) continue;   // only -inf
+              mzero = !__any(nz != 0u);
+              if (!mzero) MaskSlice<bf16>::runs_of_pairs(mwp, mwp2, md);
             }
           } else if constexpr (MASKED) {
             if (mpack) {
@@ -751,12 +752,14 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
           const int key0 = kt * BN + sb * 32;
           if (MASKED || (CAUSAL && key0 + 31 > q0 + a.coff) || key0 + 32 > a.Nk) {
             if constexpr (MASKED) {
-              unsigned mv[16];
-              if (MADD && madd) MaskSlice<bf16>::expand_runs(md, mv);
-              else if (!MADD && mpack) MaskSlice<bf16>::expand_words(mw, mv);
-              else ms.load_keys(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
+              if (!mzero) {
+                unsigned mv[16];
+                if (MADD && madd) MaskSlice<bf16>::expand_runs(md, mv);
+                else if (!MADD && mpack) MaskSlice<bf16>::expand_words(mw, mv);
+                else ms.load_keys(mv, qrow * ms.sq + (key0 + 4 * (lane >> 5)) * ms.sk);
 #pragma unroll
-              for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
+                for (int i = 0; i < 16; ++i) s[i] = ms.apply(s[i], mv[i]);
+              }
             }
             const int lb = key0 + 4 * (lane >> 5);
             keep_rows(s, -kNoBound, min(a.Nk - lb, CAUSAL ? qrow + a.coff + 1 - lb : kNoBound));

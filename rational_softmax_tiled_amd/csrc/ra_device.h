@@ -793,6 +793,18 @@ struct MaskSlice {
   static __device__ __forceinline__ unsigned biased_halves(unsigned dw) {
     return ((dw & 0x7fff7fffu) + 0x7fff7fffu) & kept_halves(dw);
   }
+  // Flags of a lane's runs as loaded (before the trade): `nz` nonzero when some element is not
+  // +-0, `ni` nonzero when some element is not -inf.  Taken over the wave, they find the blocks
+  // that are all zero or all -inf without the trade.
+  static __device__ __forceinline__ void run_flags(const u32x4& x0, const u32x4& x1, unsigned& nz, unsigned& ni) {
+    nz = 0;
+    ni = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nz |= (x0[i] | x1[i]) & 0x7fff7fffu;
+      ni |= (x0[i] ^ 0xff80ff80u) | (x1[i] ^ 0xff80ff80u);
+    }
+  }
   // A 0 / -inf block as the boolean words above (byte e of word j: element 4 j + e, 0x80 where
   // kept, 0 where -inf): the bytes holding bits 15 and 31 of the two dwords' flags, by a byte
   // permute.  ORs into `biased` where an element is neither, and then the words do not describe

@@ -409,10 +409,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
           if constexpr (MADD) {
-            unsigned d[8], biased = 0;
-            MaskSlice<T>::runs_of_pairs(mw_next[sb], mw_next2[sb], d);
-            MaskSlice<T>::add_words_of_runs(d, mw[sb], biased);
-            if (__any(biased != 0u)) mbias |= 1u << sb;
+            // a block of only +-0 keeps everything, one of only -inf nothing: no trade for either
+            unsigned nz, ni;
+            MaskSlice<T>::run_flags(mw_next[sb], mw_next2[sb], nz, ni);
+            const bool all_zero = !__any(nz != 0u), all_ninf = !__any(ni != 0u);
+            if (all_zero || all_ninf) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) mw[sb][j] = all_zero ? 0x80808080u : 0u;
+            } else {
+              unsigned d[8], biased = 0;
+              MaskSlice<T>::runs_of_pairs(mw_next[sb], mw_next2[sb], d);
+              MaskSlice<T>::add_words_of_runs(d, mw[sb], biased);
+              if (__any(biased != 0u)) mbias |= 1u << sb;
+            }
           } else {
             MaskSlice<T>::words_of_pairs(mw_next[sb], mw[sb]);
           }
