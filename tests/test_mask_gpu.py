@@ -259,10 +259,14 @@ def test_key_padding_lengths(gpu_lib, causal):
         assert np.isfinite(res[n]).all(), n
 
 
-def test_masked_backward_without_stats_is_identical(gpu_lib):
-    B, Hq, Hkv, Nq, Nk, D = 2, 4, 2, 100, 170, 128
+@pytest.mark.parametrize("layout,Nq,Nk", [("head_bias", 100, 170),       # Nk % 4 != 0: per element
+                                          ("documents_mixed", 160, 160)])  # packed additive runs
+def test_masked_backward_without_stats_is_identical(gpu_lib, layout, Nq, Nk):
+    """The backward's own pass 1 (no saved statistics: the forward kernel without an output)
+    gives the same gradients as the saved statistics."""
+    B, Hq, Hkv, D = 2, 4, 2, 128
     inp = rand_inputs(B, Hq, Hkv, Nq, Nk, D, "bf16", seed=11)
-    mask_np, t, kind, strides = make_mask("head_bias", B, Hq, Nq, Nk, "bf16", seed=12)
+    mask_np, t, kind, strides = make_mask(layout, B, Hq, Nq, Nk, "bf16", seed=12)
     scale = float(np.float32(1 / np.sqrt(D)))
     a = run(gpu_lib, inp, "bottom_right", scale, "bf16", mask=(t, kind, strides))
     b = run(gpu_lib, inp, "bottom_right", scale, "bf16", mask=(t, kind, strides), use_stats=False)
