@@ -265,6 +265,7 @@ MASK_CASES = [
     (2, 4, 2, 130, 130, 64, 1, "keypad", "bf16"),           # Nk % 4 != 0: the general masked kernels
     (1, 4, 2, 100, 140, 128, 0, "head_bias", "bf16"),       # additive, per query head, -inf entries
     (1, 4, 2, 256, 256, 128, 1, "documents_mixed", "bf16"),  # additive 0 / -inf blocks read ahead as words
+    (2, 2, 1, 200, 200, 64, 2, "documents_mixed", "bf16"),    # the same at D = 64, ragged tail
     (1, 2, 1, 77, 90, 64, 2, "full_bool", "f32"),
 ]
 
